@@ -1,0 +1,178 @@
+"""CPU oracle for the MoL delta path: a ctypes binding over `oracle.c`.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the package smoke check and by the
+benchmark's CPU-baseline leg, never by the GPU path. See `oracle.c` for what each
+function computes and which passage of the pages it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16 = 0, 1
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with the host C compiler (-O2, no -march=native, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-fopenmp",
+                        "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.oracle_num_threads.argtypes, L.oracle_num_threads.restype = [], ctypes.c_int
+        L.oracle_set_num_threads.argtypes, L.oracle_set_num_threads.restype = [ctypes.c_int], None
+        L.oracle_bf16_from_double.argtypes = [ctypes.c_double]
+        L.oracle_bf16_from_double.restype = ctypes.c_uint16
+        L.oracle_bf16_round_array.argtypes, L.oracle_bf16_round_array.restype = [P, P, I64], None
+        L.oracle_virtual_topk.argtypes = [P, P, I64, I32, I32, I32, P]
+        L.oracle_virtual_topk.restype = ctypes.c_int
+        L.oracle_align_block_size.argtypes = [P, P, I64, I32, I32, I32, I32, P, I64, P, I64, P]
+        L.oracle_align_block_size.restype = ctypes.c_int
+        L.oracle_lora_shrink.argtypes = [ctypes.c_int, P, I64, I32, P, I32, I32, P, P, I32,
+                                         I64, I32, P, P]
+        L.oracle_lora_shrink.restype = ctypes.c_int
+        L.oracle_lora_expand.argtypes = [ctypes.c_int, P, I32, I32, P, I32, P, I32, P, P, I32,
+                                         I64, I32, P, P, I64]
+        L.oracle_lora_expand.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dt(a) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"oracle takes float32 or bf16 bits (uint16), not {a.dtype}")
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    lib().oracle_set_num_threads(int(n))
+
+
+def bf16_from_double(v) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    lib().oracle_bf16_round_array(_ptr(v), _ptr(out), v.size)
+    return out
+
+
+def virtual_topk(topk_ids, lora_ids, E: int, S: int) -> np.ndarray:
+    t = np.ascontiguousarray(topk_ids, dtype=np.int32)
+    l = np.ascontiguousarray(lora_ids, dtype=np.int32)
+    M, k = t.shape
+    out = np.empty_like(t)
+    rc = lib().oracle_virtual_topk(_ptr(t), _ptr(l), M, k, E, S, _ptr(out))
+    if rc:
+        raise ValueError(f"oracle_virtual_topk: {rc}")
+    return out
+
+
+def align_block_size(ids, lora_ids, E: int, S: int, block_m: int):
+    """Returns (sorted_ids[:npp], expert_ids[:npp/BM], npp)."""
+    t = np.ascontiguousarray(ids, dtype=np.int32)
+    M, k = t.shape
+    numel = M * k
+    V = E * S
+    nz = min(numel, V + 1)
+    cap_blocks = max(1, (numel + nz * (block_m - 1) + block_m - 1) // block_m)
+    sorted_ids = np.empty(cap_blocks * block_m, dtype=np.int32)
+    expert_ids = np.empty(cap_blocks, dtype=np.int32)
+    npp = np.zeros(1, dtype=np.int32)
+    l = None if lora_ids is None else np.ascontiguousarray(lora_ids, dtype=np.int32)
+    rc = lib().oracle_align_block_size(_ptr(t), _ptr(l), M, k, E, S, block_m,
+                                       _ptr(sorted_ids), sorted_ids.size,
+                                       _ptr(expert_ids), expert_ids.size, _ptr(npp))
+    if rc:
+        raise ValueError(f"oracle_align_block_size: {rc}")
+    n = int(npp[0])
+    return sorted_ids[:n].copy(), expert_ids[: n // block_m].copy(), n
+
+
+def lora_shrink(xin, row_div: int, A, sorted_ids, expert_ids, npp: int, numel: int,
+                block_m: int, pair_mask=None, s=None) -> np.ndarray:
+    """s [numel, R] float64; rows of pairs that get no delta stay as given (NaN)."""
+    xin = np.ascontiguousarray(xin)
+    A = np.ascontiguousarray(A)
+    V, R, K = A.shape
+    if s is None:
+        s = np.full((numel, R), np.nan, dtype=np.float64)
+    srt = np.ascontiguousarray(sorted_ids, dtype=np.int32)
+    eid = np.ascontiguousarray(expert_ids, dtype=np.int32)
+    mask = None if pair_mask is None else np.ascontiguousarray(pair_mask, dtype=np.uint8)
+    rc = lib().oracle_lora_shrink(_dt(A), _ptr(xin), xin.shape[1], row_div, _ptr(A), R, K,
+                                  _ptr(srt), _ptr(eid), npp, numel, block_m, _ptr(mask),
+                                  _ptr(s))
+    if rc:
+        raise ValueError(f"oracle_lora_shrink: {rc}")
+    return s
+
+
+def lora_expand(s, slices: int, B, scale, E: int, sorted_ids, expert_ids, npp: int,
+                numel: int, block_m: int, out, pair_mask=None) -> np.ndarray:
+    """Adds the delta into `out` [numel, N] (float32 or bf16 bits) in place."""
+    s = np.ascontiguousarray(s, dtype=np.float64)
+    B = np.ascontiguousarray(B)
+    V, N, r = B.shape
+    R = s.shape[1]
+    assert out.flags.c_contiguous and out.dtype == B.dtype
+    sc = np.ascontiguousarray(scale, dtype=np.float32)
+    srt = np.ascontiguousarray(sorted_ids, dtype=np.int32)
+    eid = np.ascontiguousarray(expert_ids, dtype=np.int32)
+    mask = None if pair_mask is None else np.ascontiguousarray(pair_mask, dtype=np.uint8)
+    rc = lib().oracle_lora_expand(_dt(B), _ptr(s), R, slices, _ptr(B), N, _ptr(sc), E,
+                                  _ptr(srt), _ptr(eid), npp, numel, block_m, _ptr(mask),
+                                  _ptr(out), out.shape[1])
+    if rc:
+        raise ValueError(f"oracle_lora_expand: {rc}")
+    return out
+
+
+def run_layer(inp, outs=None, pair_mask=None):
+    """The whole path on one layer's inputs: align with the remap inline, then each
+    stage's shrink and expand. `outs` (one array per stage, [numel, N]) start at zero
+    unless given. Returns (routing, s per stage, out per stage)."""
+    cfg = inp.cfg
+    numel = cfg.numel
+    srt, eid, npp = align_block_size(inp.topk_ids, inp.lora_ids, cfg.E, cfg.S, cfg.block_m)
+    ss, oo = [], []
+    for si, (st, sin) in enumerate(zip(cfg.stages, inp.stages)):
+        s = lora_shrink(sin.xin, sin.row_div, sin.A, srt, eid, npp, numel, cfg.block_m,
+                        pair_mask=pair_mask)
+        if outs is None:
+            out = np.zeros((numel, st.N), dtype=sin.B.dtype)
+        else:
+            out = outs[si]
+        lora_expand(s, st.slices, sin.B, inp.scale, cfg.E, srt, eid, npp, numel,
+                    cfg.block_m, out, pair_mask=pair_mask)
+        ss.append(s)
+        oo.append(out)
+    return (srt, eid, npp), ss, oo

@@ -1,0 +1,87 @@
+"""The pins are sensitive: plausible mistakes planted in copies of the oracle (compiled
+here, on the CPU) must each make at least one pin fail."""
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import test_oracle_pins as P
+
+# (name, original text, mutated text) applied to oracle.c
+MUTANTS = [
+    ("remap_multiplier", "return t + l * E;", "return t + l * S;"),
+    ("remap_sentinel_dropped", "if (t < 0) return t;", "if (t < 0) return -1;"),
+    ("remap_slot_range", "l < 0 || l >= S", "l < 0 || l > S"),
+    ("align_unstable", "for (int64_t p = 0; p < numel; ++p) {\n            int32_t b = key[p];",
+     "for (int64_t p = numel - 1; p >= 0; --p) {\n            int32_t b = key[p];"),
+    ("align_overpad", "total += (count[b] + BM - 1) / BM * BM;",
+     "total += (count[b] / BM + 1) * BM;"),
+    ("align_sentinel_tag", "(b == V) ? -1 : (int32_t)b", "(int32_t)b"),
+    ("align_pad_value", "sorted_ids[i] = (int32_t)numel;", "sorted_ids[i] = -1;"),
+    ("shrink_drops_last_k", "for (int32_t k = 0; k < K; ++k)", "for (int32_t k = 0; k < K - 1; ++k)"),
+    ("shrink_transposed_A", "load_elem(A, arow + k, dtype)",
+     "load_elem(A, (int64_t)e * R * K + (int64_t)k * R + i, dtype)"),
+    ("shrink_row_of_pair", "(p / row_div) * ld_x", "(p % row_div) * ld_x"),
+    ("expand_slice", "const int32_t g = n / width;", "const int32_t g = 0;"),
+    ("expand_scale_slot", "(double)scale[e / E]", "(double)scale[0]"),
+    ("expand_truncates", "nearbyint(ldexp(a, -q))", "trunc(ldexp(a, -q))"),
+    ("expand_sign", "acc += load_elem(B, brow + jj, dtype) * s[",
+     "acc -= load_elem(B, brow + jj, dtype) * s["),
+]
+
+
+def _battery(lib):
+    """Run every oracle pin against `lib`; return the names of the pins that failed."""
+    failed = []
+    cases = [
+        ("bf16_literals", lambda: [P.test_bf16_literal_cases(lib, v, b) for v, b in [
+            (1.0 + 2.0 ** -8, 0x3F80), (1.0 + 3 * 2.0 ** -8, 0x3F82), (2.0 ** -134, 0)]]),
+        ("bf16_torch", lambda: P.test_bf16_matches_torch_on_float32_values(lib)),
+        ("remap_cases", lambda: P.test_remap_worked_cases(lib)),
+        ("remap_invariants", lambda: P.test_remap_invariants(lib)),
+        ("align_bruteforce", lambda: P.test_align_matches_stable_argsort_bruteforce(lib)),
+        ("align_inline", lambda: P.test_align_inline_remap_equals_remap_then_align(lib)),
+        ("align_sentinel", lambda: P.test_align_sentinel_only_and_empty(lib)),
+        ("identity_f32", lambda: P.test_delta_equals_per_pair_identity(lib, P.configs.C0)),
+        ("identity_bf16", lambda: P.test_delta_equals_per_pair_identity(lib, P.SMALL_BF16)),
+        ("gemm_chain", lambda: P.test_one_bucket_is_a_plain_gemm_chain(lib)),
+        ("linearity", lambda: P.test_linearity_in_scale_and_zero_A(lib)),
+    ]
+    for name, fn in cases:
+        try:
+            fn()
+        except (AssertionError, ValueError):
+            failed.append(name)
+    return failed
+
+
+@pytest.fixture(scope="module")
+def mutant_dir():
+    with tempfile.TemporaryDirectory() as d:
+        yield d
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(mutant_dir, name, old, new):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "oracle.c")).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique"
+    path_c = os.path.join(mutant_dir, f"{name}.c")
+    path_so = os.path.join(mutant_dir, f"{name}.so")
+    open(path_c, "w").write(src.replace(old, new))
+    subprocess.run(["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-fopenmp", "-o", path_so,
+                    path_c, "-lm"], check=True)
+    saved_lib, saved_path = oracle._lib, oracle._LIB
+    try:
+        oracle._lib, oracle._LIB = None, path_so
+        failed = _battery(oracle)
+    finally:
+        oracle._lib, oracle._LIB = saved_lib, saved_path
+    assert failed, f"mutant {name} passed every pin"
+
+
+def test_unmutated_oracle_passes_battery():
+    oracle.build()
+    assert _battery(oracle) == []

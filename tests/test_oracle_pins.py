@@ -1,0 +1,303 @@
+"""Pins for the CPU oracle: it is checked against things other than itself.
+
+* remap      - hand-worked cases of the pages' rule and its invariants: negative ids
+               come back bit-for-bit (any negative value), a valid pair decodes back to
+               (expert, slot), every other pair is -1 (virtual-experts remap snippet in
+               the sglang PR 24171 summary; the -1 "no adapter" contract of MindLab
+               sglang PR 24).
+* align      - numpy's stable argsort + per-bucket padding on many random tiny cases,
+               plus the structural invariants of a padded counting sort.
+* shrink/expand - the per-pair identity delta = scale * B_e (A_e x) with numpy matmuls,
+               the one-bucket special case that is a plain GEMM chain (X A^T) B^T,
+               linearity in scale, zero A, and token permutation.
+* bf16 rounding - literal IEEE cases, torch's float32 -> bfloat16 conversion, and an
+               integer round-half-even on the binary64 bit pattern.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from tests import pins
+from virtual_expert_routed_amd import configs, inputs
+
+
+# ----------------------------------------------------------------------------- bf16
+
+
+@pytest.mark.parametrize("value,bits", [
+    (1.0, 0x3F80),
+    (-2.5, 0xC020),
+    (1.0 + 2.0 ** -8, 0x3F80),            # tie -> even (down)
+    (1.0 + 3 * 2.0 ** -8, 0x3F82),        # tie -> even (up)
+    (1.0 + 2.0 ** -8 + 2.0 ** -40, 0x3F81),  # just above the tie -> up
+    (2.0 ** -126, 0x0080),                # smallest normal
+    (2.0 ** -133, 0x0001),                # smallest subnormal
+    (2.0 ** -134, 0x0000),                # tie between 0 and 2^-133 -> even (0)
+    (3 * 2.0 ** -134, 0x0002),            # tie between 1 and 2 quanta -> even (2)
+    (255 * 2.0 ** 120, 0x7F7F),           # largest finite
+    (255.5 * 2.0 ** 120, 0x7F80),         # tie towards 256*2^120 -> overflow
+    (float("inf"), 0x7F80),
+    (-0.0, 0x8000),
+])
+def test_bf16_literal_cases(oracle_lib, value, bits):
+    assert int(oracle_lib.bf16_from_double(np.array([value]))[0]) == bits
+
+
+def test_bf16_nan(oracle_lib):
+    b = int(oracle_lib.bf16_from_double(np.array([np.nan]))[0])
+    assert (b & 0x7F80) == 0x7F80 and (b & 0x7F) != 0
+
+
+def test_bf16_matches_torch_on_float32_values(oracle_lib):
+    rng = np.random.default_rng(1)
+    f = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32),
+        (rng.standard_normal(20000) * 1e-38).astype(np.float32),   # subnormal range
+        (rng.standard_normal(20000) * 1e37).astype(np.float32),
+    ])
+    ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle_lib.bf16_from_double(f.astype(np.float64))
+    assert np.array_equal(got, ref)
+
+
+def test_bf16_matches_integer_rne_on_doubles(oracle_lib):
+    rng = np.random.default_rng(2)
+    d = rng.standard_normal(300000) * np.exp(rng.uniform(-20, 20, 300000))
+    # exact ties and near-ties in double (not representable as float32)
+    base = pins.bf16_bits_to_f64(rng.integers(0x0100, 0x7F00, 1000, dtype=np.uint16))
+    d = np.concatenate([d, base * (1 + 2.0 ** -8), base * (1 + 2.0 ** -8 + 2.0 ** -50),
+                        base * (1 + 2.0 ** -8 - 2.0 ** -50)])
+    assert np.array_equal(oracle_lib.bf16_from_double(d), pins.bf16_rne_bits(d))
+
+
+# ---------------------------------------------------------------------------- remap
+
+
+def test_remap_worked_cases(oracle_lib):
+    E, S = 4, 3
+    topk = np.array([[0, 3], [2, -1], [1, -7], [4, 0], [3, 1], [-2147483648, 2]], np.int32)
+    lora = np.array([0, 2, -1, 1, 3, 1], np.int32)
+    want = np.array([[0, 3], [10, -1], [-1, -7], [-1, 4], [-1, -1], [-2147483648, 6]],
+                    np.int32)
+    assert np.array_equal(oracle_lib.virtual_topk(topk, lora, E, S), want)
+
+
+def test_remap_invariants(oracle_lib):
+    rng = np.random.default_rng(3)
+    M, k, E, S = 400, 6, 16, 5
+    topk = rng.integers(-40, E + 6, size=(M, k), dtype=np.int32)
+    topk[0, 0] = np.iinfo(np.int32).min
+    lora = rng.integers(-2, S + 2, size=M, dtype=np.int32)
+    v = oracle_lib.virtual_topk(topk, lora, E, S)
+    l = np.repeat(lora, k).reshape(M, k)
+    neg = topk < 0
+    assert np.array_equal(v[neg], topk[neg])                      # sentinels untouched
+    ok = (~neg) & (topk < E) & (l >= 0) & (l < S)
+    assert np.all((v[ok] >= 0) & (v[ok] < E * S))
+    assert np.array_equal(v[ok] % E, topk[ok]) and np.array_equal(v[ok] // E, l[ok])
+    assert np.all(v[(~neg) & (~ok)] == -1)
+
+
+# ---------------------------------------------------------------------------- align
+
+
+def _check_align_invariants(srt, eid, npp, key, V, BM):
+    numel = key.size
+    assert npp % BM == 0 and npp == srt.size and eid.size == npp // BM
+    counts = np.bincount(key, minlength=V + 1)
+    assert npp == int(np.sum(-(-counts // BM) * BM))
+    real = srt[srt < numel]
+    assert np.array_equal(np.sort(real), np.arange(numel))        # each pair exactly once
+    assert np.all(srt[srt >= numel] == numel)                     # padding value
+    blocks = srt.reshape(-1, BM) if npp else srt.reshape(0, BM)
+    last = -2
+    seen_sentinel = False
+    for b, row in enumerate(blocks):
+        members = row[row < numel]
+        assert members.size > 0                                   # no empty blocks
+        kk = np.unique(key[members])
+        assert kk.size == 1
+        want = -1 if kk[0] == V else kk[0]
+        assert eid[b] == want
+        if eid[b] == -1:
+            seen_sentinel = True
+        else:
+            assert not seen_sentinel and eid[b] >= last           # sentinel blocks last
+            last = eid[b]
+        assert np.all(np.diff(members) > 0)                       # stable inside a block
+    nz = min(numel, V + 1)
+    assert npp // BM <= -(-(numel + nz * (BM - 1)) // BM)
+
+
+def test_align_matches_stable_argsort_bruteforce(oracle_lib):
+    rng = np.random.default_rng(4)
+    cases = 0
+    for numel, V, BM in itertools.product(range(0, 13), range(1, 7), (1, 2, 4)):
+        for _ in range(4):
+            ids = rng.integers(-3, V + 3, size=(numel, 1), dtype=np.int32)
+            got = oracle_lib.align_block_size(ids, None, V, 1, BM)
+            want = pins.align_by_argsort(ids, None, V, 1, BM)
+            assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+            assert got[2] == want[2]
+            key = pins.keys_of(ids, None, V, 1)
+            _check_align_invariants(got[0], got[1], got[2], key, V, BM)
+            cases += 1
+    assert cases == 13 * 6 * 3 * 4
+
+
+def test_align_inline_remap_equals_remap_then_align(oracle_lib):
+    rng = np.random.default_rng(5)
+    for _ in range(50):
+        M, k = int(rng.integers(0, 40)), int(rng.integers(1, 5))
+        E, S, BM = int(rng.integers(1, 9)), int(rng.integers(1, 5)), int(rng.integers(1, 9))
+        topk = rng.integers(-2, E + 2, size=(M, k), dtype=np.int32)
+        lora = rng.integers(-1, S + 1, size=M, dtype=np.int32)
+        a = oracle_lib.align_block_size(topk, lora, E, S, BM)
+        v = oracle_lib.virtual_topk(topk, lora, E, S)
+        b = oracle_lib.align_block_size(v, None, E * S, 1, BM)
+        c = pins.align_by_argsort(topk, lora, E, S, BM)
+        for x, y, z in zip(a[:2], b[:2], c[:2]):
+            assert np.array_equal(x, y) and np.array_equal(x, z)
+        assert a[2] == b[2] == c[2]
+
+
+@pytest.mark.parametrize("cfg", [configs.C0, configs.C1, configs.C2])
+def test_align_invariants_on_configs(oracle_lib, cfg):
+    inp = inputs.generate(cfg, seed=0, tensors=False)
+    srt, eid, npp = oracle_lib.align_block_size(inp.topk_ids, inp.lora_ids, cfg.E, cfg.S,
+                                                cfg.block_m)
+    key = pins.keys_of(inp.topk_ids, inp.lora_ids, cfg.E, cfg.S)
+    _check_align_invariants(srt, eid, npp, key, cfg.V, cfg.block_m)
+    want = pins.align_by_argsort(inp.topk_ids, inp.lora_ids, cfg.E, cfg.S, cfg.block_m)
+    assert np.array_equal(srt, want[0]) and np.array_equal(eid, want[1])
+
+
+def test_align_sentinel_only_and_empty(oracle_lib):
+    srt, eid, npp = oracle_lib.align_block_size(np.full((5, 2), -1, np.int32), None, 4, 1, 4)
+    assert npp == 12 and list(eid) == [-1, -1, -1]
+    assert list(srt[:10]) == list(range(10)) and list(srt[10:]) == [10, 10]
+    srt, eid, npp = oracle_lib.align_block_size(np.zeros((0, 3), np.int32), None, 4, 1, 4)
+    assert npp == 0 and srt.size == 0 and eid.size == 0
+
+
+# ----------------------------------------------------------------------- shrink/expand
+
+
+def _run_stage(oracle_lib, inp, si, out=None, pair_mask=None):
+    cfg = inp.cfg
+    st, sin = cfg.stages[si], inp.stages[si]
+    srt, eid, npp = oracle_lib.align_block_size(inp.topk_ids, inp.lora_ids, cfg.E, cfg.S,
+                                                cfg.block_m)
+    s = oracle_lib.lora_shrink(sin.xin, sin.row_div, sin.A, srt, eid, npp, cfg.numel,
+                               cfg.block_m, pair_mask=pair_mask)
+    if out is None:
+        out = np.zeros((cfg.numel, st.N), dtype=sin.B.dtype)
+    oracle_lib.lora_expand(s, st.slices, sin.B, inp.scale, cfg.E, srt, eid, npp, cfg.numel,
+                           cfg.block_m, out, pair_mask=pair_mask)
+    return s, out
+
+
+def _small(cfg, **kw):
+    return configs.scaled(cfg, **kw)
+
+
+SMALL_BF16 = _small(configs.C1, name="c1_small", M=9, topk=3, hidden=96, E=6, S=3, rank=8,
+                    stages=configs._two_stage(96, 40, 8), sentinel_count=4, nolora_count=2)
+
+
+@pytest.mark.parametrize("cfg", [configs.C0, SMALL_BF16])
+def test_delta_equals_per_pair_identity(oracle_lib, cfg):
+    inp = inputs.generate(cfg, seed=0)
+    vids = oracle_lib.virtual_topk(inp.topk_ids, inp.lora_ids, cfg.E, cfg.S)
+    for si, st in enumerate(cfg.stages):
+        sin = inp.stages[si]
+        s, out = _run_stage(oracle_lib, inp, si)
+        s_ref, d_ref = pins.delta_per_pair(cfg.E, cfg.S, cfg.topk, vids, st, sin.xin,
+                                           sin.row_div, sin.A, sin.B, inp.scale)
+        has = ~np.isnan(s_ref[:, 0])
+        assert np.array_equal(has, ~np.isnan(s[:, 0]))
+        np.testing.assert_allclose(s[has], s_ref[has], rtol=1e-12, atol=1e-12)
+        if cfg.dtype == "f32":
+            want = d_ref.astype(np.float32)
+            np.testing.assert_allclose(out, want, rtol=1e-6, atol=1e-7)
+        else:
+            want = pins.bf16_rne_bits(d_ref)
+            # the oracle rounds its own double sum; sums differ only in the last bits of
+            # a double, so the rounded bf16 may differ only where d_ref sits on a tie
+            assert np.mean(out == want) > 0.9999
+            assert np.all(np.abs(pins.bf16_bits_to_f64(out) - d_ref)
+                          <= np.abs(d_ref) * 2.0 ** -8 + 1e-30)
+        assert np.all(out[~has] == 0)                             # no delta, untouched
+
+
+def test_one_bucket_is_a_plain_gemm_chain(oracle_lib):
+    # S = 1, E = 1, no sentinels: every pair lands on virtual expert 0, so the shrink
+    # is X A_0^T and the expand is (X A_0^T) B_0^T, a plain GEMM chain.
+    cfg = _small(configs.C0, name="one_bucket", M=37, hidden=48, E=1, topk=1, S=1, rank=6,
+                 block_m=8, stages=(configs.Stage("lora", K=48, R=6, N=20, slices=1,
+                                                  input="x"),),
+                 sentinel_count=0, lora_dist="uniform", scale=0.75)
+    inp = inputs.generate(cfg, seed=7)
+    s, out = _run_stage(oracle_lib, inp, 0)
+    X = inp.x.astype(np.float64)
+    A = inp.stages[0].A[0].astype(np.float64)
+    B = inp.stages[0].B[0].astype(np.float64)
+    np.testing.assert_allclose(s, X @ A.T, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(out, (0.75 * (X @ A.T) @ B.T).astype(np.float32),
+                               rtol=1e-6, atol=1e-7)
+
+
+def test_linearity_in_scale_and_zero_A(oracle_lib):
+    cfg = _small(configs.C0, name="lin", M=16, sentinel_count=3)
+    inp = inputs.generate(cfg, seed=11)
+    _, out1 = _run_stage(oracle_lib, inp, 0)
+    inp.scale[:] = [2.0, -0.5]
+    _, out2 = _run_stage(oracle_lib, inp, 0)
+    vids = oracle_lib.virtual_topk(inp.topk_ids, inp.lora_ids, cfg.E, cfg.S).reshape(-1)
+    for p, v in enumerate(vids):
+        if 0 <= v < cfg.V:
+            f = 2.0 if v // cfg.E == 0 else -0.5
+            np.testing.assert_allclose(out2[p], f * out1[p], rtol=1e-6, atol=1e-7)
+    inp.stages[0].A[:] = 0
+    base = inputs.base_out(cfg, 0, seed=11)
+    _, out3 = _run_stage(oracle_lib, inp, 0, out=base.copy())
+    assert np.array_equal(out3, base)
+
+
+def test_token_permutation_permutes_rows(oracle_lib):
+    cfg = SMALL_BF16
+    inp = inputs.generate(cfg, seed=3)
+    _, out = _run_stage(oracle_lib, inp, 0)
+    perm = np.random.default_rng(0).permutation(cfg.M)
+    inp.topk_ids = inp.topk_ids[perm].copy()
+    inp.lora_ids = inp.lora_ids[perm].copy()
+    inp.stages[0].xin = inp.x[perm].copy()
+    _, outp = _run_stage(oracle_lib, inp, 0)
+    pair_perm = (perm[:, None] * cfg.topk + np.arange(cfg.topk)[None, :]).reshape(-1)
+    assert np.array_equal(outp, out[pair_perm])
+
+
+def test_pair_mask_restricts_to_sampled_pairs(oracle_lib):
+    inp = inputs.generate(SMALL_BF16, seed=0)
+    s_full, o_full = _run_stage(oracle_lib, inp, 1)
+    mask = np.zeros(SMALL_BF16.numel, np.uint8)
+    mask[::3] = 1
+    s_m, o_m = _run_stage(oracle_lib, inp, 1, pair_mask=mask)
+    sel = mask.astype(bool)
+    assert np.array_equal(o_m[sel], o_full[sel]) and np.all(o_m[~sel] == 0)
+    np.testing.assert_array_equal(s_m[sel], s_full[sel])
+
+
+def test_threads_do_not_change_results(oracle_lib):
+    inp = inputs.generate(SMALL_BF16, seed=5)
+    n0 = oracle_lib.num_threads()
+    try:
+        oracle_lib.set_num_threads(1)
+        a = _run_stage(oracle_lib, inp, 0)
+        oracle_lib.set_num_threads(max(2, n0))
+        b = _run_stage(oracle_lib, inp, 0)
+    finally:
+        oracle_lib.set_num_threads(n0)
+    assert np.array_equal(a[1], b[1]) and np.array_equal(a[0], b[0], equal_nan=True)
