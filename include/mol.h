@@ -1,0 +1,198 @@
+/*
+ * mol.h - C ABI of the multi-LoRA MoE ("MoL", virtual experts) delta path on MI355X.
+ *
+ * One MoE layer with S LoRA adapters loaded into slots treats every (routed expert e,
+ * slot l) combination as a "virtual expert" v = e + l*E, V = E*S of them. A layer pass is
+ *   1. remap  - top-k base ids -> virtual ids (mol_virtual_topk, or inline in 2);
+ *   2. align  - bucket the (token, slot) pairs by virtual expert into BLOCK_M-padded
+ *               blocks (mol_align_block_size);
+ *   3. delta  - per stage, shrink s = x A_v^T (hidden -> rank) and expand
+ *               out += scale * s B_v^T (rank -> N) over the aligned blocks
+ *               (mol_lora_shrink + mol_lora_expand, or fused: mol_lora_delta).
+ * Sources: the sglang virtual-experts kernels as summarised on the PR 24171 page
+ * (remap keeping negative sentinels, sentinel bucket, -1 blocks skipped), the PR 24262
+ * page (align as histogram -> prefix sum -> expert ids -> scatter, no host sync, the
+ * 8192-bucket ceiling), and MindLab sglang PR 24 (shrink/expand stage shapes, weights
+ * laid out [E, N, K] with N = shape[1], the "-1 = no adapter" slot contract).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless marked (host). The caller owns every buffer,
+ *    including workspaces; the library keeps no device memory of its own.
+ *  - Calls only validate host-side scalars and pointers, then enqueue kernels on
+ *    `stream` (a hipStream_t; NULL = the legacy default stream) and return. No call
+ *    allocates, synchronises, or reads device memory on the host, so a sequence of calls
+ *    can be captured into a hipGraph.
+ *  - Bad *device data* cannot be reported without a sync; it has defined behaviour
+ *    instead: a base id >= E, a slot outside [0, S) and any negative id never reach a
+ *    real virtual expert (they land in the sentinel bucket and get no delta).
+ *  - Matrices are row-major; "ld" arguments are row strides in elements.
+ *  - Returns MOL_OK or an error code; nothing is enqueued when an error is returned
+ *    (except MOL_E_HIP, which reports a failed launch).
+ */
+#ifndef MOL_H
+#define MOL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define MOL_API __attribute__((visibility("default")))
+#else
+#define MOL_API
+#endif
+
+typedef int32_t mol_status;
+
+enum {
+    MOL_OK = 0,
+    MOL_E_ARG = 1,       /* NULL pointer, negative or zero size, inconsistent shapes   */
+    MOL_E_LIMIT = 2,     /* more than MOL_MAX_BUCKETS buckets, rank or block too large */
+    MOL_E_DTYPE = 3,     /* unknown dtype                                              */
+    MOL_E_ALIGN = 4,     /* a row, stride or base pointer not 16-byte aligned          */
+    MOL_E_WORKSPACE = 5, /* workspace missing or smaller than the size query says      */
+    MOL_E_HIP = 6        /* a HIP call or kernel launch failed                         */
+};
+
+enum { MOL_F32 = 0, MOL_BF16 = 1 };
+
+/* At most 8192 buckets = 8191 virtual experts + the sentinel bucket (the align kernel
+ * ceiling on the PR 24262 page). */
+#define MOL_MAX_BUCKETS 8192
+#define MOL_MAX_BLOCK_M 1024
+/* expand: r * sizeof(elem) <= 256 bytes (rank <= 128 in bf16, <= 64 in fp32) */
+#define MOL_MAX_RANK_BYTES 256
+
+/* (host) Static description of a status code. Never NULL. */
+MOL_API const char *mol_status_string(mol_status status);
+
+/* (host) ABI version of this header, 1. */
+MOL_API int32_t mol_abi_version(void);
+
+/* ---------------------------------------------------------------------------------
+ * mol_virtual_topk - remap base top-k ids to virtual ids (PR 24171 page: the fused
+ * virtual top-k ids kernel keeps a negative id and shifts the others by slot * E).
+ *   topk_ids     int32 [M, topk]   base expert ids; negative = expert-parallel sentinel
+ *   lora_ids     int32 [M]         LoRA slot per token; -1 = no adapter
+ *   virtual_ids  int32 [M, topk]   out: t if t < 0; -1 if t >= E or slot outside [0, S);
+ *                                  else t + slot * E. May not alias the inputs.
+ * M == 0 is valid and enqueues nothing. Errors: MOL_E_ARG.
+ * ------------------------------------------------------------------------------- */
+MOL_API mol_status mol_virtual_topk(const int32_t *topk_ids, const int32_t *lora_ids,
+                                    int32_t M, int32_t topk, int32_t num_experts,
+                                    int32_t num_slots, int32_t *virtual_ids, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Align sizing (host, pure). num_virtual = V = E * S.
+ *   mol_align_max_blocks: an upper bound on the number of BLOCK_M blocks any routing
+ *     of `numel` pairs can produce, cdiv(numel + min(numel, V+1) * (block_m - 1),
+ *     block_m). sorted_ids needs max_blocks * block_m entries, expert_ids max_blocks.
+ *   mol_align_workspace_bytes: device workspace mol_align_block_size needs (0 when the
+ *     one-workgroup kernel handles numel).
+ * Both return a negative -mol_status on invalid arguments (e.g. -MOL_E_LIMIT when
+ * V + 1 > MOL_MAX_BUCKETS).
+ * ------------------------------------------------------------------------------- */
+MOL_API int64_t mol_align_max_blocks(int64_t numel, int32_t num_virtual, int32_t block_m);
+MOL_API int64_t mol_align_workspace_bytes(int64_t numel, int32_t num_virtual, int32_t block_m);
+
+/* ---------------------------------------------------------------------------------
+ * mol_align_block_size - bucket the numel = M * topk pairs by virtual expert (PR 24262
+ * page: histogram, padded prefix sum, per-block expert ids, token scatter; PR 24171
+ * page: the extra sentinel bucket whose blocks are -1).
+ *   ids            int32 [M, topk]  base ids (lora_ids != NULL: remapped inline exactly
+ *                                   as mol_virtual_topk) or virtual ids (lora_ids == NULL)
+ *   lora_ids       int32 [M] or NULL
+ *   Bucket of a pair = its virtual id if in [0, V), else V (the sentinel bucket, last).
+ *   With c_b pairs in bucket b, pc_b = ceil(c_b / block_m) * block_m and off_b the
+ *   exclusive prefix sum of pc:
+ *   sorted_ids       int32 [max_blocks * block_m] out: sorted_ids[off_b + j] = the j-th
+ *                    pair of bucket b in ascending pair order (j < c_b); entries
+ *                    [off_b + c_b, off_b + pc_b) = numel (padding).
+ *   expert_ids       int32 [max_blocks] out: block i in [off_b, off_b + pc_b)/block_m
+ *                    gets b, or -1 for the sentinel bucket.
+ *   num_post_padded  int32 [1] out: sum_b pc_b.
+ *   Entries past num_post_padded (resp. num_post_padded / block_m) are left undefined.
+ *   workspace        device scratch of mol_align_workspace_bytes(), or NULL when that is 0.
+ * No atomics are used; results are bit-for-bit reproducible. M == 0 writes
+ * num_post_padded = 0 (sorted_ids and expert_ids may then be NULL).
+ * Errors: MOL_E_ARG, MOL_E_LIMIT (V + 1 > MOL_MAX_BUCKETS, block_m > MOL_MAX_BLOCK_M),
+ * MOL_E_WORKSPACE, MOL_E_HIP.
+ * ------------------------------------------------------------------------------- */
+MOL_API mol_status mol_align_block_size(const int32_t *ids, const int32_t *lora_ids,
+                                        int32_t M, int32_t topk, int32_t num_experts,
+                                        int32_t num_slots, int32_t block_m,
+                                        int32_t *sorted_ids, int32_t *expert_ids,
+                                        int32_t *num_post_padded, void *workspace,
+                                        size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * mol_lora_shrink - s[p, i] = sum_k A[v, i, k] * xin[p / row_div, k] for every real pair
+ * p of every block with expert id v >= 0 (MindLab sglang PR 24: the MoL shrink stage,
+ * hidden -> rank). fp32 accumulation.
+ *   dtype        MOL_F32 or MOL_BF16 (xin and A)
+ *   xin          [rows, ld_x] input rows; pair p reads row p / row_div (row_div = topk
+ *                for token rows, 1 for per-pair rows)
+ *   A            [V, R, K] weights, rows of K contiguous elements
+ *   sorted_ids, expert_ids, num_post_padded: the outputs of mol_align_block_size for
+ *                `numel` pairs, V = num_virtual virtual experts and this block_m
+ *   s            float32 [numel, R] out; rows of pairs that get no delta are untouched
+ * Requires K * elem and ld_x * elem to be multiples of 16 bytes and xin, A 16-byte
+ * aligned (MOL_E_ALIGN). numel == 0 enqueues nothing.
+ * ------------------------------------------------------------------------------- */
+MOL_API mol_status mol_lora_shrink(int32_t dtype, const void *xin, int64_t ld_x,
+                                   int32_t row_div, const void *A, int32_t R, int32_t K,
+                                   const int32_t *sorted_ids, const int32_t *expert_ids,
+                                   const int32_t *num_post_padded, int32_t numel,
+                                   int32_t num_virtual, int32_t block_m, float *s,
+                                   void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * mol_lora_expand - for the same pairs, with r = R / slices, w = N / slices,
+ *   out[p, n] = round(out[p, n] + slot_scale[v / E] * sum_j B[v, n, j] * s[p, (n / w) * r + j])
+ * (MindLab sglang PR 24: expand rank -> N; gate_up expands as two slices, gate from
+ * s[:, :r] and up from s[:, r:]). Sum in fp32, one fused multiply-add into the fp32 value
+ * of out, then round to nearest even for bf16.
+ *   s            float32 [numel, R] from mol_lora_shrink
+ *   B            [V, N, r] weights (dtype as out)
+ *   slot_scale   float32 [num_virtual / num_experts]
+ *   out          [numel, ld_out] read and written in place; rows of pairs without a
+ *                delta are left bit-for-bit untouched
+ * Requires R % slices == 0, N % slices == 0, r * elem a multiple of 16 bytes and at most
+ * MOL_MAX_RANK_BYTES, B 16-byte aligned.
+ * ------------------------------------------------------------------------------- */
+MOL_API mol_status mol_lora_expand(int32_t dtype, const float *s, int32_t R, int32_t slices,
+                                   const void *B, int32_t N, const float *slot_scale,
+                                   int32_t num_experts, const int32_t *sorted_ids,
+                                   const int32_t *expert_ids,
+                                   const int32_t *num_post_padded, int32_t numel,
+                                   int32_t num_virtual, int32_t block_m, void *out,
+                                   int64_t ld_out, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * mol_lora_delta - shrink then expand for one stage in ONE launch; s lives in the
+ * workspace. Same arguments and results as mol_lora_shrink followed by mol_lora_expand
+ * (bit-identical to them).
+ *   workspace    device scratch of at least mol_delta_workspace_bytes(); it MUST be
+ *                zero-filled before its first use, and every call leaves its counters
+ *                zeroed again. Calls that may overlap must not share a workspace.
+ * ------------------------------------------------------------------------------- */
+MOL_API int64_t mol_delta_workspace_bytes(int32_t numel, int32_t R, int32_t num_virtual,
+                                          int32_t block_m);
+MOL_API mol_status mol_lora_delta(int32_t dtype, const void *xin, int64_t ld_x,
+                                  int32_t row_div, const void *A, int32_t R, int32_t K,
+                                  int32_t slices, const void *B, int32_t N,
+                                  const float *slot_scale, int32_t num_experts,
+                                  const int32_t *sorted_ids, const int32_t *expert_ids,
+                                  const int32_t *num_post_padded, int32_t numel,
+                                  int32_t num_virtual, int32_t block_m, void *out,
+                                  int64_t ld_out, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOL_H */

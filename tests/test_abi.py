@@ -1,0 +1,143 @@
+"""Host-only checks of the C ABI: the library loads, exports every declared symbol, and
+rejects bad arguments before touching the device (no call here launches anything)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests import conftest
+from virtual_expert_routed_amd import binding as mb
+
+HEADER = os.path.join(conftest.ROOT, "include", "mol.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"MOL_API\s+[\w\s\*]+?\b(mol_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_five_path_calls():
+    syms = declared_symbols()
+    for name in ("mol_virtual_topk", "mol_align_block_size", "mol_lora_shrink",
+                 "mol_lora_expand", "mol_lora_delta"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol():
+    L = mb.lib()
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+    assert set(declared_symbols()) == set(mb.SIGNATURES)
+
+
+def test_only_mol_symbols_exported():
+    out = os.popen(f"nm -D --defined-only {mb.LIB_PATH}").read()
+    funcs = [ln.split()[-1] for ln in out.splitlines() if " T " in ln]
+    assert funcs and all(f.startswith("mol_") for f in funcs), funcs
+
+
+def test_version_and_status_strings():
+    L = mb.lib()
+    assert L.mol_abi_version() == 1
+    for code in range(7):
+        assert mb.status_string(code)
+    assert mb.status_string(99) == "unknown status"
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+@pytest.mark.parametrize("numel,V,BM", [(0, 8, 16), (16, 8, 16), (184, 1024, 64),
+                                        (1024, 2048, 64), (32768, 8064, 64),
+                                        (131072, 2048, 64), (5, 1, 1), (7, 8191, 1024)])
+def test_align_max_blocks_formula(numel, V, BM):
+    nz = min(numel, V + 1)
+    assert mb.mol_align_max_blocks(numel, V, BM) == _cdiv(numel + nz * (BM - 1), BM)
+
+
+def test_align_bucket_ceiling():
+    # 8191 virtual experts + the sentinel bucket = 8192 buckets is the largest allowed
+    assert mb.mol_align_max_blocks(10, 8191, 64) > 0
+    with pytest.raises(mb.MolError) as e:
+        mb.mol_align_max_blocks(10, 8192, 64)
+    assert e.value.status == mb.MOL_E_LIMIT
+
+
+def test_align_workspace_small_and_large():
+    assert mb.mol_align_workspace_bytes(4096, 8191, 64) == 0
+    ws = mb.mol_align_workspace_bytes(32768, 8064, 64)
+    assert ws >= (16 * 8065 + 2 * 8065) * 4 and ws % 256 == 0
+
+
+def test_delta_workspace_bytes():
+    n = mb.mol_delta_workspace_bytes(184, 64, 1024, 64)
+    mblk = mb.mol_align_max_blocks(184, 1024, 64)
+    assert n >= 184 * 64 * 4 + (64 + 2 * mblk) * 4
+
+
+P = ctypes.c_void_p
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
+
+
+def test_align_rejects_before_launch():
+    L = mb.lib()
+    # too many buckets
+    assert L.mol_align_block_size(FAKE, FAKE, 4, 2, 4096, 2, 64, FAKE, FAKE, FAKE, None, 0,
+                                  None) == mb.MOL_E_LIMIT
+    # null outputs
+    assert L.mol_align_block_size(FAKE, None, 4, 2, 8, 2, 16, None, FAKE, FAKE, None, 0,
+                                  None) == mb.MOL_E_ARG
+    assert L.mol_align_block_size(FAKE, None, 4, 2, 8, 2, 16, FAKE, FAKE, None, None, 0,
+                                  None) == mb.MOL_E_ARG
+    # bad sizes
+    assert L.mol_align_block_size(FAKE, None, -1, 2, 8, 2, 16, FAKE, FAKE, FAKE, None, 0,
+                                  None) == mb.MOL_E_ARG
+    assert L.mol_align_block_size(FAKE, None, 4, 2, 8, 2, 2048, FAKE, FAKE, FAKE, None, 0,
+                                  None) == mb.MOL_E_LIMIT
+    # large path without workspace
+    assert L.mol_align_block_size(FAKE, None, 5000, 1, 8, 2, 16, FAKE, FAKE, FAKE, None, 0,
+                                  None) == mb.MOL_E_WORKSPACE
+
+
+def test_remap_rejects_before_launch():
+    L = mb.lib()
+    assert L.mol_virtual_topk(None, FAKE, 3, 2, 4, 2, FAKE, None) == mb.MOL_E_ARG
+    assert L.mol_virtual_topk(FAKE, FAKE, 3, 0, 4, 2, FAKE, None) == mb.MOL_E_ARG
+    assert L.mol_virtual_topk(FAKE, FAKE, 0, 2, 4, 2, FAKE, None) == mb.MOL_OK  # M = 0
+
+
+def test_shrink_expand_delta_reject_before_launch():
+    L = mb.lib()
+    # shrink: unknown dtype, K not a multiple of 16 bytes, misaligned pointer
+    assert L.mol_lora_shrink(7, FAKE, 64, 1, FAKE, 8, 64, FAKE, FAKE, FAKE, 16, 8, 16, FAKE,
+                             None) == mb.MOL_E_DTYPE
+    assert L.mol_lora_shrink(mb.MOL_BF16, FAKE, 68, 1, FAKE, 8, 60, FAKE, FAKE, FAKE, 16, 8,
+                             16, FAKE, None) == mb.MOL_E_ALIGN
+    assert L.mol_lora_shrink(mb.MOL_F32, ctypes.c_void_p(0x1004), 64, 1, FAKE, 8, 64, FAKE,
+                             FAKE, FAKE, 16, 8, 16, FAKE, None) == mb.MOL_E_ALIGN
+    assert L.mol_lora_shrink(mb.MOL_F32, FAKE, 32, 1, FAKE, 8, 64, FAKE, FAKE, FAKE, 16, 8,
+                             16, FAKE, None) == mb.MOL_E_ARG           # ld_x < K
+    # expand: R % slices, rank too large, V not a multiple of E
+    assert L.mol_lora_expand(mb.MOL_BF16, FAKE, 63, 2, FAKE, 32, FAKE, 4, FAKE, FAKE, FAKE,
+                             16, 8, 16, FAKE, 32, None) == mb.MOL_E_ARG
+    assert L.mol_lora_expand(mb.MOL_BF16, FAKE, 512, 2, FAKE, 32, FAKE, 4, FAKE, FAKE, FAKE,
+                             16, 8, 16, FAKE, 32, None) == mb.MOL_E_LIMIT
+    assert L.mol_lora_expand(mb.MOL_BF16, FAKE, 16, 1, FAKE, 32, FAKE, 3, FAKE, FAKE, FAKE,
+                             16, 8, 16, FAKE, 32, None) == mb.MOL_E_ARG
+    # delta: workspace missing or too small
+    assert L.mol_lora_delta(mb.MOL_BF16, FAKE, 64, 1, FAKE, 16, 64, 1, FAKE, 32, FAKE, 4,
+                            FAKE, FAKE, FAKE, 16, 8, 16, FAKE, 32, None, 0,
+                            None) == mb.MOL_E_WORKSPACE
+    assert L.mol_lora_delta(mb.MOL_BF16, FAKE, 64, 1, FAKE, 16, 64, 1, FAKE, 32, FAKE, 4,
+                            FAKE, FAKE, FAKE, 16, 8, 16, FAKE, 32, FAKE, 64,
+                            None) == mb.MOL_E_WORKSPACE
+    # numel == 0 is a no-op
+    assert L.mol_lora_delta(mb.MOL_BF16, None, 64, 1, None, 16, 64, 1, None, 32, None, 4,
+                            None, None, None, 0, 8, 16, None, 32, None, 0, None) == mb.MOL_OK
+
+
+def test_library_is_built_for_gfx950():
+    from virtual_expert_routed_amd import build
+    assert any("gfx950" in ln for ln in build.code_objects(mb.LIB_PATH))

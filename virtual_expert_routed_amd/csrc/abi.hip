@@ -1,0 +1,324 @@
+// C ABI of libmol: host-side validation, sizing and launch (declared in include/mol.h).
+// Every check happens before any HIP call, so argument errors never touch the device.
+#include "../../include/mol.h"
+
+#include <atomic>
+#include <limits>
+
+#include "mol_internal.h"
+
+namespace {
+
+constexpr int64_t kI32Max = std::numeric_limits<int32_t>::max();
+
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round256(int64_t a) { return (a + 255) / 256 * 256; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Max dynamic LDS per workgroup, cached per device (only the one-workgroup align asks).
+std::atomic<int> g_lds_bytes[64];
+
+int device_lds_bytes() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 65536;
+  int v = g_lds_bytes[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int attr = 0;
+    if (hipDeviceGetAttribute(&attr, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+            hipSuccess ||
+        attr <= 0)
+      attr = 65536;
+    v = attr < 163840 ? attr : 163840;
+    g_lds_bytes[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+int bits_for(int32_t v) {  // bits needed to represent values in [0, v]
+  int b = 0;
+  while (b < 31 && (int64_t(1) << b) <= v) ++b;
+  return b;
+}
+
+mol_status hip_status(hipError_t e) { return e == hipSuccess ? MOL_OK : MOL_E_HIP; }
+
+// number of blocks any routing of numel pairs over V virtual experts can produce
+int64_t max_blocks_of(int64_t numel, int64_t V, int64_t BM) {
+  const int64_t nz = numel < V + 1 ? numel : V + 1;
+  return cdiv64(numel + nz * (BM - 1), BM);
+}
+
+int64_t align_check(int64_t numel, int32_t V, int32_t BM) {
+  if (numel < 0 || V < 1 || BM < 1) return -MOL_E_ARG;
+  if ((int64_t)V + 1 > MOL_MAX_BUCKETS || BM > MOL_MAX_BLOCK_M) return -MOL_E_LIMIT;
+  if (numel > kI32Max) return -MOL_E_LIMIT;
+  const int64_t mb = max_blocks_of(numel, V, BM);
+  if (mb * BM > kI32Max) return -MOL_E_LIMIT;
+  return mb;
+}
+
+struct StageCheck {
+  mol_status st;
+  int64_t max_blocks;
+};
+
+// checks shared by shrink, expand and delta (routing arguments)
+StageCheck routing_check(const int32_t* sorted_ids, const int32_t* expert_ids,
+                         const int32_t* npp, int32_t numel, int32_t V, int32_t BM) {
+  const int64_t mb = align_check(numel, V, BM);
+  if (mb < 0) return {(mol_status)(-mb), 0};
+  if (numel > 0 && (!sorted_ids || !expert_ids || !npp)) return {MOL_E_ARG, 0};
+  return {MOL_OK, mb};
+}
+
+mol_status shrink_check(int32_t dtype, const void* xin, int64_t ld_x, int32_t row_div,
+                        const void* A, int32_t R, int32_t K, int32_t numel, float* s) {
+  if (dtype != MOL_F32 && dtype != MOL_BF16) return MOL_E_DTYPE;
+  if (R < 1 || K < 1 || row_div < 1 || ld_x < K) return MOL_E_ARG;
+  if (numel > 0 && (!xin || !A || !s)) return MOL_E_ARG;
+  const int esz = dtype == MOL_BF16 ? 2 : 4;
+  if (((int64_t)K * esz) % 16 || (ld_x * esz) % 16) return MOL_E_ALIGN;
+  if (numel > 0 && (!aligned16(xin) || !aligned16(A))) return MOL_E_ALIGN;
+  return MOL_OK;
+}
+
+mol_status expand_check(int32_t dtype, int32_t R, int32_t slices, const void* B, int32_t N,
+                        const float* scale, int32_t E, int32_t V, int32_t numel,
+                        const void* out, int64_t ld_out) {
+  if (dtype != MOL_F32 && dtype != MOL_BF16) return MOL_E_DTYPE;
+  if (R < 1 || slices < 1 || N < 1 || E < 1 || R % slices || N % slices || ld_out < N ||
+      V % E)
+    return MOL_E_ARG;
+  if (numel > 0 && (!B || !scale || !out)) return MOL_E_ARG;
+  const int esz = dtype == MOL_BF16 ? 2 : 4;
+  const int64_t rbytes = (int64_t)(R / slices) * esz;
+  if (rbytes % 16) return MOL_E_ALIGN;
+  if (rbytes > MOL_MAX_RANK_BYTES || R > 1024) return MOL_E_LIMIT;
+  if (numel > 0 && (!aligned16(B) || (reinterpret_cast<uintptr_t>(out) % esz)))
+    return MOL_E_ALIGN;
+  return MOL_OK;
+}
+
+mol::DeltaArgs make_delta_args(const void* xin, int64_t ld_x, int32_t row_div, const void* A,
+                               int32_t R, int32_t K, int32_t slices, const void* B,
+                               int32_t N, const float* scale, int32_t E,
+                               const int32_t* sorted_ids, const int32_t* expert_ids,
+                               const int32_t* npp, int32_t numel, int32_t V, int32_t BM,
+                               float* s, void* out, int64_t ld_out, int64_t max_blocks) {
+  mol::DeltaArgs a{};
+  a.xin = xin;
+  a.ld_x = ld_x;
+  a.row_div = row_div;
+  a.A = A;
+  a.R = R;
+  a.K = K;
+  a.slices = slices;
+  a.B = B;
+  a.N = N;
+  a.scale = scale;
+  a.E = E;
+  a.sorted = sorted_ids;
+  a.expert_ids = expert_ids;
+  a.npp = npp;
+  a.numel = numel;
+  a.V = V;
+  a.BM = BM;
+  a.s = s;
+  a.out = out;
+  a.ld_out = ld_out;
+  a.max_blocks = (int32_t)max_blocks;
+  a.nchunk = (int32_t)cdiv64(N, mol::kExpandCols);
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+MOL_API const char* mol_status_string(mol_status status) {
+  switch (status) {
+    case MOL_OK: return "ok";
+    case MOL_E_ARG: return "invalid argument";
+    case MOL_E_LIMIT: return "size beyond a supported limit";
+    case MOL_E_DTYPE: return "unsupported dtype";
+    case MOL_E_ALIGN: return "pointer, row or stride not 16-byte aligned";
+    case MOL_E_WORKSPACE: return "workspace missing or too small";
+    case MOL_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+MOL_API int32_t mol_abi_version(void) { return 1; }
+
+MOL_API mol_status mol_virtual_topk(const int32_t* topk_ids, const int32_t* lora_ids,
+                                    int32_t M, int32_t topk, int32_t num_experts,
+                                    int32_t num_slots, int32_t* virtual_ids, void* stream) {
+  if (M < 0 || topk < 1 || num_experts < 1 || num_slots < 1) return MOL_E_ARG;
+  if ((int64_t)M * topk > kI32Max || (int64_t)num_experts * num_slots > kI32Max)
+    return MOL_E_LIMIT;
+  if (M == 0) return MOL_OK;
+  if (!topk_ids || !lora_ids || !virtual_ids) return MOL_E_ARG;
+  return hip_status(mol::launch_virtual_topk(topk_ids, lora_ids, M, topk, num_experts,
+                                             num_slots, virtual_ids, (hipStream_t)stream));
+}
+
+MOL_API int64_t mol_align_max_blocks(int64_t numel, int32_t num_virtual, int32_t block_m) {
+  return align_check(numel, num_virtual, block_m);
+}
+
+MOL_API int64_t mol_align_workspace_bytes(int64_t numel, int32_t num_virtual,
+                                          int32_t block_m) {
+  const int64_t mb = align_check(numel, num_virtual, block_m);
+  if (mb < 0) return mb;
+  if (numel <= mol::kAlignSmallMax) return 0;
+  const int64_t nb = (int64_t)num_virtual + 1;
+  const int64_t ntiles = cdiv64(numel, mol::kAlignTile);
+  return round256((ntiles * nb + 2 * nb) * (int64_t)sizeof(int32_t));
+}
+
+MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_ids,
+                                        int32_t M, int32_t topk, int32_t num_experts,
+                                        int32_t num_slots, int32_t block_m,
+                                        int32_t* sorted_ids, int32_t* expert_ids,
+                                        int32_t* num_post_padded, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  if (M < 0 || topk < 1 || num_experts < 1 || num_slots < 1 || block_m < 1)
+    return MOL_E_ARG;
+  const int64_t V64 = (int64_t)num_experts * num_slots;
+  if (V64 + 1 > MOL_MAX_BUCKETS || block_m > MOL_MAX_BLOCK_M) return MOL_E_LIMIT;
+  const int64_t numel = (int64_t)M * topk;
+  const int64_t mb = align_check(numel, (int32_t)V64, block_m);
+  if (mb < 0) return (mol_status)(-mb);
+  if (!num_post_padded) return MOL_E_ARG;
+  if (numel > 0 && (!ids || !sorted_ids || !expert_ids)) return MOL_E_ARG;
+  const int64_t need = mol_align_workspace_bytes(numel, (int32_t)V64, block_m);
+  if (need > 0 && (!workspace || workspace_bytes < (size_t)need)) return MOL_E_WORKSPACE;
+
+  mol::AlignArgs a{};
+  a.ids = ids;
+  a.lora = lora_ids;
+  a.topk = topk;
+  a.E = num_experts;
+  a.S = num_slots;
+  a.numel = (int32_t)numel;
+  a.V = (int32_t)V64;
+  a.BM = block_m;
+  a.nbits = bits_for(a.V);
+  a.sorted = sorted_ids;
+  a.expert_ids = expert_ids;
+  a.npp = num_post_padded;
+  const hipStream_t st = (hipStream_t)stream;
+  const int nb = a.V + 1;
+  if (numel <= mol::kAlignSmallMax) {
+    const int lds_ints = device_lds_bytes() / (int)sizeof(int) - 64;
+    int waves = lds_ints / nb;
+    if (waves > 16) waves = 16;
+    if (waves < 1) return MOL_E_LIMIT;
+    const size_t lds = ((size_t)waves * nb + 64) * sizeof(int);
+    return hip_status(mol::launch_align_small(a, waves, lds, st));
+  }
+  a.ntiles = (int32_t)cdiv64(numel, mol::kAlignTile);
+  int32_t* ws = static_cast<int32_t*>(workspace);
+  a.counts = ws;
+  a.bucket_off = ws + (int64_t)a.ntiles * nb;
+  a.bucket_cnt = a.bucket_off + nb;
+  return hip_status(mol::launch_align_large(a, st));
+}
+
+MOL_API mol_status mol_lora_shrink(int32_t dtype, const void* xin, int64_t ld_x,
+                                   int32_t row_div, const void* A, int32_t R, int32_t K,
+                                   const int32_t* sorted_ids, const int32_t* expert_ids,
+                                   const int32_t* num_post_padded, int32_t numel,
+                                   int32_t num_virtual, int32_t block_m, float* s,
+                                   void* stream) {
+  const StageCheck rc =
+      routing_check(sorted_ids, expert_ids, num_post_padded, numel, num_virtual, block_m);
+  if (rc.st != MOL_OK) return rc.st;
+  const mol_status sc = shrink_check(dtype, xin, ld_x, row_div, A, R, K, numel, s);
+  if (sc != MOL_OK) return sc;
+  if (numel == 0) return MOL_OK;
+  const bool bf16 = dtype == MOL_BF16;
+  const int rpi = mol::shrink_rows_per_item(K, bf16 ? 2 : 4);
+  const int64_t rgroups = cdiv64(R, rpi);
+  const int64_t grid = rc.max_blocks * rgroups;
+  if (grid > kI32Max) return MOL_E_LIMIT;
+  mol::DeltaArgs a = make_delta_args(xin, ld_x, row_div, A, R, K, 1, nullptr, 1, nullptr, 1,
+                                     sorted_ids, expert_ids, num_post_padded, numel,
+                                     num_virtual, block_m, s, nullptr, 0, rc.max_blocks);
+  a.rgroups = (int32_t)rgroups;
+  return hip_status(mol::launch_shrink(a, bf16, rpi, (int)grid, (hipStream_t)stream));
+}
+
+MOL_API mol_status mol_lora_expand(int32_t dtype, const float* s, int32_t R, int32_t slices,
+                                   const void* B, int32_t N, const float* slot_scale,
+                                   int32_t num_experts, const int32_t* sorted_ids,
+                                   const int32_t* expert_ids,
+                                   const int32_t* num_post_padded, int32_t numel,
+                                   int32_t num_virtual, int32_t block_m, void* out,
+                                   int64_t ld_out, void* stream) {
+  const StageCheck rc =
+      routing_check(sorted_ids, expert_ids, num_post_padded, numel, num_virtual, block_m);
+  if (rc.st != MOL_OK) return rc.st;
+  const mol_status ec = expand_check(dtype, R, slices, B, N, slot_scale, num_experts,
+                                     num_virtual, numel, out, ld_out);
+  if (ec != MOL_OK) return ec;
+  if (numel > 0 && !s) return MOL_E_ARG;
+  if (numel == 0) return MOL_OK;
+  const bool bf16 = dtype == MOL_BF16;
+  mol::DeltaArgs a = make_delta_args(nullptr, 0, 1, nullptr, R, 1, slices, B, N, slot_scale,
+                                     num_experts, sorted_ids, expert_ids, num_post_padded,
+                                     numel, num_virtual, block_m, const_cast<float*>(s), out,
+                                     ld_out, rc.max_blocks);
+  const int64_t grid = rc.max_blocks * a.nchunk;
+  if (grid > kI32Max) return MOL_E_LIMIT;
+  return hip_status(mol::launch_expand(a, bf16, (int)grid, (hipStream_t)stream));
+}
+
+MOL_API int64_t mol_delta_workspace_bytes(int32_t numel, int32_t R, int32_t num_virtual,
+                                          int32_t block_m) {
+  const int64_t mb = align_check(numel, num_virtual, block_m);
+  if (mb < 0) return mb;
+  if (R < 1) return -MOL_E_ARG;
+  return round256((int64_t)numel * R * (int64_t)sizeof(float)) +
+         round256((64 + 2 * mb) * (int64_t)sizeof(int32_t));
+}
+
+MOL_API mol_status mol_lora_delta(int32_t dtype, const void* xin, int64_t ld_x,
+                                  int32_t row_div, const void* A, int32_t R, int32_t K,
+                                  int32_t slices, const void* B, int32_t N,
+                                  const float* slot_scale, int32_t num_experts,
+                                  const int32_t* sorted_ids, const int32_t* expert_ids,
+                                  const int32_t* num_post_padded, int32_t numel,
+                                  int32_t num_virtual, int32_t block_m, void* out,
+                                  int64_t ld_out, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  const StageCheck rc =
+      routing_check(sorted_ids, expert_ids, num_post_padded, numel, num_virtual, block_m);
+  if (rc.st != MOL_OK) return rc.st;
+  float dummy = 0.f;
+  mol_status c = shrink_check(dtype, xin, ld_x, row_div, A, R, K, numel, &dummy);
+  if (c != MOL_OK) return c;
+  c = expand_check(dtype, R, slices, B, N, slot_scale, num_experts, num_virtual, numel, out,
+                   ld_out);
+  if (c != MOL_OK) return c;
+  if (numel == 0) return MOL_OK;
+  const int64_t need = mol_delta_workspace_bytes(numel, R, num_virtual, block_m);
+  if (need < 0) return (mol_status)(-need);
+  if (!workspace || workspace_bytes < (size_t)need) return MOL_E_WORKSPACE;
+  if (!aligned16(workspace)) return MOL_E_ALIGN;
+  const bool bf16 = dtype == MOL_BF16;
+  const int rpi = mol::shrink_rows_per_item(K, bf16 ? 2 : 4);
+  float* s = static_cast<float*>(workspace);
+  mol::DeltaArgs a = make_delta_args(xin, ld_x, row_div, A, R, K, slices, B, N, slot_scale,
+                                     num_experts, sorted_ids, expert_ids, num_post_padded,
+                                     numel, num_virtual, block_m, s, out, ld_out,
+                                     rc.max_blocks);
+  a.rgroups = (int32_t)cdiv64(R, rpi);
+  a.sync = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                      round256((int64_t)numel * R * (int64_t)sizeof(float)));
+  const int64_t grid = rc.max_blocks * (a.rgroups + (int64_t)a.nchunk);
+  if (grid > kI32Max) return MOL_E_LIMIT;
+  return hip_status(mol::launch_delta(a, bf16, rpi, (int)grid, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,288 @@
+// Remap and align_block_size for the MoL delta path on gfx950.
+//
+// align_block_size groups the (token, slot) pairs by virtual expert into BLOCK_M-padded
+// buckets: histogram -> padded exclusive prefix sum -> one expert id per block -> scatter
+// of the pair indices, with one extra sentinel bucket (id V) whose blocks are tagged -1
+// (sglang PR 24262 page, implementation item 1; PR 24171 page, the sentinel-bucket
+// snippet and risk item 2). Inside a bucket the pairs keep ascending order, so the
+// result is unique and reproducible.
+//
+// Design (no atomics anywhere):
+//  * the pairs are cut into contiguous tiles; one wave64 owns a tile and walks it in
+//    chunks of 64 in ascending order;
+//  * inside a chunk, lanes holding the same bucket find each other with one ballot per
+//    key bit (<= 13 ballots); the lowest lane of a group is its leader and the rank of a
+//    lane is the number of group members below it (mbcnt);
+//  * each tile has a private per-bucket counter row (LDS), so a walk only touches its
+//    own row: counts on the first walk, then cursors on the second;
+//  * cursor[tile][b] = off_b + (pairs of bucket b in earlier tiles): prefix sums in
+//    tile order, which gives the stable order across tiles.
+// numel <= 4096 runs as ONE workgroup (16 waves, every row in LDS, one launch); larger
+// inputs run three kernels (count per tile -> scan -> scatter) through a workspace.
+#include "mol_internal.h"
+
+namespace mol {
+namespace {
+
+__device__ __forceinline__ uint64_t wave_ballot(bool p) {
+  return __builtin_amdgcn_ballot_w64(p);
+}
+
+// number of set bits of m in lanes below this lane
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Lanes of this wave whose `key` equals this lane's (only lanes with `valid` take part).
+__device__ __forceinline__ uint64_t match_key(int key, bool valid, int nbits) {
+  uint64_t peers = wave_ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t ones = wave_ballot(valid && bit);
+    peers &= bit ? ones : ~ones;
+  }
+  return peers;
+}
+
+__device__ __forceinline__ int remap_one(int32_t t, int32_t l, int32_t E, int32_t S) {
+  return t < 0 ? t : ((t >= E || l < 0 || l >= S) ? -1 : t + l * E);
+}
+
+__device__ __forceinline__ int bucket_of(const AlignArgs& a, int p) {
+  const int32_t t = a.ids[p];
+  const int32_t v = a.lora ? remap_one(t, a.lora[p / a.topk], a.E, a.S) : t;
+  return (v >= 0 && v < a.V) ? v : a.V;
+}
+
+// Count the pairs [begin, end) into this walker's private row `hist` (LDS).
+__device__ __forceinline__ void count_walk(const AlignArgs& a, int begin, int end,
+                                           int* hist) {
+  const int lane = lanes_below(~0ull);
+  for (int c = begin; c < end; c += 64) {
+    const int p = c + lane;
+    const bool valid = p < end;
+    const int key = valid ? bucket_of(a, p) : 0;
+    const uint64_t peers = match_key(key, valid, a.nbits);
+    if (valid && lanes_below(peers) == 0) hist[key] += __popcll(peers);
+  }
+}
+
+// Scatter the pairs [begin, end) in ascending order; `cursor` (LDS) holds this walker's
+// next free slot per bucket.
+__device__ __forceinline__ void scatter_walk(const AlignArgs& a, int begin, int end,
+                                             int* cursor) {
+  const int lane = lanes_below(~0ull);
+  for (int c = begin; c < end; c += 64) {
+    const int p = c + lane;
+    const bool valid = p < end;
+    const int key = valid ? bucket_of(a, p) : 0;
+    const uint64_t peers = match_key(key, valid, a.nbits);
+    if (valid) {
+      const int rank = lanes_below(peers);
+      const int base = cursor[key];  // every member reads before the leader writes
+      if (rank == 0) cursor[key] = base + __popcll(peers);
+      a.sorted[base + rank] = p;
+    }
+  }
+}
+
+// Exclusive prefix sum of one int per thread over the workgroup (<= 16 waves).
+// `sh` is >= 33 ints of LDS; *total gets the sum over all threads.
+__device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += t;
+  }
+  if (lane == 63) sh[wid] = inc;
+  __syncthreads();
+  if (wid == 0) {
+    const int w = lane < nw ? sh[lane] : 0;
+    int winc = w;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(winc, d, 64);
+      if (lane >= d) winc += t;
+    }
+    if (lane < nw) sh[16 + lane] = winc - w;
+    if (lane == 63) sh[32] = winc;
+  }
+  __syncthreads();
+  *total = sh[32];
+  return sh[16 + wid] + inc - v;
+}
+
+__device__ __forceinline__ int round_up(int c, int m) { return (c + m - 1) / m * m; }
+
+// expert ids and padding entries of bucket b (c pairs at padded offset off), by `lanes`
+// cooperating threads starting at `first`.
+__device__ __forceinline__ void write_bucket_tail(const AlignArgs& a, int b, int c, int off,
+                                                  int first, int lanes) {
+  const int pc = round_up(c, a.BM);
+  const int eid = (b == a.V) ? -1 : b;
+  const int blk0 = off / a.BM;
+  for (int j = first; j < pc / a.BM; j += lanes) a.expert_ids[blk0 + j] = eid;
+  for (int j = c + first; j < pc; j += lanes) a.sorted[off + j] = a.numel;
+}
+
+__global__ void __launch_bounds__(256) virtual_topk_kernel(const int32_t* __restrict__ topk,
+                                                         const int32_t* __restrict__ lora,
+                                                         int32_t numel, int32_t k, int32_t E,
+                                                         int32_t S, int32_t* __restrict__ out) {
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (p >= numel) return;
+  out[p] = remap_one(topk[p], lora[p / k], E, S);
+}
+
+// One workgroup of 1024 threads; LDS = waves * (V+1) + 64 ints.
+__global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a, int waves) {
+  extern __shared__ int lds[];
+  const int NB = a.V + 1;
+  int* table = lds;                // [waves][NB]
+  int* sh = lds + waves * NB;      // scan scratch
+  const int tid = threadIdx.x, wid = tid >> 6;
+  for (int i = tid; i < waves * NB; i += blockDim.x) table[i] = 0;
+  __syncthreads();
+
+  const int per = ((a.numel + waves - 1) / waves + 63) / 64 * 64;
+  const int begin = min(a.numel, wid * per);
+  const int end = min(a.numel, begin + per);
+  if (wid < waves) count_walk(a, begin, end, table + wid * NB);
+  __syncthreads();
+
+  // each thread owns a contiguous range of buckets for the scan
+  const int bpt = (NB + (int)blockDim.x - 1) / (int)blockDim.x;
+  const int b0 = min(NB, tid * bpt), b1 = min(NB, b0 + bpt);
+  int mine = 0;
+  for (int b = b0; b < b1; ++b) {
+    int c = 0;
+    for (int w = 0; w < waves; ++w) c += table[w * NB + b];
+    mine += round_up(c, a.BM);
+  }
+  int total;
+  int off = block_excl_scan(mine, sh, &total);
+  for (int b = b0; b < b1; ++b) {
+    int run = off, c = 0;
+    for (int w = 0; w < waves; ++w) {
+      const int cw = table[w * NB + b];
+      table[w * NB + b] = run;  // this wave's first slot in bucket b
+      run += cw;
+      c += cw;
+    }
+    write_bucket_tail(a, b, c, off, 0, 1);
+    off += round_up(c, a.BM);
+  }
+  if (tid == 0) *a.npp = total;
+  __syncthreads();
+  if (wid < waves) scatter_walk(a, begin, end, table + wid * NB);
+}
+
+// Three-kernel path, kernel 1: per-tile counts -> counts[tile][b].
+__global__ void __launch_bounds__(64) align_count_kernel(AlignArgs a) {
+  extern __shared__ int lds[];
+  const int NB = a.V + 1;
+  const int t = blockIdx.x, lane = threadIdx.x;
+  for (int i = lane; i < NB; i += 64) lds[i] = 0;
+  __syncthreads();
+  const int begin = t * kAlignTile;
+  const int end = min(a.numel, begin + kAlignTile);
+  count_walk(a, begin, end, lds);
+  __syncthreads();
+  int32_t* row = a.counts + (int64_t)t * NB;
+  for (int i = lane; i < NB; i += 64) row[i] = lds[i];
+}
+
+// Kernel 2 (one workgroup of 1024): bucket totals, padded offsets, per-tile cursors.
+__global__ void __launch_bounds__(1024) align_scan_kernel(AlignArgs a) {
+  extern __shared__ int lds[];
+  const int NB = a.V + 1;
+  int* ctot = lds;        // [NB]
+  int* sh = lds + NB;     // scan scratch
+  const int tid = threadIdx.x;
+  // column pass (coalesced): counts -> exclusive prefix over tiles, totals to LDS
+  for (int b = tid; b < NB; b += blockDim.x) {
+    int run = 0;
+    for (int t = 0; t < a.ntiles; ++t) {
+      int32_t* q = a.counts + (int64_t)t * NB + b;
+      const int c = *q;
+      *q = run;
+      run += c;
+    }
+    ctot[b] = run;
+  }
+  __syncthreads();
+  const int bpt = (NB + (int)blockDim.x - 1) / (int)blockDim.x;
+  const int b0 = min(NB, tid * bpt), b1 = min(NB, b0 + bpt);
+  int mine = 0;
+  for (int b = b0; b < b1; ++b) mine += round_up(ctot[b], a.BM);
+  int total;
+  int off = block_excl_scan(mine, sh, &total);
+  for (int b = b0; b < b1; ++b) {
+    const int c = ctot[b];
+    a.bucket_cnt[b] = c;
+    a.bucket_off[b] = off;
+    ctot[b] = off;
+    off += round_up(c, a.BM);
+  }
+  if (tid == 0) *a.npp = total;
+  __syncthreads();
+  // cursor pass (coalesced): cursor[t][b] = off_b + pairs of b in tiles before t
+  for (int b = tid; b < NB; b += blockDim.x) {
+    const int o = ctot[b];
+    for (int t = 0; t < a.ntiles; ++t) a.counts[(int64_t)t * NB + b] += o;
+  }
+}
+
+// Kernel 3: padding + expert ids for this tile's share of the buckets, then the scatter.
+__global__ void __launch_bounds__(64) align_scatter_kernel(AlignArgs a) {
+  extern __shared__ int lds[];
+  const int NB = a.V + 1;
+  const int t = blockIdx.x, lane = threadIdx.x;
+  const int32_t* row = a.counts + (int64_t)t * NB;
+  for (int i = lane; i < NB; i += 64) lds[i] = row[i];
+  const int bb0 = (int)((int64_t)NB * t / a.ntiles);
+  const int bb1 = (int)((int64_t)NB * (t + 1) / a.ntiles);
+  for (int b = bb0; b < bb1; ++b)
+    write_bucket_tail(a, b, a.bucket_cnt[b], a.bucket_off[b], lane, 64);
+  __syncthreads();
+  const int begin = t * kAlignTile;
+  const int end = min(a.numel, begin + kAlignTile);
+  scatter_walk(a, begin, end, lds);
+}
+
+}  // namespace
+
+hipError_t launch_virtual_topk(const int32_t* topk_ids, const int32_t* lora_ids, int32_t M,
+                               int32_t topk, int32_t E, int32_t S, int32_t* out,
+                               hipStream_t stream) {
+  const int32_t numel = M * topk;
+  const unsigned grid = (unsigned)((numel + 255) / 256);
+  hipLaunchKernelGGL(virtual_topk_kernel, dim3(grid), dim3(256), 0, stream, topk_ids,
+                     lora_ids, numel, topk, E, S, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_align_small(const AlignArgs& a, int waves, size_t lds_bytes,
+                              hipStream_t stream) {
+  hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(1024), lds_bytes, stream, a, waves);
+  return hipGetLastError();
+}
+
+hipError_t launch_align_large(const AlignArgs& a, hipStream_t stream) {
+  const size_t nb_bytes = (size_t)(a.V + 1) * sizeof(int);
+  hipLaunchKernelGGL(align_count_kernel, dim3(a.ntiles), dim3(64), nb_bytes, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(1024), nb_bytes + 64 * sizeof(int),
+                     stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(align_scatter_kernel, dim3(a.ntiles), dim3(64), nb_bytes, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace mol

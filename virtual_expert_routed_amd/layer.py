@@ -1,0 +1,114 @@
+"""One MoL layer resident on the GPU: uploaded inputs, routing buffers, workspaces and
+outputs, and the calls that run the path on them through the C ABI.
+
+Plumbing only: torch allocates device memory and supplies the stream; every step of the
+path (remap, align, shrink, expand) runs in libmol's kernels.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as mb
+from .inputs import LayerInputs
+
+
+def to_device(a: np.ndarray, device, bf16: bool) -> torch.Tensor:
+    if bf16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+            torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+class DeviceLayer:
+    def __init__(self, inp: LayerInputs, device="cuda", outs=None):
+        cfg = inp.cfg
+        self.cfg = cfg
+        self.device = torch.device(device)
+        bf16 = cfg.dtype == "bf16"
+        self.bf16 = bf16
+        dev = self.device
+        self.topk_ids = torch.from_numpy(inp.topk_ids).to(dev)
+        self.lora_ids = torch.from_numpy(inp.lora_ids).to(dev)
+        self.scale = torch.from_numpy(inp.scale).to(dev)
+        x = to_device(inp.x, dev, bf16)
+        self.A, self.B, self.xin, self.row_div = [], [], [], []
+        for st, sin in zip(cfg.stages, inp.stages):
+            self.A.append(to_device(sin.A, dev, bf16))
+            self.B.append(to_device(sin.B, dev, bf16))
+            self.xin.append(x if st.input == "x" else to_device(sin.xin, dev, bf16))
+            self.row_div.append(sin.row_div)
+        numel, V, BM = cfg.numel, cfg.V, cfg.block_m
+        nblk = mb.mol_align_max_blocks(numel, V, BM)
+        self.max_blocks = nblk
+        self.sorted_ids = torch.empty(max(1, nblk * BM), dtype=torch.int32, device=dev)
+        self.expert_ids = torch.empty(max(1, nblk), dtype=torch.int32, device=dev)
+        self.npp = torch.empty(1, dtype=torch.int32, device=dev)
+        wsb = mb.mol_align_workspace_bytes(numel, V, BM)
+        self.align_ws = torch.empty(max(256, wsb), dtype=torch.uint8, device=dev)
+        self.delta_ws = [mb.new_delta_workspace(numel, st.R, V, BM, dev) for st in cfg.stages]
+        self.s = [torch.empty((max(1, numel), st.R), dtype=torch.float32, device=dev)
+                  for st in cfg.stages]
+        odt = torch.bfloat16 if bf16 else torch.float32
+        if outs is None:
+            self.out = [torch.zeros((numel, st.N), dtype=odt, device=dev) for st in cfg.stages]
+        else:
+            self.out = [to_device(o, dev, bf16) for o in outs]
+
+    # ---------------------------------------------------------------------------- steps
+    def align(self):
+        c = self.cfg
+        mb.mol_align_block_size(self.topk_ids, self.lora_ids, c.E, c.S, c.block_m,
+                                self.sorted_ids, self.expert_ids, self.npp, self.align_ws)
+
+    def remap(self):
+        c = self.cfg
+        return mb.mol_virtual_topk(self.topk_ids, self.lora_ids, c.E, c.S)
+
+    def routing(self):
+        return self.sorted_ids, self.expert_ids, self.npp
+
+    def shrink(self, si: int):
+        c = self.cfg
+        mb.mol_lora_shrink(self.xin[si], self.row_div[si], self.A[si], *self.routing(),
+                           c.numel, c.V, c.block_m, s=self.s[si])
+        return self.s[si]
+
+    def expand(self, si: int):
+        c = self.cfg
+        st = c.stages[si]
+        mb.mol_lora_expand(self.s[si], st.slices, self.B[si], self.scale, c.E, *self.routing(),
+                           c.numel, c.V, c.block_m, self.out[si])
+        return self.out[si]
+
+    def delta(self, si: int):
+        c = self.cfg
+        st = c.stages[si]
+        mb.mol_lora_delta(self.xin[si], self.row_div[si], self.A[si], st.slices, self.B[si],
+                          self.scale, c.E, *self.routing(), c.numel, c.V, c.block_m,
+                          self.out[si], self.delta_ws[si])
+        return self.out[si]
+
+    def run(self, fused: bool = True):
+        """The whole path: align (remap inline), then every stage's shrink + expand."""
+        self.align()
+        for si in range(len(self.cfg.stages)):
+            if fused:
+                self.delta(si)
+            else:
+                self.shrink(si)
+                self.expand(si)
+        return self.out
+
+    # ------------------------------------------------------------------------ readback
+    def routing_host(self):
+        npp = int(self.npp.item())
+        BM = self.cfg.block_m
+        return (self.sorted_ids[:npp].cpu().numpy(), self.expert_ids[: npp // BM].cpu().numpy(),
+                npp)
+
+    def out_host(self, si: int) -> np.ndarray:
+        o = self.out[si]
+        if self.bf16:
+            return o.view(torch.int16).cpu().numpy().view(np.uint16)
+        return o.cpu().numpy()
