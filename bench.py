@@ -119,96 +119,88 @@ def main():
     torch.cuda.synchronize()
     stats = [layer_stats(dl) for dl in layers]
 
-    ev = {}  # per-layer event pairs around the gate_up and down deltas
-
-    def step_body(dl, evs=None):
+    def step_body(dl):
         dl.align()
         for si in range(len(cfg.stages)):
-            if evs is not None:
-                evs[si][0].record()
             dl.delta(si)
-            if evs is not None:
-                evs[si][1].record()
 
-    timing_src = "graph-events"
     graphs = None
     if args.mode == "graph":
-        try:
-            graphs = []
-            s = torch.cuda.Stream()
-            s.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(s):
-                for l, dl in enumerate(layers):
-                    evs = [(torch.cuda.Event(enable_timing=True, external=True),
-                            torch.cuda.Event(enable_timing=True, external=True))
-                           for _ in cfg.stages]
-                    g = torch.cuda.CUDAGraph()
-                    with torch.cuda.graph(g, stream=s):
-                        step_body(dl, evs)
-                    graphs.append(g)
-                    ev[l] = evs
-            torch.cuda.current_stream().wait_stream(s)
-            torch.cuda.synchronize()
-            for g in graphs:   # replays before the timed region
+        graphs = []
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for dl in layers:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=s):
+                    step_body(dl)
+                graphs.append(g)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            for g in graphs:
                 g.replay()
-            torch.cuda.synchronize()
-        except Exception as exc:  # capture unsupported: time eager launches instead
-            log(f"[bench] graph capture failed ({exc}); timing eager launches")
-            graphs = None
-    if graphs is None:
-        timing_src = "eager-events"
-        for l in range(L):
-            ev[l] = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                     for _ in cfg.stages]
+        torch.cuda.synchronize()
 
+    # ---- timed region: K steps, one layer each
     K = args.steps
-    log(f"[bench] timing {K} steps ({'graph' if graphs else 'eager'})")
-    per_kernel = [[] for _ in cfg.stages]
+    log(f"[bench] timing {K} steps ({args.mode})")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record()
     if graphs is not None:
         for i in range(K):
             graphs[i % L].replay()
     else:
         for i in range(K):
-            step_body(layers[i % L], ev[i % L])
+            step_body(layers[i % L])
+    ev1.record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    elapsed = t1 - t0
-    # event times: each layer's events hold its last replay/step of the timed region
-    for l in range(min(L, K)):
-        for si in range(len(cfg.stages)):
-            a, b = ev[l][si]
-            per_kernel[si].append(a.elapsed_time(b) * 1e3)   # us
+    elapsed = time.perf_counter() - t0
+    gpu_elapsed = ev0.elapsed_time(ev1) * 1e-3
 
-    # a second pass collecting every launch's event time (same timed-region shape)
-    samples = [[] for _ in cfg.stages]
-    rounds = max(1, min(K, 64) // L)
-    for _ in range(rounds):
-        for l in range(L):
-            if graphs is not None:
-                graphs[l].replay()
-            else:
-                step_body(layers[l], ev[l])
+    # ---- per-kernel times: HIP events around every launch, recorded on the launch stream.
+    # A GPU sleep queued first lets the host enqueue all the steps ahead of the GPU, so
+    # the events bracket back-to-back kernels rather than host launch latency.
+    nt = max(L, min(K, 8 * L))
+    nst = len(cfg.stages)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 2)] for _ in range(nt)]
+    spacer_ms = 0.0
+    if hasattr(torch.cuda, "_sleep"):
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        torch.cuda._sleep(1 << 20)
+        c1.record()
         torch.cuda.synchronize()
-        for l in range(L):
-            for si in range(len(cfg.stages)):
-                a, b = ev[l][si]
-                samples[si].append(a.elapsed_time(b) * 1e3)
-    for si in range(len(cfg.stages)):
-        samples[si].extend(per_kernel[si])
+        per_cycle_ms = max(c0.elapsed_time(c1), 1e-3) / (1 << 20)
+        spacer_ms = 30.0
+        torch.cuda._sleep(int(spacer_ms / per_cycle_ms))
+    for i in range(nt):
+        dl = layers[i % L]
+        e = evs[i]
+        e[0].record()
+        dl.align()
+        e[1].record()
+        for si in range(nst):
+            dl.delta(si)
+            e[2 + si].record()
+    torch.cuda.synchronize()
+    align_us = [evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in range(nt)]
+    samples = [[evs[i][1 + si].elapsed_time(evs[i][2 + si]) * 1e3 for i in range(nt)]
+               for si in range(nst)]
+    stage_b = [[stage_bytes(cfg, st, stats[i % L]) for i in range(nt)] for st in cfg.stages]
 
     steps_P = sum(stats[i % L]["P"] for i in range(K))
     ms_per_step = elapsed / K * 1e3
     value = steps_P / elapsed
-    stage_b = [[stage_bytes(cfg, st, stats[l]) for l in range(L)]
-               for st in cfg.stages]
     dom = 0   # gate_up delta carries the most bytes
     dom_us = float(np.mean(samples[dom]))
     dom_bytes = float(np.mean(stage_b[dom]))
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    delta_us = sum(float(np.mean(samples[si])) for si in range(len(cfg.stages)))
+    delta_us = sum(float(np.mean(samples[si])) for si in range(nst))
     delta_bytes = sum(float(np.mean(b)) for b in stage_b)
+    timing_src = f"hip-events, eager launches queued behind a {spacer_ms:.0f} ms GPU sleep"
 
     result = {
         "metric": METRIC,
@@ -226,10 +218,12 @@ def main():
         "config": {
             "workload": cfg.name, "tokens": cfg.M, "hidden": cfg.hidden, "experts": cfg.E,
             "topk": cfg.topk, "lora_slots": cfg.S, "virtual_experts": cfg.V, "rank": cfg.rank,
-            "block_m": cfg.block_m, "layers_rotated": L, "mode": "graph" if graphs else "eager",
+            "block_m": cfg.block_m, "layers_rotated": L, "mode": args.mode,
             "accumulate": "fp32",
         },
         "us_per_layer": ms_per_step * 1e3,
+        "us_per_layer_gpu_events": gpu_elapsed / K * 1e6,
+        "align_us": float(np.mean(align_us)),
         "pairs_per_layer": float(np.mean([s["P"] for s in stats])),
         "touched_virtual_experts": float(np.mean([s["D"] for s in stats])),
         "delta_us": {st.name: float(np.mean(samples[si])) for si, st in enumerate(cfg.stages)},

@@ -191,6 +191,12 @@ MOL_API mol_status mol_lora_delta(int32_t dtype, const void *xin, int64_t ld_x,
                                   int64_t ld_out, void *workspace, size_t workspace_bytes,
                                   void *stream);
 
+/* (host) Testing and tuning control, process-wide: how many times an expand work item of
+ * mol_lora_delta polls for its block's shrink results before computing them itself
+ * (the results are bit-identical for every value; only speed changes). 0 makes every
+ * expand item compute its own s; a negative value restores the default. */
+MOL_API void mol_set_delta_spin_limit(int32_t polls);
+
 #ifdef __cplusplus
 }
 #endif

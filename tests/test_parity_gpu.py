@@ -233,6 +233,55 @@ def test_empty_batch():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("cfg", [configs.C0, configs.C1, configs.C2], ids=IDS[:3])
+def test_fused_fallback_is_bit_identical(cfg):
+    """With a zero poll budget every expand item computes its block's s itself; the
+    result must not change by a single bit."""
+    case = get_case(cfg)
+    dl = DeviceLayer(case.inp)
+    dl.align()
+    ref = []
+    for si in range(len(cfg.stages)):
+        dl.shrink(si)
+        dl.expand(si)
+        ref.append(dl.out[si].clone())
+        dl.out[si].zero_()
+    try:
+        mb.mol_set_delta_spin_limit(0)
+        for si in range(len(cfg.stages)):
+            dl.delta(si)
+        torch.cuda.synchronize()
+    finally:
+        mb.mol_set_delta_spin_limit(-1)
+    for si in range(len(cfg.stages)):
+        assert torch.equal(dl.out[si], ref[si]), f"{cfg.name} stage {si}"
+
+
+@pytest.mark.parametrize("cfg", [configs.C1, configs.C2], ids=IDS[1:3])
+def test_fused_never_reads_stale_s(cfg):
+    """Poison the workspace's s rows with NaN and feed two different activations through
+    the same workspace: a read of s before it is written would show up as NaN or as the
+    previous call's values."""
+    case = get_case(cfg)
+    dl = DeviceLayer(case.inp)
+    dl.align()
+    for si, st in enumerate(cfg.stages):
+        s_bytes = cfg.numel * st.R * 4
+        for flip in (1.0, -0.5):
+            dl.delta_ws[si][:s_bytes].view(torch.float32).fill_(float("nan"))
+            if flip != 1.0:
+                dl.xin[si].mul_(flip)
+            dl.out[si].zero_()
+            dl.shrink(si)
+            dl.expand(si)
+            ref = dl.out[si].clone()
+            dl.out[si].zero_()
+            dl.delta(si)
+            torch.cuda.synchronize()
+            assert torch.equal(dl.out[si], ref), f"{cfg.name} stage {si} flip {flip}"
+            assert not torch.isnan(dl.out[si].float()).any()
+
+
 def test_hip_graph_replays_match_eager():
     cfg = configs.C1
     case = get_case(cfg)

@@ -34,6 +34,7 @@ SIGNATURES = {
     "mol_lora_expand": (_I32, [_I32, _P, _I32, _I32, _P, _I32, _P, _I32, _P, _P, _P, _I32, _I32,
                                _I32, _P, _I64, _P]),
     "mol_delta_workspace_bytes": (_I64, [_I32, _I32, _I32, _I32]),
+    "mol_set_delta_spin_limit": (None, [_I32]),
     "mol_lora_delta": (_I32, [_I32, _P, _I64, _I32, _P, _I32, _I32, _I32, _P, _I32, _P, _I32,
                               _P, _P, _P, _I32, _I32, _I32, _P, _I64, _P, _SZ, _P]),
 }
@@ -196,6 +197,10 @@ def mol_lora_expand(s, slices: int, B, slot_scale, num_experts: int, sorted_ids,
         _ptr(sorted_ids), _ptr(expert_ids), _ptr(num_post_padded), numel, num_virtual, block_m,
         _ptr(out), out.stride(0), _stream(B)))
     return out
+
+
+def mol_set_delta_spin_limit(polls: int) -> None:
+    lib().mol_set_delta_spin_limit(int(polls))
 
 
 def new_delta_workspace(numel: int, R: int, num_virtual: int, block_m: int, device):

@@ -15,6 +15,9 @@ int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round256(int64_t a) { return (a + 255) / 256 * 256; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Polls an expand item of the fused delta makes before computing s itself.
+std::atomic<int> g_spin_limit{mol::kDefaultSpinLimit};
+
 // Max dynamic LDS per workgroup, cached per device (only the one-workgroup align asks).
 std::atomic<int> g_lds_bytes[64];
 
@@ -210,12 +213,16 @@ MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_
   const hipStream_t st = (hipStream_t)stream;
   const int nb = a.V + 1;
   if (numel <= mol::kAlignSmallMax) {
-    const int lds_ints = device_lds_bytes() / (int)sizeof(int) - 64;
-    int waves = lds_ints / nb;
+    // counter rows + scan scratch + cached bucket ids (uint16 each)
+    const int64_t fixed = 64 * (int64_t)sizeof(int) + (numel + 1) / 2 * 2 * 2;
+    int64_t waves = (device_lds_bytes() - fixed) / ((int64_t)nb * (int64_t)sizeof(int));
+    const int64_t useful = cdiv64(numel, 256);  // a wave walks at least 4 chunks of 64
+    if (waves > useful) waves = useful;
     if (waves > 16) waves = 16;
-    if (waves < 1) return MOL_E_LIMIT;
-    const size_t lds = ((size_t)waves * nb + 64) * sizeof(int);
-    return hip_status(mol::launch_align_small(a, waves, lds, st));
+    if (waves < 1) waves = 1;
+    const size_t lds = (size_t)waves * nb * sizeof(int) + (size_t)fixed;
+    if ((int64_t)lds > device_lds_bytes()) return MOL_E_LIMIT;
+    return hip_status(mol::launch_align_small(a, (int)waves, lds, st));
   }
   a.ntiles = (int32_t)cdiv64(numel, mol::kAlignTile);
   int32_t* ws = static_cast<int32_t*>(workspace);
@@ -280,7 +287,11 @@ MOL_API int64_t mol_delta_workspace_bytes(int32_t numel, int32_t R, int32_t num_
   if (mb < 0) return mb;
   if (R < 1) return -MOL_E_ARG;
   return round256((int64_t)numel * R * (int64_t)sizeof(float)) +
-         round256((64 + 2 * mb) * (int64_t)sizeof(int32_t));
+         round256(mb * (int64_t)sizeof(int32_t));
+}
+
+MOL_API void mol_set_delta_spin_limit(int32_t polls) {
+  g_spin_limit.store(polls < 0 ? mol::kDefaultSpinLimit : polls, std::memory_order_relaxed);
 }
 
 MOL_API mol_status mol_lora_delta(int32_t dtype, const void* xin, int64_t ld_x,
@@ -316,6 +327,9 @@ MOL_API mol_status mol_lora_delta(int32_t dtype, const void* xin, int64_t ld_x,
   a.rgroups = (int32_t)cdiv64(R, rpi);
   a.sync = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
                                       round256((int64_t)numel * R * (int64_t)sizeof(float)));
+  a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  // block counters pack both participant counts in 16 bits each
+  if (a.rgroups >= 0x8000 || a.nchunk >= 0x8000) return MOL_E_LIMIT;
   const int64_t grid = rc.max_blocks * (a.rgroups + (int64_t)a.nchunk);
   if (grid > kI32Max) return MOL_E_LIMIT;
   return hip_status(mol::launch_delta(a, bf16, rpi, (int)grid, (hipStream_t)stream));

@@ -138,20 +138,53 @@ __global__ void __launch_bounds__(256) virtual_topk_kernel(const int32_t* __rest
   out[p] = remap_one(topk[p], lora[p / k], E, S);
 }
 
-// One workgroup of 1024 threads; LDS = waves * (V+1) + 64 ints.
+// Count (then scatter) the pairs [begin, end) whose bucket ids are cached in LDS.
+__device__ __forceinline__ void count_walk_cached(const AlignArgs& a, const uint16_t* keys,
+                                                  int begin, int end, int* hist) {
+  const int lane = lanes_below(~0ull);
+  for (int c = begin; c < end; c += 64) {
+    const int p = c + lane;
+    const bool valid = p < end;
+    const int key = valid ? keys[p] : 0;
+    const uint64_t peers = match_key(key, valid, a.nbits);
+    if (valid && lanes_below(peers) == 0) hist[key] += __popcll(peers);
+  }
+}
+
+__device__ __forceinline__ void scatter_walk_cached(const AlignArgs& a, const uint16_t* keys,
+                                                    int begin, int end, int* cursor) {
+  const int lane = lanes_below(~0ull);
+  for (int c = begin; c < end; c += 64) {
+    const int p = c + lane;
+    const bool valid = p < end;
+    const int key = valid ? keys[p] : 0;
+    const uint64_t peers = match_key(key, valid, a.nbits);
+    if (valid) {
+      const int rank = lanes_below(peers);
+      const int base = cursor[key];  // every member reads before the leader writes
+      if (rank == 0) cursor[key] = base + __popcll(peers);
+      a.sorted[base + rank] = p;
+    }
+  }
+}
+
+// One workgroup of 1024 threads for numel <= 4096. LDS: `waves` counter rows of V+1 ints,
+// 64 ints of scan scratch, then the numel bucket ids (uint16).
 __global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a, int waves) {
   extern __shared__ int lds[];
   const int NB = a.V + 1;
-  int* table = lds;                // [waves][NB]
-  int* sh = lds + waves * NB;      // scan scratch
+  int* table = lds;                                   // [waves][NB]
+  int* sh = lds + waves * NB;                         // scan scratch
+  uint16_t* keys = reinterpret_cast<uint16_t*>(sh + 64);
   const int tid = threadIdx.x, wid = tid >> 6;
   for (int i = tid; i < waves * NB; i += blockDim.x) table[i] = 0;
+  for (int p = tid; p < a.numel; p += blockDim.x) keys[p] = (uint16_t)bucket_of(a, p);
   __syncthreads();
 
   const int per = ((a.numel + waves - 1) / waves + 63) / 64 * 64;
   const int begin = min(a.numel, wid * per);
   const int end = min(a.numel, begin + per);
-  if (wid < waves) count_walk(a, begin, end, table + wid * NB);
+  if (wid < waves) count_walk_cached(a, keys, begin, end, table + wid * NB);
   __syncthreads();
 
   // each thread owns a contiguous range of buckets for the scan
@@ -173,12 +206,16 @@ __global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a, int wave
       run += cw;
       c += cw;
     }
-    write_bucket_tail(a, b, c, off, 0, 1);
-    off += round_up(c, a.BM);
+    const int nblk = round_up(c, a.BM) / a.BM;
+    const int eid = (b == a.V) ? -1 : b;
+    for (int j = 0; j < nblk; ++j) a.expert_ids[off / a.BM + j] = eid;
+    off += nblk * a.BM;
   }
   if (tid == 0) *a.npp = total;
+  // padding value everywhere first (coalesced); the scatter below overwrites real slots
+  for (int i = tid; i < total; i += blockDim.x) a.sorted[i] = a.numel;
   __syncthreads();
-  if (wid < waves) scatter_walk(a, begin, end, table + wid * NB);
+  if (wid < waves) scatter_walk_cached(a, keys, begin, end, table + wid * NB);
 }
 
 // Three-kernel path, kernel 1: per-tile counts -> counts[tile][b].

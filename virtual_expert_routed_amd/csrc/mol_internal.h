@@ -54,9 +54,12 @@ struct DeltaArgs {
   float* s;              // [numel, R]
   void* out;
   int64_t ld_out;
-  int32_t* sync;         // fused kernel: [64 + 2 * max_blocks] zero-initialised counters
+  int32_t* sync;         // fused kernel: [max_blocks] zero-initialised block counters
   int32_t max_blocks;
+  int32_t spin_limit;    // fused kernel: polls before an expand item computes s itself
 };
+
+constexpr int kDefaultSpinLimit = 1 << 16;
 
 // host-side launchers (return the launch status)
 hipError_t launch_virtual_topk(const int32_t* topk_ids, const int32_t* lora_ids, int32_t M,
