@@ -130,7 +130,6 @@ mol::DeltaArgs make_delta_args(const void* xin, int64_t ld_x, int32_t row_div, c
   a.out = out;
   a.ld_out = ld_out;
   a.max_blocks = (int32_t)max_blocks;
-  a.nchunk = (int32_t)cdiv64(N, mol::kExpandCols);
   return a;
 }
 
@@ -213,10 +212,10 @@ MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_
   const hipStream_t st = (hipStream_t)stream;
   const int nb = a.V + 1;
   if (numel <= mol::kAlignSmallMax) {
-    // counter rows + scan scratch + cached bucket ids (uint16 each)
-    const int64_t fixed = 64 * (int64_t)sizeof(int) + (numel + 1) / 2 * 2 * 2;
+    // counter rows + scan scratch + per pair a bucket id and a rank (uint16 each)
+    const int64_t fixed = 64 * (int64_t)sizeof(int) + ((numel + 1) & ~1LL) * 2 * 2;
     int64_t waves = (device_lds_bytes() - fixed) / ((int64_t)nb * (int64_t)sizeof(int));
-    const int64_t useful = cdiv64(numel, 256);  // a wave walks at least 4 chunks of 64
+    const int64_t useful = cdiv64(numel, 64);  // one chunk of 64 pairs per wave at least
     if (waves > useful) waves = useful;
     if (waves > 16) waves = 16;
     if (waves < 1) waves = 1;
@@ -276,6 +275,7 @@ MOL_API mol_status mol_lora_expand(int32_t dtype, const float* s, int32_t R, int
                                      num_experts, sorted_ids, expert_ids, num_post_padded,
                                      numel, num_virtual, block_m, const_cast<float*>(s), out,
                                      ld_out, rc.max_blocks);
+  a.nchunk = (int32_t)cdiv64(N, mol::expand_cols_per_item(R, slices, bf16 ? 2 : 4));
   const int64_t grid = rc.max_blocks * a.nchunk;
   if (grid > kI32Max) return MOL_E_LIMIT;
   return hip_status(mol::launch_expand(a, bf16, (int)grid, (hipStream_t)stream));
@@ -325,6 +325,7 @@ MOL_API mol_status mol_lora_delta(int32_t dtype, const void* xin, int64_t ld_x,
                                      numel, num_virtual, block_m, s, out, ld_out,
                                      rc.max_blocks);
   a.rgroups = (int32_t)cdiv64(R, rpi);
+  a.nchunk = (int32_t)cdiv64(N, mol::expand_cols_per_item(R, slices, bf16 ? 2 : 4));
   a.sync = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
                                       round256((int64_t)numel * R * (int64_t)sizeof(float)));
   a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);

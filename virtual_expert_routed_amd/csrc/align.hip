@@ -138,56 +138,91 @@ __global__ void __launch_bounds__(256) virtual_topk_kernel(const int32_t* __rest
   out[p] = remap_one(topk[p], lora[p / k], E, S);
 }
 
-// Count (then scatter) the pairs [begin, end) whose bucket ids are cached in LDS.
-__device__ __forceinline__ void count_walk_cached(const AlignArgs& a, const uint16_t* keys,
-                                                  int begin, int end, int* hist) {
-  const int lane = lanes_below(~0ull);
-  for (int c = begin; c < end; c += 64) {
-    const int p = c + lane;
-    const bool valid = p < end;
-    const int key = valid ? keys[p] : 0;
-    const uint64_t peers = match_key(key, valid, a.nbits);
-    if (valid && lanes_below(peers) == 0) hist[key] += __popcll(peers);
+// All 13 key bits, unrolled: bits above the largest bucket id are zero for every lane
+// and leave the mask unchanged.
+__device__ __forceinline__ uint64_t match_key13(int key, bool valid) {
+  uint64_t peers = wave_ballot(valid);
+#pragma unroll
+  for (int b = 0; b < 13; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t ones = wave_ballot(valid && bit);
+    peers &= bit ? ones : ~ones;
   }
+  return peers;
 }
 
-__device__ __forceinline__ void scatter_walk_cached(const AlignArgs& a, const uint16_t* keys,
-                                                    int begin, int end, int* cursor) {
-  const int lane = lanes_below(~0ull);
-  for (int c = begin; c < end; c += 64) {
-    const int p = c + lane;
-    const bool valid = p < end;
-    const int key = valid ? keys[p] : 0;
-    const uint64_t peers = match_key(key, valid, a.nbits);
-    if (valid) {
-      const int rank = lanes_below(peers);
-      const int base = cursor[key];  // every member reads before the leader writes
-      if (rank == 0) cursor[key] = base + __popcll(peers);
-      a.sorted[base + rank] = p;
-    }
-  }
-}
+constexpr int kMaxBucketsPerThread = kMaxBuckets / 1024;  // 8
 
-// One workgroup of 1024 threads for numel <= 4096. LDS: `waves` counter rows of V+1 ints,
-// 64 ints of scan scratch, then the numel bucket ids (uint16).
+// One workgroup of 1024 threads for numel <= 4096.
+// LDS: `waves` counter rows of V+1 ints, 64 ints of scan scratch, then per pair its
+// bucket id and its rank among the earlier pairs of the same bucket in its wave's range
+// (uint16 each).
+//   A  every thread: bucket ids of its pairs (ids and slots loaded together) -> LDS;
+//      counter rows zeroed.
+//   B  wave w walks its contiguous range in chunks of 64, in order: ballot-matched peers
+//      give each pair's rank in the chunk, the group leader adds the group to row w and
+//      hands the row's previous value to its peers, so rank_in_range = old + rank.
+//   C  bucket totals, padded exclusive scan, expert ids; row w of bucket b becomes
+//      off_b + (pairs of b in ranges before w).
+//   D  every thread: sorted[row[w(p)][b(p)] + rank_in_range(p)] = p, fully parallel;
+//      each wave writes the padding of the non-empty buckets its threads own.
 __global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a, int waves) {
   extern __shared__ int lds[];
   const int NB = a.V + 1;
   int* table = lds;                                   // [waves][NB]
   int* sh = lds + waves * NB;                         // scan scratch
   uint16_t* keys = reinterpret_cast<uint16_t*>(sh + 64);
-  const int tid = threadIdx.x, wid = tid >> 6;
+  uint16_t* rel = keys + ((a.numel + 1) & ~1);
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int numel = a.numel;
+
+  // A: four pairs per thread per round, loads of ids and slots issued together
+  for (int base = 0; base < numel; base += 4 * 1024) {
+    int t[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = base + i * 1024 + tid;
+      const int pc = p < numel ? p : 0;
+      t[i] = a.ids[pc];
+      l[i] = a.lora ? a.lora[pc / a.topk] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = base + i * 1024 + tid;
+      if (p < numel) {
+        const int v = a.lora ? remap_one(t[i], l[i], a.E, a.S) : t[i];
+        keys[p] = (uint16_t)((v >= 0 && v < a.V) ? v : a.V);
+      }
+    }
+  }
   for (int i = tid; i < waves * NB; i += blockDim.x) table[i] = 0;
-  for (int p = tid; p < a.numel; p += blockDim.x) keys[p] = (uint16_t)bucket_of(a, p);
   __syncthreads();
 
-  const int per = ((a.numel + waves - 1) / waves + 63) / 64 * 64;
-  const int begin = min(a.numel, wid * per);
-  const int end = min(a.numel, begin + per);
-  if (wid < waves) count_walk_cached(a, keys, begin, end, table + wid * NB);
+  // B
+  const int per = ((numel + waves - 1) / waves + 63) / 64 * 64;
+  if (wid < waves) {
+    int* row = table + wid * NB;
+    const int begin = min(numel, wid * per);
+    const int end = min(numel, begin + per);
+    for (int c = begin; c < end; c += 64) {
+      const int p = c + lane;
+      const bool valid = p < end;
+      const int key = valid ? keys[p] : 0;
+      const uint64_t peers = match_key13(key, valid);
+      const int rank = lanes_below(peers);
+      const int leader = valid ? __builtin_ctzll(peers) : lane;
+      int old = 0;
+      if (valid && rank == 0) {
+        old = row[key];
+        row[key] = old + __popcll(peers);
+      }
+      old = __shfl(old, leader, 64);
+      if (valid) rel[p] = (uint16_t)(old + rank);
+    }
+  }
   __syncthreads();
 
-  // each thread owns a contiguous range of buckets for the scan
+  // C: each thread owns a contiguous range of buckets
   const int bpt = (NB + (int)blockDim.x - 1) / (int)blockDim.x;
   const int b0 = min(NB, tid * bpt), b1 = min(NB, b0 + bpt);
   int mine = 0;
@@ -198,24 +233,49 @@ __global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a, int wave
   }
   int total;
   int off = block_excl_scan(mine, sh, &total);
-  for (int b = b0; b < b1; ++b) {
-    int run = off, c = 0;
-    for (int w = 0; w < waves; ++w) {
-      const int cw = table[w * NB + b];
-      table[w * NB + b] = run;  // this wave's first slot in bucket b
-      run += cw;
-      c += cw;
+  // padding of this thread's buckets, kept as (first slot, count) per owned bucket
+  int pad_from[kMaxBucketsPerThread], pad_cnt[kMaxBucketsPerThread];
+#pragma unroll
+  for (int k = 0; k < kMaxBucketsPerThread; ++k) {
+    pad_cnt[k] = 0;
+    pad_from[k] = 0;
+    const int b = b0 + k;
+    if (b < b1) {
+      int run = off, c = 0;
+      for (int w = 0; w < waves; ++w) {
+        const int cw = table[w * NB + b];
+        table[w * NB + b] = run;
+        run += cw;
+        c += cw;
+      }
+      const int pc = round_up(c, a.BM);
+      const int eid = (b == a.V) ? -1 : b;
+      for (int j = 0; j < pc / a.BM; ++j) a.expert_ids[off / a.BM + j] = eid;
+      pad_from[k] = off + c;
+      pad_cnt[k] = pc - c;
+      off += pc;
     }
-    const int nblk = round_up(c, a.BM) / a.BM;
-    const int eid = (b == a.V) ? -1 : b;
-    for (int j = 0; j < nblk; ++j) a.expert_ids[off / a.BM + j] = eid;
-    off += nblk * a.BM;
   }
   if (tid == 0) *a.npp = total;
-  // padding value everywhere first (coalesced); the scatter below overwrites real slots
-  for (int i = tid; i < total; i += blockDim.x) a.sorted[i] = a.numel;
   __syncthreads();
-  if (wid < waves) scatter_walk_cached(a, keys, begin, end, table + wid * NB);
+
+  // D
+  for (int p = tid; p < numel; p += blockDim.x) {
+    const int w = p / per;
+    a.sorted[table[w * NB + keys[p]] + rel[p]] = p;
+  }
+  // padding: the wave's lanes fill one padded bucket after another
+#pragma unroll
+  for (int k = 0; k < kMaxBucketsPerThread; ++k) {
+    uint64_t todo = wave_ballot(pad_cnt[k] > 0);
+    while (todo) {
+      const int src = __builtin_ctzll(todo);
+      todo &= todo - 1;
+      const int from = __shfl(pad_from[k], src, 64);
+      const int cnt = __shfl(pad_cnt[k], src, 64);
+      for (int j = lane; j < cnt; j += 64) a.sorted[from + j] = numel;
+    }
+  }
 }
 
 // Three-kernel path, kernel 1: per-tile counts -> counts[tile][b].

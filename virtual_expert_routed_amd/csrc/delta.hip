@@ -89,22 +89,34 @@ __device__ __forceinline__ float dot16_s(const uint4& b, const float* s, float a
   return acc;
 }
 
+constexpr int kThreads = 256;
 constexpr int kPidSlots = 64;     // pair ids staged per pass over a block
+constexpr int kSLdsFloats = 4096; // s rows staged per expand pass (16 KiB)
+constexpr int kPG = 4;            // pairs sharing one pass over the held weight vectors
+constexpr int kSeg = 8;           // 16-byte weight vectors a lane holds at once
+
+// output columns per thread of an expand item, from the 16-byte vectors per weight row
+__host__ __device__ constexpr int cols_per_thread(int rv) { return rv >= 8 ? 1 : 8 / rv; }
 
 __device__ __forceinline__ bool real_pair(int p, int numel) {
   return (unsigned)p < (unsigned)numel;
 }
 
+__device__ __forceinline__ bool real_expert(int e, int V) { return (unsigned)e < (unsigned)V; }
+
 // blocks that carry work: [0, npp / BM) clamped to the launched bound
-__device__ __forceinline__ int live_blocks(const DeltaArgs& a) {
-  const int nb = *a.npp / a.BM;
+__device__ __forceinline__ int live_blocks(const DeltaArgs& a, int npp) {
+  const int nb = npp / a.BM;
   return nb < 0 ? 0 : (nb > a.max_blocks ? a.max_blocks : nb);
 }
 
-__device__ __forceinline__ bool real_expert(int e, int V) { return (unsigned)e < (unsigned)V; }
-constexpr int kSLdsFloats = 4096; // s rows staged per expand pass (16 KiB)
-
-constexpr int kPG = 4;  // pairs sharing one pass over the held weight vectors
+// Expert id of block blk if the block carries work, else -1. Both loads go out together
+// (blk < max_blocks, so the expert id read is in bounds even past the live blocks).
+__device__ __forceinline__ int block_expert(const DeltaArgs& a, int blk) {
+  const int npp = *a.npp;
+  const int e = a.expert_ids[blk];
+  return (blk < live_blocks(a, npp) && real_expert(e, a.V)) ? e : -1;
+}
 
 // agent-coherent accesses used to hand s from shrink to expand items of one launch
 __device__ __forceinline__ void st_coherent(float* p, float v) {
@@ -114,16 +126,58 @@ __device__ __forceinline__ float ld_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Dot products of rows rg*RPI + tid/LPR of A_e with the input rows of the pairs p[0..PG)
-// (ids that are not real pairs are skipped). Afterwards lane 0 of each row's lane group
-// holds the full sum in acc[i]. Each lane sums its vectors lr, lr+LPR, lr+2*LPR, ... in
-// ascending order and the lanes are combined by a fixed xor tree, so the result depends
-// only on (K, LPR) - not on SEG (vectors held at once) or PG (pairs per pass).
-template <bool BF16, int LPR, int SEG = 8, int PG = 4>
-__device__ __forceinline__ void shrink_rows(const DeltaArgs& a, int e, int rg, const int* p,
-                                            float* acc) {
+// Branch-free loads: an address that is not needed is clamped to a valid one (the first
+// element of the same array) and the value discarded afterwards, so a run of loads issues
+// back to back instead of each sitting in its own branch with its own wait.
+__device__ __forceinline__ uint4 ld16_if(const char* base, int64_t off, bool ok) {
+  const uint4 v = ld16(base + (ok ? off : 0));
+  return ok ? v : make_uint4(0, 0, 0, 0);
+}
+
+// Entry j0 + lane of block blk for the lanes of wave 0 (numel for entries past the block).
+__device__ __forceinline__ int load_pid(const DeltaArgs& a, int blk, int j0) {
+  const int j = j0 + (int)threadIdx.x;
+  const int v = a.sorted[(int64_t)blk * a.BM + (j < a.BM ? j : 0)];
+  return j < a.BM ? v : a.numel;
+}
+
+// Wave 0 publishes its pair ids and the number of real ones (they form a prefix).
+__device__ __forceinline__ void publish_pids(const DeltaArgs& a, int pv, int* pid, int* nreal) {
+  if (threadIdx.x < kPidSlots) {
+    pid[threadIdx.x] = pv;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(real_pair(pv, a.numel));
+    if (threadIdx.x == 0) *nreal = (int)__popcll(m);
+  }
+}
+
+// ------------------------------------------------------------------------------ shrink
+// Lane lr of a row's LPR-lane group owns the 16-byte vectors lr, lr+LPR, lr+2*LPR, ...
+// of the row, sums their products in ascending order, and the lanes are combined by a
+// fixed xor tree: the result depends only on (K, LPR), not on how many vectors (kSeg) or
+// pairs (kPG) are processed together, which is what lets the fallback path below
+// reproduce the shrink items bit for bit.
+
+template <bool BF16, int LPR>
+__device__ __forceinline__ void load_a_seg(const char* arow, bool row_ok, int m0, int nvec,
+                                           uint4* av) {
+  const int lr = threadIdx.x % LPR;
+#pragma unroll
+  for (int sg = 0; sg < kSeg; ++sg) {
+    const int v = lr + (m0 + sg) * LPR;
+    av[sg] = ld16_if(arow, (int64_t)v * 16, row_ok && v < nvec);
+  }
+}
+
+// One shrink work item: rows [rg*RPI, rg*RPI+RPI) of s for every real pair of block blk.
+// The x segments of kPG pairs at a time are staged once in LDS (xs) instead of every row
+// group of lanes reading them again.
+template <bool BF16, int LPR, bool COHERENT>
+__device__ __forceinline__ void shrink_item(const DeltaArgs& a, int blk, int rg, int e, int pv0,
+                                            int* pid, int* nreal, uint4* xs) {
   constexpr int ESZ = BF16 ? 2 : 4;
-  constexpr int RPI = 256 / LPR;
+  constexpr int RPI = kThreads / LPR;
+  constexpr int SEGV = kSeg * LPR;              // vectors of one x segment
+  constexpr int XPT = kPG * SEGV / kThreads;    // x vectors each thread stages
   const int tid = threadIdx.x;
   const int lr = tid % LPR;
   const int row = rg * RPI + tid / LPR;
@@ -134,201 +188,256 @@ __device__ __forceinline__ void shrink_rows(const DeltaArgs& a, int e, int rg, c
       (const char*)a.A + ((int64_t)e * a.R + (row_ok ? row : 0)) * (int64_t)a.K * ESZ;
   const char* xbase = (const char*)a.xin;
   const int64_t xstride = a.ld_x * ESZ;
-#pragma unroll
-  for (int i = 0; i < PG; ++i) acc[i] = 0.f;
-  for (int m0 = 0; m0 < vpl; m0 += SEG) {
-    uint4 av[SEG];
-#pragma unroll
-    for (int sg = 0; sg < SEG; ++sg) {
-      const int v = lr + (m0 + sg) * LPR;
-      av[sg] = (row_ok && v < nvec) ? ld16(arow + (int64_t)v * 16) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < PG; ++i) {
-      if (real_pair(p[i], a.numel)) {
-        const char* xr = xbase + (int64_t)(p[i] / a.row_div) * xstride;
-#pragma unroll
-        for (int sg = 0; sg < SEG; ++sg) {
-          const int v = lr + (m0 + sg) * LPR;
-          if (v < nvec) acc[i] = dot16<BF16>(av[sg], ld16(xr + (int64_t)v * 16), acc[i]);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < PG; ++i) {
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) acc[i] += __shfl_xor(acc[i], off, 64);
-  }
-}
-
-// Stage the ids of block entries [j0, j0 + n) into pid (numel marks a padding entry).
-__device__ __forceinline__ void stage_pids(const DeltaArgs& a, int blk, int j0, int n, int* pid) {
-  const int tid = threadIdx.x;
-  if (tid < n) {
-    const int j = j0 + tid;
-    pid[tid] = j < a.BM ? a.sorted[blk * a.BM + j] : a.numel;
-  }
-}
-
-// One shrink work item: rows [rg*RPI, rg*RPI+RPI) of s for every real pair of block blk.
-template <bool BF16, int LPR, bool COHERENT>
-__device__ __forceinline__ void shrink_item(const DeltaArgs& a, int blk, int rg, int* pid) {
-  constexpr int RPI = 256 / LPR;
-  const int tid = threadIdx.x;
-  const int lr = tid % LPR;
-  const int row = rg * RPI + tid / LPR;
-  const int e = a.expert_ids[blk];
   for (int j0 = 0; j0 < a.BM; j0 += kPidSlots) {
+    const int pv = j0 == 0 ? pv0 : (tid < kPidSlots ? load_pid(a, blk, j0) : 0);
+    uint4 av[kSeg];
+    load_a_seg<BF16, LPR>(arow, row_ok, 0, nvec, av);  // weights go out with the ids
     __syncthreads();
-    stage_pids(a, blk, j0, kPidSlots, pid);
+    publish_pids(a, pv, pid, nreal);
     __syncthreads();
-    for (int q0 = 0; q0 < kPidSlots; q0 += kPG) {
-      int p[kPG];
-#pragma unroll
-      for (int i = 0; i < kPG; ++i) p[i] = pid[q0 + i];
-      if (!real_pair(p[0], a.numel)) return;  // real entries are a prefix of the block
+    const int nr = *nreal;
+    for (int q0 = 0; q0 < nr; q0 += kPG) {
       float acc[kPG];
-      shrink_rows<BF16, LPR>(a, e, rg, p, acc);
-      if (lr == 0 && row < a.R) {
+#pragma unroll
+      for (int i = 0; i < kPG; ++i) acc[i] = 0.f;
+      for (int m0 = 0; m0 < vpl; m0 += kSeg) {
+        if (m0 > 0 || q0 > 0) load_a_seg<BF16, LPR>(arow, row_ok, m0, nvec, av);
+        uint4 xv[XPT];
+#pragma unroll
+        for (int t = 0; t < XPT; ++t) {
+          const int i = tid + t * kThreads;
+          const int q = i / SEGV;
+          const int v = m0 * LPR + (i - q * SEGV);
+          const int pq = pid[q0 + q];
+          const bool ok = q0 + q < nr && v < nvec;
+          xv[t] = ld16_if(xbase, (int64_t)(ok ? pq / a.row_div : 0) * xstride + (int64_t)v * 16, ok);
+        }
+        __syncthreads();  // earlier readers of xs are done
+#pragma unroll
+        for (int t = 0; t < XPT; ++t) xs[tid + t * kThreads] = xv[t];
+        __syncthreads();
 #pragma unroll
         for (int i = 0; i < kPG; ++i) {
-          if (!real_pair(p[i], a.numel)) continue;
-          float* d = a.s + (int64_t)p[i] * a.R + row;
+          if (q0 + i >= nr) break;
+#pragma unroll
+          for (int sg = 0; sg < kSeg; ++sg) {
+            const int v = lr + (m0 + sg) * LPR;
+            if (v < nvec) acc[i] = dot16<BF16>(av[sg], xs[i * SEGV + sg * LPR + lr], acc[i]);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kPG; ++i) {
+#pragma unroll
+        for (int off = LPR / 2; off > 0; off >>= 1) acc[i] += __shfl_xor(acc[i], off, 64);
+      }
+      if (lr == 0 && row_ok) {
+#pragma unroll
+        for (int i = 0; i < kPG; ++i) {
+          if (q0 + i >= nr) break;
+          float* d = a.s + (int64_t)pid[q0 + i] * a.R + row;
           if constexpr (COHERENT) st_coherent(d, acc[i]); else *d = acc[i];
         }
       }
     }
+    if (nr < kPidSlots) return;  // the block's real entries ended in this pass
   }
 }
 
-// s rows of the pairs pid[0..pg) into s_lds [pg][R], read from a.s.
-template <bool COHERENT>
-__device__ __forceinline__ void load_s_rows(const DeltaArgs& a, const int* pid, int pg,
-                                            float* s_lds) {
-  const int R = a.R;
-  for (int i = threadIdx.x; i < pg * R; i += blockDim.x) {
-    const int q = i / R, c = i - q * R;
-    const int p = pid[q];
-    float v = 0.f;
-    if (real_pair(p, a.numel)) {
-      const float* src = a.s + (int64_t)p * R + c;
-      v = COHERENT ? ld_coherent(src) : *src;
-    }
-    s_lds[i] = v;
-  }
-}
-
-// s rows of the pairs pid[0..pg) into s_lds [pg][R], computed here with exactly the
-// arithmetic of the shrink items (used when they are not done in time).
+// The shrink sum of one row (lane group) for one pair, read straight from global memory
+// one vector at a time: few registers, and the same sums as shrink_item.
 template <bool BF16, int LPR>
-__device__ __forceinline__ void compute_s_rows(const DeltaArgs& a, int e, const int* pid, int pg,
+__device__ __forceinline__ float shrink_one(const DeltaArgs& a, int e, int row, int p) {
+  constexpr int ESZ = BF16 ? 2 : 4;
+  const int lr = threadIdx.x % LPR;
+  const bool row_ok = row < a.R;
+  const int nvec = a.K * ESZ / 16;
+  const char* arow =
+      (const char*)a.A + ((int64_t)e * a.R + (row_ok ? row : 0)) * (int64_t)a.K * ESZ;
+  const char* xr = (const char*)a.xin + (int64_t)(p / a.row_div) * a.ld_x * ESZ;
+  float acc = 0.f;
+  for (int v = lr; v < nvec; v += LPR)
+    acc = dot16<BF16>(ld16_if(arow, (int64_t)v * 16, row_ok), ld16(xr + (int64_t)v * 16), acc);
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  return acc;
+}
+
+// s rows of the pairs pid[0..nr) into s_lds [nr][R], computed here with the arithmetic of
+// the shrink items (used when they are not done in time).
+template <bool BF16, int LPR>
+__device__ __forceinline__ void compute_s_rows(const DeltaArgs& a, int e, const int* pid, int nr,
                                                float* s_lds) {
-  constexpr int RPI = 256 / LPR;
-  const int tid = threadIdx.x;
-  const int lr = tid % LPR;
+  constexpr int RPI = kThreads / LPR;
+  const int lr = threadIdx.x % LPR;
   for (int rg = 0; rg < a.rgroups; ++rg) {
-    const int row = rg * RPI + tid / LPR;
-    for (int q = 0; q < pg; ++q) {
-      const int p = pid[q];
-      if (!real_pair(p, a.numel)) break;
-      float acc;
-      shrink_rows<BF16, LPR, 1, 1>(a, e, rg, &p, &acc);  // light on registers, same sums
+    const int row = rg * RPI + threadIdx.x / LPR;
+    for (int q = 0; q < nr; ++q) {
+      const float acc = shrink_one<BF16, LPR>(a, e, row, pid[q]);
       if (lr == 0 && row < a.R) s_lds[q * a.R + row] = acc;
     }
   }
 }
 
-// out[p, n] += for the pairs pid[0..pg) of this pass, s rows staged in s_lds [pg][R].
-template <bool BF16, int RV>
-__device__ __forceinline__ void expand_outputs(const DeltaArgs& a, const uint4* bv, const int* pid,
-                                               int pg, const float* s_lds, int n, int soff,
-                                               float sc) {
-  constexpr int VE = BF16 ? 8 : 4;
-  if (n >= a.N) return;
-  for (int q = 0; q < pg; ++q) {
-    const int p = pid[q];
-    if (!real_pair(p, a.numel)) break;
-    const float* sv = s_lds + q * a.R + soff;
-    float acc = 0.f;
+// ------------------------------------------------------------------------------ expand
+
+// s rows of the pairs pid[0..nr) into s_lds [nr][R] (nr * R <= kSLdsFloats), read from
+// a.s four loads per thread at a time.
+template <bool COHERENT>
+__device__ __forceinline__ void load_s_rows(const DeltaArgs& a, const int* pid, int nr,
+                                            float* s_lds) {
+  const int R = a.R;
+  const int total = nr * R;
+  for (int base = 0; base < total; base += 4 * kThreads) {
+    float v[4];
 #pragma unroll
-    for (int v = 0; v < RV; ++v) acc = dot16_s<BF16>(bv[v], sv + v * VE, acc);
-    if constexpr (BF16) {
-      uint16_t* o = (uint16_t*)a.out + (int64_t)p * a.ld_out + n;
-      const float old = __uint_as_float((uint32_t)*o << 16);
-      *o = f32_to_bf16_rne(fmaf(sc, acc, old));
-    } else {
-      float* o = (float*)a.out + (int64_t)p * a.ld_out + n;
-      *o = fmaf(sc, acc, *o);
+    for (int t = 0; t < 4; ++t) {
+      const int i = base + t * kThreads + threadIdx.x;
+      const bool ok = i < total;
+      const int q = ok ? i / R : 0;
+      const float* src = a.s + (int64_t)pid[q] * R + (ok ? i - q * R : 0);
+      v[t] = COHERENT ? ld_coherent(src) : *src;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int i = base + t * kThreads + threadIdx.x;
+      if (i < total) s_lds[i] = v[t];
     }
   }
 }
 
-template <bool BF16, int RV>
-__device__ __forceinline__ void load_b_row(const DeltaArgs& a, int e, int n, uint4* bv) {
+template <bool BF16, int RV, int CPT>
+__device__ __forceinline__ void load_b_rows(const DeltaArgs& a, int e, const int* n,
+                                            uint4 (*bv)[RV]) {
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int r = RV * 16 / ESZ;
-  const bool n_ok = n < a.N;
-  const char* brow = (const char*)a.B + ((int64_t)e * a.N + (n_ok ? n : 0)) * (int64_t)(r * ESZ);
+  const char* bexp = (const char*)a.B + (int64_t)e * a.N * (int64_t)(r * ESZ);
 #pragma unroll
-  for (int v = 0; v < RV; ++v) bv[v] = n_ok ? ld16(brow + v * 16) : make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < CPT; ++j) {
+    const bool ok = n[j] < a.N;
+#pragma unroll
+    for (int v = 0; v < RV; ++v)
+      bv[j][v] = ld16_if(bexp, (int64_t)n[j] * (r * ESZ) + v * 16, ok);
+  }
 }
 
-// One expand work item: columns [chunk*256, chunk*256+256) for every real pair of block
-// blk. FUSED: s comes from this launch's shrink items (or is computed here, see above).
+template <bool BF16>
+__device__ __forceinline__ float load_out(const DeltaArgs& a, int p, int n, bool ok) {
+  const int64_t i = ok ? (int64_t)p * a.ld_out + n : 0;
+  float v;
+  if constexpr (BF16)
+    v = __uint_as_float((uint32_t)((const uint16_t*)a.out)[i] << 16);
+  else
+    v = ((const float*)a.out)[i];
+  return ok ? v : 0.f;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_out(const DeltaArgs& a, int p, int n, float v) {
+  if constexpr (BF16)
+    ((uint16_t*)a.out)[(int64_t)p * a.ld_out + n] = f32_to_bf16_rne(v);
+  else
+    ((float*)a.out)[(int64_t)p * a.ld_out + n] = v;
+}
+
+// out[p, n] = round(out[p, n] + sc * <B_v[n], s_p[slice(n)]>) for this pass's pairs; the
+// old values of the first kPG pairs were loaded ahead into ov.
+template <bool BF16, int RV, int CPT>
+__device__ __forceinline__ void expand_outputs(const DeltaArgs& a, const uint4 (*bv)[RV],
+                                               const int* pid, int nr, const float* s_lds,
+                                               const int* n, const int* soff, float sc,
+                                               const float (*ov)[CPT]) {
+  constexpr int VE = BF16 ? 8 : 4;
+#pragma unroll 1
+  for (int q = 0; q < nr; ++q) {
+    const int p = pid[q];
+    const float* s_row = s_lds + q * a.R;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      if (n[j] >= a.N) continue;
+      const float* sv = s_row + soff[j];
+      float acc = 0.f;
+#pragma unroll
+      for (int v = 0; v < RV; ++v) {
+        // keep the weights packed across pairs: unpacking them once for all pairs would
+        // hold RV*8 more floats per column live, for no gain at one or two pairs a block
+        uint4 b = bv[j][v];
+        asm volatile("" : "+v"(b.x), "+v"(b.y), "+v"(b.z), "+v"(b.w));
+        acc = dot16_s<BF16>(b, sv + v * VE, acc);
+      }
+      float old;
+      if (q < kPG) {
+        old = q == 0 ? ov[0][j] : q == 1 ? ov[1][j] : q == 2 ? ov[2][j] : ov[3][j];
+      } else {
+        old = load_out<BF16>(a, p, n[j], true);
+      }
+      store_out<BF16>(a, p, n[j], fmaf(sc, acc, old));
+    }
+  }
+}
+
+// One expand work item: CPT*256 output columns for every real pair of block blk.
+// FUSED: s comes from this launch's shrink items (or is computed here, see above).
 template <bool BF16, int LPR, int RV, bool FUSED>
-__device__ __forceinline__ void expand_item(const DeltaArgs& a, int blk, int chunk, int* pid,
-                                            float* s_lds, int* flag) {
+__device__ __forceinline__ void expand_item(const DeltaArgs& a, int blk, int chunk, int e,
+                                            int pv0, int* pid, int* nreal, float* s_lds,
+                                            int* flag) {
+  constexpr int CPT = cols_per_thread(RV);
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int r = RV * 16 / ESZ;
   const int tid = threadIdx.x;
-  const int n = chunk * kExpandCols + tid;
-  const int e = a.expert_ids[blk];
   const int width = a.N / a.slices;
-  const int soff = (n < a.N ? n / width : 0) * r;
-  const float sc = a.scale[e / a.E];
   const int pg = min(kPidSlots, kSLdsFloats / a.R);
-  uint4 bv[RV];
-  load_b_row<BF16, RV>(a, e, n, bv);  // weights first: they do not depend on s
+  int n[CPT], soff[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    n[j] = chunk * (CPT * kThreads) + j * kThreads + tid;
+    soff[j] = (n[j] < a.N ? n[j] / width : 0) * r;
+  }
+  const float sc = a.scale[e / a.E];
+  int pv = tid < pg ? pv0 : a.numel;
+  uint4 bv[CPT][RV];
+  load_b_rows<BF16, RV, CPT>(a, e, n, bv);  // the weights go out with the first ids
   bool ready = true;
-  if constexpr (FUSED) {
-    if (tid == 0) {
-      int ok = 0;
-      for (int it = 0; it < a.spin_limit; ++it) {
-        const int w = __hip_atomic_load(a.sync + blk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((w & 0xffff) >= a.rgroups) {
-          ok = 1;
-          break;
+  for (int j0 = 0; j0 < a.BM; j0 += pg) {
+    if (j0 > 0) pv = tid < pg ? load_pid(a, blk, j0) : a.numel;
+    if (tid >= pg) pv = a.numel;
+    __syncthreads();
+    publish_pids(a, pv, pid, nreal);
+    if constexpr (FUSED) {
+      if (j0 == 0 && tid == 0) {
+        int ok = 0;
+        for (int it = 0; it < a.spin_limit; ++it) {
+          const int w =
+              __hip_atomic_load(a.sync + blk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((w & 0xffff) >= a.rgroups) {
+            ok = 1;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
         }
-        __builtin_amdgcn_s_sleep(2);
+        *flag = ok;
       }
-      *flag = ok;
     }
     __syncthreads();
-    ready = *flag != 0;
-  }
-  if (ready) {
-    for (int j0 = 0; j0 < a.BM; j0 += pg) {
-      __syncthreads();
-      stage_pids(a, blk, j0, pg, pid);
-      __syncthreads();
-      if (!real_pair(pid[0], a.numel)) break;
-      load_s_rows<FUSED>(a, pid, pg, s_lds);
-      __syncthreads();
-      expand_outputs<BF16, RV>(a, bv, pid, pg, s_lds, n, soff, sc);
+    const int nr = *nreal;
+    if (nr == 0) break;
+    if constexpr (FUSED) ready = *flag != 0;
+    float ov[kPG][CPT];  // old out values of the first pairs, loaded before s is needed
+#pragma unroll
+    for (int q = 0; q < kPG; ++q) {
+      const int p = pid[q];
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) ov[q][j] = load_out<BF16>(a, p, n[j], q < nr && n[j] < a.N);
     }
-  } else if constexpr (FUSED) {
-    for (int j0 = 0; j0 < a.BM; j0 += pg) {
-      __syncthreads();
-      stage_pids(a, blk, j0, pg, pid);
-      __syncthreads();
-      if (!real_pair(pid[0], a.numel)) break;
-      compute_s_rows<BF16, LPR>(a, e, pid, pg, s_lds);
-      __syncthreads();
-      uint4 bw[RV];
-      load_b_row<BF16, RV>(a, e, n, bw);
-      expand_outputs<BF16, RV>(a, bw, pid, pg, s_lds, n, soff, sc);
+    if (ready) {
+      load_s_rows<FUSED>(a, pid, nr, s_lds);
+    } else if constexpr (FUSED) {
+      compute_s_rows<BF16, LPR>(a, e, pid, nr, s_lds);
     }
+    __syncthreads();
+    expand_outputs<BF16, RV, CPT>(a, bv, pid, nr, s_lds, n, soff, sc, ov);
+    if (nr < pg) break;  // the block's real entries ended in this pass
   }
 }
 
@@ -342,37 +451,51 @@ __device__ __forceinline__ void arrive(const DeltaArgs& a, int blk, int inc) {
     __hip_atomic_store(a.sync + blk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+template <int LPR>
+struct ShrinkLds {
+  static constexpr int kVecs = kPG * kSeg * LPR;
+};
+
 template <bool BF16, int LPR>
-__global__ void __launch_bounds__(256) shrink_kernel(DeltaArgs a) {
+__global__ void __launch_bounds__(kThreads) shrink_kernel(DeltaArgs a) {
   __shared__ int pid[kPidSlots];
+  __shared__ int nreal;
+  __shared__ uint4 xs[ShrinkLds<LPR>::kVecs];
   const int blk = blockIdx.x / a.rgroups, rg = blockIdx.x % a.rgroups;
-  if (blk >= live_blocks(a)) return;
-  if (!real_expert(a.expert_ids[blk], a.V)) return;
-  shrink_item<BF16, LPR, false>(a, blk, rg, pid);
+  const int pv0 = threadIdx.x < kPidSlots ? load_pid(a, blk, 0) : 0;  // with the expert id
+  const int e = block_expert(a, blk);
+  if (e < 0) return;
+  shrink_item<BF16, LPR, false>(a, blk, rg, e, pv0, pid, &nreal, xs);
 }
 
 template <bool BF16, int RV>
-__global__ void __launch_bounds__(256) expand_kernel(DeltaArgs a) {
+__global__ void __launch_bounds__(kThreads) expand_kernel(DeltaArgs a) {
   __shared__ int pid[kPidSlots];
+  __shared__ int nreal;
   __shared__ float s_lds[kSLdsFloats];
   const int blk = blockIdx.x / a.nchunk, c = blockIdx.x % a.nchunk;
-  if (blk >= live_blocks(a)) return;
-  if (!real_expert(a.expert_ids[blk], a.V)) return;
-  expand_item<BF16, 64, RV, false>(a, blk, c, pid, s_lds, nullptr);
+  const int pv0 = threadIdx.x < kPidSlots ? load_pid(a, blk, 0) : 0;
+  const int e = block_expert(a, blk);
+  if (e < 0) return;
+  expand_item<BF16, 64, RV, false>(a, blk, c, e, pv0, pid, &nreal, s_lds, nullptr);
 }
 
 template <bool BF16, int LPR, int RV>
-__global__ void __launch_bounds__(256) delta_fused_kernel(DeltaArgs a) {
+__global__ void __launch_bounds__(kThreads) delta_fused_kernel(DeltaArgs a) {
+  constexpr int kXsBytes = ShrinkLds<LPR>::kVecs * 16;
+  constexpr int kSBytes = kSLdsFloats * 4;
   __shared__ int pid[kPidSlots];
-  __shared__ float s_lds[kSLdsFloats];
+  __shared__ int nreal;
   __shared__ int flag;
-  const int nb = live_blocks(a);
+  __shared__ uint4 smem[(kXsBytes > kSBytes ? kXsBytes : kSBytes) / 16];  // xs or s rows
   const int nshrink = a.max_blocks * a.rgroups;
   const int bid = blockIdx.x;
   if (bid < nshrink) {
     const int blk = bid / a.rgroups, rg = bid % a.rgroups;
-    if (blk >= nb || !real_expert(a.expert_ids[blk], a.V)) return;
-    shrink_item<BF16, LPR, true>(a, blk, rg, pid);
+    const int pv0 = threadIdx.x < kPidSlots ? load_pid(a, blk, 0) : 0;
+    const int e = block_expert(a, blk);
+    if (e < 0) return;
+    shrink_item<BF16, LPR, true>(a, blk, rg, e, pv0, pid, &nreal, smem);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's s stores have completed
     __syncthreads();
     if (threadIdx.x == 0) arrive(a, blk, 1);
@@ -380,8 +503,11 @@ __global__ void __launch_bounds__(256) delta_fused_kernel(DeltaArgs a) {
   }
   const int u = bid - nshrink;
   const int blk = u / a.nchunk, c = u % a.nchunk;
-  if (blk >= nb || !real_expert(a.expert_ids[blk], a.V)) return;
-  expand_item<BF16, LPR, RV, true>(a, blk, c, pid, s_lds, &flag);
+  const int pv0 = threadIdx.x < kPidSlots ? load_pid(a, blk, 0) : 0;
+  const int e = block_expert(a, blk);
+  if (e < 0) return;
+  expand_item<BF16, LPR, RV, true>(a, blk, c, e, pv0, pid, &nreal,
+                                   reinterpret_cast<float*>(smem), &flag);
   __syncthreads();
   if (threadIdx.x == 0) arrive(a, blk, 1 << 16);
 }
@@ -440,6 +566,11 @@ int rank_vectors(const DeltaArgs& a, bool bf16) {
 }
 
 }  // namespace
+
+int expand_cols_per_item(int32_t R, int32_t slices, int elem_bytes) {
+  const int rv = (R / slices) * elem_bytes / 16;
+  return cols_per_thread(rv) * kThreads;
+}
 
 int shrink_rows_per_item(int32_t K, int elem_bytes) {
   const int64_t row_bytes = (int64_t)K * elem_bytes;

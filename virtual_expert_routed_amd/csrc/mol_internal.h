@@ -9,7 +9,6 @@ namespace mol {
 constexpr int kMaxBuckets = 8192;     // V + 1 <= 8192
 constexpr int kAlignSmallMax = 4096;  // pairs the one-workgroup align handles
 constexpr int kAlignTile = 2048;      // pairs per tile of the three-kernel align
-constexpr int kExpandCols = 256;      // output columns per expand work item
 constexpr int kShrinkItemBytes = 32768;  // target weight bytes per shrink work item
 
 struct AlignArgs {
@@ -71,6 +70,8 @@ hipError_t launch_align_large(const AlignArgs& a, hipStream_t stream);
 
 // rows per shrink item (power of two in [4, 32]) for contraction length K
 int shrink_rows_per_item(int32_t K, int elem_bytes);
+// output columns per expand item for rank R / slices
+int expand_cols_per_item(int32_t R, int32_t slices, int elem_bytes);
 
 hipError_t launch_shrink(const DeltaArgs& a, bool bf16, int rows_per_item, int grid,
                          hipStream_t stream);
