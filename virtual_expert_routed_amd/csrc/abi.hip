@@ -2,6 +2,7 @@
 // Every check happens before any HIP call, so argument errors never touch the device.
 #include "../../include/mol.h"
 
+#include <algorithm>
 #include <atomic>
 #include <limits>
 
@@ -82,6 +83,7 @@ mol_status shrink_check(int32_t dtype, const void* xin, int64_t ld_x, int32_t ro
   const int esz = dtype == MOL_BF16 ? 2 : 4;
   if (((int64_t)K * esz) % 16 || (ld_x * esz) % 16) return MOL_E_ALIGN;
   if (numel > 0 && (!aligned16(xin) || !aligned16(A))) return MOL_E_ALIGN;
+  if ((int64_t)R * K * esz >= (int64_t(1) << 31)) return MOL_E_LIMIT;  // one expert's A
   return MOL_OK;
 }
 
@@ -97,6 +99,7 @@ mol_status expand_check(int32_t dtype, int32_t R, int32_t slices, const void* B,
   const int64_t rbytes = (int64_t)(R / slices) * esz;
   if (rbytes % 16) return MOL_E_ALIGN;
   if (rbytes > MOL_MAX_RANK_BYTES || R > 1024) return MOL_E_LIMIT;
+  if ((int64_t)N * rbytes >= (int64_t(1) << 31)) return MOL_E_LIMIT;  // one expert's B
   if (numel > 0 && (!aligned16(B) || (reinterpret_cast<uintptr_t>(out) % esz)))
     return MOL_E_ALIGN;
   return MOL_OK;
@@ -215,7 +218,7 @@ MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_
     // counter rows + scan scratch + per pair a bucket id and a rank (uint16 each)
     const int64_t fixed = 64 * (int64_t)sizeof(int) + ((numel + 1) & ~1LL) * 2 * 2;
     int64_t waves = (device_lds_bytes() - fixed) / ((int64_t)nb * (int64_t)sizeof(int));
-    const int64_t useful = cdiv64(numel, 64);  // one chunk of 64 pairs per wave at least
+    const int64_t useful = cdiv64(numel, 128);  // two chunks of 64 pairs per wave at least
     if (waves > useful) waves = useful;
     if (waves > 16) waves = 16;
     if (waves < 1) waves = 1;
@@ -324,14 +327,18 @@ MOL_API mol_status mol_lora_delta(int32_t dtype, const void* xin, int64_t ld_x,
                                      num_experts, sorted_ids, expert_ids, num_post_padded,
                                      numel, num_virtual, block_m, s, out, ld_out,
                                      rc.max_blocks);
+  // one workgroup per (block, part): rgroups parts also shrink; every part expands cpp
+  // columns
   a.rgroups = (int32_t)cdiv64(R, rpi);
-  a.nchunk = (int32_t)cdiv64(N, mol::expand_cols_per_item(R, slices, bf16 ? 2 : 4));
+  const int64_t parts = std::max<int64_t>(a.rgroups, cdiv64(N, mol::kFusedMaxCols));
+  a.nchunk = (int32_t)parts;
+  a.cpp = (int32_t)cdiv64(N, parts);
   a.sync = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
                                       round256((int64_t)numel * R * (int64_t)sizeof(float)));
   a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   // block counters pack both participant counts in 16 bits each
   if (a.rgroups >= 0x8000 || a.nchunk >= 0x8000) return MOL_E_LIMIT;
-  const int64_t grid = rc.max_blocks * (a.rgroups + (int64_t)a.nchunk);
+  const int64_t grid = rc.max_blocks * (int64_t)a.nchunk;
   if (grid > kI32Max) return MOL_E_LIMIT;
   return hip_status(mol::launch_delta(a, bf16, rpi, (int)grid, (hipStream_t)stream));
 }

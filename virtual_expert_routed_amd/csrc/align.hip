@@ -87,27 +87,30 @@ __device__ __forceinline__ void scatter_walk(const AlignArgs& a, int begin, int 
   }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts of 1, 2, 4, 8 inside
+// each row of 16 lanes, then the row broadcasts of lane 15 and lane 31 carry the row
+// totals into the rows above. Lanes with no source lane take 0.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
 // Exclusive prefix sum of one int per thread over the workgroup (<= 16 waves).
 // `sh` is >= 33 ints of LDS; *total gets the sum over all threads.
 __device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int t = __shfl_up(inc, d, 64);
-    if (lane >= d) inc += t;
-  }
+  const int inc = wave_incl_scan(v);
   if (lane == 63) sh[wid] = inc;
   __syncthreads();
   if (wid == 0) {
     const int w = lane < nw ? sh[lane] : 0;
-    int winc = w;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int t = __shfl_up(winc, d, 64);
-      if (lane >= d) winc += t;
-    }
+    const int winc = wave_incl_scan(w);
     if (lane < nw) sh[16 + lane] = winc - w;
     if (lane == 63) sh[32] = winc;
   }
@@ -227,9 +230,12 @@ __global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a, int wave
   const int b0 = min(NB, tid * bpt), b1 = min(NB, b0 + bpt);
   int mine = 0;
   for (int b = b0; b < b1; ++b) {
-    int c = 0;
-    for (int w = 0; w < waves; ++w) c += table[w * NB + b];
-    mine += round_up(c, a.BM);
+    int c[4] = {0, 0, 0, 0};
+    for (int w = 0; w < waves; w += 4) {  // independent reads, summed in a fixed order
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] += (w + i < waves) ? table[(w + i) * NB + b] : 0;
+    }
+    mine += round_up((c[0] + c[1]) + (c[2] + c[3]), a.BM);
   }
   int total;
   int off = block_excl_scan(mine, sh, &total);
@@ -271,8 +277,8 @@ __global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a, int wave
     while (todo) {
       const int src = __builtin_ctzll(todo);
       todo &= todo - 1;
-      const int from = __shfl(pad_from[k], src, 64);
-      const int cnt = __shfl(pad_cnt[k], src, 64);
+      const int from = __builtin_amdgcn_readlane(pad_from[k], src);
+      const int cnt = __builtin_amdgcn_readlane(pad_cnt[k], src);
       for (int j = lane; j < cnt; j += 64) a.sorted[from + j] = numel;
     }
   }

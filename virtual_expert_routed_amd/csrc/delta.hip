@@ -134,6 +134,21 @@ __device__ __forceinline__ uint4 ld16_if(const char* base, int64_t off, bool ok)
   return ok ? v : make_uint4(0, 0, 0, 0);
 }
 
+// Raw buffer loads over one expert's weight matrix: the resource covers exactly that
+// matrix, offsets are 32-bit, and an offset past its end reads as zero in hardware, so
+// masked lanes need neither a branch nor a select nor a 64-bit address of their own.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kBufferFlags = 0x00020000;  // raw 32-bit-element buffer, gfx9 data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t expert_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferFlags);
+}
+
+__device__ __forceinline__ uint4 buf16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return *reinterpret_cast<const uint4*>(&v);
+}
+
 // Entry j0 + lane of block blk for the lanes of wave 0 (numel for entries past the block).
 __device__ __forceinline__ int load_pid(const DeltaArgs& a, int blk, int j0) {
   const int j = j0 + (int)threadIdx.x;
@@ -157,14 +172,15 @@ __device__ __forceinline__ void publish_pids(const DeltaArgs& a, int pv, int* pi
 // pairs (kPG) are processed together, which is what lets the fallback path below
 // reproduce the shrink items bit for bit.
 
-template <bool BF16, int LPR>
-__device__ __forceinline__ void load_a_seg(const char* arow, bool row_ok, int m0, int nvec,
-                                           uint4* av) {
+// The kSeg vectors of one segment of this lane's row of A_e (zero past the row or matrix).
+template <int LPR>
+__device__ __forceinline__ void load_a_seg(__amdgpu_buffer_rsrc_t ra, uint32_t row_off, bool row_ok,
+                                           int m0, int nvec, uint4* av) {
   const int lr = threadIdx.x % LPR;
 #pragma unroll
   for (int sg = 0; sg < kSeg; ++sg) {
     const int v = lr + (m0 + sg) * LPR;
-    av[sg] = ld16_if(arow, (int64_t)v * 16, row_ok && v < nvec);
+    av[sg] = buf16(ra, (row_ok && v < nvec) ? row_off + (uint32_t)v * 16u : kOutOfRange);
   }
 }
 
@@ -184,14 +200,15 @@ __device__ __forceinline__ void shrink_item(const DeltaArgs& a, int blk, int rg,
   const bool row_ok = row < a.R;
   const int nvec = a.K * ESZ / 16;
   const int vpl = (nvec + LPR - 1) / LPR;
-  const char* arow =
-      (const char*)a.A + ((int64_t)e * a.R + (row_ok ? row : 0)) * (int64_t)a.K * ESZ;
+  const int64_t abytes = (int64_t)a.R * a.K * ESZ;
+  const __amdgpu_buffer_rsrc_t ra = expert_rsrc((const char*)a.A + (int64_t)e * abytes, abytes);
+  const uint32_t row_off = (uint32_t)(row_ok ? row : 0) * (uint32_t)(a.K * ESZ);
   const char* xbase = (const char*)a.xin;
   const int64_t xstride = a.ld_x * ESZ;
   for (int j0 = 0; j0 < a.BM; j0 += kPidSlots) {
     const int pv = j0 == 0 ? pv0 : (tid < kPidSlots ? load_pid(a, blk, j0) : 0);
     uint4 av[kSeg];
-    load_a_seg<BF16, LPR>(arow, row_ok, 0, nvec, av);  // weights go out with the ids
+    load_a_seg<LPR>(ra, row_off, row_ok, 0, nvec, av);  // weights go out with the ids
     __syncthreads();
     publish_pids(a, pv, pid, nreal);
     __syncthreads();
@@ -201,7 +218,7 @@ __device__ __forceinline__ void shrink_item(const DeltaArgs& a, int blk, int rg,
 #pragma unroll
       for (int i = 0; i < kPG; ++i) acc[i] = 0.f;
       for (int m0 = 0; m0 < vpl; m0 += kSeg) {
-        if (m0 > 0 || q0 > 0) load_a_seg<BF16, LPR>(arow, row_ok, m0, nvec, av);
+        if (m0 > 0 || q0 > 0) load_a_seg<LPR>(ra, row_off, row_ok, m0, nvec, av);
         uint4 xv[XPT];
 #pragma unroll
         for (int t = 0; t < XPT; ++t) {
@@ -310,15 +327,17 @@ template <bool BF16, int RV, int CPT>
 __device__ __forceinline__ void load_b_rows(const DeltaArgs& a, int e, const int* n,
                                             uint4 (*bv)[RV]) {
   constexpr int ESZ = BF16 ? 2 : 4;
-  constexpr int r = RV * 16 / ESZ;
-  const char* bexp = (const char*)a.B + (int64_t)e * a.N * (int64_t)(r * ESZ);
+  constexpr int RB = RV * 16;  // bytes of one weight row
+  const int64_t bbytes = (int64_t)a.N * RB;
+  const __amdgpu_buffer_rsrc_t rb = expert_rsrc((const char*)a.B + (int64_t)e * bbytes, bbytes);
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
     const bool ok = n[j] < a.N;
 #pragma unroll
     for (int v = 0; v < RV; ++v)
-      bv[j][v] = ld16_if(bexp, (int64_t)n[j] * (r * ESZ) + v * 16, ok);
+      bv[j][v] = buf16(rb, ok ? (uint32_t)n[j] * RB + v * 16 : kOutOfRange);
   }
+  (void)ESZ;
 }
 
 template <bool BF16>
@@ -480,36 +499,81 @@ __global__ void __launch_bounds__(kThreads) expand_kernel(DeltaArgs a) {
   expand_item<BF16, 64, RV, false>(a, blk, c, e, pv0, pid, &nreal, s_lds, nullptr);
 }
 
+// Fused delta: block blk is served by a.nchunk consecutive workgroups (parts). Part g
+// issues the weight loads of its a.cpp expand columns first, computes shrink row group g
+// when g < a.rgroups and publishes it, then waits for the block's other row groups and
+// expands its own columns. Parts of one block are adjacent in the grid, so they run side
+// by side; no part waits for a workgroup later in the grid, and the bounded wait falls
+// back to computing s in place (same sums) if the others are late.
 template <bool BF16, int LPR, int RV>
 __global__ void __launch_bounds__(kThreads) delta_fused_kernel(DeltaArgs a) {
   constexpr int kXsBytes = ShrinkLds<LPR>::kVecs * 16;
   constexpr int kSBytes = kSLdsFloats * 4;
+  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int VE = 16 / ESZ;
+  constexpr int r = RV * VE;
   __shared__ int pid[kPidSlots];
   __shared__ int nreal;
   __shared__ int flag;
   __shared__ uint4 smem[(kXsBytes > kSBytes ? kXsBytes : kSBytes) / 16];  // xs or s rows
-  const int nshrink = a.max_blocks * a.rgroups;
-  const int bid = blockIdx.x;
-  if (bid < nshrink) {
-    const int blk = bid / a.rgroups, rg = bid % a.rgroups;
-    const int pv0 = threadIdx.x < kPidSlots ? load_pid(a, blk, 0) : 0;
-    const int e = block_expert(a, blk);
-    if (e < 0) return;
-    shrink_item<BF16, LPR, true>(a, blk, rg, e, pv0, pid, &nreal, smem);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's s stores have completed
-    __syncthreads();
-    if (threadIdx.x == 0) arrive(a, blk, 1);
-    return;
-  }
-  const int u = bid - nshrink;
-  const int blk = u / a.nchunk, c = u % a.nchunk;
-  const int pv0 = threadIdx.x < kPidSlots ? load_pid(a, blk, 0) : 0;
+  float* s_lds = reinterpret_cast<float*>(smem);
+  const int tid = threadIdx.x;
+  const int blk = blockIdx.x / a.nchunk, g = blockIdx.x % a.nchunk;
+  const int pv0 = tid < kPidSlots ? load_pid(a, blk, 0) : 0;  // with the expert id
   const int e = block_expert(a, blk);
   if (e < 0) return;
-  expand_item<BF16, LPR, RV, true>(a, blk, c, e, pv0, pid, &nreal,
-                                   reinterpret_cast<float*>(smem), &flag);
+  // this thread's expand column; its weights go out first
+  const int n = g * a.cpp + tid;
+  const bool n_ok = tid < a.cpp && n < a.N;
+  int nc[1] = {n_ok ? n : a.N};
+  uint4 bv[1][RV];
+  load_b_rows<BF16, RV, 1>(a, e, nc, bv);
+  const int soff[1] = {(n_ok ? n / (a.N / a.slices) : 0) * r};
+  const bool shrinker = g < a.rgroups;
+  if (shrinker) {
+    shrink_item<BF16, LPR, true>(a, blk, g, e, pv0, pid, &nreal, smem);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's s stores have completed
+    __syncthreads();
+    if (tid == 0) arrive(a, blk, 1);
+  }
+  const float sc = a.scale[e / a.E];
+  const int pg = min(kPidSlots, kSLdsFloats / a.R);
+  bool ready = true;
+  for (int j0 = 0; j0 < a.BM; j0 += pg) {
+    int pv = j0 == 0 ? pv0 : (tid < pg ? load_pid(a, blk, j0) : a.numel);
+    if (tid >= pg) pv = a.numel;
+    __syncthreads();
+    publish_pids(a, pv, pid, &nreal);
+    if (j0 == 0 && tid == 0) {
+      int ok = 0;
+      for (int it = 0; it < a.spin_limit; ++it) {
+        const int w = __hip_atomic_load(a.sync + blk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((w & 0xffff) >= a.rgroups) {
+          ok = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      flag = ok;
+    }
+    __syncthreads();
+    const int nr = nreal;
+    if (nr == 0) break;
+    ready = flag != 0;
+    float ov[kPG][1];  // old out values of the first pairs, loaded before s is needed
+#pragma unroll
+    for (int q = 0; q < kPG; ++q) ov[q][0] = load_out<BF16>(a, pid[q], nc[0], q < nr && n_ok);
+    if (ready) {
+      load_s_rows<true>(a, pid, nr, s_lds);
+    } else {
+      compute_s_rows<BF16, LPR>(a, e, pid, nr, s_lds);
+    }
+    __syncthreads();
+    expand_outputs<BF16, RV, 1>(a, bv, pid, nr, s_lds, nc, soff, sc, ov);
+    if (nr < pg) break;  // the block's real entries ended in this pass
+  }
   __syncthreads();
-  if (threadIdx.x == 0) arrive(a, blk, 1 << 16);
+  if (tid == 0) arrive(a, blk, 1 << 16);
 }
 
 template <bool BF16>
