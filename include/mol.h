@@ -172,12 +172,12 @@ MOL_API mol_status mol_lora_expand(int32_t dtype, const float *s, int32_t R, int
                                    int64_t ld_out, void *stream);
 
 /* ---------------------------------------------------------------------------------
- * mol_lora_delta - shrink then expand for one stage in ONE launch; s lives in the
- * workspace. Same arguments and results as mol_lora_shrink followed by mol_lora_expand
- * (bit-identical to them).
- *   workspace    device scratch of at least mol_delta_workspace_bytes(); it MUST be
- *                zero-filled before its first use, and every call leaves its counters
- *                zeroed again. Calls that may overlap must not share a workspace.
+ * mol_lora_delta - one stage: shrink then expand, with s kept in the caller's workspace.
+ * Same arguments and results as mol_lora_shrink followed by mol_lora_expand (bit-identical
+ * to them; they are the same kernels, enqueued back to back).
+ *   workspace    device scratch of at least mol_delta_workspace_bytes(), 16-byte aligned;
+ *                no initial contents are required. Calls that may overlap must not share
+ *                a workspace.
  * ------------------------------------------------------------------------------- */
 MOL_API int64_t mol_delta_workspace_bytes(int32_t numel, int32_t R, int32_t num_virtual,
                                           int32_t block_m);
@@ -190,12 +190,6 @@ MOL_API mol_status mol_lora_delta(int32_t dtype, const void *xin, int64_t ld_x,
                                   int32_t num_virtual, int32_t block_m, void *out,
                                   int64_t ld_out, void *workspace, size_t workspace_bytes,
                                   void *stream);
-
-/* (host) Testing and tuning control, process-wide: how many times an expand work item of
- * mol_lora_delta polls for its block's shrink results before computing them itself
- * (the results are bit-identical for every value; only speed changes). 0 makes every
- * expand item compute its own s; a negative value restores the default. */
-MOL_API void mol_set_delta_spin_limit(int32_t polls);
 
 #ifdef __cplusplus
 }

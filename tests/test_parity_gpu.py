@@ -131,11 +131,11 @@ def test_shrink_expand_and_fused_delta_parity(cfg):
                    f"{cfg.name}/{st.name}/out")
         assert np.all(got[case.no_delta] == 0), "rows without a delta were written"
         del got
-        # fused single launch: bit-identical to shrink + expand
+        # one call for the stage: bit-identical to shrink + expand
         unfused = out_u.clone()
         dl.out[si].zero_()
         dl.delta(si)
-        assert torch.equal(dl.out[si], unfused), "fused delta differs from shrink+expand"
+        assert torch.equal(dl.out[si], unfused), "mol_lora_delta differs from shrink+expand"
     torch.cuda.synchronize()
 
 
@@ -233,32 +233,8 @@ def test_empty_batch():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("cfg", [configs.C0, configs.C1, configs.C2], ids=IDS[:3])
-def test_fused_fallback_is_bit_identical(cfg):
-    """With a zero poll budget every expand item computes its block's s itself; the
-    result must not change by a single bit."""
-    case = get_case(cfg)
-    dl = DeviceLayer(case.inp)
-    dl.align()
-    ref = []
-    for si in range(len(cfg.stages)):
-        dl.shrink(si)
-        dl.expand(si)
-        ref.append(dl.out[si].clone())
-        dl.out[si].zero_()
-    try:
-        mb.mol_set_delta_spin_limit(0)
-        for si in range(len(cfg.stages)):
-            dl.delta(si)
-        torch.cuda.synchronize()
-    finally:
-        mb.mol_set_delta_spin_limit(-1)
-    for si in range(len(cfg.stages)):
-        assert torch.equal(dl.out[si], ref[si]), f"{cfg.name} stage {si}"
-
-
 @pytest.mark.parametrize("cfg", [configs.C1, configs.C2], ids=IDS[1:3])
-def test_fused_never_reads_stale_s(cfg):
+def test_delta_never_reads_stale_s(cfg):
     """Poison the workspace's s rows with NaN and feed two different activations through
     the same workspace: a read of s before it is written would show up as NaN or as the
     previous call's values."""

@@ -34,7 +34,6 @@ SIGNATURES = {
     "mol_lora_expand": (_I32, [_I32, _P, _I32, _I32, _P, _I32, _P, _I32, _P, _P, _P, _I32, _I32,
                                _I32, _P, _I64, _P]),
     "mol_delta_workspace_bytes": (_I64, [_I32, _I32, _I32, _I32]),
-    "mol_set_delta_spin_limit": (None, [_I32]),
     "mol_lora_delta": (_I32, [_I32, _P, _I64, _I32, _P, _I32, _I32, _I32, _P, _I32, _P, _I32,
                               _P, _P, _P, _I32, _I32, _I32, _P, _I64, _P, _SZ, _P]),
 }
@@ -199,14 +198,10 @@ def mol_lora_expand(s, slices: int, B, slot_scale, num_experts: int, sorted_ids,
     return out
 
 
-def mol_set_delta_spin_limit(polls: int) -> None:
-    lib().mol_set_delta_spin_limit(int(polls))
-
-
 def new_delta_workspace(numel: int, R: int, num_virtual: int, block_m: int, device):
-    """A zero-filled workspace for mol_lora_delta (zeroed once; calls keep it zeroed)."""
+    """A workspace for mol_lora_delta (its contents need no initialisation)."""
     n = mol_delta_workspace_bytes(numel, R, num_virtual, block_m)
-    return torch.zeros(max(256, n), dtype=torch.uint8, device=device)
+    return torch.empty(max(256, n), dtype=torch.uint8, device=device)
 
 
 def mol_lora_delta(xin, row_div: int, A, slices: int, B, slot_scale, num_experts: int,

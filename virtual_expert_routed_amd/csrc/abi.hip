@@ -16,9 +16,6 @@ int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round256(int64_t a) { return (a + 255) / 256 * 256; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Polls an expand item of the fused delta makes before computing s itself.
-std::atomic<int> g_spin_limit{mol::kDefaultSpinLimit};
-
 // Max dynamic LDS per workgroup, cached per device (only the one-workgroup align asks).
 std::atomic<int> g_lds_bytes[64];
 
@@ -289,12 +286,7 @@ MOL_API int64_t mol_delta_workspace_bytes(int32_t numel, int32_t R, int32_t num_
   const int64_t mb = align_check(numel, num_virtual, block_m);
   if (mb < 0) return mb;
   if (R < 1) return -MOL_E_ARG;
-  return round256((int64_t)numel * R * (int64_t)sizeof(float)) +
-         round256(mb * (int64_t)sizeof(int32_t));
-}
-
-MOL_API void mol_set_delta_spin_limit(int32_t polls) {
-  g_spin_limit.store(polls < 0 ? mol::kDefaultSpinLimit : polls, std::memory_order_relaxed);
+  return round256((int64_t)numel * R * (int64_t)sizeof(float));
 }
 
 MOL_API mol_status mol_lora_delta(int32_t dtype, const void* xin, int64_t ld_x,
@@ -321,26 +313,22 @@ MOL_API mol_status mol_lora_delta(int32_t dtype, const void* xin, int64_t ld_x,
   if (!workspace || workspace_bytes < (size_t)need) return MOL_E_WORKSPACE;
   if (!aligned16(workspace)) return MOL_E_ALIGN;
   const bool bf16 = dtype == MOL_BF16;
-  const int rpi = mol::shrink_rows_per_item(K, bf16 ? 2 : 4);
+  const int esz = bf16 ? 2 : 4;
+  const int rpi = mol::shrink_rows_per_item(K, esz);
   float* s = static_cast<float*>(workspace);
   mol::DeltaArgs a = make_delta_args(xin, ld_x, row_div, A, R, K, slices, B, N, slot_scale,
                                      num_experts, sorted_ids, expert_ids, num_post_padded,
                                      numel, num_virtual, block_m, s, out, ld_out,
                                      rc.max_blocks);
-  // one workgroup per (block, part): rgroups parts also shrink; every part expands cpp
-  // columns
   a.rgroups = (int32_t)cdiv64(R, rpi);
-  const int64_t parts = std::max<int64_t>(a.rgroups, cdiv64(N, mol::kFusedMaxCols));
-  a.nchunk = (int32_t)parts;
-  a.cpp = (int32_t)cdiv64(N, parts);
-  a.sync = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
-                                      round256((int64_t)numel * R * (int64_t)sizeof(float)));
-  a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
-  // block counters pack both participant counts in 16 bits each
-  if (a.rgroups >= 0x8000 || a.nchunk >= 0x8000) return MOL_E_LIMIT;
-  const int64_t grid = rc.max_blocks * (int64_t)a.nchunk;
-  if (grid > kI32Max) return MOL_E_LIMIT;
-  return hip_status(mol::launch_delta(a, bf16, rpi, (int)grid, (hipStream_t)stream));
+  a.nchunk = (int32_t)cdiv64(N, mol::expand_cols_per_item(R, slices, esz));
+  const int64_t grid_s = rc.max_blocks * (int64_t)a.rgroups;
+  const int64_t grid_e = rc.max_blocks * (int64_t)a.nchunk;
+  if (grid_s > kI32Max || grid_e > kI32Max) return MOL_E_LIMIT;
+  const hipStream_t st = (hipStream_t)stream;
+  const hipError_t err = mol::launch_shrink(a, bf16, rpi, (int)grid_s, st);
+  if (err != hipSuccess) return MOL_E_HIP;
+  return hip_status(mol::launch_expand(a, bf16, (int)grid_e, st));
 }
 
 }  // extern "C"

@@ -6,28 +6,29 @@
 //   expand: out[p, n] = round(out[p, n] + scale[v / E] * sum_j B[v, n, j] * s[p, g(n)*r + j])
 //
 // At decode a block holds one to a few pairs, so the work is a gather of many small
-// matrix-vector products and the bound is streaming A_v and B_v from HBM. Work is split
-// so the number of work items follows the real blocks, not padded rows:
-//  * shrink item = (block, group of RPI rows of A_v): the item reads RPI full rows of
-//    A_v (about 32 KiB) once with coalesced 16-byte loads (LPR = 256/RPI lanes per row,
-//    each row's lanes reading consecutive 16-byte vectors), keeps them in registers and
-//    reuses them for up to 4 pairs at a time; the LPR partial sums are combined with a
-//    fixed xor-shuffle tree, so s is bit-reproducible and needs no split-K partials;
-//  * expand item = (block, 256 output columns): one thread per column holds the column's
-//    r weights in registers and loops over the block's pairs, with their s rows staged in
-//    LDS; out is read, added to and rounded once.
+// matrix-vector products bound by streaming A_v and B_v from HBM. On MI355X one
+// workgroup streams at most ~20 GB/s, so the weights of every touched virtual expert are
+// spread over many workgroups and the grid follows the real blocks, not padded rows:
+//  * shrink item = (block, group of RPI rows of A_v): RPI full rows of A_v (about 32 KiB)
+//    read once with coalesced 16-byte buffer loads (LPR = 256/RPI lanes per row, each
+//    row's lanes reading consecutive vectors), held in registers and reused for up to
+//    four pairs at a time. The pairs' x segments go straight into LDS (direct-to-LDS
+//    loads) once per item. The LPR partial sums are combined by a fixed xor tree, so s
+//    is bit-reproducible and needs no split-K partials.
+//  * expand item = (block, CPT*256 output columns): one thread per column holds the
+//    column's r weights in registers; the block's s rows are staged in LDS; out is read,
+//    added to and rounded once.
+// Latency chains are kept short: a block whose real pairs are within its first four
+// entries (nearly every block at decode) reads those pair ids as scalars together with
+// the expert id, so its weight, x, s and out loads all leave in one round trip. Loads are
+// branch-free (out-of-range buffer offsets read as zero; other masked addresses are
+// clamped to a valid one and their values unused), so each run of loads issues back to
+// back.
 //
-// The fused kernel runs both in one launch. Workgroups [0, S) are shrink items and the
-// rest expand items, block by block. A shrink item publishes its rows of s with
-// agent-coherent (L2-bypassing) stores, waits for them to complete, and bumps its block's
-// counter; an expand item first issues its weight loads, then polls the counter and reads
-// s with agent-coherent loads. No cache-wide writeback or invalidate is needed, and no
-// counter is shared by all workgroups. The wait is bounded: an expand item that does not
-// see its block ready in time computes the block's s itself with exactly the shrink
-// arithmetic (same lanes, same order), so the result is bit-identical either way and no
-// workgroup ever depends on the scheduling of another. Each block's counter packs the
-// finished shrink items (low 16 bits) and expand items (high 16 bits); whichever
-// participant arrives last puts it back to zero for the next call.
+// mol_lora_delta runs the shrink kernel then the expand kernel with s in the caller's
+// workspace. A single launch that hands s between workgroups was measured to cost more
+// than the kernel boundary: the handoff needs a store that reaches the coherence point, a
+// counter and a poll, each a full memory round trip under load.
 #include "mol_internal.h"
 
 namespace mol {
@@ -118,17 +119,23 @@ __device__ __forceinline__ int block_expert(const DeltaArgs& a, int blk) {
   return (blk < live_blocks(a, npp) && real_expert(e, a.V)) ? e : -1;
 }
 
-// agent-coherent accesses used to hand s from shrink to expand items of one launch
-__device__ __forceinline__ void st_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_coherent(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// The first kPG entries of block blk as scalars (numel past the block); returns how many
+// are real pairs. *all_here tells whether they are all of the block's real pairs.
+__device__ __forceinline__ int first_pairs(const DeltaArgs& a, int blk, int* p, bool* all_here) {
+  const int32_t* sp = a.sorted + (int64_t)blk * a.BM;
+  int nr = 0;
+#pragma unroll
+  for (int i = 0; i < kPG; ++i) {
+    const int v = sp[i < a.BM ? i : 0];
+    p[i] = i < a.BM ? v : a.numel;
+    nr += real_pair(p[i], a.numel) ? 1 : 0;
+  }
+  *all_here = nr < kPG || a.BM <= kPG;
+  return nr;
 }
 
-// Branch-free loads: an address that is not needed is clamped to a valid one (the first
-// element of the same array) and the value discarded afterwards, so a run of loads issues
-// back to back instead of each sitting in its own branch with its own wait.
+// Branch-free 16-byte load: a masked address is clamped to the array's first element
+// and its value replaced by zero.
 __device__ __forceinline__ uint4 ld16_if(const char* base, int64_t off, bool ok) {
   const uint4 v = ld16(base + (ok ? off : 0));
   return ok ? v : make_uint4(0, 0, 0, 0);
@@ -147,6 +154,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t expert_rsrc(const void* base, 
 __device__ __forceinline__ uint4 buf16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   return *reinterpret_cast<const uint4*>(&v);
+}
+
+// Direct-to-LDS 16-byte load: lane i of the wave writes at lds_wave_base + 16*i.
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base,
+                                   16, 0, 0);
 }
 
 // Entry j0 + lane of block blk for the lanes of wave 0 (numel for entries past the block).
@@ -168,11 +181,8 @@ __device__ __forceinline__ void publish_pids(const DeltaArgs& a, int pv, int* pi
 // ------------------------------------------------------------------------------ shrink
 // Lane lr of a row's LPR-lane group owns the 16-byte vectors lr, lr+LPR, lr+2*LPR, ...
 // of the row, sums their products in ascending order, and the lanes are combined by a
-// fixed xor tree: the result depends only on (K, LPR), not on how many vectors (kSeg) or
-// pairs (kPG) are processed together, which is what lets the fallback path below
-// reproduce the shrink items bit for bit.
+// fixed xor tree: the result depends only on (K, LPR).
 
-// The kSeg vectors of one segment of this lane's row of A_e (zero past the row or matrix).
 template <int LPR>
 __device__ __forceinline__ void load_a_seg(__amdgpu_buffer_rsrc_t ra, uint32_t row_off, bool row_ok,
                                            int m0, int nvec, uint4* av) {
@@ -184,16 +194,21 @@ __device__ __forceinline__ void load_a_seg(__amdgpu_buffer_rsrc_t ra, uint32_t r
   }
 }
 
-// One shrink work item: rows [rg*RPI, rg*RPI+RPI) of s for every real pair of block blk.
-// The x segments of kPG pairs at a time are staged once in LDS (xs) instead of every row
-// group of lanes reading them again.
-template <bool BF16, int LPR, bool COHERENT>
-__device__ __forceinline__ void shrink_item(const DeltaArgs& a, int blk, int rg, int e, int pv0,
-                                            int* pid, int* nreal, uint4* xs) {
+template <int LPR>
+struct ShrinkLds {
+  static constexpr int kVecs = kPG * kSeg * LPR;
+};
+
+// Rows [rg*RPI, rg*RPI+RPI) of s for the pairs p[0..nq) (nq <= kPG). The x segments of
+// the pairs go straight into xs (LDS); lane 0 of each row group stores the sums.
+template <bool BF16, int LPR>
+__device__ __forceinline__ void shrink_group(const DeltaArgs& a, int e, int rg, const int* p,
+                                             int nq, uint4* xs) {
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int RPI = kThreads / LPR;
-  constexpr int SEGV = kSeg * LPR;              // vectors of one x segment
-  constexpr int XPT = kPG * SEGV / kThreads;    // x vectors each thread stages
+  constexpr int SEGV = kSeg * LPR;            // vectors of one x segment
+  constexpr int XPT = kPG * SEGV / kThreads;  // x vectors each thread stages
+  static_assert(XPT >= 1 && kPG * SEGV % kThreads == 0, "x staging covers whole waves");
   const int tid = threadIdx.x;
   const int lr = tid % LPR;
   const int row = rg * RPI + tid / LPR;
@@ -205,128 +220,95 @@ __device__ __forceinline__ void shrink_item(const DeltaArgs& a, int blk, int rg,
   const uint32_t row_off = (uint32_t)(row_ok ? row : 0) * (uint32_t)(a.K * ESZ);
   const char* xbase = (const char*)a.xin;
   const int64_t xstride = a.ld_x * ESZ;
-  for (int j0 = 0; j0 < a.BM; j0 += kPidSlots) {
-    const int pv = j0 == 0 ? pv0 : (tid < kPidSlots ? load_pid(a, blk, j0) : 0);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  float acc[kPG];
+#pragma unroll
+  for (int i = 0; i < kPG; ++i) acc[i] = 0.f;
+  for (int m0 = 0; m0 < vpl; m0 += kSeg) {
     uint4 av[kSeg];
-    load_a_seg<LPR>(ra, row_off, row_ok, 0, nvec, av);  // weights go out with the ids
+    load_a_seg<LPR>(ra, row_off, row_ok, m0, nvec, av);
+    if (m0 > 0) __syncthreads();  // earlier readers of xs are done
+    // x vectors of this segment: lane i of a wave writes 16 bytes at its wave's base;
+    // entries of pairs past nq or vectors past the row read a valid address, unused
+#pragma unroll
+    for (int t = 0; t < XPT; ++t) {
+      const int i = tid + t * kThreads;
+      const int q = i / SEGV;
+      const int v = m0 * LPR + (i - q * SEGV);
+      const bool ok = q < nq && v < nvec;
+      const int pq = !ok ? 0 : q == 0 ? p[0] : q == 1 ? p[1] : q == 2 ? p[2] : p[3];
+      lds_dma16(xbase + (ok ? (int64_t)(pq / a.row_div) * xstride + (int64_t)v * 16 : 0),
+                xs + wv * 64 + t * kThreads);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the x DMA and the weights have landed
     __syncthreads();
-    publish_pids(a, pv, pid, nreal);
+#pragma unroll
+    for (int i = 0; i < kPG; ++i) {
+      if (i >= nq) break;
+#pragma unroll
+      for (int sg = 0; sg < kSeg; ++sg) {
+        const int v = lr + (m0 + sg) * LPR;
+        if (v < nvec) acc[i] = dot16<BF16>(av[sg], xs[i * SEGV + sg * LPR + lr], acc[i]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kPG; ++i) {
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc[i] += __shfl_xor(acc[i], off, 64);
+  }
+  if (lr == 0 && row_ok) {
+#pragma unroll
+    for (int i = 0; i < kPG; ++i) {
+      if (i >= nq) break;
+      a.s[(int64_t)p[i] * a.R + row] = acc[i];
+    }
+  }
+}
+
+// Shrink work item (blk, rg): all real pairs of block blk.
+template <bool BF16, int LPR>
+__device__ __forceinline__ void shrink_block(const DeltaArgs& a, int blk, int rg, int* pid,
+                                             int& nreal, uint4* xs) {
+  int p[kPG];
+  bool all_here;
+  const int n4 = first_pairs(a, blk, p, &all_here);
+  const int e = block_expert(a, blk);
+  if (e < 0) return;
+  if (all_here) {  // the common decode case: no id staging at all
+    if (n4 > 0) shrink_group<BF16, LPR>(a, e, rg, p, n4, xs);
+    return;
+  }
+  for (int j0 = 0; j0 < a.BM; j0 += kPidSlots) {
+    const int pv = threadIdx.x < kPidSlots ? load_pid(a, blk, j0) : a.numel;
     __syncthreads();
-    const int nr = *nreal;
+    publish_pids(a, pv, pid, &nreal);
+    __syncthreads();
+    const int nr = nreal;
     for (int q0 = 0; q0 < nr; q0 += kPG) {
-      float acc[kPG];
+      int pq[kPG];
 #pragma unroll
-      for (int i = 0; i < kPG; ++i) acc[i] = 0.f;
-      for (int m0 = 0; m0 < vpl; m0 += kSeg) {
-        if (m0 > 0 || q0 > 0) load_a_seg<LPR>(ra, row_off, row_ok, m0, nvec, av);
-        uint4 xv[XPT];
-#pragma unroll
-        for (int t = 0; t < XPT; ++t) {
-          const int i = tid + t * kThreads;
-          const int q = i / SEGV;
-          const int v = m0 * LPR + (i - q * SEGV);
-          const int pq = pid[q0 + q];
-          const bool ok = q0 + q < nr && v < nvec;
-          xv[t] = ld16_if(xbase, (int64_t)(ok ? pq / a.row_div : 0) * xstride + (int64_t)v * 16, ok);
-        }
-        __syncthreads();  // earlier readers of xs are done
-#pragma unroll
-        for (int t = 0; t < XPT; ++t) xs[tid + t * kThreads] = xv[t];
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < kPG; ++i) {
-          if (q0 + i >= nr) break;
-#pragma unroll
-          for (int sg = 0; sg < kSeg; ++sg) {
-            const int v = lr + (m0 + sg) * LPR;
-            if (v < nvec) acc[i] = dot16<BF16>(av[sg], xs[i * SEGV + sg * LPR + lr], acc[i]);
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < kPG; ++i) {
-#pragma unroll
-        for (int off = LPR / 2; off > 0; off >>= 1) acc[i] += __shfl_xor(acc[i], off, 64);
-      }
-      if (lr == 0 && row_ok) {
-#pragma unroll
-        for (int i = 0; i < kPG; ++i) {
-          if (q0 + i >= nr) break;
-          float* d = a.s + (int64_t)pid[q0 + i] * a.R + row;
-          if constexpr (COHERENT) st_coherent(d, acc[i]); else *d = acc[i];
-        }
-      }
+      for (int i = 0; i < kPG; ++i) pq[i] = q0 + i < nr ? pid[q0 + i] : a.numel;
+      __syncthreads();  // xs of the previous group is no longer read
+      shrink_group<BF16, LPR>(a, e, rg, pq, min(kPG, nr - q0), xs);
     }
     if (nr < kPidSlots) return;  // the block's real entries ended in this pass
   }
 }
 
-// The shrink sum of one row (lane group) for one pair, read straight from global memory
-// one vector at a time: few registers, and the same sums as shrink_item.
 template <bool BF16, int LPR>
-__device__ __forceinline__ float shrink_one(const DeltaArgs& a, int e, int row, int p) {
-  constexpr int ESZ = BF16 ? 2 : 4;
-  const int lr = threadIdx.x % LPR;
-  const bool row_ok = row < a.R;
-  const int nvec = a.K * ESZ / 16;
-  const char* arow =
-      (const char*)a.A + ((int64_t)e * a.R + (row_ok ? row : 0)) * (int64_t)a.K * ESZ;
-  const char* xr = (const char*)a.xin + (int64_t)(p / a.row_div) * a.ld_x * ESZ;
-  float acc = 0.f;
-  for (int v = lr; v < nvec; v += LPR)
-    acc = dot16<BF16>(ld16_if(arow, (int64_t)v * 16, row_ok), ld16(xr + (int64_t)v * 16), acc);
-#pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  return acc;
-}
-
-// s rows of the pairs pid[0..nr) into s_lds [nr][R], computed here with the arithmetic of
-// the shrink items (used when they are not done in time).
-template <bool BF16, int LPR>
-__device__ __forceinline__ void compute_s_rows(const DeltaArgs& a, int e, const int* pid, int nr,
-                                               float* s_lds) {
-  constexpr int RPI = kThreads / LPR;
-  const int lr = threadIdx.x % LPR;
-  for (int rg = 0; rg < a.rgroups; ++rg) {
-    const int row = rg * RPI + threadIdx.x / LPR;
-    for (int q = 0; q < nr; ++q) {
-      const float acc = shrink_one<BF16, LPR>(a, e, row, pid[q]);
-      if (lr == 0 && row < a.R) s_lds[q * a.R + row] = acc;
-    }
-  }
+__global__ void __launch_bounds__(kThreads) shrink_kernel(DeltaArgs a) {
+  __shared__ int pid[kPidSlots];
+  __shared__ int nreal;
+  __shared__ uint4 xs[ShrinkLds<LPR>::kVecs];
+  shrink_block<BF16, LPR>(a, blockIdx.x / a.rgroups, blockIdx.x % a.rgroups, pid, nreal, xs);
 }
 
 // ------------------------------------------------------------------------------ expand
 
-// s rows of the pairs pid[0..nr) into s_lds [nr][R] (nr * R <= kSLdsFloats), read from
-// a.s four loads per thread at a time.
-template <bool COHERENT>
-__device__ __forceinline__ void load_s_rows(const DeltaArgs& a, const int* pid, int nr,
-                                            float* s_lds) {
-  const int R = a.R;
-  const int total = nr * R;
-  for (int base = 0; base < total; base += 4 * kThreads) {
-    float v[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int i = base + t * kThreads + threadIdx.x;
-      const bool ok = i < total;
-      const int q = ok ? i / R : 0;
-      const float* src = a.s + (int64_t)pid[q] * R + (ok ? i - q * R : 0);
-      v[t] = COHERENT ? ld_coherent(src) : *src;
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int i = base + t * kThreads + threadIdx.x;
-      if (i < total) s_lds[i] = v[t];
-    }
-  }
-}
-
 template <bool BF16, int RV, int CPT>
 __device__ __forceinline__ void load_b_rows(const DeltaArgs& a, int e, const int* n,
                                             uint4 (*bv)[RV]) {
-  constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int RB = RV * 16;  // bytes of one weight row
   const int64_t bbytes = (int64_t)a.N * RB;
   const __amdgpu_buffer_rsrc_t rb = expert_rsrc((const char*)a.B + (int64_t)e * bbytes, bbytes);
@@ -337,7 +319,6 @@ __device__ __forceinline__ void load_b_rows(const DeltaArgs& a, int e, const int
     for (int v = 0; v < RV; ++v)
       bv[j][v] = buf16(rb, ok ? (uint32_t)n[j] * RB + v * 16 : kOutOfRange);
   }
-  (void)ESZ;
 }
 
 template <bool BF16>
@@ -359,8 +340,8 @@ __device__ __forceinline__ void store_out(const DeltaArgs& a, int p, int n, floa
     ((float*)a.out)[(int64_t)p * a.ld_out + n] = v;
 }
 
-// out[p, n] = round(out[p, n] + sc * <B_v[n], s_p[slice(n)]>) for this pass's pairs; the
-// old values of the first kPG pairs were loaded ahead into ov.
+// out[p, n] = round(out[p, n] + sc * <B_v[n], s_p[slice(n)]>) for the pairs pid[0..nr);
+// the old values of the first kPG pairs were loaded ahead into ov.
 template <bool BF16, int RV, int CPT>
 __device__ __forceinline__ void expand_outputs(const DeltaArgs& a, const uint4 (*bv)[RV],
                                                const int* pid, int nr, const float* s_lds,
@@ -396,17 +377,19 @@ __device__ __forceinline__ void expand_outputs(const DeltaArgs& a, const uint4 (
 }
 
 // One expand work item: CPT*256 output columns for every real pair of block blk.
-// FUSED: s comes from this launch's shrink items (or is computed here, see above).
-template <bool BF16, int LPR, int RV, bool FUSED>
-__device__ __forceinline__ void expand_item(const DeltaArgs& a, int blk, int chunk, int e,
-                                            int pv0, int* pid, int* nreal, float* s_lds,
-                                            int* flag) {
+template <bool BF16, int RV>
+__device__ __forceinline__ void expand_block(const DeltaArgs& a, int blk, int chunk, int* pid,
+                                             int& nreal, float* s_lds) {
   constexpr int CPT = cols_per_thread(RV);
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int r = RV * 16 / ESZ;
   const int tid = threadIdx.x;
+  int p[kPG];
+  bool all_here;
+  const int n4 = first_pairs(a, blk, p, &all_here);
+  const int e = block_expert(a, blk);
+  if (e < 0) return;
   const int width = a.N / a.slices;
-  const int pg = min(kPidSlots, kSLdsFloats / a.R);
   int n[CPT], soff[CPT];
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
@@ -414,45 +397,53 @@ __device__ __forceinline__ void expand_item(const DeltaArgs& a, int blk, int chu
     soff[j] = (n[j] < a.N ? n[j] / width : 0) * r;
   }
   const float sc = a.scale[e / a.E];
-  int pv = tid < pg ? pv0 : a.numel;
   uint4 bv[CPT][RV];
-  load_b_rows<BF16, RV, CPT>(a, e, n, bv);  // the weights go out with the first ids
-  bool ready = true;
-  for (int j0 = 0; j0 < a.BM; j0 += pg) {
-    if (j0 > 0) pv = tid < pg ? load_pid(a, blk, j0) : a.numel;
-    if (tid >= pg) pv = a.numel;
-    __syncthreads();
-    publish_pids(a, pv, pid, nreal);
-    if constexpr (FUSED) {
-      if (j0 == 0 && tid == 0) {
-        int ok = 0;
-        for (int it = 0; it < a.spin_limit; ++it) {
-          const int w =
-              __hip_atomic_load(a.sync + blk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if ((w & 0xffff) >= a.rgroups) {
-            ok = 1;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(2);
-        }
-        *flag = ok;
-      }
+  load_b_rows<BF16, RV, CPT>(a, e, n, bv);
+  if (all_here) {
+    if (n4 == 0) return;
+    // the block's s rows (n4 * R floats, R a multiple of 4) straight into LDS, and the old
+    // out values, all in the same round trip as the weights
+    const int nvec = n4 * a.R / 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    for (int base = 0; base < nvec; base += kThreads) {
+      const int i = base + tid;
+      const bool ok = i < nvec;
+      const int q = ok ? i / (a.R / 4) : 0;
+      const int c4 = ok ? i - q * (a.R / 4) : 0;
+      const int pq = q == 0 ? p[0] : q == 1 ? p[1] : q == 2 ? p[2] : p[3];
+      lds_dma16(a.s + (int64_t)pq * a.R + c4 * 4, s_lds + (base + wv * 64) * 4);
     }
+    if (tid < kPG) pid[tid] = tid == 0 ? p[0] : tid == 1 ? p[1] : tid == 2 ? p[2] : p[3];
+    float ov[kPG][CPT];
+#pragma unroll
+    for (int q = 0; q < kPG; ++q) {
+#pragma unroll
+      for (int j = 0; j < CPT; ++j)
+        ov[q][j] = load_out<BF16>(a, q < n4 ? p[q] : 0, n[j], q < n4 && n[j] < a.N);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    const int nr = *nreal;
+    expand_outputs<BF16, RV, CPT>(a, bv, pid, n4, s_lds, n, soff, sc, ov);
+    return;
+  }
+  const int pg = min(kPidSlots, kSLdsFloats / a.R);
+  for (int j0 = 0; j0 < a.BM; j0 += pg) {
+    const int pv = tid < pg ? load_pid(a, blk, j0) : a.numel;
+    __syncthreads();
+    publish_pids(a, pv, pid, &nreal);
+    __syncthreads();
+    const int nr = nreal;
     if (nr == 0) break;
-    if constexpr (FUSED) ready = *flag != 0;
     float ov[kPG][CPT];  // old out values of the first pairs, loaded before s is needed
 #pragma unroll
     for (int q = 0; q < kPG; ++q) {
-      const int p = pid[q];
+      const int pq = pid[q];
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) ov[q][j] = load_out<BF16>(a, p, n[j], q < nr && n[j] < a.N);
+      for (int j = 0; j < CPT; ++j) ov[q][j] = load_out<BF16>(a, pq, n[j], q < nr && n[j] < a.N);
     }
-    if (ready) {
-      load_s_rows<FUSED>(a, pid, nr, s_lds);
-    } else if constexpr (FUSED) {
-      compute_s_rows<BF16, LPR>(a, e, pid, nr, s_lds);
+    for (int i = tid; i < nr * a.R; i += kThreads) {
+      const int q = i / a.R;
+      s_lds[i] = a.s[(int64_t)pid[q] * a.R + (i - q * a.R)];
     }
     __syncthreads();
     expand_outputs<BF16, RV, CPT>(a, bv, pid, nr, s_lds, n, soff, sc, ov);
@@ -460,129 +451,21 @@ __device__ __forceinline__ void expand_item(const DeltaArgs& a, int blk, int chu
   }
 }
 
-// block counter arrival: shrink items add 1, expand items add 1 << 16; the last of the
-// rgroups + nchunk participants clears the counter
-__device__ __forceinline__ void arrive(const DeltaArgs& a, int blk, int inc) {
-  const int target = a.rgroups + (a.nchunk << 16);
-  const int old = __hip_atomic_fetch_add(a.sync + blk, inc, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-  if (old + inc == target)
-    __hip_atomic_store(a.sync + blk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-template <int LPR>
-struct ShrinkLds {
-  static constexpr int kVecs = kPG * kSeg * LPR;
-};
-
-template <bool BF16, int LPR>
-__global__ void __launch_bounds__(kThreads) shrink_kernel(DeltaArgs a) {
-  __shared__ int pid[kPidSlots];
-  __shared__ int nreal;
-  __shared__ uint4 xs[ShrinkLds<LPR>::kVecs];
-  const int blk = blockIdx.x / a.rgroups, rg = blockIdx.x % a.rgroups;
-  const int pv0 = threadIdx.x < kPidSlots ? load_pid(a, blk, 0) : 0;  // with the expert id
-  const int e = block_expert(a, blk);
-  if (e < 0) return;
-  shrink_item<BF16, LPR, false>(a, blk, rg, e, pv0, pid, &nreal, xs);
-}
-
 template <bool BF16, int RV>
 __global__ void __launch_bounds__(kThreads) expand_kernel(DeltaArgs a) {
   __shared__ int pid[kPidSlots];
   __shared__ int nreal;
-  __shared__ float s_lds[kSLdsFloats];
-  const int blk = blockIdx.x / a.nchunk, c = blockIdx.x % a.nchunk;
-  const int pv0 = threadIdx.x < kPidSlots ? load_pid(a, blk, 0) : 0;
-  const int e = block_expert(a, blk);
-  if (e < 0) return;
-  expand_item<BF16, 64, RV, false>(a, blk, c, e, pv0, pid, &nreal, s_lds, nullptr);
-}
-
-// Fused delta: block blk is served by a.nchunk consecutive workgroups (parts). Part g
-// issues the weight loads of its a.cpp expand columns first, computes shrink row group g
-// when g < a.rgroups and publishes it, then waits for the block's other row groups and
-// expands its own columns. Parts of one block are adjacent in the grid, so they run side
-// by side; no part waits for a workgroup later in the grid, and the bounded wait falls
-// back to computing s in place (same sums) if the others are late.
-template <bool BF16, int LPR, int RV>
-__global__ void __launch_bounds__(kThreads) delta_fused_kernel(DeltaArgs a) {
-  constexpr int kXsBytes = ShrinkLds<LPR>::kVecs * 16;
-  constexpr int kSBytes = kSLdsFloats * 4;
-  constexpr int ESZ = BF16 ? 2 : 4;
-  constexpr int VE = 16 / ESZ;
-  constexpr int r = RV * VE;
-  __shared__ int pid[kPidSlots];
-  __shared__ int nreal;
-  __shared__ int flag;
-  __shared__ uint4 smem[(kXsBytes > kSBytes ? kXsBytes : kSBytes) / 16];  // xs or s rows
-  float* s_lds = reinterpret_cast<float*>(smem);
-  const int tid = threadIdx.x;
-  const int blk = blockIdx.x / a.nchunk, g = blockIdx.x % a.nchunk;
-  const int pv0 = tid < kPidSlots ? load_pid(a, blk, 0) : 0;  // with the expert id
-  const int e = block_expert(a, blk);
-  if (e < 0) return;
-  // this thread's expand column; its weights go out first
-  const int n = g * a.cpp + tid;
-  const bool n_ok = tid < a.cpp && n < a.N;
-  int nc[1] = {n_ok ? n : a.N};
-  uint4 bv[1][RV];
-  load_b_rows<BF16, RV, 1>(a, e, nc, bv);
-  const int soff[1] = {(n_ok ? n / (a.N / a.slices) : 0) * r};
-  const bool shrinker = g < a.rgroups;
-  if (shrinker) {
-    shrink_item<BF16, LPR, true>(a, blk, g, e, pv0, pid, &nreal, smem);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's s stores have completed
-    __syncthreads();
-    if (tid == 0) arrive(a, blk, 1);
-  }
-  const float sc = a.scale[e / a.E];
-  const int pg = min(kPidSlots, kSLdsFloats / a.R);
-  bool ready = true;
-  for (int j0 = 0; j0 < a.BM; j0 += pg) {
-    int pv = j0 == 0 ? pv0 : (tid < pg ? load_pid(a, blk, j0) : a.numel);
-    if (tid >= pg) pv = a.numel;
-    __syncthreads();
-    publish_pids(a, pv, pid, &nreal);
-    if (j0 == 0 && tid == 0) {
-      int ok = 0;
-      for (int it = 0; it < a.spin_limit; ++it) {
-        const int w = __hip_atomic_load(a.sync + blk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((w & 0xffff) >= a.rgroups) {
-          ok = 1;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-      flag = ok;
-    }
-    __syncthreads();
-    const int nr = nreal;
-    if (nr == 0) break;
-    ready = flag != 0;
-    float ov[kPG][1];  // old out values of the first pairs, loaded before s is needed
-#pragma unroll
-    for (int q = 0; q < kPG; ++q) ov[q][0] = load_out<BF16>(a, pid[q], nc[0], q < nr && n_ok);
-    if (ready) {
-      load_s_rows<true>(a, pid, nr, s_lds);
-    } else {
-      compute_s_rows<BF16, LPR>(a, e, pid, nr, s_lds);
-    }
-    __syncthreads();
-    expand_outputs<BF16, RV, 1>(a, bv, pid, nr, s_lds, nc, soff, sc, ov);
-    if (nr < pg) break;  // the block's real entries ended in this pass
-  }
-  __syncthreads();
-  if (tid == 0) arrive(a, blk, 1 << 16);
+  __shared__ __attribute__((aligned(16))) float s_lds[kSLdsFloats];
+  expand_block<BF16, RV>(a, blockIdx.x / a.nchunk, blockIdx.x % a.nchunk, pid, nreal, s_lds);
 }
 
 template <bool BF16>
 hipError_t shrink_dispatch(const DeltaArgs& a, int lpr, int grid, hipStream_t st) {
   switch (lpr) {
-    case 8: hipLaunchKernelGGL((shrink_kernel<BF16, 8>), dim3(grid), dim3(256), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((shrink_kernel<BF16, 16>), dim3(grid), dim3(256), 0, st, a); break;
-    case 32: hipLaunchKernelGGL((shrink_kernel<BF16, 32>), dim3(grid), dim3(256), 0, st, a); break;
-    case 64: hipLaunchKernelGGL((shrink_kernel<BF16, 64>), dim3(grid), dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((shrink_kernel<BF16, 8>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((shrink_kernel<BF16, 16>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((shrink_kernel<BF16, 32>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((shrink_kernel<BF16, 64>), dim3(grid), dim3(kThreads), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -591,42 +474,14 @@ hipError_t shrink_dispatch(const DeltaArgs& a, int lpr, int grid, hipStream_t st
 template <bool BF16>
 hipError_t expand_dispatch(const DeltaArgs& a, int rv, int grid, hipStream_t st) {
   switch (rv) {
-    case 1: hipLaunchKernelGGL((expand_kernel<BF16, 1>), dim3(grid), dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((expand_kernel<BF16, 2>), dim3(grid), dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((expand_kernel<BF16, 4>), dim3(grid), dim3(256), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((expand_kernel<BF16, 8>), dim3(grid), dim3(256), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((expand_kernel<BF16, 16>), dim3(grid), dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((expand_kernel<BF16, 1>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((expand_kernel<BF16, 2>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((expand_kernel<BF16, 4>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((expand_kernel<BF16, 8>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((expand_kernel<BF16, 16>), dim3(grid), dim3(kThreads), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
-}
-
-template <bool BF16, int LPR>
-hipError_t delta_dispatch_rv(const DeltaArgs& a, int rv, int grid, hipStream_t st) {
-  switch (rv) {
-    case 1: hipLaunchKernelGGL((delta_fused_kernel<BF16, LPR, 1>), dim3(grid), dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((delta_fused_kernel<BF16, LPR, 2>), dim3(grid), dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((delta_fused_kernel<BF16, LPR, 4>), dim3(grid), dim3(256), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((delta_fused_kernel<BF16, LPR, 8>), dim3(grid), dim3(256), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((delta_fused_kernel<BF16, LPR, 16>), dim3(grid), dim3(256), 0, st, a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-template <bool BF16>
-hipError_t delta_dispatch(const DeltaArgs& a, int lpr, int rv, int grid, hipStream_t st) {
-  switch (lpr) {
-    case 8: return delta_dispatch_rv<BF16, 8>(a, rv, grid, st);
-    case 16: return delta_dispatch_rv<BF16, 16>(a, rv, grid, st);
-    case 32: return delta_dispatch_rv<BF16, 32>(a, rv, grid, st);
-    case 64: return delta_dispatch_rv<BF16, 64>(a, rv, grid, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-int rank_vectors(const DeltaArgs& a, bool bf16) {
-  return (a.R / a.slices) * (bf16 ? 2 : 4) / 16;
 }
 
 }  // namespace
@@ -645,23 +500,15 @@ int shrink_rows_per_item(int32_t K, int elem_bytes) {
 
 hipError_t launch_shrink(const DeltaArgs& a, bool bf16, int rows_per_item, int grid,
                          hipStream_t stream) {
-  const int lpr = 256 / rows_per_item;
+  const int lpr = kThreads / rows_per_item;
   return bf16 ? shrink_dispatch<true>(a, lpr, grid, stream)
               : shrink_dispatch<false>(a, lpr, grid, stream);
 }
 
 hipError_t launch_expand(const DeltaArgs& a, bool bf16, int grid, hipStream_t stream) {
-  const int rv = rank_vectors(a, bf16);
+  const int rv = (a.R / a.slices) * (bf16 ? 2 : 4) / 16;
   return bf16 ? expand_dispatch<true>(a, rv, grid, stream)
               : expand_dispatch<false>(a, rv, grid, stream);
-}
-
-hipError_t launch_delta(const DeltaArgs& a, bool bf16, int rows_per_item, int grid,
-                        hipStream_t stream) {
-  const int lpr = 256 / rows_per_item;
-  const int rv = rank_vectors(a, bf16);
-  return bf16 ? delta_dispatch<true>(a, lpr, rv, grid, stream)
-              : delta_dispatch<false>(a, lpr, rv, grid, stream);
 }
 
 }  // namespace mol

@@ -49,18 +49,12 @@ struct DeltaArgs {
   int32_t V;             // virtual experts: expert ids outside [0, V) are skipped
   int32_t BM;
   int32_t rgroups;       // shrink work items per block (row groups of A)
-  int32_t nchunk;        // expand work items per block (column chunks of B); in the fused
-                         // kernel: workgroups per block
-  int32_t cpp;           // fused kernel: expand columns per workgroup (<= 256)
+  int32_t nchunk;        // expand work items per block (column chunks of B)
   float* s;              // [numel, R]
   void* out;
   int64_t ld_out;
-  int32_t* sync;         // fused kernel: [max_blocks] zero-initialised block counters
   int32_t max_blocks;
-  int32_t spin_limit;    // fused kernel: polls before an expand item computes s itself
 };
-
-constexpr int kDefaultSpinLimit = 1 << 16;
 
 // host-side launchers (return the launch status)
 hipError_t launch_virtual_topk(const int32_t* topk_ids, const int32_t* lora_ids, int32_t M,
@@ -74,12 +68,9 @@ hipError_t launch_align_large(const AlignArgs& a, hipStream_t stream);
 int shrink_rows_per_item(int32_t K, int elem_bytes);
 // output columns per expand item for rank R / slices
 int expand_cols_per_item(int32_t R, int32_t slices, int elem_bytes);
-constexpr int kFusedMaxCols = 256;  // fused kernel: expand columns per workgroup
 
 hipError_t launch_shrink(const DeltaArgs& a, bool bf16, int rows_per_item, int grid,
                          hipStream_t stream);
 hipError_t launch_expand(const DeltaArgs& a, bool bf16, int grid, hipStream_t stream);
-hipError_t launch_delta(const DeltaArgs& a, bool bf16, int rows_per_item, int grid,
-                        hipStream_t stream);
 
 }  // namespace mol
