@@ -2,7 +2,7 @@
 """Benchmark of the MoL delta path on one MI355X.
 
 One step = one layer pass of the whole path on one batch: align_block_size (remap inline)
-+ the gate_up delta (shrink + expand, one fused launch) + the down delta. The default
++ the gate_up delta (shrink + expand) + the down delta (shrink + expand). The default
 workload is the decode layer of 23 tokens (hidden 2048, moe_intermediate 768, 128 experts,
 top-8, 8 LoRA slots = 1024 virtual experts, rank 32, BLOCK_M 64).
 
@@ -13,9 +13,9 @@ the timed region. Each layer's step is captured once into a hipGraph (torch.cuda
 and the timed region replays them (`--mode eager` launches directly instead).
 
 Prints one JSON line: routed pairs/s over the timed steps as `value`, microseconds per
-layer, the roofline of the dominant kernel (the gate_up fused delta) from HIP events
-around its launches inside the timed region, and the CPU oracle timed on the host cores
-on a bounded sample of the same layers.
+layer, per-kernel times and the roofline of the dominant (longest) kernel from HIP events
+around its launches, and the CPU oracle timed on the host cores on a bounded sample of
+the same layers.
 """
 from __future__ import annotations
 
@@ -46,7 +46,8 @@ def parse():
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle sample budget (0 = skip the CPU baseline)")
-    ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB elementwise copy (counter calibration)")
     return ap.parse_args()
 
 
@@ -69,18 +70,94 @@ def layer_stats(dl):
             "valid_blocks": int(valid_blocks.sum())}
 
 
+def _sizes(cfg, st, stats):
+    esz = 2 if cfg.dtype == "bf16" else 4
+    rows = stats["T"] if st.input == "x" else stats["P"]
+    idx = 4 * (stats["P"] + stats["valid_blocks"])
+    return esz, rows, idx
+
+
 def stage_bytes(cfg, st, stats):
     """Algorithmic HBM bytes of one stage's delta: every touched virtual expert's A and B
     once, the input rows the pairs read, and each pair's output row read and written,
-    plus the routing entries of the real pairs and their blocks."""
-    esz = 2 if cfg.dtype == "bf16" else 4
+    plus the routing entries of the real pairs and their blocks. The fp32 rank-space
+    intermediate s is not counted: a fused delta need not move it through HBM."""
+    esz, rows, idx = _sizes(cfg, st, stats)
     P, D = stats["P"], stats["D"]
-    rows = stats["T"] if st.input == "x" else P
-    w = D * (st.R * st.K + st.N * st.r) * esz
-    act = rows * st.K * esz
-    out = 2 * P * st.N * esz
-    idx = 4 * (P + stats["valid_blocks"])
-    return w + act + out + idx
+    return D * (st.R * st.K + st.N * st.r) * esz + rows * st.K * esz \
+        + 2 * P * st.N * esz + idx
+
+
+def shrink_bytes(cfg, st, stats):
+    """Algorithmic bytes of one shrink launch: A of every touched virtual expert, the
+    input rows, the fp32 s rows it writes, and the routing entries."""
+    esz, rows, idx = _sizes(cfg, st, stats)
+    return stats["D"] * st.R * st.K * esz + rows * st.K * esz + stats["P"] * st.R * 4 + idx
+
+
+def expand_bytes(cfg, st, stats):
+    """Algorithmic bytes of one expand launch: B of every touched virtual expert, the
+    fp32 s rows, each pair's output row read and written, and the routing entries."""
+    esz, _, idx = _sizes(cfg, st, stats)
+    P = stats["P"]
+    return stats["D"] * st.N * st.r * esz + P * st.R * 4 + 2 * P * st.N * esz + idx
+
+
+def kernel_name(cfg, st, kind):
+    """The kernel instantiation libmol launches for this stage, as a profiler names it.
+    Shrink: rows per work item start at 4 and double while two such items' A rows fit
+    32 KiB (at most 32); lanes per row = 256 / rows per item. Expand: 16-byte vectors
+    per B row = r * element size / 16."""
+    esz = 2 if cfg.dtype == "bf16" else 4
+    b = "true" if cfg.dtype == "bf16" else "false"
+    if kind == "shrink":
+        rpi = 4
+        while rpi < 32 and rpi * 2 * st.K * esz <= 32768:
+            rpi *= 2
+        return f"shrink_kernel<{b}, {256 // rpi}>"
+    return f"expand_kernel<{b}, {st.r * esz // 16}>"
+
+
+def delta_source_sha256():
+    import hashlib
+    path = os.path.join(ROOT, "virtual_expert_routed_amd", "csrc", "delta.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` at `workload` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter on a copy of known size).
+    None when there is no summary for this kernel, or the kernel source has changed since
+    the counters were taken."""
+    import re
+    path = os.path.join(ROOT, "profiles", f"pmc_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None, "no counter summary for this workload"
+    text = open(path).read()
+    fields = dict(re.findall(r"^(\w+):\s*(.+?)\s*$", text, flags=re.M))
+    if fields.get("kernel") != kernel:
+        return None, f"counter summary covers {fields.get('kernel')}, not {kernel}"
+    if fields.get("kernel_source_sha256") != delta_source_sha256():
+        return None, "kernel source changed since the counters were taken"
+    return float(fields["traffic_bytes_per_launch"]), os.path.relpath(path, ROOT)
+
+
+def copy_calibration(torch):
+    """An elementwise copy (negation) of 1 GiB of fp32, three launches: the known-size
+    kernel the FETCH_SIZE and WRITE_SIZE counters are scaled by."""
+    n = (1 << 30) // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / 3
+    return {"kernel": "torch.neg fp32 1 GiB -> 1 GiB", "bytes_read": n * 4,
+            "bytes_written": n * 4, "us": us, "GB/s": 2 * n * 4 / (us * 1e-6) / 1e9}
 
 
 def main():
@@ -116,6 +193,8 @@ def main():
     log(f"[bench] warmup {args.warmup} steps")
     for i in range(max(1, args.warmup)):
         layers[i % L].run()
+    for dl in layers:   # every layer's routing, whatever the warm-up count
+        dl.align()
     torch.cuda.synchronize()
     stats = [layer_stats(dl) for dl in layers]
 
@@ -124,7 +203,10 @@ def main():
         for si in range(len(cfg.stages)):
             dl.delta(si)
 
-    graphs = None
+    # A serving engine captures a whole forward pass, all layers, into one graph; likewise
+    # the rotation of L layers is one graph here, and single-layer graphs cover a K that
+    # is not a multiple of L.
+    graph_all, graphs = None, None
     if args.mode == "graph":
         graphs = []
         s = torch.cuda.Stream()
@@ -135,9 +217,14 @@ def main():
                 with torch.cuda.graph(g, stream=s):
                     step_body(dl)
                 graphs.append(g)
+            graph_all = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph_all, stream=s):
+                for dl in layers:
+                    step_body(dl)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         for _ in range(2):
+            graph_all.replay()
             for g in graphs:
                 g.replay()
         torch.cuda.synchronize()
@@ -150,8 +237,10 @@ def main():
     t0 = time.perf_counter()
     ev0.record()
     if graphs is not None:
-        for i in range(K):
-            graphs[i % L].replay()
+        for _ in range(K // L):
+            graph_all.replay()
+        for i in range(K % L):
+            graphs[i].replay()
     else:
         for i in range(K):
             step_body(layers[i % L])
@@ -159,13 +248,25 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     gpu_elapsed = ev0.elapsed_time(ev1) * 1e-3
+    # the layers each step used (the rotation restarts after the full-graph replays)
+    step_layers = [i % L for i in range(L * (K // L))] + list(range(K % L)) \
+        if graphs is not None else [i % L for i in range(K)]
 
-    # ---- per-kernel times: HIP events around every launch, recorded on the launch stream.
-    # A GPU sleep queued first lets the host enqueue all the steps ahead of the GPU, so
-    # the events bracket back-to-back kernels rather than host launch latency.
-    nt = max(L, min(K, 8 * L))
+    # ---- per-kernel times: HIP events on the launch stream around runs of L launches of
+    # one kernel (one per layer), so each run is timed back to back like the kernels of a
+    # step and the event overhead is spread over L launches. Captured graphs cannot hold
+    # timing events on ROCm, so this pass launches the same kernels eagerly on the same
+    # layers (mol_lora_shrink and mol_lora_expand run the kernels mol_lora_delta
+    # enqueues), in dependency order: all aligns, then each stage's shrinks, then its
+    # expands. A GPU sleep queued first lets the host enqueue everything ahead of the GPU.
     nst = len(cfg.stages)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 2)] for _ in range(nt)]
+    rounds = max(1, min(K, 8 * L) // L)
+    launches = [("align", None, lambda dl: dl.align())]
+    for si in range(nst):
+        launches.append(("shrink", si, lambda dl, si=si: dl.shrink(si)))
+        launches.append(("expand", si, lambda dl, si=si: dl.expand(si)))
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in launches] for _ in range(rounds)]
     spacer_ms = 0.0
     if hasattr(torch.cuda, "_sleep"):
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -176,31 +277,39 @@ def main():
         per_cycle_ms = max(c0.elapsed_time(c1), 1e-3) / (1 << 20)
         spacer_ms = 30.0
         torch.cuda._sleep(int(spacer_ms / per_cycle_ms))
-    for i in range(nt):
-        dl = layers[i % L]
-        e = evs[i]
-        e[0].record()
-        dl.align()
-        e[1].record()
-        for si in range(nst):
-            dl.delta(si)
-            e[2 + si].record()
+    for r in range(rounds):
+        for j, (_, _, fn) in enumerate(launches):
+            evs[r][j][0].record()
+            for dl in layers:
+                fn(dl)
+            evs[r][j][1].record()
     torch.cuda.synchronize()
-    align_us = [evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in range(nt)]
-    samples = [[evs[i][1 + si].elapsed_time(evs[i][2 + si]) * 1e3 for i in range(nt)]
-               for si in range(nst)]
-    stage_b = [[stage_bytes(cfg, st, stats[i % L]) for i in range(nt)] for st in cfg.stages]
 
-    steps_P = sum(stats[i % L]["P"] for i in range(K))
+    def per_launch_us(j):
+        return float(np.mean([evs[r][j][0].elapsed_time(evs[r][j][1]) for r in range(rounds)])
+                     ) * 1e3 / L
+
+    align_us = per_launch_us(0)
+    kernels = []
+    for j, (kind, si, _) in enumerate(launches[1:], start=1):
+        st = cfg.stages[si]
+        fn = shrink_bytes if kind == "shrink" else expand_bytes
+        kernels.append({"label": f"{kind} {st.name}", "kernel": kernel_name(cfg, st, kind),
+                        "us": per_launch_us(j),
+                        "bytes": float(np.mean([fn(cfg, st, s) for s in stats]))})
+    stage_b = [float(np.mean([stage_bytes(cfg, st, s) for s in stats])) for st in cfg.stages]
+
+    steps_P = sum(stats[l]["P"] for l in step_layers)
     ms_per_step = elapsed / K * 1e3
     value = steps_P / elapsed
-    dom = 0   # gate_up delta carries the most bytes
-    dom_us = float(np.mean(samples[dom]))
-    dom_bytes = float(np.mean(stage_b[dom]))
-    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    delta_us = sum(float(np.mean(samples[si])) for si in range(nst))
-    delta_bytes = sum(float(np.mean(b)) for b in stage_b)
-    timing_src = f"hip-events, eager launches queued behind a {spacer_ms:.0f} ms GPU sleep"
+    dom = max(kernels, key=lambda k: k["us"])
+    achieved = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
+    delta_us = sum(k["us"] for k in kernels)
+    delta_bytes = sum(stage_b)
+    timing_src = (f"hip-events around runs of {L} back-to-back launches of one kernel (one per "
+                  f"layer), {rounds} runs each, eager, queued behind a {spacer_ms:.0f} ms GPU "
+                  f"sleep")
+    traffic, traffic_src = measured_traffic(cfg.name, dom["kernel"])
 
     result = {
         "metric": METRIC,
@@ -223,24 +332,29 @@ def main():
         },
         "us_per_layer": ms_per_step * 1e3,
         "us_per_layer_gpu_events": gpu_elapsed / K * 1e6,
-        "align_us": float(np.mean(align_us)),
+        "align_us": align_us,
         "pairs_per_layer": float(np.mean([s["P"] for s in stats])),
         "touched_virtual_experts": float(np.mean([s["D"] for s in stats])),
-        "delta_us": {st.name: float(np.mean(samples[si])) for si, st in enumerate(cfg.stages)},
+        "kernels": [{"label": k["label"], "kernel": k["kernel"], "us": k["us"],
+                     "GB/s": k["bytes"] / (k["us"] * 1e-6) / 1e9} for k in kernels],
+        "delta_us": delta_us,
         "delta_hbm_frac": delta_bytes / (delta_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
         "kernel_timing": timing_src,
         "roofline": {
-            "kernel": f"delta_fused_kernel ({cfg.stages[dom].name})",
+            "kernel": f"{dom['kernel']} ({dom['label']})",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
-            "bytes_per_launch": dom_bytes,
-            "us_per_launch": dom_us,
+            "traffic": traffic,
+            "traffic_source": traffic_src,
+            "bytes_per_launch": dom["bytes"],
+            "us_per_launch": dom["us"],
         },
     }
+    if args.calibrate_copy:
+        result["copy_calibration"] = copy_calibration(torch)
 
     if args.cpu_seconds > 0:
         import oracle
