@@ -1,6 +1,6 @@
 // C ABI of libmol: host-side validation, sizing and launch (declared in include/mol.h).
 // Every check happens before any HIP call, so argument errors never touch the device.
-#include "../../include/mol.h"
+#include "mol.h"
 
 #include <algorithm>
 #include <atomic>
@@ -221,7 +221,9 @@ MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_
     if (waves < 1) waves = 1;
     const size_t lds = (size_t)waves * nb * sizeof(int) + (size_t)fixed;
     if ((int64_t)lds > device_lds_bytes()) return MOL_E_LIMIT;
-    return hip_status(mol::launch_align_small(a, (int)waves, lds, st));
+    // workgroups that split the output writes (each one rebuilds the routing in LDS)
+    const int groups = (int)std::max<int64_t>(1, std::min<int64_t>(16, cdiv64(numel, 16)));
+    return hip_status(mol::launch_align_small(a, (int)waves, groups, lds, st));
   }
   a.ntiles = (int32_t)cdiv64(numel, mol::kAlignTile);
   int32_t* ws = static_cast<int32_t*>(workspace);

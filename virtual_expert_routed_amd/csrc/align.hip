@@ -156,7 +156,10 @@ __device__ __forceinline__ uint64_t match_key13(int key, bool valid) {
 
 constexpr int kMaxBucketsPerThread = kMaxBuckets / 1024;  // 8
 
-// One workgroup of 1024 threads for numel <= 4096.
+// numel <= 4096: G workgroups of 1024 threads. Every workgroup builds the whole routing in
+// its own LDS (the ids are a few KiB, so the repeated reads hit L2), then writes only
+// its share of the outputs: the pairs p with p % G == g, and the expert ids and padding
+// of the buckets b with b % G == g. No workgroup waits for another.
 // LDS: `waves` counter rows of V+1 ints, 64 ints of scan scratch, then per pair its
 // bucket id and its rank among the earlier pairs of the same bucket in its wave's range
 // (uint16 each).
@@ -167,8 +170,8 @@ constexpr int kMaxBucketsPerThread = kMaxBuckets / 1024;  // 8
 //      hands the row's previous value to its peers, so rank_in_range = old + rank.
 //   C  bucket totals, padded exclusive scan, expert ids; row w of bucket b becomes
 //      off_b + (pairs of b in ranges before w).
-//   D  every thread: sorted[row[w(p)][b(p)] + rank_in_range(p)] = p, fully parallel;
-//      each wave writes the padding of the non-empty buckets its threads own.
+//   D  sorted[row[w(p)][b(p)] + rank_in_range(p)] = p for this workgroup's pairs; each
+//      wave writes the padding of this workgroup's non-empty buckets its threads own.
 __global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a, int waves) {
   extern __shared__ int lds[];
   const int NB = a.V + 1;
@@ -178,6 +181,7 @@ __global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a, int wave
   uint16_t* rel = keys + ((a.numel + 1) & ~1);
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
   const int numel = a.numel;
+  const int g = blockIdx.x, G = gridDim.x;
 
   // A: four pairs per thread per round, loads of ids and slots issued together
   for (int base = 0; base < numel; base += 4 * 1024) {
@@ -225,17 +229,20 @@ __global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a, int wave
   }
   __syncthreads();
 
-  // C: each thread owns a contiguous range of buckets
+  // C: each thread owns a contiguous range of buckets. The counts of a bucket are read
+  // from every row before any is used (rows past `waves` read row 0 and count 0), so
+  // the reads of one bucket issue back to back.
   const int bpt = (NB + (int)blockDim.x - 1) / (int)blockDim.x;
   const int b0 = min(NB, tid * bpt), b1 = min(NB, b0 + bpt);
   int mine = 0;
   for (int b = b0; b < b1; ++b) {
-    int c[4] = {0, 0, 0, 0};
-    for (int w = 0; w < waves; w += 4) {  // independent reads, summed in a fixed order
+    int c = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) c[i] += (w + i < waves) ? table[(w + i) * NB + b] : 0;
+    for (int w = 0; w < 16; ++w) {
+      const int x = table[(w < waves ? w : 0) * NB + b];
+      c += w < waves ? x : 0;
     }
-    mine += round_up((c[0] + c[1]) + (c[2] + c[3]), a.BM);
+    mine += round_up(c, a.BM);
   }
   int total;
   int off = block_excl_scan(mine, sh, &total);
@@ -247,26 +254,34 @@ __global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a, int wave
     pad_from[k] = 0;
     const int b = b0 + k;
     if (b < b1) {
-      int run = off, c = 0;
-      for (int w = 0; w < waves; ++w) {
-        const int cw = table[w * NB + b];
-        table[w * NB + b] = run;
-        run += cw;
-        c += cw;
+      int cw[16];
+#pragma unroll
+      for (int w = 0; w < 16; ++w) {
+        const int x = table[(w < waves ? w : 0) * NB + b];
+        cw[w] = w < waves ? x : 0;
       }
+      int run = off;
+#pragma unroll
+      for (int w = 0; w < 16; ++w) {
+        if (w < waves) table[w * NB + b] = run;
+        run += cw[w];
+      }
+      const int c = run - off;
       const int pc = round_up(c, a.BM);
-      const int eid = (b == a.V) ? -1 : b;
-      for (int j = 0; j < pc / a.BM; ++j) a.expert_ids[off / a.BM + j] = eid;
-      pad_from[k] = off + c;
-      pad_cnt[k] = pc - c;
+      if (b % G == g) {
+        const int eid = (b == a.V) ? -1 : b;
+        for (int j = 0; j < pc / a.BM; ++j) a.expert_ids[off / a.BM + j] = eid;
+        pad_from[k] = off + c;
+        pad_cnt[k] = pc - c;
+      }
       off += pc;
     }
   }
-  if (tid == 0) *a.npp = total;
+  if (tid == 0 && g == 0) *a.npp = total;
   __syncthreads();
 
   // D
-  for (int p = tid; p < numel; p += blockDim.x) {
+  for (int p = g + tid * G; p < numel; p += (int)blockDim.x * G) {
     const int w = p / per;
     a.sorted[table[w * NB + keys[p]] + rel[p]] = p;
   }
@@ -369,9 +384,10 @@ hipError_t launch_virtual_topk(const int32_t* topk_ids, const int32_t* lora_ids,
   return hipGetLastError();
 }
 
-hipError_t launch_align_small(const AlignArgs& a, int waves, size_t lds_bytes,
+hipError_t launch_align_small(const AlignArgs& a, int waves, int groups, size_t lds_bytes,
                               hipStream_t stream) {
-  hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(1024), lds_bytes, stream, a, waves);
+  hipLaunchKernelGGL(align_small_kernel, dim3(groups), dim3(1024), lds_bytes, stream, a,
+                     waves);
   return hipGetLastError();
 }
 

@@ -15,7 +15,7 @@
 //    four pairs at a time. The pairs' x segments go straight into LDS (direct-to-LDS
 //    loads) once per item. The LPR partial sums are combined by a fixed xor tree, so s
 //    is bit-reproducible and needs no split-K partials.
-//  * expand item = (block, CPT*256 output columns): one thread per column holds the
+//  * expand item = (block, 256 output columns): one thread per column holds the
 //    column's r weights in registers; the block's s rows are staged in LDS; out is read,
 //    added to and rounded once.
 // Latency chains are kept short: a block whose real pairs are within its first four
@@ -96,8 +96,10 @@ constexpr int kSLdsFloats = 4096; // s rows staged per expand pass (16 KiB)
 constexpr int kPG = 4;            // pairs sharing one pass over the held weight vectors
 constexpr int kSeg = 8;           // 16-byte weight vectors a lane holds at once
 
-// output columns per thread of an expand item, from the 16-byte vectors per weight row
-__host__ __device__ constexpr int cols_per_thread(int rv) { return rv >= 8 ? 1 : 8 / rv; }
+// Output columns per thread of an expand item. One: at decode, twice as many items of
+// half the weight bytes keep more loads in flight than two columns per thread (measured
+// on MI355X: 12-23 % faster expands at 23 and 128 tokens), and every rank fits.
+__host__ __device__ constexpr int cols_per_thread(int /*rv*/) { return 1; }
 
 __device__ __forceinline__ bool real_pair(int p, int numel) {
   return (unsigned)p < (unsigned)numel;
@@ -340,38 +342,61 @@ __device__ __forceinline__ void store_out(const DeltaArgs& a, int p, int n, floa
     ((float*)a.out)[(int64_t)p * a.ld_out + n] = v;
 }
 
-// out[p, n] = round(out[p, n] + sc * <B_v[n], s_p[slice(n)]>) for the pairs pid[0..nr);
-// the old values of the first kPG pairs were loaded ahead into ov.
+// out[p, n] = round(out[p, n] + sc * <B_v[n], s_p[slice(n)]>) for the pairs pid[0..nr),
+// kPG pairs at a time; ov holds the old values of the first kPG pairs (loaded ahead by the
+// caller), and the old values of each next group are loaded while the current one is
+// computed, so a block of many pairs costs one dependent round trip per kPG pairs.
 template <bool BF16, int RV, int CPT>
 __device__ __forceinline__ void expand_outputs(const DeltaArgs& a, const uint4 (*bv)[RV],
                                                const int* pid, int nr, const float* s_lds,
                                                const int* n, const int* soff, float sc,
                                                const float (*ov)[CPT]) {
   constexpr int VE = BF16 ? 8 : 4;
+  float cur[kPG][CPT];
+#pragma unroll
+  for (int i = 0; i < kPG; ++i) {
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) cur[i][j] = ov[i][j];
+  }
 #pragma unroll 1
-  for (int q = 0; q < nr; ++q) {
-    const int p = pid[q];
-    const float* s_row = s_lds + q * a.R;
+  for (int q0 = 0; q0 < nr; q0 += kPG) {
+    float nxt[kPG][CPT] = {};
+    if (q0 + kPG < nr) {  // uniform over the workgroup
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      if (n[j] >= a.N) continue;
-      const float* sv = s_row + soff[j];
-      float acc = 0.f;
+      for (int i = 0; i < kPG; ++i) {
+        const int q = q0 + kPG + i;
+        const bool qok = q < nr;
+        const int pq = pid[qok ? q : 0];
 #pragma unroll
-      for (int v = 0; v < RV; ++v) {
-        // keep the weights packed across pairs: unpacking them once for all pairs would
-        // hold RV*8 more floats per column live, for no gain at one or two pairs a block
-        uint4 b = bv[j][v];
-        asm volatile("" : "+v"(b.x), "+v"(b.y), "+v"(b.z), "+v"(b.w));
-        acc = dot16_s<BF16>(b, sv + v * VE, acc);
+        for (int j = 0; j < CPT; ++j) nxt[i][j] = load_out<BF16>(a, pq, n[j], qok && n[j] < a.N);
       }
-      float old;
-      if (q < kPG) {
-        old = q == 0 ? ov[0][j] : q == 1 ? ov[1][j] : q == 2 ? ov[2][j] : ov[3][j];
-      } else {
-        old = load_out<BF16>(a, p, n[j], true);
+    }
+#pragma unroll
+    for (int i = 0; i < kPG; ++i) {
+      const int q = q0 + i;
+      if (q >= nr) break;
+      const int p = pid[q];
+      const float* s_row = s_lds + q * a.R;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        if (n[j] >= a.N) continue;
+        const float* sv = s_row + soff[j];
+        float acc = 0.f;
+#pragma unroll
+        for (int v = 0; v < RV; ++v) {
+          // keep the weights packed across pairs: unpacking them once for all pairs would
+          // hold RV*8 more floats per column live, for no gain at one or two pairs a block
+          uint4 b = bv[j][v];
+          asm volatile("" : "+v"(b.x), "+v"(b.y), "+v"(b.z), "+v"(b.w));
+          acc = dot16_s<BF16>(b, sv + v * VE, acc);
+        }
+        store_out<BF16>(a, p, n[j], fmaf(sc, acc, cur[i][j]));
       }
-      store_out<BF16>(a, p, n[j], fmaf(sc, acc, old));
+    }
+#pragma unroll
+    for (int i = 0; i < kPG; ++i) {
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) cur[i][j] = nxt[i][j];
     }
   }
 }

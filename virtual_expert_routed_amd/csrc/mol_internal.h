@@ -60,7 +60,7 @@ struct DeltaArgs {
 hipError_t launch_virtual_topk(const int32_t* topk_ids, const int32_t* lora_ids, int32_t M,
                                int32_t topk, int32_t E, int32_t S, int32_t* out,
                                hipStream_t stream);
-hipError_t launch_align_small(const AlignArgs& a, int waves, size_t lds_bytes,
+hipError_t launch_align_small(const AlignArgs& a, int waves, int groups, size_t lds_bytes,
                               hipStream_t stream);
 hipError_t launch_align_large(const AlignArgs& a, hipStream_t stream);
 
