@@ -104,18 +104,26 @@ def expand_bytes(cfg, st, stats):
 
 
 def kernel_name(cfg, st, kind):
-    """The kernel instantiation libmol launches for this stage, as a profiler names it.
+    """The kernel instantiations libmol launches for this stage, as a profiler names them.
     Shrink: rows per work item start at 4 and double while two such items' A rows fit
     32 KiB (at most 32); lanes per row = 256 / rows per item. Expand: 16-byte vectors
     per B row = r * element size / 16."""
     esz = 2 if cfg.dtype == "bf16" else 4
     b = "true" if cfg.dtype == "bf16" else "false"
+    # from 4096 pairs (bf16, BLOCK_M >= 16) blocks of >= 16 pairs go to the MFMA kernels,
+    # launched after the VALU kernel of the same call; the expand also needs r % 32 == 0,
+    # r <= 128 and a slice width that is a multiple of 64
+    mfma = cfg.dtype == "bf16" and cfg.numel >= 4096 and cfg.block_m >= 16
     if kind == "shrink":
         rpi = 4
         while rpi < 32 and rpi * 2 * st.K * esz <= 32768:
             rpi *= 2
-        return f"shrink_kernel<{b}, {256 // rpi}>"
-    return f"expand_kernel<{b}, {st.r * esz // 16}>"
+        name = f"shrink_kernel<{b}, {256 // rpi}>"
+        return name + " + shrink_mfma_kernel" if mfma else name
+    name = f"expand_kernel<{b}, {st.r * esz // 16}>"
+    if mfma and st.r % 32 == 0 and st.r <= 128 and (st.N // st.slices) % 64 == 0:
+        name += f" + expand_mfma_kernel<{st.r // 32}>"
+    return name
 
 
 def delta_source_sha256():

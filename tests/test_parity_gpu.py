@@ -197,6 +197,22 @@ EDGE = [
     _edge_cfg(name="ceiling_large", M=3000, topk=4, E=4095, S=2, hidden=64, rank=8,
               stages=configs._two_stage(64, 32, 8), nolora_count=0, block_m=8,
               sentinel_count=100),
+    # from 4096 pairs on, blocks of >= 16 real pairs take the bf16 MFMA kernels and the
+    # rest the VALU kernels: full blocks, ragged last blocks and small buckets side by side
+    _edge_cfg(name="mfma_blocks", M=1024, topk=4, E=8, S=2, hidden=256, rank=32,
+              stages=configs._two_stage(256, 128, 32), block_m=64, sentinel_count=40,
+              nolora_count=30),
+    _edge_cfg(name="mfma_r64_zipf", M=2048, topk=2, E=16, S=2, hidden=256, rank=64,
+              stages=configs._two_stage(256, 192, 64), block_m=64, sentinel_count=20,
+              nolora_count=50, expert_dist="zipf"),
+    _edge_cfg(name="mfma_bm128", M=1024, topk=4, E=8, S=2, hidden=128, rank=32,
+              stages=configs._two_stage(128, 64, 32), block_m=128, sentinel_count=10,
+              nolora_count=10),
+    # k tails past the 256-wide staged chunk, and an expand slice width (136) that is not a
+    # multiple of 64, which keeps the expand on the VALU kernel
+    _edge_cfg(name="mfma_ragged_k", M=1024, topk=4, E=8, S=2, hidden=264, rank=32,
+              stages=configs._two_stage(264, 136, 32), block_m=64, sentinel_count=10,
+              nolora_count=10),
 ]
 
 

@@ -35,11 +35,6 @@ int device_lds_bytes() {
   return v;
 }
 
-int bits_for(int32_t v) {  // bits needed to represent values in [0, v]
-  int b = 0;
-  while (b < 31 && (int64_t(1) << b) <= v) ++b;
-  return b;
-}
 
 mol_status hip_status(hipError_t e) { return e == hipSuccess ? MOL_OK : MOL_E_HIP; }
 
@@ -174,8 +169,8 @@ MOL_API int64_t mol_align_workspace_bytes(int64_t numel, int32_t num_virtual,
   if (mb < 0) return mb;
   if (numel <= mol::kAlignSmallMax) return 0;
   const int64_t nb = (int64_t)num_virtual + 1;
-  const int64_t ntiles = cdiv64(numel, mol::kAlignTile);
-  return round256((ntiles * nb + 2 * nb) * (int64_t)sizeof(int32_t));
+  const int64_t ntiles = cdiv64(numel, mol::align_tile(numel));
+  return round256((ntiles * nb + nb) * (int64_t)sizeof(int32_t));
 }
 
 MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_ids,
@@ -205,7 +200,6 @@ MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_
   a.numel = (int32_t)numel;
   a.V = (int32_t)V64;
   a.BM = block_m;
-  a.nbits = bits_for(a.V);
   a.sorted = sorted_ids;
   a.expert_ids = expert_ids;
   a.npp = num_post_padded;
@@ -225,13 +219,59 @@ MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_
     const int groups = (int)std::max<int64_t>(1, std::min<int64_t>(16, cdiv64(numel, 16)));
     return hip_status(mol::launch_align_small(a, (int)waves, groups, lds, st));
   }
-  a.ntiles = (int32_t)cdiv64(numel, mol::kAlignTile);
+  a.tile = (int32_t)mol::align_tile(numel);
+  a.ntiles = (int32_t)cdiv64(numel, a.tile);
   int32_t* ws = static_cast<int32_t*>(workspace);
   a.counts = ws;
-  a.bucket_off = ws + (int64_t)a.ntiles * nb;
-  a.bucket_cnt = a.bucket_off + nb;
-  return hip_status(mol::launch_align_large(a, st));
+  a.totals = ws + (int64_t)a.ntiles * nb;
+  // offsets, cursors and the tile's keys in LDS
+  const size_t lds = (size_t)(2 * nb + 64) * sizeof(int) + (size_t)a.tile * 2;
+  if ((int64_t)lds > device_lds_bytes()) return MOL_E_LIMIT;
+  return hip_status(mol::launch_align_large(a, lds, st));
 }
+
+}  // extern "C"
+
+namespace {
+
+// Blocks with at least this many real pairs take the bf16 MFMA kernels (0: none do). The
+// MFMA kernels are only launched for batches large enough to hold such blocks in numbers.
+int32_t shrink_mfma_min(bool bf16, int32_t numel, int32_t block_m) {
+  return (bf16 && numel >= mol::kMfmaMinNumel && block_m >= mol::kMfmaMinPairs)
+             ? mol::kMfmaMinPairs
+             : 0;
+}
+
+// The MFMA expand also needs whole 32-wide rank steps, 64-column groups inside one slice,
+// and 8-byte aligned groups of four out elements.
+int32_t expand_mfma_min(bool bf16, int32_t numel, int32_t block_m, int32_t R, int32_t slices,
+                        int32_t N, const void* out, int64_t ld_out) {
+  const int32_t r = R / slices;
+  const bool shape_ok = r % 32 == 0 && r <= 128 && (N / slices) % 64 == 0 && ld_out % 4 == 0 &&
+                        reinterpret_cast<uintptr_t>(out) % 8 == 0;
+  return shape_ok ? shrink_mfma_min(bf16, numel, block_m) : 0;
+}
+
+// VALU shrink over every block (skipping the MFMA ones), then the MFMA shrink if enabled.
+hipError_t shrink_all(mol::DeltaArgs a, bool bf16, int rpi, int64_t grid, int32_t mfma_min,
+                      hipStream_t st) {
+  a.mfma_min = mfma_min;
+  hipError_t e = mol::launch_shrink(a, bf16, rpi, (int)grid, st);
+  if (e != hipSuccess || mfma_min == 0) return e;
+  return mol::launch_shrink_mfma(a, (int)(a.max_blocks * cdiv64(a.R, 64)), st);
+}
+
+hipError_t expand_all(mol::DeltaArgs a, bool bf16, int64_t grid, int32_t mfma_min,
+                      hipStream_t st) {
+  a.mfma_min = mfma_min;
+  hipError_t e = mol::launch_expand(a, bf16, (int)grid, st);
+  if (e != hipSuccess || mfma_min == 0) return e;
+  return mol::launch_expand_mfma(a, (int)grid, st);
+}
+
+}  // namespace
+
+extern "C" {
 
 MOL_API mol_status mol_lora_shrink(int32_t dtype, const void* xin, int64_t ld_x,
                                    int32_t row_div, const void* A, int32_t R, int32_t K,
@@ -254,7 +294,9 @@ MOL_API mol_status mol_lora_shrink(int32_t dtype, const void* xin, int64_t ld_x,
                                      sorted_ids, expert_ids, num_post_padded, numel,
                                      num_virtual, block_m, s, nullptr, 0, rc.max_blocks);
   a.rgroups = (int32_t)rgroups;
-  return hip_status(mol::launch_shrink(a, bf16, rpi, (int)grid, (hipStream_t)stream));
+  const int32_t mm = shrink_mfma_min(bf16, numel, block_m);
+  if (mm > 0 && rc.max_blocks * cdiv64(R, 64) > kI32Max) return MOL_E_LIMIT;
+  return hip_status(shrink_all(a, bf16, rpi, grid, mm, (hipStream_t)stream));
 }
 
 MOL_API mol_status mol_lora_expand(int32_t dtype, const float* s, int32_t R, int32_t slices,
@@ -280,7 +322,8 @@ MOL_API mol_status mol_lora_expand(int32_t dtype, const float* s, int32_t R, int
   a.nchunk = (int32_t)cdiv64(N, mol::expand_cols_per_item(R, slices, bf16 ? 2 : 4));
   const int64_t grid = rc.max_blocks * a.nchunk;
   if (grid > kI32Max) return MOL_E_LIMIT;
-  return hip_status(mol::launch_expand(a, bf16, (int)grid, (hipStream_t)stream));
+  const int32_t mm = expand_mfma_min(bf16, numel, block_m, R, slices, N, out, ld_out);
+  return hip_status(expand_all(a, bf16, grid, mm, (hipStream_t)stream));
 }
 
 MOL_API int64_t mol_delta_workspace_bytes(int32_t numel, int32_t R, int32_t num_virtual,
@@ -327,10 +370,13 @@ MOL_API mol_status mol_lora_delta(int32_t dtype, const void* xin, int64_t ld_x,
   const int64_t grid_s = rc.max_blocks * (int64_t)a.rgroups;
   const int64_t grid_e = rc.max_blocks * (int64_t)a.nchunk;
   if (grid_s > kI32Max || grid_e > kI32Max) return MOL_E_LIMIT;
+  const int32_t mm_s = shrink_mfma_min(bf16, numel, block_m);
+  const int32_t mm_e = expand_mfma_min(bf16, numel, block_m, R, slices, N, out, ld_out);
+  if (mm_s > 0 && rc.max_blocks * cdiv64(R, 64) > kI32Max) return MOL_E_LIMIT;
   const hipStream_t st = (hipStream_t)stream;
-  const hipError_t err = mol::launch_shrink(a, bf16, rpi, (int)grid_s, st);
+  const hipError_t err = shrink_all(a, bf16, rpi, grid_s, mm_s, st);
   if (err != hipSuccess) return MOL_E_HIP;
-  return hip_status(mol::launch_expand(a, bf16, (int)grid_e, st));
+  return hip_status(expand_all(a, bf16, grid_e, mm_e, st));
 }
 
 }  // extern "C"

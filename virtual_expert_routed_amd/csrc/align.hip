@@ -7,18 +7,20 @@
 // snippet and risk item 2). Inside a bucket the pairs keep ascending order, so the
 // result is unique and reproducible.
 //
-// Design (no atomics anywhere):
-//  * the pairs are cut into contiguous tiles; one wave64 owns a tile and walks it in
-//    chunks of 64 in ascending order;
+// Design (the order of the pairs never depends on atomics or on timing):
+//  * the pairs are cut into contiguous ranges; one wave64 walks a range in chunks of 64
+//    in ascending order;
 //  * inside a chunk, lanes holding the same bucket find each other with one ballot per
-//    key bit (<= 13 ballots); the lowest lane of a group is its leader and the rank of a
+//    key bit (13 ballots); the lowest lane of a group is its leader and the rank of a
 //    lane is the number of group members below it (mbcnt);
-//  * each tile has a private per-bucket counter row (LDS), so a walk only touches its
-//    own row: counts on the first walk, then cursors on the second;
-//  * cursor[tile][b] = off_b + (pairs of bucket b in earlier tiles): prefix sums in
-//    tile order, which gives the stable order across tiles.
-// numel <= 4096 runs as ONE workgroup (16 waves, every row in LDS, one launch); larger
-// inputs run three kernels (count per tile -> scan -> scatter) through a workspace.
+//  * each range has a private per-bucket counter row (LDS), so a walk only touches its
+//    own row;
+//  * cursor[range][b] = off_b + (pairs of bucket b in earlier ranges): prefix sums in
+//    range order, which gives the stable order across ranges.
+// numel <= 4096 runs as up to 16 workgroups that each build the whole routing in LDS and
+// split the writes (one launch); larger inputs run three kernels (count per tile -> scan
+// over tiles -> scatter) through a workspace. The only atomics are the LDS histogram adds
+// of the count kernel, whose result does not depend on their order.
 #include "mol_internal.h"
 
 namespace mol {
@@ -34,17 +36,6 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Lanes of this wave whose `key` equals this lane's (only lanes with `valid` take part).
-__device__ __forceinline__ uint64_t match_key(int key, bool valid, int nbits) {
-  uint64_t peers = wave_ballot(valid);
-  for (int b = 0; b < nbits; ++b) {
-    const bool bit = (key >> b) & 1;
-    const uint64_t ones = wave_ballot(valid && bit);
-    peers &= bit ? ones : ~ones;
-  }
-  return peers;
-}
-
 __device__ __forceinline__ int remap_one(int32_t t, int32_t l, int32_t E, int32_t S) {
   return t < 0 ? t : ((t >= E || l < 0 || l >= S) ? -1 : t + l * E);
 }
@@ -53,38 +44,6 @@ __device__ __forceinline__ int bucket_of(const AlignArgs& a, int p) {
   const int32_t t = a.ids[p];
   const int32_t v = a.lora ? remap_one(t, a.lora[p / a.topk], a.E, a.S) : t;
   return (v >= 0 && v < a.V) ? v : a.V;
-}
-
-// Count the pairs [begin, end) into this walker's private row `hist` (LDS).
-__device__ __forceinline__ void count_walk(const AlignArgs& a, int begin, int end,
-                                           int* hist) {
-  const int lane = lanes_below(~0ull);
-  for (int c = begin; c < end; c += 64) {
-    const int p = c + lane;
-    const bool valid = p < end;
-    const int key = valid ? bucket_of(a, p) : 0;
-    const uint64_t peers = match_key(key, valid, a.nbits);
-    if (valid && lanes_below(peers) == 0) hist[key] += __popcll(peers);
-  }
-}
-
-// Scatter the pairs [begin, end) in ascending order; `cursor` (LDS) holds this walker's
-// next free slot per bucket.
-__device__ __forceinline__ void scatter_walk(const AlignArgs& a, int begin, int end,
-                                             int* cursor) {
-  const int lane = lanes_below(~0ull);
-  for (int c = begin; c < end; c += 64) {
-    const int p = c + lane;
-    const bool valid = p < end;
-    const int key = valid ? bucket_of(a, p) : 0;
-    const uint64_t peers = match_key(key, valid, a.nbits);
-    if (valid) {
-      const int rank = lanes_below(peers);
-      const int base = cursor[key];  // every member reads before the leader writes
-      if (rank == 0) cursor[key] = base + __popcll(peers);
-      a.sorted[base + rank] = p;
-    }
-  }
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts of 1, 2, 4, 8 inside
@@ -299,77 +258,121 @@ __global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a, int wave
   }
 }
 
-// Three-kernel path, kernel 1: per-tile counts -> counts[tile][b].
-__global__ void __launch_bounds__(64) align_count_kernel(AlignArgs a) {
-  extern __shared__ int lds[];
+// numel > 4096: three kernels over a workspace, the pairs cut into ntiles tiles.
+//   count    one workgroup per tile: the tile's histogram in LDS (counts commute, so LDS
+//            atomics are exact here) -> counts[t][b].
+//   scan     one thread per bucket: counts[t][b] becomes the number of pairs of bucket b
+//            in the tiles before t; totals[b] = all pairs of b.
+//   scatter  one workgroup per tile: each one scans the padded totals itself (bucket
+//            offsets in LDS, no extra launch), then wave 0 walks the tile in ascending
+//            order and puts pair p at off_b + (pairs of b in earlier tiles) + (rank of p
+//            among the earlier pairs of b in the tile), while the other waves write the
+//            expert ids and the padding of this tile's share of the buckets.
+__global__ void __launch_bounds__(256) align_count_kernel(AlignArgs a) {
+  extern __shared__ int hist[];
   const int NB = a.V + 1;
-  const int t = blockIdx.x, lane = threadIdx.x;
-  for (int i = lane; i < NB; i += 64) lds[i] = 0;
+  const int t = blockIdx.x, tid = threadIdx.x;
+  for (int i = tid; i < NB; i += 256) hist[i] = 0;
   __syncthreads();
-  const int begin = t * kAlignTile;
-  const int end = min(a.numel, begin + kAlignTile);
-  count_walk(a, begin, end, lds);
+  const int begin = t * a.tile;
+  const int end = min(a.numel, begin + a.tile);
+  for (int base = begin; base < end; base += 4 * 256) {
+    int key[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = base + i * 256 + tid;
+      key[i] = p < end ? bucket_of(a, p) : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (key[i] >= 0) atomicAdd(&hist[key[i]], 1);
+  }
   __syncthreads();
   int32_t* row = a.counts + (int64_t)t * NB;
-  for (int i = lane; i < NB; i += 64) row[i] = lds[i];
+  for (int i = tid; i < NB; i += 256) row[i] = hist[i];
 }
 
-// Kernel 2 (one workgroup of 1024): bucket totals, padded offsets, per-tile cursors.
-__global__ void __launch_bounds__(1024) align_scan_kernel(AlignArgs a) {
-  extern __shared__ int lds[];
+__global__ void __launch_bounds__(256) align_scan_kernel(AlignArgs a) {
   const int NB = a.V + 1;
-  int* ctot = lds;        // [NB]
-  int* sh = lds + NB;     // scan scratch
-  const int tid = threadIdx.x;
-  // column pass (coalesced): counts -> exclusive prefix over tiles, totals to LDS
-  for (int b = tid; b < NB; b += blockDim.x) {
-    int run = 0;
-    for (int t = 0; t < a.ntiles; ++t) {
-      int32_t* q = a.counts + (int64_t)t * NB + b;
-      const int c = *q;
-      *q = run;
-      run += c;
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b >= NB) return;
+  int run = 0;
+  for (int t0 = 0; t0 < a.ntiles; t0 += 8) {
+    int c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {  // eight independent reads per round trip
+      const int t = t0 + i < a.ntiles ? t0 + i : 0;
+      c[i] = a.counts[(int64_t)t * NB + b];
     }
-    ctot[b] = run;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (t0 + i < a.ntiles) {
+        a.counts[(int64_t)(t0 + i) * NB + b] = run;
+        run += c[i];
+      }
+    }
   }
-  __syncthreads();
-  const int bpt = (NB + (int)blockDim.x - 1) / (int)blockDim.x;
-  const int b0 = min(NB, tid * bpt), b1 = min(NB, b0 + bpt);
-  int mine = 0;
-  for (int b = b0; b < b1; ++b) mine += round_up(ctot[b], a.BM);
-  int total;
-  int off = block_excl_scan(mine, sh, &total);
-  for (int b = b0; b < b1; ++b) {
-    const int c = ctot[b];
-    a.bucket_cnt[b] = c;
-    a.bucket_off[b] = off;
-    ctot[b] = off;
-    off += round_up(c, a.BM);
-  }
-  if (tid == 0) *a.npp = total;
-  __syncthreads();
-  // cursor pass (coalesced): cursor[t][b] = off_b + pairs of b in tiles before t
-  for (int b = tid; b < NB; b += blockDim.x) {
-    const int o = ctot[b];
-    for (int t = 0; t < a.ntiles; ++t) a.counts[(int64_t)t * NB + b] += o;
-  }
+  a.totals[b] = run;
 }
 
-// Kernel 3: padding + expert ids for this tile's share of the buckets, then the scatter.
-__global__ void __launch_bounds__(64) align_scatter_kernel(AlignArgs a) {
+constexpr int kScanBucketsPerThread = kMaxBuckets / 256;  // 32
+
+__global__ void __launch_bounds__(256) align_scatter_kernel(AlignArgs a) {
   extern __shared__ int lds[];
   const int NB = a.V + 1;
-  const int t = blockIdx.x, lane = threadIdx.x;
-  const int32_t* row = a.counts + (int64_t)t * NB;
-  for (int i = lane; i < NB; i += 64) lds[i] = row[i];
-  const int bb0 = (int)((int64_t)NB * t / a.ntiles);
-  const int bb1 = (int)((int64_t)NB * (t + 1) / a.ntiles);
-  for (int b = bb0; b < bb1; ++b)
-    write_bucket_tail(a, b, a.bucket_cnt[b], a.bucket_off[b], lane, 64);
+  int* off = lds;               // [NB] padded offset of each bucket
+  int* cur = lds + NB;          // [NB] next slot of each bucket for this tile
+  int* sh = lds + 2 * NB;       // scan scratch (64)
+  uint16_t* keys = reinterpret_cast<uint16_t*>(sh + 64);  // [tile]
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int wid = tid >> 6, lane = tid & 63;
+  const int begin = t * a.tile;
+  const int end = min(a.numel, begin + a.tile);
+  for (int p = begin + tid; p < end; p += 256) keys[p - begin] = (uint16_t)bucket_of(a, p);
+  // padded exclusive scan of the totals: thread tid owns buckets [b0, b1)
+  const int bpt = (NB + 255) / 256;
+  const int b0 = min(NB, tid * bpt), b1 = min(NB, b0 + bpt);
+  int cnt[kScanBucketsPerThread];
+  int mine = 0;
+#pragma unroll
+  for (int k = 0; k < kScanBucketsPerThread; ++k) {
+    const int b = b0 + k;
+    cnt[k] = b < b1 ? a.totals[b] : 0;
+    mine += round_up(cnt[k], a.BM);
+  }
+  int total;
+  int o = block_excl_scan(mine, sh, &total);
+#pragma unroll
+  for (int k = 0; k < kScanBucketsPerThread; ++k) {
+    const int b = b0 + k;
+    if (b < b1) {
+      off[b] = o;
+      o += round_up(cnt[k], a.BM);
+    }
+  }
+  if (t == 0 && tid == 0) *a.npp = total;
   __syncthreads();
-  const int begin = t * kAlignTile;
-  const int end = min(a.numel, begin + kAlignTile);
-  scatter_walk(a, begin, end, lds);
+  const int32_t* row = a.counts + (int64_t)t * NB;
+  for (int b = tid; b < NB; b += 256) cur[b] = off[b] + row[b];
+  __syncthreads();
+  if (wid == 0) {
+    for (int c = begin; c < end; c += 64) {
+      const int p = c + lane;
+      const bool valid = p < end;
+      const int key = valid ? keys[p - begin] : 0;
+      const uint64_t peers = match_key13(key, valid);
+      if (valid) {
+        const int rank = lanes_below(peers);
+        const int base = cur[key];  // every member reads before the leader writes
+        if (rank == 0) cur[key] = base + __popcll(peers);
+        a.sorted[base + rank] = p;
+      }
+    }
+  } else {
+    const int bb0 = (int)((int64_t)NB * t / a.ntiles);
+    const int bb1 = (int)((int64_t)NB * (t + 1) / a.ntiles);
+    for (int b = bb0; b < bb1; ++b) write_bucket_tail(a, b, a.totals[b], off[b], tid - 64, 192);
+  }
 }
 
 }  // namespace
@@ -391,16 +394,17 @@ hipError_t launch_align_small(const AlignArgs& a, int waves, int groups, size_t 
   return hipGetLastError();
 }
 
-hipError_t launch_align_large(const AlignArgs& a, hipStream_t stream) {
+hipError_t launch_align_large(const AlignArgs& a, size_t scatter_lds_bytes,
+                              hipStream_t stream) {
   const size_t nb_bytes = (size_t)(a.V + 1) * sizeof(int);
-  hipLaunchKernelGGL(align_count_kernel, dim3(a.ntiles), dim3(64), nb_bytes, stream, a);
+  hipLaunchKernelGGL(align_count_kernel, dim3(a.ntiles), dim3(256), nb_bytes, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(align_scan_kernel, dim3(1), dim3(1024), nb_bytes + 64 * sizeof(int),
-                     stream, a);
+  hipLaunchKernelGGL(align_scan_kernel, dim3((a.V + 1 + 255) / 256), dim3(256), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(align_scatter_kernel, dim3(a.ntiles), dim3(64), nb_bytes, stream, a);
+  hipLaunchKernelGGL(align_scatter_kernel, dim3(a.ntiles), dim3(256), scatter_lds_bytes,
+                     stream, a);
   return hipGetLastError();
 }
 

@@ -29,156 +29,10 @@
 // workspace. A single launch that hands s between workgroups was measured to cost more
 // than the kernel boundary: the handoff needs a store that reaches the coherence point, a
 // counter and a poll, each a full memory round trip under load.
-#include "mol_internal.h"
+#include "delta_common.h"
 
 namespace mol {
 namespace {
-
-__device__ __forceinline__ uint4 ld16(const void* p) {
-  return *reinterpret_cast<const uint4*>(p);
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-// acc += <a, x> over one 16-byte vector of each
-template <bool BF16>
-__device__ __forceinline__ float dot16(const uint4& a, const uint4& x, float acc) {
-  if constexpr (BF16) {
-    acc = fmaf(bf16_lo(a.x), bf16_lo(x.x), acc);
-    acc = fmaf(bf16_hi(a.x), bf16_hi(x.x), acc);
-    acc = fmaf(bf16_lo(a.y), bf16_lo(x.y), acc);
-    acc = fmaf(bf16_hi(a.y), bf16_hi(x.y), acc);
-    acc = fmaf(bf16_lo(a.z), bf16_lo(x.z), acc);
-    acc = fmaf(bf16_hi(a.z), bf16_hi(x.z), acc);
-    acc = fmaf(bf16_lo(a.w), bf16_lo(x.w), acc);
-    acc = fmaf(bf16_hi(a.w), bf16_hi(x.w), acc);
-  } else {
-    acc = fmaf(__uint_as_float(a.x), __uint_as_float(x.x), acc);
-    acc = fmaf(__uint_as_float(a.y), __uint_as_float(x.y), acc);
-    acc = fmaf(__uint_as_float(a.z), __uint_as_float(x.z), acc);
-    acc = fmaf(__uint_as_float(a.w), __uint_as_float(x.w), acc);
-  }
-  return acc;
-}
-
-// acc += <b, s[0:VE]> with b one 16-byte vector of weights, s fp32 in LDS
-template <bool BF16>
-__device__ __forceinline__ float dot16_s(const uint4& b, const float* s, float acc) {
-  if constexpr (BF16) {
-    acc = fmaf(bf16_lo(b.x), s[0], acc);
-    acc = fmaf(bf16_hi(b.x), s[1], acc);
-    acc = fmaf(bf16_lo(b.y), s[2], acc);
-    acc = fmaf(bf16_hi(b.y), s[3], acc);
-    acc = fmaf(bf16_lo(b.z), s[4], acc);
-    acc = fmaf(bf16_hi(b.z), s[5], acc);
-    acc = fmaf(bf16_lo(b.w), s[6], acc);
-    acc = fmaf(bf16_hi(b.w), s[7], acc);
-  } else {
-    acc = fmaf(__uint_as_float(b.x), s[0], acc);
-    acc = fmaf(__uint_as_float(b.y), s[1], acc);
-    acc = fmaf(__uint_as_float(b.z), s[2], acc);
-    acc = fmaf(__uint_as_float(b.w), s[3], acc);
-  }
-  return acc;
-}
-
-constexpr int kThreads = 256;
-constexpr int kPidSlots = 64;     // pair ids staged per pass over a block
-constexpr int kSLdsFloats = 4096; // s rows staged per expand pass (16 KiB)
-constexpr int kPG = 4;            // pairs sharing one pass over the held weight vectors
-constexpr int kSeg = 8;           // 16-byte weight vectors a lane holds at once
-
-// Output columns per thread of an expand item. One: at decode, twice as many items of
-// half the weight bytes keep more loads in flight than two columns per thread (measured
-// on MI355X: 12-23 % faster expands at 23 and 128 tokens), and every rank fits.
-__host__ __device__ constexpr int cols_per_thread(int /*rv*/) { return 1; }
-
-__device__ __forceinline__ bool real_pair(int p, int numel) {
-  return (unsigned)p < (unsigned)numel;
-}
-
-__device__ __forceinline__ bool real_expert(int e, int V) { return (unsigned)e < (unsigned)V; }
-
-// blocks that carry work: [0, npp / BM) clamped to the launched bound
-__device__ __forceinline__ int live_blocks(const DeltaArgs& a, int npp) {
-  const int nb = npp / a.BM;
-  return nb < 0 ? 0 : (nb > a.max_blocks ? a.max_blocks : nb);
-}
-
-// Expert id of block blk if the block carries work, else -1. Both loads go out together
-// (blk < max_blocks, so the expert id read is in bounds even past the live blocks).
-__device__ __forceinline__ int block_expert(const DeltaArgs& a, int blk) {
-  const int npp = *a.npp;
-  const int e = a.expert_ids[blk];
-  return (blk < live_blocks(a, npp) && real_expert(e, a.V)) ? e : -1;
-}
-
-// The first kPG entries of block blk as scalars (numel past the block); returns how many
-// are real pairs. *all_here tells whether they are all of the block's real pairs.
-__device__ __forceinline__ int first_pairs(const DeltaArgs& a, int blk, int* p, bool* all_here) {
-  const int32_t* sp = a.sorted + (int64_t)blk * a.BM;
-  int nr = 0;
-#pragma unroll
-  for (int i = 0; i < kPG; ++i) {
-    const int v = sp[i < a.BM ? i : 0];
-    p[i] = i < a.BM ? v : a.numel;
-    nr += real_pair(p[i], a.numel) ? 1 : 0;
-  }
-  *all_here = nr < kPG || a.BM <= kPG;
-  return nr;
-}
-
-// Branch-free 16-byte load: a masked address is clamped to the array's first element
-// and its value replaced by zero.
-__device__ __forceinline__ uint4 ld16_if(const char* base, int64_t off, bool ok) {
-  const uint4 v = ld16(base + (ok ? off : 0));
-  return ok ? v : make_uint4(0, 0, 0, 0);
-}
-
-// Raw buffer loads over one expert's weight matrix: the resource covers exactly that
-// matrix, offsets are 32-bit, and an offset past its end reads as zero in hardware, so
-// masked lanes need neither a branch nor a select nor a 64-bit address of their own.
-constexpr uint32_t kOutOfRange = 0x80000000u;
-constexpr int kBufferFlags = 0x00020000;  // raw 32-bit-element buffer, gfx9 data format
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t expert_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferFlags);
-}
-
-__device__ __forceinline__ uint4 buf16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return *reinterpret_cast<const uint4*>(&v);
-}
-
-// Direct-to-LDS 16-byte load: lane i of the wave writes at lds_wave_base + 16*i.
-__device__ __forceinline__ void lds_dma16(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base,
-                                   16, 0, 0);
-}
-
-// Entry j0 + lane of block blk for the lanes of wave 0 (numel for entries past the block).
-__device__ __forceinline__ int load_pid(const DeltaArgs& a, int blk, int j0) {
-  const int j = j0 + (int)threadIdx.x;
-  const int v = a.sorted[(int64_t)blk * a.BM + (j < a.BM ? j : 0)];
-  return j < a.BM ? v : a.numel;
-}
-
-// Wave 0 publishes its pair ids and the number of real ones (they form a prefix).
-__device__ __forceinline__ void publish_pids(const DeltaArgs& a, int pv, int* pid, int* nreal) {
-  if (threadIdx.x < kPidSlots) {
-    pid[threadIdx.x] = pv;
-    const uint64_t m = __builtin_amdgcn_ballot_w64(real_pair(pv, a.numel));
-    if (threadIdx.x == 0) *nreal = (int)__popcll(m);
-  }
-}
 
 // ------------------------------------------------------------------------------ shrink
 // Lane lr of a row's LPR-lane group owns the 16-byte vectors lr, lr+LPR, lr+2*LPR, ...
@@ -277,6 +131,7 @@ __device__ __forceinline__ void shrink_block(const DeltaArgs& a, int blk, int rg
   const int n4 = first_pairs(a, blk, p, &all_here);
   const int e = block_expert(a, blk);
   if (e < 0) return;
+  if (a.mfma_min > 0 && block_has(a, blk, a.mfma_min)) return;  // the MFMA kernel's block
   if (all_here) {  // the common decode case: no id staging at all
     if (n4 > 0) shrink_group<BF16, LPR>(a, e, rg, p, n4, xs);
     return;
@@ -321,25 +176,6 @@ __device__ __forceinline__ void load_b_rows(const DeltaArgs& a, int e, const int
     for (int v = 0; v < RV; ++v)
       bv[j][v] = buf16(rb, ok ? (uint32_t)n[j] * RB + v * 16 : kOutOfRange);
   }
-}
-
-template <bool BF16>
-__device__ __forceinline__ float load_out(const DeltaArgs& a, int p, int n, bool ok) {
-  const int64_t i = ok ? (int64_t)p * a.ld_out + n : 0;
-  float v;
-  if constexpr (BF16)
-    v = __uint_as_float((uint32_t)((const uint16_t*)a.out)[i] << 16);
-  else
-    v = ((const float*)a.out)[i];
-  return ok ? v : 0.f;
-}
-
-template <bool BF16>
-__device__ __forceinline__ void store_out(const DeltaArgs& a, int p, int n, float v) {
-  if constexpr (BF16)
-    ((uint16_t*)a.out)[(int64_t)p * a.ld_out + n] = f32_to_bf16_rne(v);
-  else
-    ((float*)a.out)[(int64_t)p * a.ld_out + n] = v;
 }
 
 // out[p, n] = round(out[p, n] + sc * <B_v[n], s_p[slice(n)]>) for the pairs pid[0..nr),
@@ -414,6 +250,7 @@ __device__ __forceinline__ void expand_block(const DeltaArgs& a, int blk, int ch
   const int n4 = first_pairs(a, blk, p, &all_here);
   const int e = block_expert(a, blk);
   if (e < 0) return;
+  if (a.mfma_min > 0 && block_has(a, blk, a.mfma_min)) return;  // the MFMA kernel's block
   const int width = a.N / a.slices;
   int n[CPT], soff[CPT];
 #pragma unroll
@@ -513,7 +350,7 @@ hipError_t expand_dispatch(const DeltaArgs& a, int rv, int grid, hipStream_t st)
 
 int expand_cols_per_item(int32_t R, int32_t slices, int elem_bytes) {
   const int rv = (R / slices) * elem_bytes / 16;
-  return cols_per_thread(rv) * kThreads;
+  return cols_per_thread(rv) * kThreads;  // = kExpandCols
 }
 
 int shrink_rows_per_item(int32_t K, int elem_bytes) {

@@ -1,0 +1,306 @@
+// bf16 MFMA shrink and expand for the aligned blocks that hold many pairs (MindLab sglang
+// PR 24: the MoL shrink hidden -> rank and expand rank -> N stages; same definitions as
+// the VALU kernels):
+//
+//   shrink: s[p, i]   = sum_k A[v, i, k] * xin[p / row_div, k]
+//   expand: out[p, n] = round(out[p, n] + scale[v / E] * sum_j B[v, n, j] * s[p, g(n)*r + j])
+//
+// At prefill a hot virtual expert's block carries up to BLOCK_M real pairs, so a block is a
+// real dense tile and the products run on v_mfma_f32_16x16x32_bf16 (fp32 accumulation).
+// These kernels take only blocks with at least mfma_min real pairs; the VALU kernels of the
+// same launch skip exactly those blocks, so every block is computed once.
+//
+// MFMA 16x16x32 operand layout (lane l of a wave): A holds row l % 16, k = 8*(l/16)..+8;
+// B holds column l % 16, k = 8*(l/16)..+8; the 16x16 fp32 result holds column l % 16,
+// rows 4*(l/16)..+4.
+//
+//  * shrink item = (block, 64 rows of A_v); wave w owns the block's pairs 16w..16w+15
+//    (MFMA A operand = their x rows, straight from global) and all 64 rows of A_v (MFMA B
+//    operand), which are staged per 256-wide k chunk in LDS by direct-to-LDS loads,
+//    double buffered, with an XOR swizzle of the 16-byte slots so the fragment reads are
+//    free of bank conflicts. Pairs of a block beyond 64 are done 64 at a time.
+//  * expand item = (block, 256 output columns); the product is taken transposed, D = B_v s^T,
+//    so a lane's four results are four adjacent columns of one out row (one 8-byte read and
+//    write). MFMA A operand = rows of B_v (held in registers for the whole block), B operand
+//    = s rows split into a bf16 high part and a bf16 remainder, two MFMAs per step, which
+//    keeps s to about 16 significant bits instead of bf16's 8.
+#include "delta_common.h"
+
+namespace mol {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kRowsPerPass = 64;  // pairs of a block per pass (4 waves x 16)
+constexpr int kKChunk = 256;      // shrink: k elements staged per chunk
+constexpr int kSlots = kKChunk / 8;  // 16-byte slots of one staged row
+constexpr int kWRows = 64;        // shrink: rows of A_v per work item
+
+__device__ __forceinline__ floatx4_t mfma16(const uint4& a, const uint4& b, floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8_t*>(&a),
+                                                 *reinterpret_cast<const bf16x8_t*>(&b), c, 0,
+                                                 0, 0);
+}
+
+// The pair ids of rows j0..j0+63 of block blk into pid (numel past the block); returns the
+// number of real ones (a prefix). Every thread of the workgroup takes part.
+__device__ __forceinline__ int stage_rows(const DeltaArgs& a, int blk, int j0, int* pid,
+                                          int* nrows_lds) {
+  const int tid = threadIdx.x;
+  __syncthreads();  // the previous pass is done with pid
+  if (tid < kRowsPerPass) {
+    const int j = j0 + tid;
+    const int v = a.sorted[(int64_t)blk * a.BM + (j < a.BM ? j : 0)];
+    const int pv = j < a.BM ? v : a.numel;
+    pid[tid] = pv;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(real_pair(pv, a.numel));
+    if (tid == 0) *nrows_lds = (int)__popcll(m);
+  }
+  __syncthreads();
+  return *nrows_lds;
+}
+
+// ------------------------------------------------------------------------------ shrink
+
+// A_v rows r0..r0+63, k chunk kc0..kc0+255 -> LDS tile [64 rows][32 slots], slot of 16-byte
+// vector kv of row rr at (kv ^ (rr & 15)). Lane i of wave instruction t writes LDS slot
+// (4t + w) * 64 + i, so it fetches the global vector that belongs there. Rows past R and
+// vectors past K read a valid weight instead (finite; they meet zero x or are never stored).
+__device__ __forceinline__ void stage_w(const DeltaArgs& a, const char* av, int r0, int kc0,
+                                        uint4* tile) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nvec = a.K / 8;
+#pragma unroll
+  for (int t = 0; t < kWRows * kSlots / 256; ++t) {
+    const int P = (4 * t + w) * 64 + lane;
+    const int rr = P / kSlots, slot = P % kSlots;
+    const int kv = (kc0 / 8) + (slot ^ (rr & 15));
+    const bool ok = r0 + rr < a.R && kv < nvec;
+    const int64_t off = ok ? ((int64_t)(r0 + rr) * a.K + (int64_t)kv * 8) * 2 : 0;
+    lds_dma16(av + off, tile + (4 * t + w) * 64);
+  }
+}
+
+// x fragments of this wave's 16 pairs for the chunk at kc0: step st holds k = kc0 + 32 st +
+// 8 (l/16) .. +8 of pair row l % 16 (zero past K or for rows that are not real pairs).
+__device__ __forceinline__ void load_x(const DeltaArgs& a, int p, bool real, int kc0,
+                                       uint4* xf) {
+  const int lane = threadIdx.x & 63;
+  const int64_t rowoff = real ? (int64_t)(p / a.row_div) * a.ld_x : 0;
+  const char* xb = (const char*)a.xin;
+#pragma unroll
+  for (int st = 0; st < kKChunk / 32; ++st) {
+    const int k = kc0 + 32 * st + 8 * (lane >> 4);
+    const bool ok = real && k < a.K;
+    xf[st] = ld16_if(xb, (rowoff + k) * 2, ok);
+  }
+}
+
+__global__ void __launch_bounds__(256) shrink_mfma_kernel(DeltaArgs a) {
+  __shared__ __attribute__((aligned(16))) uint4 wt[2][kWRows * kSlots];  // 2 x 32 KiB
+  __shared__ int pid[kRowsPerPass];
+  __shared__ int nrows_lds;
+  const int nrt = (a.R + kWRows - 1) / kWRows;
+  const int blk = blockIdx.x / nrt, r0 = (blockIdx.x % nrt) * kWRows;
+  const int e = block_expert(a, blk);
+  if (e < 0 || !block_has(a, blk, a.mfma_min)) return;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const char* av = (const char*)a.A + (int64_t)e * a.R * a.K * 2;
+  const int nchunks = (a.K + kKChunk - 1) / kKChunk;
+  for (int j0 = 0; j0 < a.BM; j0 += kRowsPerPass) {
+    const int nrows = stage_rows(a, blk, j0, pid, &nrows_lds);
+    if (nrows == 0) break;
+    const bool live = 16 * w < nrows;  // uniform over the wave
+    const int m = 16 * w + (lane & 15);
+    const int p = pid[m];
+    const bool real = m < nrows;
+    floatx4_t acc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    uint4 xf[kKChunk / 32], xn[kKChunk / 32];
+    stage_w(a, av, r0, 0, wt[0]);
+    if (live) load_x(a, p, real, 0, xf);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+      const int buf = c & 1;
+      if (c + 1 < nchunks) {  // next chunk in flight while this one is multiplied
+        stage_w(a, av, r0, (c + 1) * kKChunk, wt[buf ^ 1]);
+        if (live) load_x(a, p, real, (c + 1) * kKChunk, xn);
+      }
+      if (live) {
+#pragma unroll
+        for (int st = 0; st < kKChunk / 32; ++st) {
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) {
+            const int rr = nt * 16 + (lane & 15);
+            const int slot = (4 * st + (lane >> 4)) ^ (rr & 15);
+            const uint4 wf = wt[buf][rr * kSlots + slot];
+            acc[nt] = mfma16(xf[st], wf, acc[nt]);
+          }
+        }
+      }
+      if (c + 1 < nchunks) {
+#pragma unroll
+        for (int st = 0; st < kKChunk / 32; ++st) xf[st] = xn[st];
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();  // chunk c+1 has landed and chunk c is no longer read
+    }
+    if (live) {
+      // result rows 4 (l/16) + i of this wave's tile = pairs, column l % 16 = row of A_v
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int mi = 16 * w + 4 * (lane >> 4) + i;
+        const int pi = pid[mi];
+        if (mi < nrows) {
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) {
+            const int row = r0 + nt * 16 + (lane & 15);
+            if (row < a.R) a.s[(int64_t)pi * a.R + row] = acc[nt][i];
+          }
+        }
+      }
+    }
+    if (nrows < kRowsPerPass) break;
+  }
+}
+
+// ------------------------------------------------------------------------------ expand
+
+// bf16 high part and bf16 remainder of 8 fp32 values (RNE both), packed for MFMA.
+__device__ __forceinline__ void split_bf16(const uint4& f0, const uint4& f1, uint4* hi,
+                                           uint4* lo) {
+  const float v[8] = {__uint_as_float(f0.x), __uint_as_float(f0.y), __uint_as_float(f0.z),
+                      __uint_as_float(f0.w), __uint_as_float(f1.x), __uint_as_float(f1.y),
+                      __uint_as_float(f1.z), __uint_as_float(f1.w)};
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint16_t h0 = f32_to_bf16_rne(v[2 * i]), h1 = f32_to_bf16_rne(v[2 * i + 1]);
+    const uint16_t l0 = f32_to_bf16_rne(v[2 * i] - __uint_as_float((uint32_t)h0 << 16));
+    const uint16_t l1 = f32_to_bf16_rne(v[2 * i + 1] - __uint_as_float((uint32_t)h1 << 16));
+    h[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    l[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+  }
+  *hi = make_uint4(h[0], h[1], h[2], h[3]);
+  *lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+constexpr int kMaxKSteps = 4;  // r <= 128
+
+template <int KS>
+__device__ __forceinline__ void expand_mfma_block(const DeltaArgs& a, int blk, int chunk,
+                                                  int e, int* pid, int* nrows_lds) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = a.R / a.slices, width = a.N / a.slices;
+  const int c0 = chunk * kExpandCols + 64 * w;  // this wave's 64 columns, one slice
+  const int g = (c0 < a.N ? c0 : 0) / width;
+  const float sc = a.scale[e / a.E];
+  // rows of B_v for the wave's columns: A operand, tile nt, step st
+  const int64_t bbytes = (int64_t)a.N * r * 2;
+  const __amdgpu_buffer_rsrc_t rb = expert_rsrc((const char*)a.B + (int64_t)e * bbytes, bbytes);
+  uint4 bf[4][KS];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int n = c0 + 16 * nt + (lane & 15);
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      const int k = 32 * st + 8 * (lane >> 4);
+      bf[nt][st] = buf16(rb, n < a.N ? (uint32_t)((n * r + k) * 2) : kOutOfRange);
+    }
+  }
+  const char* sb = (const char*)a.s;
+  for (int j0 = 0; j0 < a.BM; j0 += kRowsPerPass) {
+    const int nrows = stage_rows(a, blk, j0, pid, nrows_lds);
+    if (nrows == 0) break;
+#pragma unroll 1
+    for (int pt = 0; pt < 4; ++pt) {
+      if (16 * pt >= nrows) break;  // uniform
+      const int m = 16 * pt + (lane & 15);
+      const bool real = m < nrows;
+      const int p = pid[m];
+      // s row of pair m, slice g: B operand (k = 32 st + 8 (l/16) .. +8), split hi + lo
+      uint4 sh[KS], sl[KS];
+      const int64_t srow = real ? ((int64_t)p * a.R + (int64_t)g * r) * 4 : 0;
+#pragma unroll
+      for (int st = 0; st < KS; ++st) {
+        const int k = 32 * st + 8 * (lane >> 4);
+        const uint4 f0 = ld16_if(sb, srow + (int64_t)k * 4, real);
+        const uint4 f1 = ld16_if(sb, srow + (int64_t)k * 4 + 16, real);
+        split_bf16(f0, f1, &sh[st], &sl[st]);
+      }
+      // old out values: column pair (l % 16) of the tile, columns n..n+3
+      uint2 ov[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int n = c0 + 16 * nt + 4 * (lane >> 4);
+        const bool ok = real && n < a.N;
+        const int64_t off = ok ? ((int64_t)p * a.ld_out + n) * 2 : 0;
+        const uint2 v = *reinterpret_cast<const uint2*>((const char*)a.out + off);
+        ov[nt] = ok ? v : make_uint2(0, 0);
+      }
+      floatx4_t acc[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        acc[nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+          acc[nt] = mfma16(bf[nt][st], sh[st], acc[nt]);
+          acc[nt] = mfma16(bf[nt][st], sl[st], acc[nt]);
+        }
+      }
+      if (real) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int n = c0 + 16 * nt + 4 * (lane >> 4);
+          if (n < a.N) {
+            const float o0 = bf16_lo(ov[nt].x), o1 = bf16_hi(ov[nt].x);
+            const float o2 = bf16_lo(ov[nt].y), o3 = bf16_hi(ov[nt].y);
+            const uint32_t w0 = (uint32_t)f32_to_bf16_rne(fmaf(sc, acc[nt][0], o0)) |
+                                ((uint32_t)f32_to_bf16_rne(fmaf(sc, acc[nt][1], o1)) << 16);
+            const uint32_t w1 = (uint32_t)f32_to_bf16_rne(fmaf(sc, acc[nt][2], o2)) |
+                                ((uint32_t)f32_to_bf16_rne(fmaf(sc, acc[nt][3], o3)) << 16);
+            *reinterpret_cast<uint2*>((char*)a.out + ((int64_t)p * a.ld_out + n) * 2) =
+                make_uint2(w0, w1);
+          }
+        }
+      }
+    }
+    if (nrows < kRowsPerPass) break;
+  }
+}
+
+template <int KS>
+__global__ void __launch_bounds__(256) expand_mfma_kernel(DeltaArgs a) {
+  __shared__ int pid[kRowsPerPass];
+  __shared__ int nrows_lds;
+  const int blk = blockIdx.x / a.nchunk, chunk = blockIdx.x % a.nchunk;
+  const int e = block_expert(a, blk);
+  if (e < 0 || !block_has(a, blk, a.mfma_min)) return;
+  expand_mfma_block<KS>(a, blk, chunk, e, pid, &nrows_lds);
+}
+
+}  // namespace
+
+hipError_t launch_shrink_mfma(const DeltaArgs& a, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(shrink_mfma_kernel, dim3(grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_expand_mfma(const DeltaArgs& a, int grid, hipStream_t stream) {
+  switch ((a.R / a.slices) / 32) {
+    case 1: hipLaunchKernelGGL((expand_mfma_kernel<1>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((expand_mfma_kernel<2>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((expand_mfma_kernel<3>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((expand_mfma_kernel<4>), dim3(grid), dim3(256), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mol

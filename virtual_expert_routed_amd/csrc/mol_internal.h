@@ -8,8 +8,9 @@ namespace mol {
 
 constexpr int kMaxBuckets = 8192;     // V + 1 <= 8192
 constexpr int kAlignSmallMax = 4096;  // pairs the one-workgroup align handles
-constexpr int kAlignTile = 2048;      // pairs per tile of the three-kernel align
 constexpr int kShrinkItemBytes = 32768;  // target weight bytes per shrink work item
+constexpr int kMfmaMinPairs = 16;        // a block takes the MFMA path from this many pairs
+constexpr int kMfmaMinNumel = 4096;      // MFMA kernels are launched from this many pairs
 
 struct AlignArgs {
   const int32_t* ids;
@@ -20,15 +21,22 @@ struct AlignArgs {
   int32_t numel;
   int32_t V;             // number of virtual experts; bucket V is the sentinel bucket
   int32_t BM;
-  int32_t nbits;         // bits needed to hold a bucket id in [0, V]
   int32_t* sorted;
   int32_t* expert_ids;
   int32_t* npp;
-  int32_t* counts;       // three-kernel path: [ntiles][V+1] counts, then cursors
-  int32_t* bucket_off;   // three-kernel path: [V+1] padded offsets
-  int32_t* bucket_cnt;   // three-kernel path: [V+1] counts
+  int32_t* counts;       // three-kernel path: [ntiles][V+1] counts, then earlier-tile counts
+  int32_t* totals;       // three-kernel path: [V+1] pairs per bucket
   int32_t ntiles;
+  int32_t tile;          // three-kernel path: pairs per tile
 };
+
+// Tiles of the three-kernel align: at most 64 of them up to 1M pairs (the column scan walks
+// the tiles one by one), at least 512 pairs each, a multiple of 64.
+inline int64_t align_tile(int64_t numel) {
+  int64_t t = (numel + 63) / 64;
+  t = t < 512 ? 512 : (t > 16384 ? 16384 : t);
+  return (t + 63) / 64 * 64;
+}
 
 struct DeltaArgs {
   const void* xin;
@@ -54,6 +62,8 @@ struct DeltaArgs {
   void* out;
   int64_t ld_out;
   int32_t max_blocks;
+  int32_t mfma_min;      // > 0: blocks with at least this many real pairs go to the MFMA
+                         // kernels and the VALU kernels skip them; 0: VALU kernels only
 };
 
 // host-side launchers (return the launch status)
@@ -62,7 +72,7 @@ hipError_t launch_virtual_topk(const int32_t* topk_ids, const int32_t* lora_ids,
                                hipStream_t stream);
 hipError_t launch_align_small(const AlignArgs& a, int waves, int groups, size_t lds_bytes,
                               hipStream_t stream);
-hipError_t launch_align_large(const AlignArgs& a, hipStream_t stream);
+hipError_t launch_align_large(const AlignArgs& a, size_t scatter_lds_bytes, hipStream_t stream);
 
 // rows per shrink item (power of two in [4, 32]) for contraction length K
 int shrink_rows_per_item(int32_t K, int elem_bytes);
@@ -72,5 +82,8 @@ int expand_cols_per_item(int32_t R, int32_t slices, int elem_bytes);
 hipError_t launch_shrink(const DeltaArgs& a, bool bf16, int rows_per_item, int grid,
                          hipStream_t stream);
 hipError_t launch_expand(const DeltaArgs& a, bool bf16, int grid, hipStream_t stream);
+// bf16 MFMA kernels for the blocks with at least a.mfma_min real pairs
+hipError_t launch_shrink_mfma(const DeltaArgs& a, int grid, hipStream_t stream);
+hipError_t launch_expand_mfma(const DeltaArgs& a, int grid, hipStream_t stream);
 
 }  // namespace mol
