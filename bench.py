@@ -110,10 +110,11 @@ def kernel_name(cfg, st, kind):
     per B row = r * element size / 16."""
     esz = 2 if cfg.dtype == "bf16" else 4
     b = "true" if cfg.dtype == "bf16" else "false"
-    # from 4096 pairs (bf16, BLOCK_M >= 16) blocks of >= 16 pairs go to the MFMA kernels,
-    # launched after the VALU kernel of the same call; the expand also needs r % 32 == 0,
-    # r <= 128 and a slice width that is a multiple of 64
-    mfma = cfg.dtype == "bf16" and cfg.numel >= 4096 and cfg.block_m >= 16
+    # from 4096 pairs and 8 pairs per bucket on average (bf16, BLOCK_M >= 4) blocks of >= 4
+    # pairs go to the MFMA kernels, launched after the VALU kernel of the same call; the
+    # expand also needs r % 32 == 0, r <= 128 and a slice width that is a multiple of 64
+    mfma = (cfg.dtype == "bf16" and cfg.numel >= 4096 and cfg.numel >= 8 * (cfg.V + 1)
+            and cfg.block_m >= 4)
     if kind == "shrink":
         rpi = 4
         while rpi < 32 and rpi * 2 * st.K * esz <= 32768:

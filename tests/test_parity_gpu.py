@@ -197,8 +197,9 @@ EDGE = [
     _edge_cfg(name="ceiling_large", M=3000, topk=4, E=4095, S=2, hidden=64, rank=8,
               stages=configs._two_stage(64, 32, 8), nolora_count=0, block_m=8,
               sentinel_count=100),
-    # from 4096 pairs on, blocks of >= 16 real pairs take the bf16 MFMA kernels and the
-    # rest the VALU kernels: full blocks, ragged last blocks and small buckets side by side
+    # from 4096 pairs (8 per bucket on average) on, blocks of >= 4 real pairs take the bf16
+    # MFMA kernels and the rest the VALU kernels: full blocks, ragged last blocks and small
+    # buckets side by side
     _edge_cfg(name="mfma_blocks", M=1024, topk=4, E=8, S=2, hidden=256, rank=32,
               stages=configs._two_stage(256, 128, 32), block_m=64, sentinel_count=40,
               nolora_count=30),

@@ -235,21 +235,25 @@ MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_
 namespace {
 
 // Blocks with at least this many real pairs take the bf16 MFMA kernels (0: none do). The
-// MFMA kernels are only launched for batches large enough to hold such blocks in numbers.
-int32_t shrink_mfma_min(bool bf16, int32_t numel, int32_t block_m) {
-  return (bf16 && numel >= mol::kMfmaMinNumel && block_m >= mol::kMfmaMinPairs)
+// MFMA kernels are only launched for batches large enough to hold such blocks in numbers:
+// from 4096 pairs and 8 pairs per bucket on average. Their grid spans every possible
+// block, so a launch whose blocks are all small would only cost its empty workgroups.
+int32_t shrink_mfma_min(bool bf16, int32_t numel, int32_t num_virtual, int32_t block_m) {
+  return (bf16 && numel >= mol::kMfmaMinNumel &&
+          (int64_t)numel >= 8 * ((int64_t)num_virtual + 1) && block_m >= mol::kMfmaMinPairs)
              ? mol::kMfmaMinPairs
              : 0;
 }
 
-// The MFMA expand also needs whole 32-wide rank steps, 64-column groups inside one slice,
-// and 8-byte aligned groups of four out elements.
-int32_t expand_mfma_min(bool bf16, int32_t numel, int32_t block_m, int32_t R, int32_t slices,
-                        int32_t N, const void* out, int64_t ld_out) {
+// The MFMA expand also needs whole 32-wide rank steps, s rows of at most 256 floats (they
+// are staged in LDS), 64-column groups inside one slice, and 8-byte aligned groups of four
+// out elements.
+int32_t expand_mfma_min(bool bf16, int32_t numel, int32_t num_virtual, int32_t block_m,
+                        int32_t R, int32_t slices, int32_t N, const void* out, int64_t ld_out) {
   const int32_t r = R / slices;
-  const bool shape_ok = r % 32 == 0 && r <= 128 && (N / slices) % 64 == 0 && ld_out % 4 == 0 &&
-                        reinterpret_cast<uintptr_t>(out) % 8 == 0;
-  return shape_ok ? shrink_mfma_min(bf16, numel, block_m) : 0;
+  const bool shape_ok = r % 32 == 0 && r <= 128 && R <= 256 && (N / slices) % 64 == 0 &&
+                        ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 8 == 0;
+  return shape_ok ? shrink_mfma_min(bf16, numel, num_virtual, block_m) : 0;
 }
 
 // VALU shrink over every block (skipping the MFMA ones), then the MFMA shrink if enabled.
@@ -294,7 +298,7 @@ MOL_API mol_status mol_lora_shrink(int32_t dtype, const void* xin, int64_t ld_x,
                                      sorted_ids, expert_ids, num_post_padded, numel,
                                      num_virtual, block_m, s, nullptr, 0, rc.max_blocks);
   a.rgroups = (int32_t)rgroups;
-  const int32_t mm = shrink_mfma_min(bf16, numel, block_m);
+  const int32_t mm = shrink_mfma_min(bf16, numel, num_virtual, block_m);
   if (mm > 0 && rc.max_blocks * cdiv64(R, 64) > kI32Max) return MOL_E_LIMIT;
   return hip_status(shrink_all(a, bf16, rpi, grid, mm, (hipStream_t)stream));
 }
@@ -322,7 +326,8 @@ MOL_API mol_status mol_lora_expand(int32_t dtype, const float* s, int32_t R, int
   a.nchunk = (int32_t)cdiv64(N, mol::expand_cols_per_item(R, slices, bf16 ? 2 : 4));
   const int64_t grid = rc.max_blocks * a.nchunk;
   if (grid > kI32Max) return MOL_E_LIMIT;
-  const int32_t mm = expand_mfma_min(bf16, numel, block_m, R, slices, N, out, ld_out);
+  const int32_t mm =
+      expand_mfma_min(bf16, numel, num_virtual, block_m, R, slices, N, out, ld_out);
   return hip_status(expand_all(a, bf16, grid, mm, (hipStream_t)stream));
 }
 
@@ -370,8 +375,9 @@ MOL_API mol_status mol_lora_delta(int32_t dtype, const void* xin, int64_t ld_x,
   const int64_t grid_s = rc.max_blocks * (int64_t)a.rgroups;
   const int64_t grid_e = rc.max_blocks * (int64_t)a.nchunk;
   if (grid_s > kI32Max || grid_e > kI32Max) return MOL_E_LIMIT;
-  const int32_t mm_s = shrink_mfma_min(bf16, numel, block_m);
-  const int32_t mm_e = expand_mfma_min(bf16, numel, block_m, R, slices, N, out, ld_out);
+  const int32_t mm_s = shrink_mfma_min(bf16, numel, num_virtual, block_m);
+  const int32_t mm_e =
+      expand_mfma_min(bf16, numel, num_virtual, block_m, R, slices, N, out, ld_out);
   if (mm_s > 0 && rc.max_blocks * cdiv64(R, 64) > kI32Max) return MOL_E_LIMIT;
   const hipStream_t st = (hipStream_t)stream;
   const hipError_t err = shrink_all(a, bf16, rpi, grid_s, mm_s, st);

@@ -128,10 +128,10 @@ __device__ __forceinline__ void shrink_block(const DeltaArgs& a, int blk, int rg
                                              int& nreal, uint4* xs) {
   int p[kPG];
   bool all_here;
-  const int n4 = first_pairs(a, blk, p, &all_here);
+  bool mfma;
+  const int n4 = first_pairs(a, blk, p, &all_here, &mfma);
   const int e = block_expert(a, blk);
-  if (e < 0) return;
-  if (a.mfma_min > 0 && block_has(a, blk, a.mfma_min)) return;  // the MFMA kernel's block
+  if (e < 0 || mfma) return;  // no delta, or the MFMA kernel's block
   if (all_here) {  // the common decode case: no id staging at all
     if (n4 > 0) shrink_group<BF16, LPR>(a, e, rg, p, n4, xs);
     return;
@@ -247,10 +247,10 @@ __device__ __forceinline__ void expand_block(const DeltaArgs& a, int blk, int ch
   const int tid = threadIdx.x;
   int p[kPG];
   bool all_here;
-  const int n4 = first_pairs(a, blk, p, &all_here);
+  bool mfma;
+  const int n4 = first_pairs(a, blk, p, &all_here, &mfma);
   const int e = block_expert(a, blk);
-  if (e < 0) return;
-  if (a.mfma_min > 0 && block_has(a, blk, a.mfma_min)) return;  // the MFMA kernel's block
+  if (e < 0 || mfma) return;  // no delta, or the MFMA kernel's block
   const int width = a.N / a.slices;
   int n[CPT], soff[CPT];
 #pragma unroll

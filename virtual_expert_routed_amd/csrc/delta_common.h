@@ -103,9 +103,14 @@ __device__ __forceinline__ bool block_has(const DeltaArgs& a, int blk, int t) {
 }
 
 // The first kPG entries of block blk as scalars (numel past the block); returns how many
-// are real pairs. *all_here tells whether they are all of the block's real pairs.
-__device__ __forceinline__ int first_pairs(const DeltaArgs& a, int blk, int* p, bool* all_here) {
+// are real pairs. *all_here tells whether they are all of the block's real pairs; *mfma
+// whether the block belongs to the MFMA kernels (entry mfma_min - 1 is real), read in the
+// same batch of loads.
+__device__ __forceinline__ int first_pairs(const DeltaArgs& a, int blk, int* p, bool* all_here,
+                                           bool* mfma) {
   const int32_t* sp = a.sorted + (int64_t)blk * a.BM;
+  const bool use = a.mfma_min > 0 && a.mfma_min <= a.BM;
+  const int vm = sp[use ? a.mfma_min - 1 : 0];
   int nr = 0;
 #pragma unroll
   for (int i = 0; i < kPG; ++i) {
@@ -114,6 +119,7 @@ __device__ __forceinline__ int first_pairs(const DeltaArgs& a, int blk, int* p, 
     nr += real_pair(p[i], a.numel) ? 1 : 0;
   }
   *all_here = nr < kPG || a.BM <= kPG;
+  *mfma = use && real_pair(vm, a.numel);
   return nr;
 }
 

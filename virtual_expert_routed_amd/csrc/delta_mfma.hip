@@ -16,14 +16,16 @@
 //
 //  * shrink item = (block, 64 rows of A_v); wave w owns the block's pairs 16w..16w+15
 //    (MFMA A operand = their x rows, straight from global) and all 64 rows of A_v (MFMA B
-//    operand), which are staged per 256-wide k chunk in LDS by direct-to-LDS loads,
+//    operand), which are staged per 128-wide k chunk in LDS by direct-to-LDS loads,
 //    double buffered, with an XOR swizzle of the 16-byte slots so the fragment reads are
 //    free of bank conflicts. Pairs of a block beyond 64 are done 64 at a time.
 //  * expand item = (block, 256 output columns); the product is taken transposed, D = B_v s^T,
 //    so a lane's four results are four adjacent columns of one out row (one 8-byte read and
 //    write). MFMA A operand = rows of B_v (held in registers for the whole block), B operand
-//    = s rows split into a bf16 high part and a bf16 remainder, two MFMAs per step, which
-//    keeps s to about 16 significant bits instead of bf16's 8.
+//    = s rows, staged once per item in LDS (swizzled like the shrink's tile) and split into
+//    a bf16 high part and a bf16 remainder, two MFMAs per step, which keeps s to about 16
+//    significant bits instead of bf16's 8. The old out values of the next 16 pairs are
+//    loaded while the current 16 are multiplied.
 #include "delta_common.h"
 
 namespace mol {
@@ -33,7 +35,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRowsPerPass = 64;  // pairs of a block per pass (4 waves x 16)
-constexpr int kKChunk = 256;      // shrink: k elements staged per chunk
+constexpr int kKChunk = 128;      // shrink: k elements staged per chunk
 constexpr int kSlots = kKChunk / 8;  // 16-byte slots of one staged row
 constexpr int kWRows = 64;        // shrink: rows of A_v per work item
 
@@ -190,17 +192,56 @@ __device__ __forceinline__ void split_bf16(const uint4& f0, const uint4& f1, uin
   *lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
-constexpr int kMaxKSteps = 4;  // r <= 128
+// Old out values of this lane's pair in pair tile pt: columns n..n+3 of each of the wave's
+// four column tiles (zero for rows that are not real pairs).
+__device__ __forceinline__ void load_ov(const DeltaArgs& a, const int* pid, int nrows, int pt,
+                                        int c0, uint2* ov) {
+  const int lane = threadIdx.x & 63;
+  const int m = 16 * pt + (lane & 15);
+  const bool real = m < nrows;
+  const int p = pid[m];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int n = c0 + 16 * nt + 4 * (lane >> 4);
+    const bool ok = real && n < a.N;
+    const int64_t off = ok ? ((int64_t)p * a.ld_out + n) * 2 : 0;
+    const uint2 v = *reinterpret_cast<const uint2*>((const char*)a.out + off);
+    ov[nt] = ok ? v : make_uint2(0, 0);
+  }
+}
+
+// The s rows (R floats) of the pass's pairs -> LDS [64 rows][R/4 slots of 16 bytes], the
+// vector kv of row m at slot kv ^ (m & mask): the fragment reads of 16 rows then hit
+// distinct banks. Lane i of wave instruction t writes slot (4t + w) * 64 + i and fetches
+// the vector that belongs there; rows past the real pairs copy the first pair's row (a
+// written row; its products land in columns that are never stored).
+__device__ __forceinline__ void stage_s(const DeltaArgs& a, const int* pid, int nrows, int mask,
+                                       uint4* s_lds) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int spr = a.R / 4;
+  const char* sb = (const char*)a.s;
+  for (int t = 0; t < a.R / 16; ++t) {
+    const int P = (4 * t + w) * 64 + lane;
+    const int m = P / spr, slot = P % spr;
+    const int kv = slot ^ (m & mask);
+    const int pm = pid[m < nrows ? m : 0];
+    lds_dma16(sb + ((int64_t)pm * a.R + 4 * kv) * 4, s_lds + (4 * t + w) * 64);
+  }
+}
 
 template <int KS>
 __device__ __forceinline__ void expand_mfma_block(const DeltaArgs& a, int blk, int chunk,
-                                                  int e, int* pid, int* nrows_lds) {
+                                                  int e, int* pid, int* nrows_lds,
+                                                  uint4* s_lds) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = a.R / a.slices, width = a.N / a.slices;
   const int c0 = chunk * kExpandCols + 64 * w;  // this wave's 64 columns, one slice
   const int g = (c0 < a.N ? c0 : 0) / width;
   const float sc = a.scale[e / a.E];
+  const int spr = a.R / 4;
+  const int mask = min(16, spr & -spr) - 1;
   // rows of B_v for the wave's columns: A operand, tile nt, step st
   const int64_t bbytes = (int64_t)a.N * r * 2;
   const __amdgpu_buffer_rsrc_t rb = expert_rsrc((const char*)a.B + (int64_t)e * bbytes, bbytes);
@@ -214,35 +255,28 @@ __device__ __forceinline__ void expand_mfma_block(const DeltaArgs& a, int blk, i
       bf[nt][st] = buf16(rb, n < a.N ? (uint32_t)((n * r + k) * 2) : kOutOfRange);
     }
   }
-  const char* sb = (const char*)a.s;
   for (int j0 = 0; j0 < a.BM; j0 += kRowsPerPass) {
     const int nrows = stage_rows(a, blk, j0, pid, nrows_lds);
     if (nrows == 0) break;
+    stage_s(a, pid, nrows, mask, s_lds);
+    uint2 ov[4];
+    load_ov(a, pid, nrows, 0, c0, ov);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int ntiles = (nrows + 15) / 16;
 #pragma unroll 1
-    for (int pt = 0; pt < 4; ++pt) {
-      if (16 * pt >= nrows) break;  // uniform
+    for (int pt = 0; pt < ntiles; ++pt) {
+      uint2 ovn[4];
+      if (pt + 1 < ntiles) load_ov(a, pid, nrows, pt + 1, c0, ovn);  // uniform
       const int m = 16 * pt + (lane & 15);
-      const bool real = m < nrows;
-      const int p = pid[m];
       // s row of pair m, slice g: B operand (k = 32 st + 8 (l/16) .. +8), split hi + lo
       uint4 sh[KS], sl[KS];
-      const int64_t srow = real ? ((int64_t)p * a.R + (int64_t)g * r) * 4 : 0;
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
-        const int k = 32 * st + 8 * (lane >> 4);
-        const uint4 f0 = ld16_if(sb, srow + (int64_t)k * 4, real);
-        const uint4 f1 = ld16_if(sb, srow + (int64_t)k * 4 + 16, real);
+        const int kv0 = (g * r + 32 * st + 8 * (lane >> 4)) / 4;
+        const uint4 f0 = s_lds[m * spr + (kv0 ^ (m & mask))];
+        const uint4 f1 = s_lds[m * spr + ((kv0 + 1) ^ (m & mask))];
         split_bf16(f0, f1, &sh[st], &sl[st]);
-      }
-      // old out values: column pair (l % 16) of the tile, columns n..n+3
-      uint2 ov[4];
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int n = c0 + 16 * nt + 4 * (lane >> 4);
-        const bool ok = real && n < a.N;
-        const int64_t off = ok ? ((int64_t)p * a.ld_out + n) * 2 : 0;
-        const uint2 v = *reinterpret_cast<const uint2*>((const char*)a.out + off);
-        ov[nt] = ok ? v : make_uint2(0, 0);
       }
       floatx4_t acc[4];
 #pragma unroll
@@ -254,7 +288,8 @@ __device__ __forceinline__ void expand_mfma_block(const DeltaArgs& a, int blk, i
           acc[nt] = mfma16(bf[nt][st], sl[st], acc[nt]);
         }
       }
-      if (real) {
+      if (m < nrows) {
+        const int p = pid[m];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
           const int n = c0 + 16 * nt + 4 * (lane >> 4);
@@ -270,6 +305,10 @@ __device__ __forceinline__ void expand_mfma_block(const DeltaArgs& a, int blk, i
           }
         }
       }
+      if (pt + 1 < ntiles) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) ov[nt] = ovn[nt];
+      }
     }
     if (nrows < kRowsPerPass) break;
   }
@@ -277,12 +316,13 @@ __device__ __forceinline__ void expand_mfma_block(const DeltaArgs& a, int blk, i
 
 template <int KS>
 __global__ void __launch_bounds__(256) expand_mfma_kernel(DeltaArgs a) {
+  extern __shared__ uint4 s_lds[];  // [64][R/4]
   __shared__ int pid[kRowsPerPass];
   __shared__ int nrows_lds;
   const int blk = blockIdx.x / a.nchunk, chunk = blockIdx.x % a.nchunk;
   const int e = block_expert(a, blk);
   if (e < 0 || !block_has(a, blk, a.mfma_min)) return;
-  expand_mfma_block<KS>(a, blk, chunk, e, pid, &nrows_lds);
+  expand_mfma_block<KS>(a, blk, chunk, e, pid, &nrows_lds, s_lds);
 }
 
 }  // namespace
@@ -293,11 +333,12 @@ hipError_t launch_shrink_mfma(const DeltaArgs& a, int grid, hipStream_t stream) 
 }
 
 hipError_t launch_expand_mfma(const DeltaArgs& a, int grid, hipStream_t stream) {
+  const size_t lds = (size_t)kRowsPerPass * a.R * sizeof(float);  // s rows of one pass
   switch ((a.R / a.slices) / 32) {
-    case 1: hipLaunchKernelGGL((expand_mfma_kernel<1>), dim3(grid), dim3(256), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((expand_mfma_kernel<2>), dim3(grid), dim3(256), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((expand_mfma_kernel<3>), dim3(grid), dim3(256), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((expand_mfma_kernel<4>), dim3(grid), dim3(256), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((expand_mfma_kernel<1>), dim3(grid), dim3(256), lds, stream, a); break;
+    case 2: hipLaunchKernelGGL((expand_mfma_kernel<2>), dim3(grid), dim3(256), lds, stream, a); break;
+    case 3: hipLaunchKernelGGL((expand_mfma_kernel<3>), dim3(grid), dim3(256), lds, stream, a); break;
+    case 4: hipLaunchKernelGGL((expand_mfma_kernel<4>), dim3(grid), dim3(256), lds, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

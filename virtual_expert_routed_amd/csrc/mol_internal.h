@@ -9,7 +9,7 @@ namespace mol {
 constexpr int kMaxBuckets = 8192;     // V + 1 <= 8192
 constexpr int kAlignSmallMax = 4096;  // pairs the one-workgroup align handles
 constexpr int kShrinkItemBytes = 32768;  // target weight bytes per shrink work item
-constexpr int kMfmaMinPairs = 16;        // a block takes the MFMA path from this many pairs
+constexpr int kMfmaMinPairs = 4;         // a block takes the MFMA path from this many pairs
 constexpr int kMfmaMinNumel = 4096;      // MFMA kernels are launched from this many pairs
 
 struct AlignArgs {
