@@ -127,6 +127,18 @@ def kernel_name(cfg, st, kind):
     return name
 
 
+def reference_ctas(grid_m, n, block_n=64):
+    """Launch grid of a stage in the reference geometry: one CTA per (M block of the
+    worst-case routing buffer, N tile)."""
+    return grid_m * -(-n // block_n)
+
+
+def reference_grid_m(cfg):
+    """Blocks of the reference's worst-case routing buffer: every one of the V + 1 buckets
+    padded by BLOCK_M - 1 (here the delta grids follow the real pairs instead)."""
+    return -(-(cfg.numel + (cfg.V + 1) * (cfg.block_m - 1)) // cfg.block_m)
+
+
 def delta_source_sha256():
     import hashlib
     path = os.path.join(ROOT, "virtual_expert_routed_amd", "csrc", "delta.hip")
@@ -347,6 +359,10 @@ def main():
         "kernels": [{"label": k["label"], "kernel": k["kernel"], "us": k["us"],
                      "GB/s": k["bytes"] / (k["us"] * 1e-6) / 1e9} for k in kernels],
         "delta_us": delta_us,
+        "reference_geometry_ctas": {
+            f"{kind} {st.name}": reference_ctas(reference_grid_m(cfg), st.R if kind == "shrink"
+                                                else st.N // st.slices)
+            for st in cfg.stages for kind in ("shrink", "expand")},
         "delta_hbm_frac": delta_bytes / (delta_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
         "kernel_timing": timing_src,
         "roofline": {
