@@ -246,13 +246,13 @@ int32_t shrink_mfma_min(bool bf16, int32_t numel, int32_t num_virtual, int32_t b
 }
 
 // The MFMA expand also needs whole 32-wide rank steps, s rows of at most 256 floats (they
-// are staged in LDS), 64-column groups inside one slice, and 8-byte aligned groups of four
-// out elements.
+// are staged in LDS), 64-column groups inside one slice, and 16-byte aligned groups of
+// eight out elements.
 int32_t expand_mfma_min(bool bf16, int32_t numel, int32_t num_virtual, int32_t block_m,
                         int32_t R, int32_t slices, int32_t N, const void* out, int64_t ld_out) {
   const int32_t r = R / slices;
   const bool shape_ok = r % 32 == 0 && r <= 128 && R <= 256 && (N / slices) % 64 == 0 &&
-                        ld_out % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 8 == 0;
+                        ld_out % 8 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0;
   return shape_ok ? shrink_mfma_min(bf16, numel, num_virtual, block_m) : 0;
 }
 
@@ -262,7 +262,8 @@ hipError_t shrink_all(mol::DeltaArgs a, bool bf16, int rpi, int64_t grid, int32_
   a.mfma_min = mfma_min;
   hipError_t e = mol::launch_shrink(a, bf16, rpi, (int)grid, st);
   if (e != hipSuccess || mfma_min == 0) return e;
-  return mol::launch_shrink_mfma(a, (int)(a.max_blocks * cdiv64(a.R, 64)), st);
+  return mol::launch_shrink_mfma(
+      a, (int)(a.max_blocks * cdiv64(a.R, mol::shrink_mfma_row_tile(a.R))), st);
 }
 
 hipError_t expand_all(mol::DeltaArgs a, bool bf16, int64_t grid, int32_t mfma_min,

@@ -14,18 +14,21 @@
 // B holds column l % 16, k = 8*(l/16)..+8; the 16x16 fp32 result holds column l % 16,
 // rows 4*(l/16)..+4.
 //
-//  * shrink item = (block, 64 rows of A_v); wave w owns the block's pairs 16w..16w+15
-//    (MFMA A operand = their x rows, straight from global) and all 64 rows of A_v (MFMA B
-//    operand), which are staged per 128-wide k chunk in LDS by direct-to-LDS loads,
-//    double buffered, with an XOR swizzle of the 16-byte slots so the fragment reads are
-//    free of bank conflicts. Pairs of a block beyond 64 are done 64 at a time.
-//  * expand item = (block, 256 output columns); the product is taken transposed, D = B_v s^T,
-//    so a lane's four results are four adjacent columns of one out row (one 8-byte read and
-//    write). MFMA A operand = rows of B_v (held in registers for the whole block), B operand
-//    = s rows, staged once per item in LDS (swizzled like the shrink's tile) and split into
-//    a bf16 high part and a bf16 remainder, two MFMAs per step, which keeps s to about 16
-//    significant bits instead of bf16's 8. The old out values of the next 16 pairs are
-//    loaded while the current 16 are multiplied.
+//  * shrink item = (block, 64 or 128 rows of A_v: 128 when R > 64, so that a block with
+//    R <= 128 reads its gathered x rows once); wave w owns the block's pairs 16w..16w+15
+//    (MFMA A operand = their x rows, straight from global) and all the item's rows of A_v
+//    (MFMA B operand), which are staged per k chunk (128 wide for 64 rows, 64 for 128) in
+//    LDS by direct-to-LDS loads, double buffered, with an XOR swizzle of the 16-byte slots
+//    so the fragment reads are free of bank conflicts. Pairs of a block beyond 64 are done
+//    64 at a time.
+//  * expand item = (block, 256 output columns); the product is taken transposed, D = B_v s^T
+//    (MFMA A operand = rows of B_v, held in registers for the whole block; B operand = s
+//    rows). Only the slices of s that the item's columns use are staged, once per item, in
+//    LDS (swizzled like the shrink's tile), and split into a bf16 high part and a bf16
+//    remainder, two MFMAs per step, which keeps s to about 16 significant bits instead of
+//    bf16's 8. Each 16-pair tile of results goes through an LDS tile so that out is read and
+//    written in whole 512-byte row segments (16-byte vectors); the old out values of the
+//    next 16 pairs are loaded while the current 16 are multiplied.
 #include "delta_common.h"
 
 namespace mol {
@@ -35,9 +38,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRowsPerPass = 64;  // pairs of a block per pass (4 waves x 16)
-constexpr int kKChunk = 128;      // shrink: k elements staged per chunk
-constexpr int kSlots = kKChunk / 8;  // 16-byte slots of one staged row
-constexpr int kWRows = 64;        // shrink: rows of A_v per work item
+constexpr int kKChunk = 128;      // shrink: k elements staged per chunk at 64 rows
 
 __device__ __forceinline__ floatx4_t mfma16(const uint4& a, const uint4& b, floatx4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8_t*>(&a),
@@ -65,20 +66,34 @@ __device__ __forceinline__ int stage_rows(const DeltaArgs& a, int blk, int j0, i
 
 // ------------------------------------------------------------------------------ shrink
 
-// A_v rows r0..r0+63, k chunk kc0..kc0+255 -> LDS tile [64 rows][32 slots], slot of 16-byte
-// vector kv of row rr at (kv ^ (rr & 15)). Lane i of wave instruction t writes LDS slot
+// A shrink item covers 64 * NRT rows of A_v (NRT = 2 when R > 64, so an item with R <= 128
+// reads the block's gathered x rows once), staged per k chunk of kKChunk / NRT: always
+// 16 KiB of LDS per buffer, i.e. 1024 slots of 16 bytes.
+template <int NRT>
+struct ShrinkGeom {
+  static constexpr int kRows = 64 * NRT;
+  static constexpr int kChunk = kKChunk / NRT;  // k elements per staged chunk
+  static constexpr int kSlots = kChunk / 8;     // 16-byte slots of one staged row
+  static constexpr int kSteps = kChunk / 32;    // MFMA k steps per chunk
+  static_assert(kRows * kSlots == 1024, "16 KiB per buffer");
+};
+
+// A_v rows r0..r0+kRows-1, k chunk kc0.. -> LDS tile [kRows][kSlots], slot of 16-byte vector
+// kv of row rr at (kv ^ (rr & (kSlots - 1))). Lane i of wave instruction t writes LDS slot
 // (4t + w) * 64 + i, so it fetches the global vector that belongs there. Rows past R and
 // vectors past K read a valid weight instead (finite; they meet zero x or are never stored).
+template <int NRT>
 __device__ __forceinline__ void stage_w(const DeltaArgs& a, const char* av, int r0, int kc0,
                                         uint4* tile) {
+  using G = ShrinkGeom<NRT>;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nvec = a.K / 8;
 #pragma unroll
-  for (int t = 0; t < kWRows * kSlots / 256; ++t) {
+  for (int t = 0; t < G::kRows * G::kSlots / 256; ++t) {
     const int P = (4 * t + w) * 64 + lane;
-    const int rr = P / kSlots, slot = P % kSlots;
-    const int kv = (kc0 / 8) + (slot ^ (rr & 15));
+    const int rr = P / G::kSlots, slot = P % G::kSlots;
+    const int kv = (kc0 / 8) + (slot ^ (rr & (G::kSlots - 1)));
     const bool ok = r0 + rr < a.R && kv < nvec;
     const int64_t off = ok ? ((int64_t)(r0 + rr) * a.K + (int64_t)kv * 8) * 2 : 0;
     lds_dma16(av + off, tile + (4 * t + w) * 64);
@@ -87,31 +102,35 @@ __device__ __forceinline__ void stage_w(const DeltaArgs& a, const char* av, int 
 
 // x fragments of this wave's 16 pairs for the chunk at kc0: step st holds k = kc0 + 32 st +
 // 8 (l/16) .. +8 of pair row l % 16 (zero past K or for rows that are not real pairs).
+template <int NRT>
 __device__ __forceinline__ void load_x(const DeltaArgs& a, int p, bool real, int kc0,
                                        uint4* xf) {
   const int lane = threadIdx.x & 63;
   const int64_t rowoff = real ? (int64_t)(p / a.row_div) * a.ld_x : 0;
   const char* xb = (const char*)a.xin;
 #pragma unroll
-  for (int st = 0; st < kKChunk / 32; ++st) {
+  for (int st = 0; st < ShrinkGeom<NRT>::kSteps; ++st) {
     const int k = kc0 + 32 * st + 8 * (lane >> 4);
     const bool ok = real && k < a.K;
     xf[st] = ld16_if(xb, (rowoff + k) * 2, ok);
   }
 }
 
+template <int NRT>
 __global__ void __launch_bounds__(256) shrink_mfma_kernel(DeltaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint4 wt[2][kWRows * kSlots];  // 2 x 32 KiB
+  using G = ShrinkGeom<NRT>;
+  constexpr int NT = 4 * NRT;  // 16-row tiles of A_v per wave
+  __shared__ __attribute__((aligned(16))) uint4 wt[2][1024];  // 2 x 16 KiB
   __shared__ int pid[kRowsPerPass];
   __shared__ int nrows_lds;
-  const int nrt = (a.R + kWRows - 1) / kWRows;
-  const int blk = blockIdx.x / nrt, r0 = (blockIdx.x % nrt) * kWRows;
+  const int nrt = (a.R + G::kRows - 1) / G::kRows;
+  const int blk = blockIdx.x / nrt, r0 = (blockIdx.x % nrt) * G::kRows;
   const int e = block_expert(a, blk);
   if (e < 0 || !block_has(a, blk, a.mfma_min)) return;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const char* av = (const char*)a.A + (int64_t)e * a.R * a.K * 2;
-  const int nchunks = (a.K + kKChunk - 1) / kKChunk;
+  const int nchunks = (a.K + G::kChunk - 1) / G::kChunk;
   for (int j0 = 0; j0 < a.BM; j0 += kRowsPerPass) {
     const int nrows = stage_rows(a, blk, j0, pid, &nrows_lds);
     if (nrows == 0) break;
@@ -119,35 +138,35 @@ __global__ void __launch_bounds__(256) shrink_mfma_kernel(DeltaArgs a) {
     const int m = 16 * w + (lane & 15);
     const int p = pid[m];
     const bool real = m < nrows;
-    floatx4_t acc[4];
+    floatx4_t acc[NT];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    uint4 xf[kKChunk / 32], xn[kKChunk / 32];
-    stage_w(a, av, r0, 0, wt[0]);
-    if (live) load_x(a, p, real, 0, xf);
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    uint4 xf[G::kSteps], xn[G::kSteps];
+    stage_w<NRT>(a, av, r0, 0, wt[0]);
+    if (live) load_x<NRT>(a, p, real, 0, xf);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int c = 0; c < nchunks; ++c) {
       const int buf = c & 1;
       if (c + 1 < nchunks) {  // next chunk in flight while this one is multiplied
-        stage_w(a, av, r0, (c + 1) * kKChunk, wt[buf ^ 1]);
-        if (live) load_x(a, p, real, (c + 1) * kKChunk, xn);
+        stage_w<NRT>(a, av, r0, (c + 1) * G::kChunk, wt[buf ^ 1]);
+        if (live) load_x<NRT>(a, p, real, (c + 1) * G::kChunk, xn);
       }
       if (live) {
 #pragma unroll
-        for (int st = 0; st < kKChunk / 32; ++st) {
+        for (int st = 0; st < G::kSteps; ++st) {
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
+          for (int nt = 0; nt < NT; ++nt) {
             const int rr = nt * 16 + (lane & 15);
-            const int slot = (4 * st + (lane >> 4)) ^ (rr & 15);
-            const uint4 wf = wt[buf][rr * kSlots + slot];
+            const int slot = (4 * st + (lane >> 4)) ^ (rr & (G::kSlots - 1));
+            const uint4 wf = wt[buf][rr * G::kSlots + slot];
             acc[nt] = mfma16(xf[st], wf, acc[nt]);
           }
         }
       }
       if (c + 1 < nchunks) {
 #pragma unroll
-        for (int st = 0; st < kKChunk / 32; ++st) xf[st] = xn[st];
+        for (int st = 0; st < G::kSteps; ++st) xf[st] = xn[st];
       }
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();  // chunk c+1 has landed and chunk c is no longer read
@@ -160,7 +179,7 @@ __global__ void __launch_bounds__(256) shrink_mfma_kernel(DeltaArgs a) {
         const int pi = pid[mi];
         if (mi < nrows) {
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
+          for (int nt = 0; nt < NT; ++nt) {
             const int row = r0 + nt * 16 + (lane & 15);
             if (row < a.R) a.s[(int64_t)pi * a.R + row] = acc[nt][i];
           }
@@ -192,55 +211,61 @@ __device__ __forceinline__ void split_bf16(const uint4& f0, const uint4& f1, uin
   *lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
-// Old out values of this lane's pair in pair tile pt: columns n..n+3 of each of the wave's
-// four column tiles (zero for rows that are not real pairs).
-__device__ __forceinline__ void load_ov(const DeltaArgs& a, const int* pid, int nrows, int pt,
-                                        int c0, uint2* ov) {
-  const int lane = threadIdx.x & 63;
-  const int m = 16 * pt + (lane & 15);
-  const bool real = m < nrows;
-  const int p = pid[m];
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int n = c0 + 16 * nt + 4 * (lane >> 4);
-    const bool ok = real && n < a.N;
-    const int64_t off = ok ? ((int64_t)p * a.ld_out + n) * 2 : 0;
-    const uint2 v = *reinterpret_cast<const uint2*>((const char*)a.out + off);
-    ov[nt] = ok ? v : make_uint2(0, 0);
-  }
-}
-
-// The s rows (R floats) of the pass's pairs -> LDS [64 rows][R/4 slots of 16 bytes], the
+// s columns [cb, cb + rs) of the pass's pairs -> LDS [64 rows][rs/4 slots of 16 bytes], the
 // vector kv of row m at slot kv ^ (m & mask): the fragment reads of 16 rows then hit
 // distinct banks. Lane i of wave instruction t writes slot (4t + w) * 64 + i and fetches
 // the vector that belongs there; rows past the real pairs copy the first pair's row (a
 // written row; its products land in columns that are never stored).
-__device__ __forceinline__ void stage_s(const DeltaArgs& a, const int* pid, int nrows, int mask,
-                                       uint4* s_lds) {
+__device__ __forceinline__ void stage_s(const DeltaArgs& a, const int* pid, int nrows, int cb,
+                                       int rs, int mask, uint4* s_lds) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int spr = a.R / 4;
+  const int spr = rs / 4;
   const char* sb = (const char*)a.s;
-  for (int t = 0; t < a.R / 16; ++t) {
+  for (int t = 0; t < rs / 16; ++t) {
     const int P = (4 * t + w) * 64 + lane;
     const int m = P / spr, slot = P % spr;
     const int kv = slot ^ (m & mask);
     const int pm = pid[m < nrows ? m : 0];
-    lds_dma16(sb + ((int64_t)pm * a.R + 4 * kv) * 4, s_lds + (4 * t + w) * 64);
+    lds_dma16(sb + ((int64_t)pm * a.R + cb + 4 * kv) * 4, s_lds + (4 * t + w) * 64);
+  }
+}
+
+constexpr int kTileStride = kExpandCols + 4;  // fp32 result tile row, padded against conflicts
+
+// The out rows of pair tile pt as the epilogue reads them: thread t holds the 16-byte
+// vectors t and t + 256 of the tile's 16 rows x 32 vectors (8 bf16 each), so every wave
+// reads two rows' 512 contiguous bytes. Vectors of rows that are not real pairs read zero.
+__device__ __forceinline__ void load_out_tile(const DeltaArgs& a, const int* pid, int nrows,
+                                              int pt, int chunk, uint4* ov) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int v = t + 256 * h;
+    const int m = 16 * pt + v / 32;
+    const int n = chunk * kExpandCols + (v % 32) * 8;
+    const bool ok = m < nrows && n < a.N;
+    const int64_t off = ok ? ((int64_t)pid[m] * a.ld_out + n) * 2 : 0;
+    ov[h] = ld16_if((const char*)a.out, off, ok);
   }
 }
 
 template <int KS>
 __device__ __forceinline__ void expand_mfma_block(const DeltaArgs& a, int blk, int chunk,
                                                   int e, int* pid, int* nrows_lds,
-                                                  uint4* s_lds) {
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+                                                  uint4* s_lds, float* tile) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = a.R / a.slices, width = a.N / a.slices;
-  const int c0 = chunk * kExpandCols + 64 * w;  // this wave's 64 columns, one slice
-  const int g = (c0 < a.N ? c0 : 0) / width;
   const float sc = a.scale[e / a.E];
-  const int spr = a.R / 4;
+  // the slices this item's columns fall in: only their part of s is staged
+  const int cfirst = chunk * kExpandCols;
+  const int clast = min(a.N, cfirst + kExpandCols) - 1;
+  const int g0 = cfirst / width, cb = g0 * r, rs = (clast / width - g0 + 1) * r;
+  const int c0 = cfirst + 64 * w;  // this wave's 64 columns, one slice
+  const int g = c0 < a.N ? c0 / width : g0;
+  const int spr = rs / 4;
   const int mask = min(16, spr & -spr) - 1;
   // rows of B_v for the wave's columns: A operand, tile nt, step st
   const int64_t bbytes = (int64_t)a.N * r * 2;
@@ -258,56 +283,65 @@ __device__ __forceinline__ void expand_mfma_block(const DeltaArgs& a, int blk, i
   for (int j0 = 0; j0 < a.BM; j0 += kRowsPerPass) {
     const int nrows = stage_rows(a, blk, j0, pid, nrows_lds);
     if (nrows == 0) break;
-    stage_s(a, pid, nrows, mask, s_lds);
-    uint2 ov[4];
-    load_ov(a, pid, nrows, 0, c0, ov);
+    stage_s(a, pid, nrows, cb, rs, mask, s_lds);
+    uint4 ov[2];
+    load_out_tile(a, pid, nrows, 0, chunk, ov);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int ntiles = (nrows + 15) / 16;
 #pragma unroll 1
     for (int pt = 0; pt < ntiles; ++pt) {
-      uint2 ovn[4];
-      if (pt + 1 < ntiles) load_ov(a, pid, nrows, pt + 1, c0, ovn);  // uniform
+      uint4 ovn[2];
+      if (pt + 1 < ntiles) load_out_tile(a, pid, nrows, pt + 1, chunk, ovn);  // uniform
       const int m = 16 * pt + (lane & 15);
       // s row of pair m, slice g: B operand (k = 32 st + 8 (l/16) .. +8), split hi + lo
       uint4 sh[KS], sl[KS];
 #pragma unroll
       for (int st = 0; st < KS; ++st) {
-        const int kv0 = (g * r + 32 * st + 8 * (lane >> 4)) / 4;
+        const int kv0 = ((g - g0) * r + 32 * st + 8 * (lane >> 4)) / 4;
         const uint4 f0 = s_lds[m * spr + (kv0 ^ (m & mask))];
         const uint4 f1 = s_lds[m * spr + ((kv0 + 1) ^ (m & mask))];
         split_bf16(f0, f1, &sh[st], &sl[st]);
       }
-      floatx4_t acc[4];
+      // out^T tile: lane l holds pair l % 16, columns 16 nt + 4 (l/16) .. +4 of the wave's 64
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        acc[nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        floatx4_t acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int st = 0; st < KS; ++st) {
-          acc[nt] = mfma16(bf[nt][st], sh[st], acc[nt]);
-          acc[nt] = mfma16(bf[nt][st], sl[st], acc[nt]);
+          acc = mfma16(bf[nt][st], sh[st], acc);
+          acc = mfma16(bf[nt][st], sl[st], acc);
         }
+        *reinterpret_cast<floatx4_t*>(tile + (lane & 15) * kTileStride + 64 * w + 16 * nt +
+                                      4 * (lane >> 4)) = acc;
       }
-      if (m < nrows) {
-        const int p = pid[m];
+      __syncthreads();
+      // epilogue over whole rows: thread t owns vectors t and t + 256 of the 16 x 32 grid
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const int n = c0 + 16 * nt + 4 * (lane >> 4);
-          if (n < a.N) {
-            const float o0 = bf16_lo(ov[nt].x), o1 = bf16_hi(ov[nt].x);
-            const float o2 = bf16_lo(ov[nt].y), o3 = bf16_hi(ov[nt].y);
-            const uint32_t w0 = (uint32_t)f32_to_bf16_rne(fmaf(sc, acc[nt][0], o0)) |
-                                ((uint32_t)f32_to_bf16_rne(fmaf(sc, acc[nt][1], o1)) << 16);
-            const uint32_t w1 = (uint32_t)f32_to_bf16_rne(fmaf(sc, acc[nt][2], o2)) |
-                                ((uint32_t)f32_to_bf16_rne(fmaf(sc, acc[nt][3], o3)) << 16);
-            *reinterpret_cast<uint2*>((char*)a.out + ((int64_t)p * a.ld_out + n) * 2) =
-                make_uint2(w0, w1);
+      for (int h = 0; h < 2; ++h) {
+        const int v = tid + 256 * h;
+        const int q = v / 32, cv = v % 32;
+        const int mq = 16 * pt + q;
+        const int n = chunk * kExpandCols + cv * 8;
+        if (mq < nrows && n < a.N) {
+          const float* d = tile + q * kTileStride + cv * 8;
+          const uint4 o = ov[h];
+          const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+          uint32_t res[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float lo = fmaf(sc, d[2 * i], bf16_lo(ow[i]));
+            const float hi = fmaf(sc, d[2 * i + 1], bf16_hi(ow[i]));
+            res[i] = (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
           }
+          *reinterpret_cast<uint4*>((char*)a.out + ((int64_t)pid[mq] * a.ld_out + n) * 2) =
+              make_uint4(res[0], res[1], res[2], res[3]);
         }
       }
+      __syncthreads();  // the tile is rewritten by the next pair tile
       if (pt + 1 < ntiles) {
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) ov[nt] = ovn[nt];
+        ov[0] = ovn[0];
+        ov[1] = ovn[1];
       }
     }
     if (nrows < kRowsPerPass) break;
@@ -316,19 +350,25 @@ __device__ __forceinline__ void expand_mfma_block(const DeltaArgs& a, int blk, i
 
 template <int KS>
 __global__ void __launch_bounds__(256) expand_mfma_kernel(DeltaArgs a) {
-  extern __shared__ uint4 s_lds[];  // [64][R/4]
+  extern __shared__ uint4 s_lds[];  // [64][(slices of the item) * r / 4]
+  __shared__ __attribute__((aligned(16))) float tile[16 * kTileStride];
   __shared__ int pid[kRowsPerPass];
   __shared__ int nrows_lds;
   const int blk = blockIdx.x / a.nchunk, chunk = blockIdx.x % a.nchunk;
   const int e = block_expert(a, blk);
   if (e < 0 || !block_has(a, blk, a.mfma_min)) return;
-  expand_mfma_block<KS>(a, blk, chunk, e, pid, &nrows_lds, s_lds);
+  expand_mfma_block<KS>(a, blk, chunk, e, pid, &nrows_lds, s_lds, tile);
 }
 
 }  // namespace
 
+int shrink_mfma_row_tile(int32_t R) { return R > 64 ? 128 : 64; }
+
 hipError_t launch_shrink_mfma(const DeltaArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(shrink_mfma_kernel, dim3(grid), dim3(256), 0, stream, a);
+  if (shrink_mfma_row_tile(a.R) == 128)
+    hipLaunchKernelGGL((shrink_mfma_kernel<2>), dim3(grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((shrink_mfma_kernel<1>), dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -83,6 +83,8 @@ hipError_t launch_shrink(const DeltaArgs& a, bool bf16, int rows_per_item, int g
                          hipStream_t stream);
 hipError_t launch_expand(const DeltaArgs& a, bool bf16, int grid, hipStream_t stream);
 // bf16 MFMA kernels for the blocks with at least a.mfma_min real pairs
+// rows of A_v per MFMA shrink work item (the grid is max_blocks * cdiv(R, this))
+int shrink_mfma_row_tile(int32_t R);
 hipError_t launch_shrink_mfma(const DeltaArgs& a, int grid, hipStream_t stream);
 hipError_t launch_expand_mfma(const DeltaArgs& a, int grid, hipStream_t stream);
 
