@@ -140,9 +140,12 @@ def reference_grid_m(cfg):
 
 
 def delta_source_sha256():
+    """Hash of the VALU delta kernels' sources (the kernels and their device helpers)."""
     import hashlib
-    path = os.path.join(ROOT, "virtual_expert_routed_amd", "csrc", "delta.hip")
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for f in ("delta.hip", "delta_common.h"):
+        h.update(open(os.path.join(ROOT, "virtual_expert_routed_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload, kernel):
