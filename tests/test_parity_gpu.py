@@ -185,6 +185,7 @@ EDGE = [
     _edge_cfg(name="ragged_bm16"),
     _edge_cfg(name="bm1", block_m=1),
     _edge_cfg(name="bm_max", block_m=1024, M=300),
+    _edge_cfg(name="bm48_not_pow2", block_m=48, M=200),
     _edge_cfg(name="single_token", M=1, topk=2, sentinel_count=0, nolora_count=0),
     _edge_cfg(name="all_nolora", M=20, nolora_count=20),
     _edge_cfg(name="all_sentinel", M=6, topk=2, sentinel_count=12, nolora_count=0),
@@ -209,7 +210,10 @@ EDGE = [
     _edge_cfg(name="mfma_bm128", M=1024, topk=4, E=8, S=2, hidden=128, rank=32,
               stages=configs._two_stage(128, 64, 32), block_m=128, sentinel_count=10,
               nolora_count=10),
-    # k tails past the 256-wide staged chunk, and an expand slice width (136) that is not a
+    _edge_cfg(name="mfma_bm48_not_pow2", M=1024, topk=4, E=8, S=2, hidden=256, rank=32,
+              stages=configs._two_stage(256, 128, 32), block_m=48, sentinel_count=10,
+              nolora_count=10),
+    # k tails past the staged chunk, and an expand slice width (136) that is not a
     # multiple of 64, which keeps the expand on the VALU kernel
     _edge_cfg(name="mfma_ragged_k", M=1024, topk=4, E=8, S=2, hidden=264, rank=32,
               stages=configs._two_stage(264, 136, 32), block_m=64, sentinel_count=10,

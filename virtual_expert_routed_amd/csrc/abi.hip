@@ -200,6 +200,7 @@ MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_
   a.numel = (int32_t)numel;
   a.V = (int32_t)V64;
   a.BM = block_m;
+  a.bm_shift = (block_m & (block_m - 1)) == 0 ? __builtin_ctz((unsigned)block_m) : -1;
   a.sorted = sorted_ids;
   a.expert_ids = expert_ids;
   a.npp = num_post_padded;

@@ -78,16 +78,23 @@ __device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
   return sh[16 + wid] + inc - v;
 }
 
-__device__ __forceinline__ int round_up(int c, int m) { return (c + m - 1) / m * m; }
+// x / BLOCK_M and c rounded up to a multiple of BLOCK_M (shifts when BLOCK_M is a power of 2)
+__device__ __forceinline__ int bm_div(const AlignArgs& a, int x) {
+  return a.bm_shift >= 0 ? x >> a.bm_shift : x / a.BM;
+}
+__device__ __forceinline__ int bm_round(const AlignArgs& a, int c) {
+  return a.bm_shift >= 0 ? (c + a.BM - 1) & -a.BM : (c + a.BM - 1) / a.BM * a.BM;
+}
 
 // expert ids and padding entries of bucket b (c pairs at padded offset off), by `lanes`
 // cooperating threads starting at `first`.
 __device__ __forceinline__ void write_bucket_tail(const AlignArgs& a, int b, int c, int off,
                                                   int first, int lanes) {
-  const int pc = round_up(c, a.BM);
+  const int pc = bm_round(a, c);
   const int eid = (b == a.V) ? -1 : b;
-  const int blk0 = off / a.BM;
-  for (int j = first; j < pc / a.BM; j += lanes) a.expert_ids[blk0 + j] = eid;
+  const int blk0 = bm_div(a, off);
+  const int nblk = bm_div(a, pc);
+  for (int j = first; j < nblk; j += lanes) a.expert_ids[blk0 + j] = eid;
   for (int j = c + first; j < pc; j += lanes) a.sorted[off + j] = a.numel;
 }
 
@@ -196,44 +203,50 @@ __global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a, int wave
   int mine = 0;
   for (int b = b0; b < b1; ++b) {
     int c = 0;
+    for (int w0 = 0; w0 < waves; w0 += 4) {  // four rows per round, read before use
+      int x[4];
 #pragma unroll
-    for (int w = 0; w < 16; ++w) {
-      const int x = table[(w < waves ? w : 0) * NB + b];
-      c += w < waves ? x : 0;
+      for (int i = 0; i < 4; ++i) x[i] = table[min(w0 + i, waves - 1) * NB + b];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c += w0 + i < waves ? x[i] : 0;
     }
-    mine += round_up(c, a.BM);
+    mine += bm_round(a, c);
   }
   int total;
   int off = block_excl_scan(mine, sh, &total);
   // padding of this thread's buckets, kept as (first slot, count) per owned bucket
   int pad_from[kMaxBucketsPerThread], pad_cnt[kMaxBucketsPerThread];
+  int bmod = b0 % G;  // b % G for b = b0, b0 + 1, ...
 #pragma unroll
   for (int k = 0; k < kMaxBucketsPerThread; ++k) {
     pad_cnt[k] = 0;
     pad_from[k] = 0;
     const int b = b0 + k;
     if (b < b1) {
-      int cw[16];
-#pragma unroll
-      for (int w = 0; w < 16; ++w) {
-        const int x = table[(w < waves ? w : 0) * NB + b];
-        cw[w] = w < waves ? x : 0;
-      }
       int run = off;
+      for (int w0 = 0; w0 < waves; w0 += 4) {
+        int x[4];
 #pragma unroll
-      for (int w = 0; w < 16; ++w) {
-        if (w < waves) table[w * NB + b] = run;
-        run += cw[w];
+        for (int i = 0; i < 4; ++i) x[i] = table[min(w0 + i, waves - 1) * NB + b];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (w0 + i < waves) {
+            table[(w0 + i) * NB + b] = run;
+            run += x[i];
+          }
+        }
       }
       const int c = run - off;
-      const int pc = round_up(c, a.BM);
-      if (b % G == g) {
+      const int pc = bm_round(a, c);
+      if (bmod == g) {
         const int eid = (b == a.V) ? -1 : b;
-        for (int j = 0; j < pc / a.BM; ++j) a.expert_ids[off / a.BM + j] = eid;
+        const int blk0 = bm_div(a, off), nblk = bm_div(a, pc);
+        for (int j = 0; j < nblk; ++j) a.expert_ids[blk0 + j] = eid;
         pad_from[k] = off + c;
         pad_cnt[k] = pc - c;
       }
       off += pc;
+      bmod = bmod + 1 == G ? 0 : bmod + 1;
     }
   }
   if (tid == 0 && g == 0) *a.npp = total;
@@ -338,7 +351,7 @@ __global__ void __launch_bounds__(256) align_scatter_kernel(AlignArgs a) {
   for (int k = 0; k < kScanBucketsPerThread; ++k) {
     const int b = b0 + k;
     cnt[k] = b < b1 ? a.totals[b] : 0;
-    mine += round_up(cnt[k], a.BM);
+    mine += bm_round(a, cnt[k]);
   }
   int total;
   int o = block_excl_scan(mine, sh, &total);
@@ -347,7 +360,7 @@ __global__ void __launch_bounds__(256) align_scatter_kernel(AlignArgs a) {
     const int b = b0 + k;
     if (b < b1) {
       off[b] = o;
-      o += round_up(cnt[k], a.BM);
+      o += bm_round(a, cnt[k]);
     }
   }
   if (t == 0 && tid == 0) *a.npp = total;

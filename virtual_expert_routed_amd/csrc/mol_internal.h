@@ -21,6 +21,7 @@ struct AlignArgs {
   int32_t numel;
   int32_t V;             // number of virtual experts; bucket V is the sentinel bucket
   int32_t BM;
+  int32_t bm_shift;      // log2(BM) when BM is a power of two, else -1
   int32_t* sorted;
   int32_t* expert_ids;
   int32_t* npp;
