@@ -138,8 +138,9 @@ MOL_API mol_status mol_align_block_size(const int32_t *ids, const int32_t *lora_
  *   A            [V, R, K] weights, rows of K contiguous elements
  *   sorted_ids, expert_ids, num_post_padded: the outputs of mol_align_block_size for
  *                `numel` pairs, V = num_virtual virtual experts and this block_m
- *   s            float32 [numel, R] out; rows of pairs that get no delta are untouched
- * Requires K * elem and ld_x * elem to be multiples of 16 bytes and xin, A 16-byte
+ *   s            float32 [numel, R] out, 16-byte aligned; rows of pairs that get no delta are
+ *                untouched
+ * Requires K * elem and ld_x * elem to be multiples of 16 bytes and xin, A, s 16-byte
  * aligned (MOL_E_ALIGN). numel == 0 enqueues nothing.
  * ------------------------------------------------------------------------------- */
 MOL_API mol_status mol_lora_shrink(int32_t dtype, const void *xin, int64_t ld_x,
@@ -155,13 +156,13 @@ MOL_API mol_status mol_lora_shrink(int32_t dtype, const void *xin, int64_t ld_x,
  * (MindLab sglang PR 24: expand rank -> N; gate_up expands as two slices, gate from
  * s[:, :r] and up from s[:, r:]). Sum in fp32, one fused multiply-add into the fp32 value
  * of out, then round to nearest even for bf16.
- *   s            float32 [numel, R] from mol_lora_shrink
+ *   s            float32 [numel, R] from mol_lora_shrink, 16-byte aligned
  *   B            [V, N, r] weights (dtype as out)
  *   slot_scale   float32 [num_virtual / num_experts]
  *   out          [numel, ld_out] read and written in place; rows of pairs without a
  *                delta are left bit-for-bit untouched
  * Requires R % slices == 0, N % slices == 0, r * elem a multiple of 16 bytes and at most
- * MOL_MAX_RANK_BYTES, B 16-byte aligned.
+ * MOL_MAX_RANK_BYTES, B and s 16-byte aligned (MOL_E_ALIGN), out aligned to its element.
  * ------------------------------------------------------------------------------- */
 MOL_API mol_status mol_lora_expand(int32_t dtype, const float *s, int32_t R, int32_t slices,
                                    const void *B, int32_t N, const float *slot_scale,

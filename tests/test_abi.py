@@ -118,6 +118,8 @@ def test_shrink_expand_delta_reject_before_launch():
                              FAKE, FAKE, 16, 8, 16, FAKE, None) == mb.MOL_E_ALIGN
     assert L.mol_lora_shrink(mb.MOL_F32, FAKE, 32, 1, FAKE, 8, 64, FAKE, FAKE, FAKE, 16, 8,
                              16, FAKE, None) == mb.MOL_E_ARG           # ld_x < K
+    assert L.mol_lora_shrink(mb.MOL_BF16, FAKE, 64, 1, FAKE, 8, 64, FAKE, FAKE, FAKE, 16, 8,
+                             16, ctypes.c_void_p(0x1008), None) == mb.MOL_E_ALIGN  # s
     # expand: R % slices, rank too large, V not a multiple of E
     assert L.mol_lora_expand(mb.MOL_BF16, FAKE, 63, 2, FAKE, 32, FAKE, 4, FAKE, FAKE, FAKE,
                              16, 8, 16, FAKE, 32, None) == mb.MOL_E_ARG
@@ -125,6 +127,8 @@ def test_shrink_expand_delta_reject_before_launch():
                              16, 8, 16, FAKE, 32, None) == mb.MOL_E_LIMIT
     assert L.mol_lora_expand(mb.MOL_BF16, FAKE, 16, 1, FAKE, 32, FAKE, 3, FAKE, FAKE, FAKE,
                              16, 8, 16, FAKE, 32, None) == mb.MOL_E_ARG
+    assert L.mol_lora_expand(mb.MOL_BF16, ctypes.c_void_p(0x1008), 16, 1, FAKE, 32, FAKE, 4,
+                             FAKE, FAKE, FAKE, 16, 8, 16, FAKE, 32, None) == mb.MOL_E_ALIGN
     # delta: workspace missing or too small
     assert L.mol_lora_delta(mb.MOL_BF16, FAKE, 64, 1, FAKE, 16, 64, 1, FAKE, 32, FAKE, 4,
                             FAKE, FAKE, FAKE, 16, 8, 16, FAKE, 32, None, 0,

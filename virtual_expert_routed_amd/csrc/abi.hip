@@ -74,7 +74,7 @@ mol_status shrink_check(int32_t dtype, const void* xin, int64_t ld_x, int32_t ro
   if (numel > 0 && (!xin || !A || !s)) return MOL_E_ARG;
   const int esz = dtype == MOL_BF16 ? 2 : 4;
   if (((int64_t)K * esz) % 16 || (ld_x * esz) % 16) return MOL_E_ALIGN;
-  if (numel > 0 && (!aligned16(xin) || !aligned16(A))) return MOL_E_ALIGN;
+  if (numel > 0 && (!aligned16(xin) || !aligned16(A) || !aligned16(s))) return MOL_E_ALIGN;
   if ((int64_t)R * K * esz >= (int64_t(1) << 31)) return MOL_E_LIMIT;  // one expert's A
   return MOL_OK;
 }
@@ -319,6 +319,7 @@ MOL_API mol_status mol_lora_expand(int32_t dtype, const float* s, int32_t R, int
                                      num_virtual, numel, out, ld_out);
   if (ec != MOL_OK) return ec;
   if (numel > 0 && !s) return MOL_E_ARG;
+  if (numel > 0 && !aligned16(s)) return MOL_E_ALIGN;  // s rows are read as 16-byte vectors
   if (numel == 0) return MOL_OK;
   const bool bf16 = dtype == MOL_BF16;
   mol::DeltaArgs a = make_delta_args(nullptr, 0, 1, nullptr, R, 1, slices, B, N, slot_scale,
@@ -353,8 +354,8 @@ MOL_API mol_status mol_lora_delta(int32_t dtype, const void* xin, int64_t ld_x,
   const StageCheck rc =
       routing_check(sorted_ids, expert_ids, num_post_padded, numel, num_virtual, block_m);
   if (rc.st != MOL_OK) return rc.st;
-  float dummy = 0.f;
-  mol_status c = shrink_check(dtype, xin, ld_x, row_div, A, R, K, numel, &dummy);
+  alignas(16) float ws_probe[4] = {};  // s lives in the workspace, checked below
+  mol_status c = shrink_check(dtype, xin, ld_x, row_div, A, R, K, numel, ws_probe);
   if (c != MOL_OK) return c;
   c = expand_check(dtype, R, slices, B, N, slot_scale, num_experts, num_virtual, numel, out,
                    ld_out);
