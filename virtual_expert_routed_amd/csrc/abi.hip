@@ -210,7 +210,9 @@ MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_
     // counter rows + scan scratch + per pair a bucket id and a rank (uint16 each)
     const int64_t fixed = 64 * (int64_t)sizeof(int) + ((numel + 1) & ~1LL) * 2 * 2;
     int64_t waves = (device_lds_bytes() - fixed) / ((int64_t)nb * (int64_t)sizeof(int));
-    const int64_t useful = cdiv64(numel, 128);  // two chunks of 64 pairs per wave at least
+    // walkers: one chunk of 64 pairs each for the smallest batches, two chunks each above
+    // (more walkers shorten the walk but add counter rows to every bucket's sums)
+    const int64_t useful = numel <= 256 ? cdiv64(numel, 64) : cdiv64(numel, 128);
     if (waves > useful) waves = useful;
     if (waves > 16) waves = 16;
     if (waves < 1) waves = 1;
