@@ -49,10 +49,10 @@ def lib():
         L.oracle_align_block_size.argtypes = [P, P, I64, I32, I32, I32, I32, P, I64, P, I64, P]
         L.oracle_align_block_size.restype = ctypes.c_int
         L.oracle_lora_shrink.argtypes = [ctypes.c_int, P, I64, I32, P, I32, I32, P, P, I32,
-                                         I64, I32, P, P]
+                                         I64, I32, P, P, I32, P, I32]
         L.oracle_lora_shrink.restype = ctypes.c_int
         L.oracle_lora_expand.argtypes = [ctypes.c_int, P, I32, I32, P, I32, P, I32, P, P, I32,
-                                         I64, I32, P, P, I64]
+                                         I64, I32, P, P, I64, P]
         L.oracle_lora_expand.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -117,9 +117,16 @@ def align_block_size(ids, lora_ids, E: int, S: int, block_m: int):
     return sorted_ids[:n].copy(), expert_ids[: n // block_m].copy(), n
 
 
+def _ranks(slot_ranks):
+    return None if slot_ranks is None else np.ascontiguousarray(slot_ranks, dtype=np.int32)
+
+
 def lora_shrink(xin, row_div: int, A, sorted_ids, expert_ids, npp: int, numel: int,
-                block_m: int, pair_mask=None, s=None) -> np.ndarray:
-    """s [numel, R] float64; rows of pairs that get no delta stay as given (NaN)."""
+                block_m: int, pair_mask=None, s=None, slices: int = 1, slot_ranks=None,
+                E: int = 1) -> np.ndarray:
+    """s [numel, R] float64; rows of pairs that get no delta stay as given (NaN). With
+    slot_ranks (int32 [S]; slot = v / E), entries past a slot's rank in each of the
+    `slices` slices are 0."""
     xin = np.ascontiguousarray(xin)
     A = np.ascontiguousarray(A)
     V, R, K = A.shape
@@ -128,17 +135,19 @@ def lora_shrink(xin, row_div: int, A, sorted_ids, expert_ids, npp: int, numel: i
     srt = np.ascontiguousarray(sorted_ids, dtype=np.int32)
     eid = np.ascontiguousarray(expert_ids, dtype=np.int32)
     mask = None if pair_mask is None else np.ascontiguousarray(pair_mask, dtype=np.uint8)
+    rk = _ranks(slot_ranks)
     rc = lib().oracle_lora_shrink(_dt(A), _ptr(xin), xin.shape[1], row_div, _ptr(A), R, K,
                                   _ptr(srt), _ptr(eid), npp, numel, block_m, _ptr(mask),
-                                  _ptr(s))
+                                  _ptr(s), slices, _ptr(rk), E)
     if rc:
         raise ValueError(f"oracle_lora_shrink: {rc}")
     return s
 
 
 def lora_expand(s, slices: int, B, scale, E: int, sorted_ids, expert_ids, npp: int,
-                numel: int, block_m: int, out, pair_mask=None) -> np.ndarray:
-    """Adds the delta into `out` [numel, N] (float32 or bf16 bits) in place."""
+                numel: int, block_m: int, out, pair_mask=None, slot_ranks=None) -> np.ndarray:
+    """Adds the delta into `out` [numel, N] (float32 or bf16 bits) in place; with
+    slot_ranks, only a slot's first rank dimensions count and rank 0 adds nothing."""
     s = np.ascontiguousarray(s, dtype=np.float64)
     B = np.ascontiguousarray(B)
     V, N, r = B.shape
@@ -148,9 +157,10 @@ def lora_expand(s, slices: int, B, scale, E: int, sorted_ids, expert_ids, npp: i
     srt = np.ascontiguousarray(sorted_ids, dtype=np.int32)
     eid = np.ascontiguousarray(expert_ids, dtype=np.int32)
     mask = None if pair_mask is None else np.ascontiguousarray(pair_mask, dtype=np.uint8)
+    rk = _ranks(slot_ranks)
     rc = lib().oracle_lora_expand(_dt(B), _ptr(s), R, slices, _ptr(B), N, _ptr(sc), E,
                                   _ptr(srt), _ptr(eid), npp, numel, block_m, _ptr(mask),
-                                  _ptr(out), out.shape[1])
+                                  _ptr(out), out.shape[1], _ptr(rk))
     if rc:
         raise ValueError(f"oracle_lora_expand: {rc}")
     return out
@@ -165,14 +175,15 @@ def run_layer(inp, outs=None, pair_mask=None):
     srt, eid, npp = align_block_size(inp.topk_ids, inp.lora_ids, cfg.E, cfg.S, cfg.block_m)
     ss, oo = [], []
     for si, (st, sin) in enumerate(zip(cfg.stages, inp.stages)):
+        ranks = getattr(inp, "slot_ranks", None)
         s = lora_shrink(sin.xin, sin.row_div, sin.A, srt, eid, npp, numel, cfg.block_m,
-                        pair_mask=pair_mask)
+                        pair_mask=pair_mask, slices=st.slices, slot_ranks=ranks, E=cfg.E)
         if outs is None:
             out = np.zeros((numel, st.N), dtype=sin.B.dtype)
         else:
             out = outs[si]
         lora_expand(s, st.slices, sin.B, inp.scale, cfg.E, srt, eid, npp, numel,
-                    cfg.block_m, out, pair_mask=pair_mask)
+                    cfg.block_m, out, pair_mask=pair_mask, slot_ranks=ranks)
         ss.append(s)
         oo.append(out)
     return (srt, eid, npp), ss, oo

@@ -24,6 +24,9 @@
  *             shrink hidden -> rank, expand rank -> N, weights laid out [E, N, K]
  *             with N = shape[1] per the code-review commit.)
  *
+ * Per-slot ranks (optional): a slot of rank rl < r uses rank dimensions [0, rl) of each
+ * slice; s is 0 past it, and a slot of rank 0 gets no delta.
+ *
  * Readings taken where the pages leave a step open (each is listed with its reason in
  * the design notes): a token with no adapter (slot -1) or a slot >= S, and a base id
  * >= E, map to virtual id -1; pairs inside a bucket keep ascending pair order; padding
@@ -187,24 +190,43 @@ int oracle_align_block_size(const int32_t *ids, const int32_t *lora_ids, int64_t
 /* For every real pair p of every aligned block with expert id e >= 0 (and, if
  * pair_mask is given, pair_mask[p] != 0):  s[p*R + i] = sum_k A[e][i][k] * xin[p/row_div][k],
  * k ascending, in double.  A is [V, R, K] row-major; xin rows are ld_x elements apart. */
+/* Rank of LoRA slot l: slot_ranks[l] clamped to [0, r], or r when no ranks are given.
+ * An adapter of rank rl uses the first rl rank dimensions of each slice of its weights;
+ * rank 0 means no delta at all, like a pair with no adapter (MindLab sglang PR 24: the
+ * lora_ranks table and its rank == 0 early return, which the "-1 guards" commit extends to
+ * the -1 slot). */
+static int32_t slot_rank(const int32_t *slot_ranks, int32_t slot, int32_t r) {
+    if (!slot_ranks) return r;
+    const int32_t v = slot_ranks[slot];
+    return v < 0 ? 0 : (v > r ? r : v);
+}
+
 int oracle_lora_shrink(int dtype, const void *xin, int64_t ld_x, int32_t row_div,
                        const void *A, int32_t R, int32_t K,
                        const int32_t *sorted_ids, const int32_t *expert_ids, int32_t npp,
-                       int64_t numel, int32_t BM, const uint8_t *pair_mask, double *s) {
+                       int64_t numel, int32_t BM, const uint8_t *pair_mask, double *s,
+                       int32_t slices, const int32_t *slot_ranks, int32_t E) {
     if ((dtype != OR_F32 && dtype != OR_BF16) || R <= 0 || K <= 0 || BM <= 0 ||
-        row_div <= 0 || ld_x < K || npp < 0 || npp % BM)
+        row_div <= 0 || ld_x < K || npp < 0 || npp % BM || slices <= 0 || R % slices ||
+        E <= 0)
         return OR_E_ARG;
+    const int32_t r = R / slices;
     const int64_t nblocks = npp / BM;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t blk = 0; blk < nblocks; ++blk) {
         const int32_t e = expert_ids[blk];
         if (e < 0) continue;
+        const int32_t rl = slot_rank(slot_ranks, e / E, r);
         for (int32_t j = 0; j < BM; ++j) {
             const int64_t p = sorted_ids[blk * BM + j];
             if (p < 0 || p >= numel) continue;
             if (pair_mask && !pair_mask[p]) continue;
             const int64_t xrow = (p / row_div) * ld_x;
             for (int32_t i = 0; i < R; ++i) {
+                if (i % r >= rl) {  /* past the adapter's rank in this slice */
+                    s[p * R + i] = 0.0;
+                    continue;
+                }
                 const int64_t arow = ((int64_t)e * R + i) * K;
                 double acc = 0.0;
                 for (int32_t k = 0; k < K; ++k)
@@ -218,8 +240,9 @@ int oracle_lora_shrink(int dtype, const void *xin, int64_t ld_x, int32_t row_div
 
 /* ---- expand ----------------------------------------------------------------------- */
 
-/* For the same pairs:  d = scale[e / E] * sum_j B[e][n][j] * s[p*R + g*r + j], j ascending,
- * with r = R/slices and g = n / (N/slices); then
+/* For the same pairs:  d = scale[e / E] * sum_{j < rl} B[e][n][j] * s[p*R + g*r + j], j
+ * ascending, with r = R/slices, g = n / (N/slices) and rl the slot's rank (r without
+ * ranks; a slot of rank 0 gets no delta); then
  *   bf16: out[p][n] = round_bf16(out[p][n] + d)   (sum and rounding from double)
  *   f32:  out[p][n] = (float)(out[p][n] + d)
  * B is [V, N, r] row-major; out rows are ld_out elements apart. Every other row of out
@@ -228,7 +251,7 @@ int oracle_lora_expand(int dtype, const double *s, int32_t R, int32_t slices,
                        const void *B, int32_t N, const float *scale, int32_t E,
                        const int32_t *sorted_ids, const int32_t *expert_ids, int32_t npp,
                        int64_t numel, int32_t BM, const uint8_t *pair_mask,
-                       void *out, int64_t ld_out) {
+                       void *out, int64_t ld_out, const int32_t *slot_ranks) {
     if ((dtype != OR_F32 && dtype != OR_BF16) || R <= 0 || slices <= 0 || R % slices ||
         N <= 0 || N % slices || E <= 0 || BM <= 0 || ld_out < N || npp < 0 || npp % BM)
         return OR_E_ARG;
@@ -240,6 +263,8 @@ int oracle_lora_expand(int dtype, const double *s, int32_t R, int32_t slices,
         const int32_t e = expert_ids[blk];
         if (e < 0) continue;
         const double sc = (double)scale[e / E];
+        const int32_t rl = slot_rank(slot_ranks, e / E, r);
+        if (rl == 0) continue;  /* rank 0: no delta, rows untouched */
         for (int32_t j = 0; j < BM; ++j) {
             const int64_t p = sorted_ids[blk * BM + j];
             if (p < 0 || p >= numel) continue;
@@ -248,7 +273,7 @@ int oracle_lora_expand(int dtype, const double *s, int32_t R, int32_t slices,
                 const int32_t g = n / width;
                 const int64_t brow = ((int64_t)e * N + n) * r;
                 double acc = 0.0;
-                for (int32_t jj = 0; jj < r; ++jj)
+                for (int32_t jj = 0; jj < rl; ++jj)
                     acc += load_elem(B, brow + jj, dtype) * s[p * R + (int64_t)g * r + jj];
                 const double d = sc * acc;
                 const int64_t o = p * ld_out + n;

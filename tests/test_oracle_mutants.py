@@ -30,6 +30,11 @@ MUTANTS = [
     ("expand_truncates", "nearbyint(ldexp(a, -q))", "trunc(ldexp(a, -q))"),
     ("expand_sign", "acc += load_elem(B, brow + jj, dtype) * s[",
      "acc -= load_elem(B, brow + jj, dtype) * s["),
+    ("rank_reads_past_end", "for (int32_t jj = 0; jj < rl; ++jj)",
+     "for (int32_t jj = 0; jj <= rl && jj < r; ++jj)"),
+    ("rank_zero_as_full", "return v < 0 ? 0 : (v > r ? r : v);",
+     "return v <= 0 ? r : (v > r ? r : v);"),
+    ("rank_shrink_ignored", "if (i % r >= rl) {", "if (0) {"),
 ]
 
 
@@ -49,6 +54,10 @@ def _battery(lib):
         ("identity_bf16", lambda: P.test_delta_equals_per_pair_identity(lib, P.SMALL_BF16)),
         ("gemm_chain", lambda: P.test_one_bucket_is_a_plain_gemm_chain(lib)),
         ("linearity", lambda: P.test_linearity_in_scale_and_zero_A(lib)),
+        ("ranked_f32", lambda: P.test_ranked_delta_equals_full_rank_on_zeroed_weights(
+            lib, P.RANKED[0])),
+        ("ranked_bf16", lambda: P.test_ranked_delta_equals_full_rank_on_zeroed_weights(
+            lib, P.RANKED[1])),
     ]
     for name, fn in cases:
         try:

@@ -15,6 +15,8 @@
 """
 import itertools
 
+import copy
+
 import numpy as np
 import pytest
 import torch
@@ -264,6 +266,55 @@ def test_linearity_in_scale_and_zero_A(oracle_lib):
     base = inputs.base_out(cfg, 0, seed=11)
     _, out3 = _run_stage(oracle_lib, inp, 0, out=base.copy())
     assert np.array_equal(out3, base)
+
+
+RANKED = [
+    _small(configs.C0, name="ranked_f32", slot_ranks=(5, 0)),
+    _small(SMALL_BF16, name="ranked_bf16", slot_ranks=(8, 3, 0)),
+]
+
+
+def _zeroed_past_rank(inp):
+    """The same layer with every weight past its slot's rank set to 0 and no rank table."""
+    z = copy.deepcopy(inp)
+    for sin in z.stages:
+        for w in (sin.A, sin.B):
+            bad = np.isnan(pins.bf16_bits_to_f64(w) if w.dtype == np.uint16 else w)
+            w[bad] = 0
+    z.slot_ranks = None
+    return z
+
+
+@pytest.mark.parametrize("cfg", RANKED, ids=[c.name for c in RANKED])
+def test_ranked_delta_equals_full_rank_on_zeroed_weights(oracle_lib, cfg):
+    # An adapter of rank rl is the full-rank path on weights that are zero past rl; the
+    # ranked inputs hold NaN there, so reading one element too many shows up. Rank 0 adds
+    # nothing: its rows keep the starting values bit for bit.
+    inp = inputs.generate(cfg, seed=4)
+    assert any(np.isnan(pins.bf16_bits_to_f64(st.A) if st.A.dtype == np.uint16 else st.A).any()
+               for st in inp.stages)
+    base = [inputs.base_out(cfg, si, seed=4) for si in range(len(cfg.stages))]
+    (srt, eid, npp), s_r, o_r = oracle_lib.run_layer(inp, outs=[b.copy() for b in base])
+    _, s_z, o_z = oracle_lib.run_layer(_zeroed_past_rank(inp), outs=[b.copy() for b in base])
+    vids = oracle_lib.virtual_topk(inp.topk_ids, inp.lora_ids, cfg.E, cfg.S).reshape(-1)
+    real = (vids >= 0) & (vids < cfg.V)
+    zero_rank = real & (np.asarray(cfg.slot_ranks)[np.where(real, vids, 0) // cfg.E] == 0)
+    for si in range(len(cfg.stages)):
+        assert np.array_equal(s_r[si][real], s_z[si][real])
+        assert not np.isnan(s_r[si][real]).any()
+        assert np.array_equal(o_r[si], o_z[si])
+        assert np.array_equal(o_r[si][zero_rank | ~real], base[si][zero_rank | ~real])
+    assert zero_rank.any()
+
+
+def test_full_ranks_equal_no_rank_table(oracle_lib):
+    cfg = _small(SMALL_BF16, name="full_ranks", slot_ranks=(8, 8, 8))
+    inp = inputs.generate(cfg, seed=2)
+    _, s1, o1 = oracle_lib.run_layer(inp)
+    inp.slot_ranks = None
+    _, s2, o2 = oracle_lib.run_layer(inp)
+    for a, b in zip(s1 + o1, s2 + o2):
+        assert np.array_equal(np.nan_to_num(a, nan=7.0), np.nan_to_num(b, nan=7.0))
 
 
 def test_token_permutation_permutes_rows(oracle_lib):

@@ -51,6 +51,7 @@ class LayerConfig:
     h_sigma: float = 1.0
     scale: float = 1.0
     zipf_s: float = 1.1
+    slot_ranks: tuple = None   # per LoRA slot rank (<= rank; 0 = no delta), None = all full
     note: str = field(default="", compare=False)
 
     @property

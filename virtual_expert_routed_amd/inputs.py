@@ -67,6 +67,7 @@ class LayerInputs:
     x: np.ndarray
     stages: list             # StageInputs per cfg.stages
     scale: np.ndarray        # [S] float32
+    slot_ranks: np.ndarray = None  # [S] int32 or None (every slot at full rank)
 
 
 def _normals(rng, shape, sigma, dtype):
@@ -135,9 +136,23 @@ def generate(cfg: LayerConfig, seed: int = 0, tensors: bool = True) -> LayerInpu
             xin, row_div = x, cfg.topk
         else:
             xin, row_div = h[st.name], 1
+        if cfg.slot_ranks is not None:
+            _poison_past_rank(cfg, st, A, B)
         stages.append(StageInputs(A=A, B=B, xin=xin, row_div=row_div))
+    ranks = None if cfg.slot_ranks is None else np.asarray(cfg.slot_ranks, dtype=np.int32)
     return LayerInputs(cfg=cfg, seed=seed, topk_ids=topk, lora_ids=lora, x=x,
-                       stages=stages, scale=scale)
+                       stages=stages, scale=scale, slot_ranks=ranks)
+
+
+def _poison_past_rank(cfg, st, A, B):
+    """A slot of rank rl < r leaves rank dimensions [rl, r) of each slice unused; fill them
+    with NaN (as stale pool memory could hold anything) so that reading them shows."""
+    nan = np.uint16(0x7FC0) if cfg.dtype == "bf16" else np.float32(np.nan)
+    for l, rl in enumerate(cfg.slot_ranks):
+        v = slice(l * cfg.E, (l + 1) * cfg.E)
+        for g in range(st.slices):
+            A[v, g * st.r + rl:(g + 1) * st.r, :] = nan
+        B[v, :, rl:] = nan
 
 
 def base_out(cfg: LayerConfig, stage_index: int, seed: int) -> np.ndarray:
