@@ -69,7 +69,7 @@ enum { MOL_F32 = 0, MOL_BF16 = 1 };
 /* (host) Static description of a status code. Never NULL. */
 MOL_API const char *mol_status_string(mol_status status);
 
-/* (host) ABI version of this header, 1. */
+/* (host) ABI version of this header, 2 (2 added the per-slot ranks). */
 MOL_API int32_t mol_abi_version(void);
 
 /* ---------------------------------------------------------------------------------
@@ -129,6 +129,14 @@ MOL_API mol_status mol_align_block_size(const int32_t *ids, const int32_t *lora_
                                         size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------
+ * Per-slot ranks (all three delta calls). slot_ranks, int32 [num_virtual / num_experts] or
+ * NULL, gives the rank rl of each LoRA slot (MindLab sglang PR 24: the lora_ranks table and
+ * its rank == 0 early return): an adapter of rank rl uses rank dimensions [0, rl) of each
+ * slice of its weights, r = R / slices. Values are clamped to [0, r]; NULL means every slot
+ * has rank r. Weights past a slot's rank are never read, whatever they hold.
+ * ------------------------------------------------------------------------------- */
+
+/* ---------------------------------------------------------------------------------
  * mol_lora_shrink - s[p, i] = sum_k A[v, i, k] * xin[p / row_div, k] for every real pair
  * p of every block with expert id v >= 0 (MindLab sglang PR 24: the MoL shrink stage,
  * hidden -> rank). fp32 accumulation.
@@ -136,29 +144,35 @@ MOL_API mol_status mol_align_block_size(const int32_t *ids, const int32_t *lora_
  *   xin          [rows, ld_x] input rows; pair p reads row p / row_div (row_div = topk
  *                for token rows, 1 for per-pair rows)
  *   A            [V, R, K] weights, rows of K contiguous elements
+ *   slices       R = slices * r; slice g holds rank dimensions [g r, g r + r)
+ *   slot_ranks, num_experts: the per-slot ranks above (slot of v = v / num_experts);
+ *                s[p, g r + i] = 0 for i >= rl
  *   sorted_ids, expert_ids, num_post_padded: the outputs of mol_align_block_size for
  *                `numel` pairs, V = num_virtual virtual experts and this block_m
  *   s            float32 [numel, R] out, 16-byte aligned; rows of pairs that get no delta are
  *                untouched
- * Requires K * elem and ld_x * elem to be multiples of 16 bytes and xin, A, s 16-byte
- * aligned (MOL_E_ALIGN). numel == 0 enqueues nothing.
+ * Requires K * elem and ld_x * elem to be multiples of 16 bytes, R % slices == 0, and xin,
+ * A, s 16-byte aligned (MOL_E_ALIGN). numel == 0 enqueues nothing.
  * ------------------------------------------------------------------------------- */
 MOL_API mol_status mol_lora_shrink(int32_t dtype, const void *xin, int64_t ld_x,
                                    int32_t row_div, const void *A, int32_t R, int32_t K,
-                                   const int32_t *sorted_ids, const int32_t *expert_ids,
-                                   const int32_t *num_post_padded, int32_t numel,
-                                   int32_t num_virtual, int32_t block_m, float *s,
-                                   void *stream);
+                                   int32_t slices, const int32_t *slot_ranks,
+                                   int32_t num_experts, const int32_t *sorted_ids,
+                                   const int32_t *expert_ids, const int32_t *num_post_padded,
+                                   int32_t numel, int32_t num_virtual, int32_t block_m,
+                                   float *s, void *stream);
 
 /* ---------------------------------------------------------------------------------
- * mol_lora_expand - for the same pairs, with r = R / slices, w = N / slices,
- *   out[p, n] = round(out[p, n] + slot_scale[v / E] * sum_j B[v, n, j] * s[p, (n / w) * r + j])
+ * mol_lora_expand - for the same pairs, with r = R / slices, w = N / slices and rl the
+ * slot's rank,
+ *   out[p, n] = round(out[p, n] + slot_scale[v / E] * sum_{j < rl} B[v, n, j] * s[p, (n / w) * r + j])
  * (MindLab sglang PR 24: expand rank -> N; gate_up expands as two slices, gate from
  * s[:, :r] and up from s[:, r:]). Sum in fp32, one fused multiply-add into the fp32 value
- * of out, then round to nearest even for bf16.
+ * of out, then round to nearest even for bf16. A slot of rank 0 adds nothing.
  *   s            float32 [numel, R] from mol_lora_shrink, 16-byte aligned
  *   B            [V, N, r] weights (dtype as out)
  *   slot_scale   float32 [num_virtual / num_experts]
+ *   slot_ranks   int32 [num_virtual / num_experts] or NULL (see above)
  *   out          [numel, ld_out] read and written in place; rows of pairs without a
  *                delta are left bit-for-bit untouched
  * Requires R % slices == 0, N % slices == 0, r * elem a multiple of 16 bytes and at most
@@ -166,8 +180,8 @@ MOL_API mol_status mol_lora_shrink(int32_t dtype, const void *xin, int64_t ld_x,
  * ------------------------------------------------------------------------------- */
 MOL_API mol_status mol_lora_expand(int32_t dtype, const float *s, int32_t R, int32_t slices,
                                    const void *B, int32_t N, const float *slot_scale,
-                                   int32_t num_experts, const int32_t *sorted_ids,
-                                   const int32_t *expert_ids,
+                                   const int32_t *slot_ranks, int32_t num_experts,
+                                   const int32_t *sorted_ids, const int32_t *expert_ids,
                                    const int32_t *num_post_padded, int32_t numel,
                                    int32_t num_virtual, int32_t block_m, void *out,
                                    int64_t ld_out, void *stream);
@@ -185,12 +199,12 @@ MOL_API int64_t mol_delta_workspace_bytes(int32_t numel, int32_t R, int32_t num_
 MOL_API mol_status mol_lora_delta(int32_t dtype, const void *xin, int64_t ld_x,
                                   int32_t row_div, const void *A, int32_t R, int32_t K,
                                   int32_t slices, const void *B, int32_t N,
-                                  const float *slot_scale, int32_t num_experts,
-                                  const int32_t *sorted_ids, const int32_t *expert_ids,
-                                  const int32_t *num_post_padded, int32_t numel,
-                                  int32_t num_virtual, int32_t block_m, void *out,
-                                  int64_t ld_out, void *workspace, size_t workspace_bytes,
-                                  void *stream);
+                                  const float *slot_scale, const int32_t *slot_ranks,
+                                  int32_t num_experts, const int32_t *sorted_ids,
+                                  const int32_t *expert_ids, const int32_t *num_post_padded,
+                                  int32_t numel, int32_t num_virtual, int32_t block_m,
+                                  void *out, int64_t ld_out, void *workspace,
+                                  size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -39,7 +39,7 @@ def test_only_mol_symbols_exported():
 
 def test_version_and_status_strings():
     L = mb.lib()
-    assert L.mol_abi_version() == 1
+    assert L.mol_abi_version() == 2
     for code in range(7):
         assert mb.status_string(code)
     assert mb.status_string(99) == "unknown status"
@@ -110,34 +110,38 @@ def test_remap_rejects_before_launch():
 def test_shrink_expand_delta_reject_before_launch():
     L = mb.lib()
     # shrink: unknown dtype, K not a multiple of 16 bytes, misaligned pointer
-    assert L.mol_lora_shrink(7, FAKE, 64, 1, FAKE, 8, 64, FAKE, FAKE, FAKE, 16, 8, 16, FAKE,
-                             None) == mb.MOL_E_DTYPE
-    assert L.mol_lora_shrink(mb.MOL_BF16, FAKE, 68, 1, FAKE, 8, 60, FAKE, FAKE, FAKE, 16, 8,
-                             16, FAKE, None) == mb.MOL_E_ALIGN
-    assert L.mol_lora_shrink(mb.MOL_F32, ctypes.c_void_p(0x1004), 64, 1, FAKE, 8, 64, FAKE,
-                             FAKE, FAKE, 16, 8, 16, FAKE, None) == mb.MOL_E_ALIGN
-    assert L.mol_lora_shrink(mb.MOL_F32, FAKE, 32, 1, FAKE, 8, 64, FAKE, FAKE, FAKE, 16, 8,
-                             16, FAKE, None) == mb.MOL_E_ARG           # ld_x < K
-    assert L.mol_lora_shrink(mb.MOL_BF16, FAKE, 64, 1, FAKE, 8, 64, FAKE, FAKE, FAKE, 16, 8,
-                             16, ctypes.c_void_p(0x1008), None) == mb.MOL_E_ALIGN  # s
+    assert L.mol_lora_shrink(7, FAKE, 64, 1, FAKE, 8, 64, 1, None, 8, FAKE, FAKE, FAKE, 16, 8,
+                             16, FAKE, None) == mb.MOL_E_DTYPE
+    assert L.mol_lora_shrink(mb.MOL_BF16, FAKE, 68, 1, FAKE, 8, 60, 1, None, 8, FAKE, FAKE,
+                             FAKE, 16, 8, 16, FAKE, None) == mb.MOL_E_ALIGN
+    assert L.mol_lora_shrink(mb.MOL_F32, ctypes.c_void_p(0x1004), 64, 1, FAKE, 8, 64, 1, None,
+                             8, FAKE, FAKE, FAKE, 16, 8, 16, FAKE, None) == mb.MOL_E_ALIGN
+    assert L.mol_lora_shrink(mb.MOL_F32, FAKE, 32, 1, FAKE, 8, 64, 1, None, 8, FAKE, FAKE,
+                             FAKE, 16, 8, 16, FAKE, None) == mb.MOL_E_ARG           # ld_x < K
+    assert L.mol_lora_shrink(mb.MOL_BF16, FAKE, 64, 1, FAKE, 8, 64, 1, None, 8, FAKE, FAKE,
+                             FAKE, 16, 8, 16, ctypes.c_void_p(0x1008), None) == mb.MOL_E_ALIGN
+    assert L.mol_lora_shrink(mb.MOL_BF16, FAKE, 64, 1, FAKE, 8, 64, 3, None, 8, FAKE, FAKE,
+                             FAKE, 16, 8, 16, FAKE, None) == mb.MOL_E_ARG     # R % slices
+    assert L.mol_lora_shrink(mb.MOL_BF16, FAKE, 64, 1, FAKE, 8, 64, 1, None, 3, FAKE, FAKE,
+                             FAKE, 16, 8, 16, FAKE, None) == mb.MOL_E_ARG     # V % E
     # expand: R % slices, rank too large, V not a multiple of E
-    assert L.mol_lora_expand(mb.MOL_BF16, FAKE, 63, 2, FAKE, 32, FAKE, 4, FAKE, FAKE, FAKE,
-                             16, 8, 16, FAKE, 32, None) == mb.MOL_E_ARG
-    assert L.mol_lora_expand(mb.MOL_BF16, FAKE, 512, 2, FAKE, 32, FAKE, 4, FAKE, FAKE, FAKE,
-                             16, 8, 16, FAKE, 32, None) == mb.MOL_E_LIMIT
-    assert L.mol_lora_expand(mb.MOL_BF16, FAKE, 16, 1, FAKE, 32, FAKE, 3, FAKE, FAKE, FAKE,
-                             16, 8, 16, FAKE, 32, None) == mb.MOL_E_ARG
-    assert L.mol_lora_expand(mb.MOL_BF16, ctypes.c_void_p(0x1008), 16, 1, FAKE, 32, FAKE, 4,
-                             FAKE, FAKE, FAKE, 16, 8, 16, FAKE, 32, None) == mb.MOL_E_ALIGN
+    assert L.mol_lora_expand(mb.MOL_BF16, FAKE, 63, 2, FAKE, 32, FAKE, None, 4, FAKE, FAKE,
+                             FAKE, 16, 8, 16, FAKE, 32, None) == mb.MOL_E_ARG
+    assert L.mol_lora_expand(mb.MOL_BF16, FAKE, 512, 2, FAKE, 32, FAKE, None, 4, FAKE, FAKE,
+                             FAKE, 16, 8, 16, FAKE, 32, None) == mb.MOL_E_LIMIT
+    assert L.mol_lora_expand(mb.MOL_BF16, FAKE, 16, 1, FAKE, 32, FAKE, None, 3, FAKE, FAKE,
+                             FAKE, 16, 8, 16, FAKE, 32, None) == mb.MOL_E_ARG
+    assert L.mol_lora_expand(mb.MOL_BF16, ctypes.c_void_p(0x1008), 16, 1, FAKE, 32, FAKE, None,
+                             4, FAKE, FAKE, FAKE, 16, 8, 16, FAKE, 32, None) == mb.MOL_E_ALIGN
     # delta: workspace missing or too small
-    assert L.mol_lora_delta(mb.MOL_BF16, FAKE, 64, 1, FAKE, 16, 64, 1, FAKE, 32, FAKE, 4,
+    assert L.mol_lora_delta(mb.MOL_BF16, FAKE, 64, 1, FAKE, 16, 64, 1, FAKE, 32, FAKE, None, 4,
                             FAKE, FAKE, FAKE, 16, 8, 16, FAKE, 32, None, 0,
                             None) == mb.MOL_E_WORKSPACE
-    assert L.mol_lora_delta(mb.MOL_BF16, FAKE, 64, 1, FAKE, 16, 64, 1, FAKE, 32, FAKE, 4,
+    assert L.mol_lora_delta(mb.MOL_BF16, FAKE, 64, 1, FAKE, 16, 64, 1, FAKE, 32, FAKE, None, 4,
                             FAKE, FAKE, FAKE, 16, 8, 16, FAKE, 32, FAKE, 64,
                             None) == mb.MOL_E_WORKSPACE
     # numel == 0 is a no-op
-    assert L.mol_lora_delta(mb.MOL_BF16, None, 64, 1, None, 16, 64, 1, None, 32, None, 4,
+    assert L.mol_lora_delta(mb.MOL_BF16, None, 64, 1, None, 16, 64, 1, None, 32, None, None, 4,
                             None, None, None, 0, 8, 16, None, 32, None, 0, None) == mb.MOL_OK
 
 

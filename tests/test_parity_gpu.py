@@ -62,10 +62,12 @@ class Case:
         self.s, self.out = [], []
         for st, sin in zip(cfg.stages, self.inp.stages):
             s = oracle.lora_shrink(sin.xin, sin.row_div, sin.A, srt, eid, npp, cfg.numel,
-                                   cfg.block_m, pair_mask=self.mask)
+                                   cfg.block_m, pair_mask=self.mask, slices=st.slices,
+                                   slot_ranks=self.inp.slot_ranks, E=cfg.E)
             out = np.zeros((cfg.numel, st.N), dtype=sin.B.dtype)
             oracle.lora_expand(s, st.slices, sin.B, self.inp.scale, cfg.E, srt, eid, npp,
-                               cfg.numel, cfg.block_m, out, pair_mask=self.mask)
+                               cfg.numel, cfg.block_m, out, pair_mask=self.mask,
+                               slot_ranks=self.inp.slot_ranks)
             self.s.append(s)
             self.out.append(out)
         vids = oracle.virtual_topk(self.inp.topk_ids, self.inp.lora_ids, cfg.E, cfg.S)
@@ -213,6 +215,13 @@ EDGE = [
     _edge_cfg(name="mfma_bm48_not_pow2", M=1024, topk=4, E=8, S=2, hidden=256, rank=32,
               stages=configs._two_stage(256, 128, 32), block_m=48, sentinel_count=10,
               nolora_count=10),
+    # per-slot ranks: the weights past a slot's rank hold NaN, rank 5 and 20 end inside a
+    # 16-byte weight vector, rank 0 adds nothing (VALU bf16 and fp32, and MFMA)
+    _edge_cfg(name="ranked_bf16", slot_ranks=(16, 5, 0)),
+    _edge_cfg(name="ranked_f32", dtype="f32", M=19, rank=4, E=5, S=2, slot_ranks=(3, 0)),
+    _edge_cfg(name="ranked_mfma", M=1024, topk=4, E=8, S=2, hidden=256, rank=32,
+              stages=configs._two_stage(256, 128, 32), block_m=64, sentinel_count=10,
+              nolora_count=10, slot_ranks=(20, 32)),
     # k tails past the staged chunk, and an expand slice width (136) that is not a
     # multiple of 64, which keeps the expand on the VALU kernel
     _edge_cfg(name="mfma_ragged_k", M=1024, topk=4, E=8, S=2, hidden=264, rank=32,
@@ -237,6 +246,11 @@ def test_edge_cases(cfg):
         within_tol(got[case.rows], as_f64(case.out[si], cfg)[case.rows],
                    f"{cfg.name}/{st.name}")
         assert np.all(got[case.no_delta] == 0)
+        if cfg.slot_ranks is not None:
+            s = dl.delta_ws[si][:cfg.numel * st.R * 4].view(torch.float32).view(cfg.numel, st.R)
+            s = s.cpu().numpy()
+            within_tol(s[case.rows], case.s[si][case.rows], f"{cfg.name}/{st.name}/s")
+            assert np.all(np.isfinite(s[case.rows]))
     torch.cuda.synchronize()
 
 

@@ -29,13 +29,13 @@ SIGNATURES = {
     "mol_align_workspace_bytes": (_I64, [_I64, _I32, _I32]),
     "mol_align_block_size": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _SZ,
                                     _P]),
-    "mol_lora_shrink": (_I32, [_I32, _P, _I64, _I32, _P, _I32, _I32, _P, _P, _P, _I32, _I32,
-                               _I32, _P, _P]),
-    "mol_lora_expand": (_I32, [_I32, _P, _I32, _I32, _P, _I32, _P, _I32, _P, _P, _P, _I32, _I32,
-                               _I32, _P, _I64, _P]),
+    "mol_lora_shrink": (_I32, [_I32, _P, _I64, _I32, _P, _I32, _I32, _I32, _P, _I32, _P, _P,
+                               _P, _I32, _I32, _I32, _P, _P]),
+    "mol_lora_expand": (_I32, [_I32, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _P, _P, _I32,
+                               _I32, _I32, _P, _I64, _P]),
     "mol_delta_workspace_bytes": (_I64, [_I32, _I32, _I32, _I32]),
-    "mol_lora_delta": (_I32, [_I32, _P, _I64, _I32, _P, _I32, _I32, _I32, _P, _I32, _P, _I32,
-                              _P, _P, _P, _I32, _I32, _I32, _P, _I64, _P, _SZ, _P]),
+    "mol_lora_delta": (_I32, [_I32, _P, _I64, _I32, _P, _I32, _I32, _I32, _P, _I32, _P, _P,
+                              _I32, _P, _P, _P, _I32, _I32, _I32, _P, _I64, _P, _SZ, _P]),
 }
 
 
@@ -165,8 +165,15 @@ def mol_align_block_size(ids, lora_ids, num_experts: int, num_slots: int, block_
     return sorted_ids, expert_ids, num_post_padded
 
 
+def _ranks(slot_ranks):
+    if slot_ranks is not None:
+        _need(slot_ranks, "slot_ranks", torch.int32)
+    return _ptr(slot_ranks)
+
+
 def mol_lora_shrink(xin, row_div: int, A, sorted_ids, expert_ids, num_post_padded,
-                    numel: int, num_virtual: int, block_m: int, s=None):
+                    numel: int, num_virtual: int, block_m: int, s=None, slices: int = 1,
+                    slot_ranks=None, num_experts: int = None):
     _need(xin, "xin", contiguous=False)
     _need(A, "A")
     if xin.stride(1) != 1:
@@ -175,15 +182,17 @@ def mol_lora_shrink(xin, row_div: int, A, sorted_ids, expert_ids, num_post_padde
     if s is None:
         s = torch.empty((max(1, numel), R), dtype=torch.float32, device=A.device)
     _need(s, "s", torch.float32)
+    E = num_virtual if num_experts is None else num_experts
     _check("mol_lora_shrink", lib().mol_lora_shrink(
-        _dtype_code(A), _ptr(xin), xin.stride(0), row_div, _ptr(A), R, K, _ptr(sorted_ids),
-        _ptr(expert_ids), _ptr(num_post_padded), numel, num_virtual, block_m, _ptr(s),
-        _stream(A)))
+        _dtype_code(A), _ptr(xin), xin.stride(0), row_div, _ptr(A), R, K, slices,
+        _ranks(slot_ranks), E, _ptr(sorted_ids), _ptr(expert_ids), _ptr(num_post_padded),
+        numel, num_virtual, block_m, _ptr(s), _stream(A)))
     return s
 
 
 def mol_lora_expand(s, slices: int, B, slot_scale, num_experts: int, sorted_ids, expert_ids,
-                    num_post_padded, numel: int, num_virtual: int, block_m: int, out):
+                    num_post_padded, numel: int, num_virtual: int, block_m: int, out,
+                    slot_ranks=None):
     _need(B, "B")
     _need(s, "s", torch.float32)
     _need(slot_scale, "slot_scale", torch.float32)
@@ -192,9 +201,10 @@ def mol_lora_expand(s, slices: int, B, slot_scale, num_experts: int, sorted_ids,
         raise ValueError("out rows must be contiguous")
     V, N, r = B.shape
     _check("mol_lora_expand", lib().mol_lora_expand(
-        _dtype_code(B), _ptr(s), s.shape[1], slices, _ptr(B), N, _ptr(slot_scale), num_experts,
-        _ptr(sorted_ids), _ptr(expert_ids), _ptr(num_post_padded), numel, num_virtual, block_m,
-        _ptr(out), out.stride(0), _stream(B)))
+        _dtype_code(B), _ptr(s), s.shape[1], slices, _ptr(B), N, _ptr(slot_scale),
+        _ranks(slot_ranks), num_experts, _ptr(sorted_ids), _ptr(expert_ids),
+        _ptr(num_post_padded), numel, num_virtual, block_m, _ptr(out), out.stride(0),
+        _stream(B)))
     return out
 
 
@@ -206,7 +216,7 @@ def new_delta_workspace(numel: int, R: int, num_virtual: int, block_m: int, devi
 
 def mol_lora_delta(xin, row_div: int, A, slices: int, B, slot_scale, num_experts: int,
                    sorted_ids, expert_ids, num_post_padded, numel: int, num_virtual: int,
-                   block_m: int, out, workspace):
+                   block_m: int, out, workspace, slot_ranks=None):
     _need(xin, "xin", contiguous=False)
     _need(A, "A")
     _need(B, "B")
@@ -219,7 +229,7 @@ def mol_lora_delta(xin, row_div: int, A, slices: int, B, slot_scale, num_experts
     _, N, r = B.shape
     _check("mol_lora_delta", lib().mol_lora_delta(
         _dtype_code(A), _ptr(xin), xin.stride(0), row_div, _ptr(A), R, K, slices, _ptr(B), N,
-        _ptr(slot_scale), num_experts, _ptr(sorted_ids), _ptr(expert_ids),
+        _ptr(slot_scale), _ranks(slot_ranks), num_experts, _ptr(sorted_ids), _ptr(expert_ids),
         _ptr(num_post_padded), numel, num_virtual, block_m, _ptr(out), out.stride(0),
         _ptr(workspace), workspace.numel(), _stream(A)))
     return out

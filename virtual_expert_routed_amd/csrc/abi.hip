@@ -145,7 +145,7 @@ MOL_API const char* mol_status_string(mol_status status) {
   }
 }
 
-MOL_API int32_t mol_abi_version(void) { return 1; }
+MOL_API int32_t mol_abi_version(void) { return 2; }
 
 MOL_API mol_status mol_virtual_topk(const int32_t* topk_ids, const int32_t* lora_ids,
                                     int32_t M, int32_t topk, int32_t num_experts,
@@ -283,24 +283,28 @@ extern "C" {
 
 MOL_API mol_status mol_lora_shrink(int32_t dtype, const void* xin, int64_t ld_x,
                                    int32_t row_div, const void* A, int32_t R, int32_t K,
-                                   const int32_t* sorted_ids, const int32_t* expert_ids,
-                                   const int32_t* num_post_padded, int32_t numel,
-                                   int32_t num_virtual, int32_t block_m, float* s,
-                                   void* stream) {
+                                   int32_t slices, const int32_t* slot_ranks,
+                                   int32_t num_experts, const int32_t* sorted_ids,
+                                   const int32_t* expert_ids, const int32_t* num_post_padded,
+                                   int32_t numel, int32_t num_virtual, int32_t block_m,
+                                   float* s, void* stream) {
   const StageCheck rc =
       routing_check(sorted_ids, expert_ids, num_post_padded, numel, num_virtual, block_m);
   if (rc.st != MOL_OK) return rc.st;
   const mol_status sc = shrink_check(dtype, xin, ld_x, row_div, A, R, K, numel, s);
   if (sc != MOL_OK) return sc;
+  if (slices < 1 || R % slices || num_experts < 1 || num_virtual % num_experts)
+    return MOL_E_ARG;
   if (numel == 0) return MOL_OK;
   const bool bf16 = dtype == MOL_BF16;
   const int rpi = mol::shrink_rows_per_item(K, bf16 ? 2 : 4);
   const int64_t rgroups = cdiv64(R, rpi);
   const int64_t grid = rc.max_blocks * rgroups;
   if (grid > kI32Max) return MOL_E_LIMIT;
-  mol::DeltaArgs a = make_delta_args(xin, ld_x, row_div, A, R, K, 1, nullptr, 1, nullptr, 1,
-                                     sorted_ids, expert_ids, num_post_padded, numel,
-                                     num_virtual, block_m, s, nullptr, 0, rc.max_blocks);
+  mol::DeltaArgs a = make_delta_args(xin, ld_x, row_div, A, R, K, slices, nullptr, 1, nullptr,
+                                     num_experts, sorted_ids, expert_ids, num_post_padded,
+                                     numel, num_virtual, block_m, s, nullptr, 0, rc.max_blocks);
+  a.ranks = slot_ranks;
   a.rgroups = (int32_t)rgroups;
   const int32_t mm = shrink_mfma_min(bf16, numel, num_virtual, block_m);
   if (mm > 0 && rc.max_blocks * cdiv64(R, 64) > kI32Max) return MOL_E_LIMIT;
@@ -309,7 +313,8 @@ MOL_API mol_status mol_lora_shrink(int32_t dtype, const void* xin, int64_t ld_x,
 
 MOL_API mol_status mol_lora_expand(int32_t dtype, const float* s, int32_t R, int32_t slices,
                                    const void* B, int32_t N, const float* slot_scale,
-                                   int32_t num_experts, const int32_t* sorted_ids,
+                                   const int32_t* slot_ranks, int32_t num_experts,
+                                   const int32_t* sorted_ids,
                                    const int32_t* expert_ids,
                                    const int32_t* num_post_padded, int32_t numel,
                                    int32_t num_virtual, int32_t block_m, void* out,
@@ -328,6 +333,7 @@ MOL_API mol_status mol_lora_expand(int32_t dtype, const float* s, int32_t R, int
                                      num_experts, sorted_ids, expert_ids, num_post_padded,
                                      numel, num_virtual, block_m, const_cast<float*>(s), out,
                                      ld_out, rc.max_blocks);
+  a.ranks = slot_ranks;
   a.nchunk = (int32_t)cdiv64(N, mol::expand_cols_per_item(R, slices, bf16 ? 2 : 4));
   const int64_t grid = rc.max_blocks * a.nchunk;
   if (grid > kI32Max) return MOL_E_LIMIT;
@@ -347,7 +353,8 @@ MOL_API int64_t mol_delta_workspace_bytes(int32_t numel, int32_t R, int32_t num_
 MOL_API mol_status mol_lora_delta(int32_t dtype, const void* xin, int64_t ld_x,
                                   int32_t row_div, const void* A, int32_t R, int32_t K,
                                   int32_t slices, const void* B, int32_t N,
-                                  const float* slot_scale, int32_t num_experts,
+                                  const float* slot_scale, const int32_t* slot_ranks,
+                                  int32_t num_experts,
                                   const int32_t* sorted_ids, const int32_t* expert_ids,
                                   const int32_t* num_post_padded, int32_t numel,
                                   int32_t num_virtual, int32_t block_m, void* out,
@@ -375,6 +382,7 @@ MOL_API mol_status mol_lora_delta(int32_t dtype, const void* xin, int64_t ld_x,
                                      num_experts, sorted_ids, expert_ids, num_post_padded,
                                      numel, num_virtual, block_m, s, out, ld_out,
                                      rc.max_blocks);
+  a.ranks = slot_ranks;
   a.rgroups = (int32_t)cdiv64(R, rpi);
   a.nchunk = (int32_t)cdiv64(N, mol::expand_cols_per_item(R, slices, esz));
   const int64_t grid_s = rc.max_blocks * (int64_t)a.rgroups;

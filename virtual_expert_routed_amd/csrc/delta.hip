@@ -58,8 +58,8 @@ struct ShrinkLds {
 // Rows [rg*RPI, rg*RPI+RPI) of s for the pairs p[0..nq) (nq <= kPG). The x segments of
 // the pairs go straight into xs (LDS); lane 0 of each row group stores the sums.
 template <bool BF16, int LPR>
-__device__ __forceinline__ void shrink_group(const DeltaArgs& a, int e, int rg, const int* p,
-                                             int nq, uint4* xs) {
+__device__ __forceinline__ void shrink_group(const DeltaArgs& a, int e, int rl, int rg,
+                                             const int* p, int nq, uint4* xs) {
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int RPI = kThreads / LPR;
   constexpr int SEGV = kSeg * LPR;            // vectors of one x segment
@@ -68,7 +68,8 @@ __device__ __forceinline__ void shrink_group(const DeltaArgs& a, int e, int rg, 
   const int tid = threadIdx.x;
   const int lr = tid % LPR;
   const int row = rg * RPI + tid / LPR;
-  const bool row_ok = row < a.R;
+  const bool row_in = row < a.R;
+  const bool row_ok = row_in && row % (a.R / a.slices) < rl;  // past the rank: zero, unread
   const int nvec = a.K * ESZ / 16;
   const int vpl = (nvec + LPR - 1) / LPR;
   const int64_t abytes = (int64_t)a.R * a.K * ESZ;
@@ -113,7 +114,7 @@ __device__ __forceinline__ void shrink_group(const DeltaArgs& a, int e, int rg, 
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc[i] += __shfl_xor(acc[i], off, 64);
   }
-  if (lr == 0 && row_ok) {
+  if (lr == 0 && row_in) {
 #pragma unroll
     for (int i = 0; i < kPG; ++i) {
       if (i >= nq) break;
@@ -132,8 +133,9 @@ __device__ __forceinline__ void shrink_block(const DeltaArgs& a, int blk, int rg
   const int n4 = first_pairs(a, blk, p, &all_here, &mfma);
   const int e = block_expert(a, blk);
   if (e < 0 || mfma) return;  // no delta, or the MFMA kernel's block
+  const int rl = slot_rank(a, e);
   if (all_here) {  // the common decode case: no id staging at all
-    if (n4 > 0) shrink_group<BF16, LPR>(a, e, rg, p, n4, xs);
+    if (n4 > 0) shrink_group<BF16, LPR>(a, e, rl, rg, p, n4, xs);
     return;
   }
   for (int j0 = 0; j0 < a.BM; j0 += kPidSlots) {
@@ -147,7 +149,7 @@ __device__ __forceinline__ void shrink_block(const DeltaArgs& a, int blk, int rg
 #pragma unroll
       for (int i = 0; i < kPG; ++i) pq[i] = q0 + i < nr ? pid[q0 + i] : a.numel;
       __syncthreads();  // xs of the previous group is no longer read
-      shrink_group<BF16, LPR>(a, e, rg, pq, min(kPG, nr - q0), xs);
+      shrink_group<BF16, LPR>(a, e, rl, rg, pq, min(kPG, nr - q0), xs);
     }
     if (nr < kPidSlots) return;  // the block's real entries ended in this pass
   }
@@ -163,10 +165,13 @@ __global__ void __launch_bounds__(kThreads) shrink_kernel(DeltaArgs a) {
 
 // ------------------------------------------------------------------------------ expand
 
+// The weight rows of this thread's columns; vectors wholly past the slot's rank rl read as
+// zero (the one that straddles rl is trimmed where it is used).
 template <bool BF16, int RV, int CPT>
-__device__ __forceinline__ void load_b_rows(const DeltaArgs& a, int e, const int* n,
+__device__ __forceinline__ void load_b_rows(const DeltaArgs& a, int e, int rl, const int* n,
                                             uint4 (*bv)[RV]) {
   constexpr int RB = RV * 16;  // bytes of one weight row
+  constexpr int VE = BF16 ? 8 : 4;
   const int64_t bbytes = (int64_t)a.N * RB;
   const __amdgpu_buffer_rsrc_t rb = expert_rsrc((const char*)a.B + (int64_t)e * bbytes, bbytes);
 #pragma unroll
@@ -174,7 +179,7 @@ __device__ __forceinline__ void load_b_rows(const DeltaArgs& a, int e, const int
     const bool ok = n[j] < a.N;
 #pragma unroll
     for (int v = 0; v < RV; ++v)
-      bv[j][v] = buf16(rb, ok ? (uint32_t)n[j] * RB + v * 16 : kOutOfRange);
+      bv[j][v] = buf16(rb, ok && v * VE < rl ? (uint32_t)n[j] * RB + v * 16 : kOutOfRange);
   }
 }
 
@@ -186,7 +191,7 @@ template <bool BF16, int RV, int CPT>
 __device__ __forceinline__ void expand_outputs(const DeltaArgs& a, const uint4 (*bv)[RV],
                                                const int* pid, int nr, const float* s_lds,
                                                const int* n, const int* soff, float sc,
-                                               const float (*ov)[CPT]) {
+                                               const float (*ov)[CPT], int rl) {
   constexpr int VE = BF16 ? 8 : 4;
   float cur[kPG][CPT];
 #pragma unroll
@@ -224,6 +229,7 @@ __device__ __forceinline__ void expand_outputs(const DeltaArgs& a, const uint4 (
           // hold RV*8 more floats per column live, for no gain at one or two pairs a block
           uint4 b = bv[j][v];
           asm volatile("" : "+v"(b.x), "+v"(b.y), "+v"(b.z), "+v"(b.w));
+          if (rl < (v + 1) * VE) b = keep_first<BF16>(b, rl - v * VE);  // uniform
           acc = dot16_s<BF16>(b, sv + v * VE, acc);
         }
         store_out<BF16>(a, p, n[j], fmaf(sc, acc, cur[i][j]));
@@ -251,6 +257,8 @@ __device__ __forceinline__ void expand_block(const DeltaArgs& a, int blk, int ch
   const int n4 = first_pairs(a, blk, p, &all_here, &mfma);
   const int e = block_expert(a, blk);
   if (e < 0 || mfma) return;  // no delta, or the MFMA kernel's block
+  const int rl = slot_rank(a, e);
+  if (rl == 0) return;  // a slot of rank 0 adds nothing
   const int width = a.N / a.slices;
   int n[CPT], soff[CPT];
 #pragma unroll
@@ -260,7 +268,7 @@ __device__ __forceinline__ void expand_block(const DeltaArgs& a, int blk, int ch
   }
   const float sc = a.scale[e / a.E];
   uint4 bv[CPT][RV];
-  load_b_rows<BF16, RV, CPT>(a, e, n, bv);
+  load_b_rows<BF16, RV, CPT>(a, e, rl, n, bv);
   if (all_here) {
     if (n4 == 0) return;
     // the block's s rows (n4 * R floats, R a multiple of 4) straight into LDS, and the old
@@ -285,7 +293,7 @@ __device__ __forceinline__ void expand_block(const DeltaArgs& a, int blk, int ch
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    expand_outputs<BF16, RV, CPT>(a, bv, pid, n4, s_lds, n, soff, sc, ov);
+    expand_outputs<BF16, RV, CPT>(a, bv, pid, n4, s_lds, n, soff, sc, ov, rl);
     return;
   }
   const int pg = min(kPidSlots, kSLdsFloats / a.R);
@@ -308,7 +316,7 @@ __device__ __forceinline__ void expand_block(const DeltaArgs& a, int blk, int ch
       s_lds[i] = a.s[(int64_t)pid[q] * a.R + (i - q * a.R)];
     }
     __syncthreads();
-    expand_outputs<BF16, RV, CPT>(a, bv, pid, nr, s_lds, n, soff, sc, ov);
+    expand_outputs<BF16, RV, CPT>(a, bv, pid, nr, s_lds, n, soff, sc, ov, rl);
     if (nr < pg) break;  // the block's real entries ended in this pass
   }
 }

@@ -123,6 +123,32 @@ __device__ __forceinline__ int first_pairs(const DeltaArgs& a, int blk, int* p, 
   return nr;
 }
 
+// Rank of the slot of virtual expert e: its slot_ranks entry clamped to [0, r], or r = R /
+// slices when there is no rank table (one load, uniform over the workgroup).
+__device__ __forceinline__ int slot_rank(const DeltaArgs& a, int e) {
+  const int r = a.R / a.slices;
+  if (!a.ranks) return r;
+  const int v = a.ranks[e / a.E];
+  return v < 0 ? 0 : (v > r ? r : v);
+}
+
+// The first `keep` elements of a 16-byte weight vector (8 bf16 or 4 fp32), the rest zero.
+template <bool BF16>
+__device__ __forceinline__ uint4 keep_first(uint4 v, int keep) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (BF16) {
+      const uint32_t lo = keep > 2 * i ? 0x0000ffffu : 0u;
+      const uint32_t hi = keep > 2 * i + 1 ? 0xffff0000u : 0u;
+      w[i] &= lo | hi;
+    } else {
+      w[i] = keep > i ? w[i] : 0u;
+    }
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // Branch-free 16-byte load: a masked address is clamped to the array's first element
 // and its value replaced by zero.
 __device__ __forceinline__ uint4 ld16_if(const char* base, int64_t off, bool ok) {

@@ -127,6 +127,7 @@ __global__ void __launch_bounds__(256) shrink_mfma_kernel(DeltaArgs a) {
   const int blk = blockIdx.x / nrt, r0 = (blockIdx.x % nrt) * G::kRows;
   const int e = block_expert(a, blk);
   if (e < 0 || !block_has(a, blk, a.mfma_min)) return;
+  const int rl = slot_rank(a, e), r = a.R / a.slices;  // rows past the rank store 0
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const char* av = (const char*)a.A + (int64_t)e * a.R * a.K * 2;
@@ -181,7 +182,7 @@ __global__ void __launch_bounds__(256) shrink_mfma_kernel(DeltaArgs a) {
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
             const int row = r0 + nt * 16 + (lane & 15);
-            if (row < a.R) a.s[(int64_t)pi * a.R + row] = acc[nt][i];
+            if (row < a.R) a.s[(int64_t)pi * a.R + row] = row % r < rl ? acc[nt][i] : 0.f;
           }
         }
       }
@@ -252,7 +253,7 @@ __device__ __forceinline__ void load_out_tile(const DeltaArgs& a, const int* pid
 
 template <int KS>
 __device__ __forceinline__ void expand_mfma_block(const DeltaArgs& a, int blk, int chunk,
-                                                  int e, int* pid, int* nrows_lds,
+                                                  int e, int rl, int* pid, int* nrows_lds,
                                                   uint4* s_lds, float* tile) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -276,8 +277,9 @@ __device__ __forceinline__ void expand_mfma_block(const DeltaArgs& a, int blk, i
     const int n = c0 + 16 * nt + (lane & 15);
 #pragma unroll
     for (int st = 0; st < KS; ++st) {
-      const int k = 32 * st + 8 * (lane >> 4);
-      bf[nt][st] = buf16(rb, n < a.N ? (uint32_t)((n * r + k) * 2) : kOutOfRange);
+      const int k = 32 * st + 8 * (lane >> 4);  // rank dimensions past rl are zero
+      bf[nt][st] = buf16(rb, n < a.N && k < rl ? (uint32_t)((n * r + k) * 2) : kOutOfRange);
+      if (rl < r) bf[nt][st] = keep_first<true>(bf[nt][st], rl - k);
     }
   }
   for (int j0 = 0; j0 < a.BM; j0 += kRowsPerPass) {
@@ -357,7 +359,9 @@ __global__ void __launch_bounds__(256) expand_mfma_kernel(DeltaArgs a) {
   const int blk = blockIdx.x / a.nchunk, chunk = blockIdx.x % a.nchunk;
   const int e = block_expert(a, blk);
   if (e < 0 || !block_has(a, blk, a.mfma_min)) return;
-  expand_mfma_block<KS>(a, blk, chunk, e, pid, &nrows_lds, s_lds, tile);
+  const int rl = slot_rank(a, e);
+  if (rl == 0) return;  // a slot of rank 0 adds nothing
+  expand_mfma_block<KS>(a, blk, chunk, e, rl, pid, &nrows_lds, s_lds, tile);
 }
 
 }  // namespace

@@ -63,6 +63,7 @@ struct DeltaArgs {
   void* out;
   int64_t ld_out;
   int32_t max_blocks;
+  const int32_t* ranks;  // [S] per-slot ranks (clamped to [0, R/slices]) or nullptr
   int32_t mfma_min;      // > 0: blocks with at least this many real pairs go to the MFMA
                          // kernels and the VALU kernels skip them; 0: VALU kernels only
 };

@@ -31,6 +31,8 @@ class DeviceLayer:
         self.topk_ids = torch.from_numpy(inp.topk_ids).to(dev)
         self.lora_ids = torch.from_numpy(inp.lora_ids).to(dev)
         self.scale = torch.from_numpy(inp.scale).to(dev)
+        ranks = getattr(inp, "slot_ranks", None)
+        self.slot_ranks = None if ranks is None else torch.from_numpy(ranks).to(dev)
         x = to_device(inp.x, dev, bf16)
         self.A, self.B, self.xin, self.row_div = [], [], [], []
         for st, sin in zip(cfg.stages, inp.stages):
@@ -71,14 +73,15 @@ class DeviceLayer:
     def shrink(self, si: int):
         c = self.cfg
         mb.mol_lora_shrink(self.xin[si], self.row_div[si], self.A[si], *self.routing(),
-                           c.numel, c.V, c.block_m, s=self.s[si])
+                           c.numel, c.V, c.block_m, s=self.s[si], slices=c.stages[si].slices,
+                           slot_ranks=self.slot_ranks, num_experts=c.E)
         return self.s[si]
 
     def expand(self, si: int):
         c = self.cfg
         st = c.stages[si]
         mb.mol_lora_expand(self.s[si], st.slices, self.B[si], self.scale, c.E, *self.routing(),
-                           c.numel, c.V, c.block_m, self.out[si])
+                           c.numel, c.V, c.block_m, self.out[si], slot_ranks=self.slot_ranks)
         return self.out[si]
 
     def delta(self, si: int):
@@ -86,7 +89,7 @@ class DeviceLayer:
         st = c.stages[si]
         mb.mol_lora_delta(self.xin[si], self.row_div[si], self.A[si], st.slices, self.B[si],
                           self.scale, c.E, *self.routing(), c.numel, c.V, c.block_m,
-                          self.out[si], self.delta_ws[si])
+                          self.out[si], self.delta_ws[si], slot_ranks=self.slot_ranks)
         return self.out[si]
 
     def run(self, fused: bool = True):
