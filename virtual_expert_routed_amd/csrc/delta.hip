@@ -166,7 +166,7 @@ __global__ void __launch_bounds__(kThreads) shrink_kernel(DeltaArgs a) {
 // ------------------------------------------------------------------------------ expand
 
 // The weight rows of this thread's columns; vectors wholly past the slot's rank rl read as
-// zero (the one that straddles rl is trimmed where it is used).
+// zero (the one that straddles rl is trimmed by trim_b_rows once the loads have landed).
 template <bool BF16, int RV, int CPT>
 __device__ __forceinline__ void load_b_rows(const DeltaArgs& a, int e, int rl, const int* n,
                                             uint4 (*bv)[RV]) {
@@ -183,6 +183,21 @@ __device__ __forceinline__ void load_b_rows(const DeltaArgs& a, int e, int rl, c
   }
 }
 
+// Zero the elements at rank rl and past of the vector that straddles rl (a slot below full
+// rank only; idempotent). Called after the weight loads have been waited for, so a full
+// rank slot pays one uniform branch and a ranked one no extra round trip.
+template <bool BF16, int RV, int CPT>
+__device__ __forceinline__ void trim_b_rows(uint4 (*bv)[RV], int rl) {
+  constexpr int VE = BF16 ? 8 : 4;
+  if (rl >= RV * VE) return;  // uniform
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+#pragma unroll
+    for (int v = 0; v < RV; ++v)
+      if (v * VE < rl && rl < (v + 1) * VE) bv[j][v] = keep_first<BF16>(bv[j][v], rl - v * VE);
+  }
+}
+
 // out[p, n] = round(out[p, n] + sc * <B_v[n], s_p[slice(n)]>) for the pairs pid[0..nr),
 // kPG pairs at a time; ov holds the old values of the first kPG pairs (loaded ahead by the
 // caller), and the old values of each next group are loaded while the current one is
@@ -191,7 +206,7 @@ template <bool BF16, int RV, int CPT>
 __device__ __forceinline__ void expand_outputs(const DeltaArgs& a, const uint4 (*bv)[RV],
                                                const int* pid, int nr, const float* s_lds,
                                                const int* n, const int* soff, float sc,
-                                               const float (*ov)[CPT], int rl) {
+                                               const float (*ov)[CPT]) {
   constexpr int VE = BF16 ? 8 : 4;
   float cur[kPG][CPT];
 #pragma unroll
@@ -229,7 +244,6 @@ __device__ __forceinline__ void expand_outputs(const DeltaArgs& a, const uint4 (
           // hold RV*8 more floats per column live, for no gain at one or two pairs a block
           uint4 b = bv[j][v];
           asm volatile("" : "+v"(b.x), "+v"(b.y), "+v"(b.z), "+v"(b.w));
-          if (rl < (v + 1) * VE) b = keep_first<BF16>(b, rl - v * VE);  // uniform
           acc = dot16_s<BF16>(b, sv + v * VE, acc);
         }
         store_out<BF16>(a, p, n[j], fmaf(sc, acc, cur[i][j]));
@@ -293,7 +307,8 @@ __device__ __forceinline__ void expand_block(const DeltaArgs& a, int blk, int ch
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    expand_outputs<BF16, RV, CPT>(a, bv, pid, n4, s_lds, n, soff, sc, ov, rl);
+    trim_b_rows<BF16, RV, CPT>(bv, rl);
+    expand_outputs<BF16, RV, CPT>(a, bv, pid, n4, s_lds, n, soff, sc, ov);
     return;
   }
   const int pg = min(kPidSlots, kSLdsFloats / a.R);
@@ -316,7 +331,8 @@ __device__ __forceinline__ void expand_block(const DeltaArgs& a, int blk, int ch
       s_lds[i] = a.s[(int64_t)pid[q] * a.R + (i - q * a.R)];
     }
     __syncthreads();
-    expand_outputs<BF16, RV, CPT>(a, bv, pid, nr, s_lds, n, soff, sc, ov, rl);
+    trim_b_rows<BF16, RV, CPT>(bv, rl);
+    expand_outputs<BF16, RV, CPT>(a, bv, pid, nr, s_lds, n, soff, sc, ov);
     if (nr < pg) break;  // the block's real entries ended in this pass
   }
 }

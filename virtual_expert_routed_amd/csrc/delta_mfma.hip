@@ -279,7 +279,6 @@ __device__ __forceinline__ void expand_mfma_block(const DeltaArgs& a, int blk, i
     for (int st = 0; st < KS; ++st) {
       const int k = 32 * st + 8 * (lane >> 4);  // rank dimensions past rl are zero
       bf[nt][st] = buf16(rb, n < a.N && k < rl ? (uint32_t)((n * r + k) * 2) : kOutOfRange);
-      if (rl < r) bf[nt][st] = keep_first<true>(bf[nt][st], rl - k);
     }
   }
   for (int j0 = 0; j0 < a.BM; j0 += kRowsPerPass) {
@@ -290,6 +289,14 @@ __device__ __forceinline__ void expand_mfma_block(const DeltaArgs& a, int blk, i
     load_out_tile(a, pid, nrows, 0, chunk, ov);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    if (rl < r) {  // uniform; after the wait, so the weight loads stay in one round trip
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+        for (int st = 0; st < KS; ++st)
+          bf[nt][st] = keep_first<true>(bf[nt][st], rl - (32 * st + 8 * (lane >> 4)));
+      }
+    }
     const int ntiles = (nrows + 15) / 16;
 #pragma unroll 1
     for (int pt = 0; pt < ntiles; ++pt) {
