@@ -54,6 +54,11 @@ def lib():
         L.oracle_lora_expand.argtypes = [ctypes.c_int, P, I32, I32, P, I32, P, I32, P, P, I32,
                                          I64, I32, P, P, I64, P]
         L.oracle_lora_expand.restype = ctypes.c_int
+        L.oracle_moe_combine.argtypes = [ctypes.c_int, P, I64, P, P, I64, I32, I32, I32, P, I64]
+        L.oracle_moe_combine.restype = ctypes.c_int
+        L.oracle_lora_expand_combine.argtypes = [ctypes.c_int, P, I32, P, I32, P, P, P, P, P,
+                                                 I64, I32, I32, I32, P, I64, P, I64]
+        L.oracle_lora_expand_combine.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -164,6 +169,47 @@ def lora_expand(s, slices: int, B, scale, E: int, sorted_ids, expert_ids, npp: i
     if rc:
         raise ValueError(f"oracle_lora_expand: {rc}")
     return out
+
+
+def moe_combine(rows, topk_ids, topk_weights, E: int) -> np.ndarray:
+    """y [M, N] (rows' dtype) = per token the weighted sum of its pair rows (rows
+    [M*topk, N]) over the pairs with a local base expert, rounded once."""
+    rows = np.ascontiguousarray(rows)
+    t = np.ascontiguousarray(topk_ids, dtype=np.int32)
+    w = np.ascontiguousarray(topk_weights, dtype=np.float32)
+    M, k = t.shape
+    assert w.shape == (M, k) and rows.shape[0] == M * k
+    N = rows.shape[1]
+    y = np.zeros((M, N), dtype=rows.dtype)
+    rc = lib().oracle_moe_combine(_dt(rows), _ptr(rows), N, _ptr(t), _ptr(w), M, k, E, N,
+                                  _ptr(y), N)
+    if rc:
+        raise ValueError(f"oracle_moe_combine: {rc}")
+    return y
+
+
+def lora_expand_combine(s, B, scale, topk_ids, lora_ids, topk_weights, E: int, S: int,
+                        base, slot_ranks=None) -> np.ndarray:
+    """The down stage's expand fused with the combine: y [M, N] from s [M*topk, R]
+    (float64), B [V, N, R], base rows [M*topk, N]; nothing rounded before the end."""
+    s = np.ascontiguousarray(s, dtype=np.float64)
+    B = np.ascontiguousarray(B)
+    base = np.ascontiguousarray(base)
+    V, N, R = B.shape
+    t = np.ascontiguousarray(topk_ids, dtype=np.int32)
+    l = np.ascontiguousarray(lora_ids, dtype=np.int32)
+    w = np.ascontiguousarray(topk_weights, dtype=np.float32)
+    M, k = t.shape
+    assert s.shape == (M * k, R) and base.shape == (M * k, N) and base.dtype == B.dtype
+    sc = np.ascontiguousarray(scale, dtype=np.float32)
+    rk = _ranks(slot_ranks)
+    y = np.zeros((M, N), dtype=B.dtype)
+    rc = lib().oracle_lora_expand_combine(_dt(B), _ptr(s), R, _ptr(B), N, _ptr(sc), _ptr(rk),
+                                          _ptr(t), _ptr(l), _ptr(w), M, k, E, S, _ptr(base),
+                                          N, _ptr(y), N)
+    if rc:
+        raise ValueError(f"oracle_lora_expand_combine: {rc}")
+    return y
 
 
 def run_layer(inp, outs=None, pair_mask=None):

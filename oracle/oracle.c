@@ -27,6 +27,13 @@
  * Per-slot ranks (optional): a slot of rank rl < r uses rank dimensions [0, rl) of each
  * slice; s is 0 past it, and a slot of rank 0 gets no delta.
  *
+ *   combine - the step after the down projection, which the pages leave implicit: each
+ *             token's output is the router-weighted sum of its top-k pair rows,
+ *             y[m, n] = sum_k w[m, k] * rows[m*topk + k, n], over the pairs whose base
+ *             expert is local (0 <= t < E; a negative t is an expert-parallel sentinel
+ *             whose expert lives on another GPU). The fused form takes the down stage's
+ *             rows as base + delta, never rounded in between.
+ *
  * Readings taken where the pages leave a step open (each is listed with its reason in
  * the design notes): a token with no adapter (slot -1) or a slot >= S, and a base id
  * >= E, map to virtual id -1; pairs inside a bucket keep ascending pair order; padding
@@ -285,6 +292,86 @@ int oracle_lora_expand(int dtype, const double *s, int32_t R, int32_t slices,
                     ob[o] = oracle_bf16_from_double(bf16_to_double(ob[o]) + d);
                 }
             }
+        }
+    }
+    return OR_OK;
+}
+
+/* ---- combine ---------------------------------------------------------------------- */
+
+static void store_rounded(int dtype, double v, void *y, int64_t o) {
+    if (dtype == OR_F32) {
+        ((float *)y)[o] = (float)v;
+    } else {
+        ((uint16_t *)y)[o] = oracle_bf16_from_double(v);
+    }
+}
+
+/* y[m][n] = round( sum over k ascending with 0 <= t[m][k] < E of
+ *                  w[m][k] * rows[m*topk + k][n] )
+ * summed in double, rounded once (bf16 to nearest even, or to float). Rows of pairs with no
+ * local expert are never read. rows are ld_rows elements apart, y rows ld_y. */
+int oracle_moe_combine(int dtype, const void *rows, int64_t ld_rows, const int32_t *topk_ids,
+                       const float *topk_weights, int64_t M, int32_t topk, int32_t E,
+                       int32_t N, void *y, int64_t ld_y) {
+    if ((dtype != OR_F32 && dtype != OR_BF16) || M < 0 || topk <= 0 || E <= 0 || N <= 0 ||
+        ld_rows < N || ld_y < N)
+        return OR_E_ARG;
+    if (M > 0 && (!rows || !topk_ids || !topk_weights || !y)) return OR_E_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int32_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int32_t k = 0; k < topk; ++k) {
+                const int64_t p = m * topk + k;
+                const int32_t t = topk_ids[p];
+                if (t < 0 || t >= E) continue;  /* no local expert: no row */
+                acc += (double)topk_weights[p] * load_elem(rows, p * ld_rows + n, dtype);
+            }
+            store_rounded(dtype, acc, y, m * ld_y + n);
+        }
+    }
+    return OR_OK;
+}
+
+/* The down stage's expand fused with the combine (one slice, rank r = R):
+ *   y[m][n] = round( sum over k ascending with 0 <= t < E of
+ *                    w[m][k] * (base[p][n] + d_p[n]) ),   p = m*topk + k,
+ * where d_p[n] = scale[l] * sum_{j < rl} B[v][n][j] * s[p*R + j] for a pair with a valid
+ * virtual expert v = t + l*E (l = lora[m] in [0, S)) and slot rank rl > 0, else 0. Nothing
+ * is rounded before the final sum. */
+int oracle_lora_expand_combine(int dtype, const double *s, int32_t R, const void *B,
+                               int32_t N, const float *scale, const int32_t *slot_ranks,
+                               const int32_t *topk_ids, const int32_t *lora_ids,
+                               const float *topk_weights, int64_t M, int32_t topk, int32_t E,
+                               int32_t S, const void *base, int64_t ld_base, void *y,
+                               int64_t ld_y) {
+    if ((dtype != OR_F32 && dtype != OR_BF16) || R <= 0 || N <= 0 || M < 0 || topk <= 0 ||
+        E <= 0 || S <= 0 || ld_base < N || ld_y < N)
+        return OR_E_ARG;
+    if (M > 0 && (!s || !B || !scale || !topk_ids || !lora_ids || !topk_weights || !base || !y))
+        return OR_E_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int32_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int32_t k = 0; k < topk; ++k) {
+                const int64_t p = m * topk + k;
+                const int32_t t = topk_ids[p];
+                if (t < 0 || t >= E) continue;
+                double row = load_elem(base, p * ld_base + n, dtype);
+                const int32_t v = virtual_id(t, lora_ids[m], E, S);
+                if (v >= 0) {
+                    const int32_t l = v / E;
+                    const int32_t rl = slot_rank(slot_ranks, l, R);
+                    const int64_t brow = ((int64_t)v * N + n) * R;
+                    double d = 0.0;
+                    for (int32_t j = 0; j < rl; ++j) d += load_elem(B, brow + j, dtype) * s[p * R + j];
+                    row += (double)scale[l] * d;
+                }
+                acc += (double)topk_weights[p] * row;
+            }
+            store_rounded(dtype, acc, y, m * ld_y + n);
         }
     }
     return OR_OK;

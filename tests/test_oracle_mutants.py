@@ -35,6 +35,21 @@ MUTANTS = [
     ("rank_zero_as_full", "return v < 0 ? 0 : (v > r ? r : v);",
      "return v <= 0 ? r : (v > r ? r : v);"),
     ("rank_shrink_ignored", "if (i % r >= rl) {", "if (0) {"),
+    ("combine_reads_sentinel_rows", "if (t < 0 || t >= E) continue;  /* no local expert: no row */",
+     "if (t >= E) continue;"),
+    ("combine_weight_of_token", "(double)topk_weights[p] * load_elem(rows",
+     "(double)topk_weights[m] * load_elem(rows"),
+    ("combine_truncates", "((float *)y)[o] = (float)v;", "((float *)y)[o] = (float)(v * (1.0 - 1e-6));"),
+    ("fused_scale_dropped", "row += (double)scale[l] * d;", "row += d;"),
+    ("fused_weight_dropped", "acc += (double)topk_weights[p] * row;", "acc += row;"),
+    ("fused_rank_ignored", "for (int32_t j = 0; j < rl; ++j) d +=",
+     "for (int32_t j = 0; j < R; ++j) d +="),
+    ("fused_no_adapter_drops_base",
+     "double row = load_elem(base, p * ld_base + n, dtype);\n"
+     "                const int32_t v = virtual_id(t, lora_ids[m], E, S);",
+     "const int32_t v = virtual_id(t, lora_ids[m], E, S);\n"
+     "                if (v < 0) continue;\n"
+     "                double row = load_elem(base, p * ld_base + n, dtype);"),
 ]
 
 
@@ -58,6 +73,18 @@ def _battery(lib):
             lib, P.RANKED[0])),
         ("ranked_bf16", lambda: P.test_ranked_delta_equals_full_rank_on_zeroed_weights(
             lib, P.RANKED[1])),
+        ("combine_matvec", lambda: [P.test_combine_is_a_batched_matvec(lib, d)
+                                    for d in ("f32", "bf16")]),
+        ("combine_local", lambda: [P.test_combine_reads_only_local_pairs(lib, d)
+                                   for d in ("f32", "bf16")]),
+        ("fused_k1", lambda: [P.test_fused_combine_one_unit_slot_equals_expand(lib, c)
+                              for c in P.FUSED]),
+        ("fused_rows", lambda: [P.test_fused_combine_equals_combine_of_expanded_rows(lib, c)
+                                for c in P.FUSED]),
+        ("fused_base", lambda: [P.test_fused_combine_without_adapters_is_the_base_combine(
+            lib, c) for c in P.FUSED]),
+        ("fused_ranked", lambda: P.test_fused_combine_ranked_equals_full_rank_on_zeroed_weights(
+            lib)),
     ]
     for name, fn in cases:
         try:

@@ -352,3 +352,149 @@ def test_threads_do_not_change_results(oracle_lib):
     finally:
         oracle_lib.set_num_threads(n0)
     assert np.array_equal(a[1], b[1]) and np.array_equal(a[0], b[0], equal_nan=True)
+
+
+# -------------------------------------------------------------------------- combine
+# The combine is the step after the down projection: per token, the router-weighted sum
+# of its pair rows over the pairs whose base expert is local (0 <= t < E).
+
+
+def _combine_case(dtype, M=13, k=4, N=40, E=6, seed=0, sentinels=True):
+    rng = np.random.default_rng(seed)
+    t = rng.integers(0, E, size=(M, k)).astype(np.int32)
+    if sentinels:
+        t.reshape(-1)[rng.choice(M * k, size=M * k // 5, replace=False)] = -1
+        t.reshape(-1)[rng.choice(M * k, size=3, replace=False)] = E + 2  # no such expert
+    w = rng.random((M, k), dtype=np.float32) + np.float32(0.05)
+    rows = rng.standard_normal((M * k, N), dtype=np.float32)
+    if dtype == "bf16":
+        rows = inputs.f32_to_bf16_bits(rows)
+    return t, w, rows
+
+
+def _local(t, E):
+    return (t >= 0) & (t < E)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_combine_is_a_batched_matvec(oracle_lib, dtype):
+    # With every expert local, y[m] = w[m] @ rows[m*k:(m+1)*k]: numpy's batched matmul in
+    # double, rounded once.
+    M, k, N, E = 13, 4, 40, 6
+    t, w, rows = _combine_case(dtype, M, k, N, E, seed=1, sentinels=False)
+    y = oracle_lib.moe_combine(rows, t, w, E)
+    ref = np.matmul(w.astype(np.float64)[:, None, :],
+                    pins.to_f64(rows).reshape(M, k, N))[:, 0, :]
+    if dtype == "f32":
+        np.testing.assert_allclose(y, ref.astype(np.float32), rtol=1e-6, atol=1e-7)
+    else:
+        want = pins.bf16_rne_bits(ref)
+        assert np.mean(y == want) > 0.999
+        assert np.all(np.abs(pins.bf16_bits_to_f64(y) - ref) <= np.abs(ref) * 2.0 ** -8)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_combine_reads_only_local_pairs(oracle_lib, dtype):
+    # Pairs whose expert is not local (negative sentinel, or an id >= E) have no row: NaN
+    # there must not reach y, which equals the batched matvec with those weights zeroed.
+    M, k, N, E = 13, 4, 40, 6
+    t, w, rows = _combine_case(dtype, M, k, N, E, seed=2)
+    off = ~_local(t, E).reshape(-1)
+    assert off.any()
+    nan = np.uint16(0x7FC0) if dtype == "bf16" else np.float32(np.nan)
+    rows[off] = nan
+    y = oracle_lib.moe_combine(rows, t, w, E)
+    w0 = np.where(_local(t, E), w, 0).astype(np.float64)
+    r0 = np.where(off[:, None], 0.0, pins.to_f64(rows)).reshape(M, k, N)
+    ref = np.matmul(w0[:, None, :], r0)[:, 0, :]
+    got = pins.to_f64(y)
+    assert np.all(np.isfinite(got))
+    np.testing.assert_allclose(got, ref, rtol=2.0 ** -8, atol=1e-30)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_combine_one_slot_unit_weight_is_the_row(oracle_lib, dtype):
+    t, _, rows = _combine_case(dtype, M=9, k=1, N=33, E=4, seed=3, sentinels=False)
+    w = np.ones((9, 1), np.float32)
+    assert np.array_equal(oracle_lib.moe_combine(rows, t, w, 4), rows)
+
+
+def _down_case(oracle_lib, cfg, seed):
+    """One layer's down stage: its s (oracle shrink over the aligned blocks), B, base rows
+    and router weights."""
+    inp = inputs.generate(cfg, seed=seed)
+    si = len(cfg.stages) - 1
+    st, sin = cfg.stages[si], inp.stages[si]
+    srt, eid, npp = oracle_lib.align_block_size(inp.topk_ids, inp.lora_ids, cfg.E, cfg.S,
+                                                cfg.block_m)
+    s = oracle_lib.lora_shrink(sin.xin, sin.row_div, sin.A, srt, eid, npp, cfg.numel,
+                               cfg.block_m, slot_ranks=inp.slot_ranks, E=cfg.E)
+    base = inputs.base_out(cfg, si, seed=seed)
+    w = inputs.topk_weights(cfg, seed)
+    return inp, st, sin, (srt, eid, npp), s, base, w
+
+
+FUSED = [
+    _small(configs.C0, name="fused_f32"),
+    _small(SMALL_BF16, name="fused_bf16"),
+]
+
+
+@pytest.mark.parametrize("cfg", FUSED, ids=[c.name for c in FUSED])
+def test_fused_combine_one_unit_slot_equals_expand(oracle_lib, cfg):
+    # topk 1 with weight 1: each token's y is its pair's expanded row, rounded once from the
+    # same double sum as the (pinned) expand.
+    cfg = _small(cfg, name=cfg.name + "_k1", topk=1)
+    inp, st, sin, (srt, eid, npp), s, base, _ = _down_case(oracle_lib, cfg, seed=6)
+    inp.scale[:] = np.linspace(0.5, 2.0, cfg.S, dtype=np.float32)
+    w = np.ones((cfg.M, 1), np.float32)
+    y = oracle_lib.lora_expand_combine(np.nan_to_num(s), sin.B, inp.scale, inp.topk_ids,
+                                       inp.lora_ids, w, cfg.E, cfg.S, base)
+    out = oracle_lib.lora_expand(s, 1, sin.B, inp.scale, cfg.E, srt, eid, npp, cfg.numel,
+                                 cfg.block_m, base.copy())
+    local = _local(inp.topk_ids, cfg.E).reshape(-1)
+    assert np.array_equal(y[local], out[local])
+    assert np.all(pins.to_f64(y[~local]) == 0)
+
+
+@pytest.mark.parametrize("cfg", FUSED, ids=[c.name for c in FUSED])
+def test_fused_combine_equals_combine_of_expanded_rows(oracle_lib, cfg):
+    # The fused form is the combine of the expanded rows taken before their rounding: in
+    # f32 the two differ by the rows' float rounding only; in bf16 by at most one
+    # rounding of each row (2^-9 relative) plus the final one.
+    inp, st, sin, (srt, eid, npp), s, base, w = _down_case(oracle_lib, cfg, seed=8)
+    inp.scale[:] = np.linspace(0.5, 2.0, cfg.S, dtype=np.float32)
+    y = oracle_lib.lora_expand_combine(np.nan_to_num(s), sin.B, inp.scale, inp.topk_ids,
+                                       inp.lora_ids, w, cfg.E, cfg.S, base)
+    rows = oracle_lib.lora_expand(s, 1, sin.B, inp.scale, cfg.E, srt, eid, npp, cfg.numel,
+                                  cfg.block_m, base.copy())
+    y2 = oracle_lib.moe_combine(rows, inp.topk_ids, w, cfg.E)
+    a, b = pins.to_f64(y), pins.to_f64(y2)
+    wabs = np.abs(w).astype(np.float64)
+    mag = np.matmul(wabs[:, None, :], np.abs(pins.to_f64(rows)).reshape(cfg.M, cfg.topk, -1))[:, 0]
+    tol = (2.0 ** -8 if cfg.dtype == "bf16" else 2.0 ** -22) * (mag + np.abs(a))
+    assert np.all(np.abs(a - b) <= tol + 1e-30)
+
+
+@pytest.mark.parametrize("cfg", FUSED, ids=[c.name for c in FUSED])
+def test_fused_combine_without_adapters_is_the_base_combine(oracle_lib, cfg):
+    # No token has an adapter: no delta anywhere, so the fused form is the combine of the
+    # base rows, term for term.
+    inp, st, sin, _, s, base, w = _down_case(oracle_lib, cfg, seed=9)
+    none = np.full(cfg.M, -1, np.int32)
+    y = oracle_lib.lora_expand_combine(np.full_like(s, np.nan), sin.B, inp.scale,
+                                       inp.topk_ids, none, w, cfg.E, cfg.S, base)
+    assert np.array_equal(y, oracle_lib.moe_combine(base, inp.topk_ids, w, cfg.E))
+
+
+def test_fused_combine_ranked_equals_full_rank_on_zeroed_weights(oracle_lib):
+    cfg = _small(SMALL_BF16, name="fused_ranked", slot_ranks=(8, 3, 0))
+    inp, st, sin, _, s, base, w = _down_case(oracle_lib, cfg, seed=10)
+    assert np.isnan(pins.bf16_bits_to_f64(sin.B)).any()
+    y = oracle_lib.lora_expand_combine(np.nan_to_num(s), sin.B, inp.scale, inp.topk_ids,
+                                       inp.lora_ids, w, cfg.E, cfg.S, base,
+                                       slot_ranks=inp.slot_ranks)
+    z = _zeroed_past_rank(inp)
+    y0 = oracle_lib.lora_expand_combine(np.nan_to_num(s), z.stages[-1].B, inp.scale,
+                                        inp.topk_ids, inp.lora_ids, w, cfg.E, cfg.S, base)
+    assert np.array_equal(y, y0)

@@ -21,6 +21,13 @@ Recipe (one numpy PCG64 stream per (config, seed), drawn in this fixed order):
    projection's input; the activation that really produces it lies outside the path).
 7. For each stage in order: A [V, R, K] then B [V, N, R/slices], both N(0, w_sigma).
 
+Outside that stream (each from its own PCG64 stream keyed by (seed, tag), so the layer's
+draws above never move):
+* base_out: nonzero starting rows for an expand's output, N(0, 1);
+* topk_weights [M, topk] float32: the router's combine weights, a softmax over `topk`
+  standard-normal logits per token (positive, summing to 1 per token, as a renormalised
+  top-k softmax router gives).
+
 Normals are drawn in float32 (numpy's standard_normal), scaled in float32, and for bf16
 configs rounded to bfloat16 with round-to-nearest-even; bf16 arrays are kept as their
 uint16 bit patterns. Weights are drawn in slabs of virtual experts so the float32
@@ -161,3 +168,11 @@ def base_out(cfg: LayerConfig, stage_index: int, seed: int) -> np.ndarray:
     st = cfg.stages[stage_index]
     rng = np.random.default_rng([seed, 1000 + stage_index])
     return _normals(rng, (cfg.M * cfg.topk, st.N), 1.0, cfg.dtype)
+
+
+def topk_weights(cfg: LayerConfig, seed: int) -> np.ndarray:
+    """Router combine weights [M, topk] float32 from their own stream (seed, 2000)."""
+    rng = np.random.default_rng([seed, 2000])
+    z = rng.standard_normal((cfg.M, cfg.topk), dtype=np.float32)
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    return np.ascontiguousarray(e / e.sum(axis=1, keepdims=True), dtype=np.float32)
