@@ -103,6 +103,22 @@ def expand_bytes(cfg, st, stats):
     return stats["D"] * st.N * st.r * esz + P * st.R * 4 + 2 * P * st.N * esz + idx
 
 
+def combine_bytes(cfg, st, n_local):
+    """Algorithmic bytes of one combine launch: the rows of the pairs with a local expert
+    read once, the per-token output written, and the ids and weights."""
+    esz = 2 if cfg.dtype == "bf16" else 4
+    return n_local * st.N * esz + cfg.M * st.N * esz + cfg.numel * 8
+
+
+def fused_combine_bytes(cfg, st, stats, n_local):
+    """Algorithmic bytes of one fused down expand + combine: B of every touched virtual
+    expert, the fp32 s rows, the base rows of the local pairs, the per-token output, and
+    the ids, slots and weights. The per-pair rows are neither read back nor written."""
+    esz = 2 if cfg.dtype == "bf16" else 4
+    return (stats["D"] * st.N * st.r * esz + stats["P"] * st.R * 4 + n_local * st.N * esz
+            + cfg.M * st.N * esz + cfg.numel * 8 + cfg.M * 4)
+
+
 def kernel_name(cfg, st, kind):
     """The kernel instantiations libmol launches for this stage, as a profiler names them.
     Shrink: rows per work item start at 4 and double while two such items' A rows fit
@@ -209,7 +225,8 @@ def main():
     for l in range(L):
         inp = inputs.generate(cfg, seed=l)
         base = [inputs.base_out(cfg, si, seed=l) for si in range(len(cfg.stages))]
-        layers.append(DeviceLayer(inp, device=dev, outs=base))
+        layers.append(DeviceLayer(inp, device=dev, outs=base,
+                                  topk_weights=inputs.topk_weights(cfg, l)))
         host_inputs.append(inp)
     torch.cuda.synchronize()
 
@@ -289,6 +306,13 @@ def main():
     for si in range(nst):
         launches.append(("shrink", si, lambda dl, si=si: dl.shrink(si)))
         launches.append(("expand", si, lambda dl, si=si: dl.expand(si)))
+    # the step after the path (reported beside it, not part of the layer time): the combine
+    # of the down stage's rows, and the down expand fused with the combine
+    # (the fused form only at decode sizes: it reads B_v per pair, once per token)
+    launches.append(("combine", nst - 1, lambda dl: dl.combine()))
+    fused_timed = cfg.M <= 1024
+    if fused_timed:
+        launches.append(("expand_combine", nst - 1, lambda dl: dl.expand_combine()))
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             for _ in launches] for _ in range(rounds)]
     spacer_ms = 0.0
@@ -316,6 +340,8 @@ def main():
     align_us = per_launch_us(0)
     kernels = []
     for j, (kind, si, _) in enumerate(launches[1:], start=1):
+        if kind not in ("shrink", "expand"):
+            continue
         st = cfg.stages[si]
         fn = shrink_bytes if kind == "shrink" else expand_bytes
         kernels.append({"label": f"{kind} {st.name}", "kernel": kernel_name(cfg, st, kind),
@@ -380,6 +406,27 @@ def main():
             "bytes_per_launch": dom["bytes"],
             "us_per_launch": dom["us"],
         },
+    }
+    down = cfg.stages[-1]
+    n_local = [int(((h.topk_ids >= 0) & (h.topk_ids < cfg.E)).sum()) for h in host_inputs]
+    cb = float(np.mean([combine_bytes(cfg, down, n) for n in n_local]))
+    fb = float(np.mean([fused_combine_bytes(cfg, down, st_, n)
+                        for st_, n in zip(stats, n_local)]))
+    comb_us = per_launch_us(2 * nst + 1)
+    fused_us = per_launch_us(2 * nst + 2) if fused_timed else None
+    down_expand_us = per_launch_us(2 * nst)
+    result["combine"] = {
+        "what": "router-weighted sum of each token's down-stage rows (not part of us_per_layer)",
+        "combine_kernel": "combine_kernel<%s>" % ("true" if cfg.dtype == "bf16" else "false"),
+        "combine_us": comb_us,
+        "combine_GB/s": cb / (comb_us * 1e-6) / 1e9,
+        "down_expand_then_combine_us": down_expand_us + comb_us,
+        "fused_kernel": "expand_combine_kernel<%s, %d>" % (
+            "true" if cfg.dtype == "bf16" else "false",
+            down.r * (2 if cfg.dtype == "bf16" else 4) // 16),
+        "fused_expand_combine_us": fused_us,
+        "fused_GB/s": fb / (fused_us * 1e-6) / 1e9 if fused_timed else None,
+        "fused_hbm_frac": fb / (fused_us * 1e-6) / 1e9 / HBM_PEAK_GBS if fused_timed else None,
     }
     if args.calibrate_copy:
         result["copy_calibration"] = copy_calibration(torch)

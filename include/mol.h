@@ -8,7 +8,9 @@
  *               blocks (mol_align_block_size);
  *   3. delta  - per stage, shrink s = x A_v^T (hidden -> rank) and expand
  *               out += scale * s B_v^T (rank -> N) over the aligned blocks
- *               (mol_lora_shrink + mol_lora_expand, or fused: mol_lora_delta).
+ *               (mol_lora_shrink + mol_lora_expand, or fused: mol_lora_delta);
+ *   4. combine - per token, the router-weighted sum of its down-stage rows
+ *               (mol_moe_combine, or fused with the down expand: mol_lora_expand_combine).
  * Sources: the sglang virtual-experts kernels as summarised on the PR 24171 page
  * (remap keeping negative sentinels, sentinel bucket, -1 blocks skipped), the PR 24262
  * page (align as histogram -> prefix sum -> expert ids -> scatter, no host sync, the
@@ -69,7 +71,7 @@ enum { MOL_F32 = 0, MOL_BF16 = 1 };
 /* (host) Static description of a status code. Never NULL. */
 MOL_API const char *mol_status_string(mol_status status);
 
-/* (host) ABI version of this header, 2 (2 added the per-slot ranks). */
+/* (host) ABI version of this header, 3 (2 added the per-slot ranks, 3 the combine). */
 MOL_API int32_t mol_abi_version(void);
 
 /* ---------------------------------------------------------------------------------
@@ -205,6 +207,58 @@ MOL_API mol_status mol_lora_delta(int32_t dtype, const void *xin, int64_t ld_x,
                                   int32_t numel, int32_t num_virtual, int32_t block_m,
                                   void *out, int64_t ld_out, void *workspace,
                                   size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * The combine after the down projection. The pages stop at the per-pair rows the down
+ * stage's delta is added into (the layer's grouped-GEMM launches counted on the MindLab
+ * sglang PR 24 page end with the down expand); the next step of an MoE layer sums each
+ * token's pair rows with its router weights. A pair whose base id is outside [0, E) has no
+ * local expert (a negative id is an expert-parallel sentinel: the expert lives on another
+ * GPU) and contributes nothing; its row is never read.
+ *
+ * mol_moe_combine -
+ *   y[m, n] = round( sum_{k ascending, 0 <= topk_ids[m, k] < E} w[m, k] * rows[m*topk + k, n] )
+ * summed in fp32 and rounded once (bf16: to nearest even).
+ *   rows          [M*topk, ld_rows] pair rows (dtype), e.g. the down stage's out
+ *   topk_ids      int32 [M, topk] base expert ids
+ *   topk_weights  float32 [M, topk] router weights
+ *   y             [M, ld_y] out (dtype); every element of [M, N] is written
+ * Requires N, ld_rows and ld_y multiples of 16 bytes' worth of elements (8 bf16, 4 fp32)
+ * and rows, y 16-byte aligned (MOL_E_ALIGN). M = 0 is a no-op.
+ * ------------------------------------------------------------------------------- */
+MOL_API mol_status mol_moe_combine(int32_t dtype, const void *rows, int64_t ld_rows,
+                                   const int32_t *topk_ids, const float *topk_weights,
+                                   int32_t M, int32_t topk, int32_t num_experts, int32_t N,
+                                   void *y, int64_t ld_y, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * mol_lora_expand_combine - the down stage's expand (one slice) fused with the combine;
+ * the per-pair rows are never written:
+ *   y[m, n] = round( sum_{k, 0 <= t < E} w[m, k] * (base[p, n] + d_p[n]) ),  p = m*topk + k,
+ *   d_p[n]  = slot_scale[l] * sum_{j < rl} B[v, n, j] * s[p, j]
+ * for a pair whose token has slot l in [0, S) (virtual expert v = t + l*E, slot rank rl >
+ * 0); otherwise d_p = 0. Summed in fp32, rounded once. It reads each pair's B_v columns,
+ * which at decode (almost every pair its own virtual expert) are the same bytes the aligned
+ * expand reads; with many tokens per virtual expert (prefill) mol_lora_expand followed by
+ * mol_moe_combine reads far fewer.
+ *   s             float32 [M*topk, R] from mol_lora_shrink of the down stage, 16-byte
+ *                 aligned; rows of pairs without a delta are not read
+ *   B             [E*S, N, R] (dtype), 16-byte aligned
+ *   slot_scale    float32 [S];  slot_ranks  int32 [S] or NULL (clamped to [0, R])
+ *   lora_ids      int32 [M] LoRA slot per token (-1: no adapter, base row only)
+ *   base          [M*topk, ld_base] the pairs' base rows (read only)
+ *   y             [M, ld_y] out
+ * Requires R * elem a multiple of 16 bytes with R / (16 / elem) a power of two up to 16
+ * (bf16 ranks 8..128, fp32 ranks 4..64; else MOL_E_LIMIT), E*S + 1 <= MOL_MAX_BUCKETS.
+ * ------------------------------------------------------------------------------- */
+MOL_API mol_status mol_lora_expand_combine(int32_t dtype, const float *s, int32_t R,
+                                           const void *B, int32_t N, const float *slot_scale,
+                                           const int32_t *slot_ranks, const int32_t *topk_ids,
+                                           const int32_t *lora_ids,
+                                           const float *topk_weights, int32_t M, int32_t topk,
+                                           int32_t num_experts, int32_t num_slots,
+                                           const void *base, int64_t ld_base, void *y,
+                                           int64_t ld_y, void *stream);
 
 #ifdef __cplusplus
 }

@@ -39,7 +39,7 @@ def test_only_mol_symbols_exported():
 
 def test_version_and_status_strings():
     L = mb.lib()
-    assert L.mol_abi_version() == 2
+    assert L.mol_abi_version() == 3
     for code in range(7):
         assert mb.status_string(code)
     assert mb.status_string(99) == "unknown status"
@@ -148,3 +148,43 @@ def test_shrink_expand_delta_reject_before_launch():
 def test_library_is_built_for_gfx950():
     from virtual_expert_routed_amd import build
     assert any("gfx950" in ln for ln in build.code_objects(mb.LIB_PATH))
+
+
+def test_combine_rejects_before_launch():
+    L = mb.lib()
+    # combine: dtype, sizes, null pointers, 16-byte rows, misaligned base
+    assert L.mol_moe_combine(5, FAKE, 64, FAKE, FAKE, 4, 2, 8, 64, FAKE, 64,
+                             None) == mb.MOL_E_DTYPE
+    assert L.mol_moe_combine(mb.MOL_BF16, FAKE, 64, FAKE, FAKE, 4, 0, 8, 64, FAKE, 64,
+                             None) == mb.MOL_E_ARG                              # topk 0
+    assert L.mol_moe_combine(mb.MOL_BF16, FAKE, 32, FAKE, FAKE, 4, 2, 8, 64, FAKE, 64,
+                             None) == mb.MOL_E_ARG                              # ld_rows < N
+    assert L.mol_moe_combine(mb.MOL_BF16, None, 64, FAKE, FAKE, 4, 2, 8, 64, FAKE, 64,
+                             None) == mb.MOL_E_ARG
+    assert L.mol_moe_combine(mb.MOL_BF16, FAKE, 60, FAKE, FAKE, 4, 2, 8, 60, FAKE, 60,
+                             None) == mb.MOL_E_ALIGN                            # N % 8
+    assert L.mol_moe_combine(mb.MOL_F32, ctypes.c_void_p(0x1008), 64, FAKE, FAKE, 4, 2, 8, 64,
+                             FAKE, 64, None) == mb.MOL_E_ALIGN
+    assert L.mol_moe_combine(mb.MOL_BF16, None, 64, None, None, 0, 2, 8, 64, None, 64,
+                             None) == mb.MOL_OK                                 # M = 0
+    # fused expand + combine: rank not built, rank bytes, bucket ceiling, alignment
+    args = dict(s=FAKE, R=32, B=FAKE, N=64, sc=FAKE, rk=None, t=FAKE, l=FAKE, w=FAKE, M=4,
+                k=2, E=8, S=2, base=FAKE, ldb=64, y=FAKE, ldy=64)
+
+    def fused(dtype=mb.MOL_BF16, **kw):
+        a = dict(args, **kw)
+        return L.mol_lora_expand_combine(dtype, a["s"], a["R"], a["B"], a["N"], a["sc"],
+                                         a["rk"], a["t"], a["l"], a["w"], a["M"], a["k"],
+                                         a["E"], a["S"], a["base"], a["ldb"], a["y"],
+                                         a["ldy"], None)
+
+    assert fused(dtype=9) == mb.MOL_E_DTYPE
+    assert fused(R=24) == mb.MOL_E_LIMIT            # 3 vectors of 8: not a power of two
+    assert fused(R=256) == mb.MOL_E_LIMIT           # past 16 vectors
+    assert fused(R=12) == mb.MOL_E_ALIGN            # 24 bytes
+    assert fused(dtype=mb.MOL_F32, R=128) == mb.MOL_E_LIMIT
+    assert fused(E=4096, S=2) == mb.MOL_E_LIMIT     # 8193 buckets
+    assert fused(l=None) == mb.MOL_E_ARG
+    assert fused(ldb=32) == mb.MOL_E_ARG
+    assert fused(s=ctypes.c_void_p(0x1008)) == mb.MOL_E_ALIGN
+    assert fused(M=0, s=None, B=None, t=None, l=None, w=None, base=None, y=None) == mb.MOL_OK

@@ -254,6 +254,30 @@ def test_edge_cases(cfg):
     torch.cuda.synchronize()
 
 
+# Batch sizes at the align kernels' selection bounds (one wave per workgroup up to 256
+# pairs; 16-wave workgroups up to 4096; three kernels above), each with small and large
+# virtual expert counts, out-of-range ids and no-adapter tokens.
+ALIGN_BOUNDS = [(M, k, E, S, bm) for (M, k) in ((1, 1), (63, 1), (16, 4), (65, 1), (32, 4),
+                                                (255, 1), (32, 8), (257, 1), (1024, 4),
+                                                (4097, 1))
+                for (E, S, bm) in ((7, 1, 16), (128, 8, 64), (4095, 2, 48))]
+
+
+@pytest.mark.parametrize("M,k,E,S,bm", ALIGN_BOUNDS)
+def test_align_sizes_at_kernel_bounds(M, k, E, S, bm):
+    announce(f"[align bounds] M={M} topk={k} E={E} S={S} BM={bm}")
+    rng = np.random.default_rng(M * 7 + k * 131 + E + S + bm)
+    ids = rng.integers(-2, E + 2, size=(M, k)).astype(np.int32)
+    lora = rng.integers(-1, S + 1, size=M).astype(np.int32)
+    srt, eid, npp = oracle.align_block_size(ids, lora, E, S, bm)
+    s2, e2, n2 = mb.mol_align_block_size(torch.from_numpy(ids).cuda(),
+                                         torch.from_numpy(lora).cuda(), E, S, bm)
+    n2 = int(n2.item())
+    assert n2 == npp
+    assert np.array_equal(s2[:n2].cpu().numpy(), srt)
+    assert np.array_equal(e2[: n2 // bm].cpu().numpy(), eid)
+
+
 def test_empty_batch():
     cfg = _edge_cfg(name="empty", M=0, sentinel_count=0, nolora_count=0)
     inp = inputs.generate(cfg, 0)

@@ -36,6 +36,9 @@ SIGNATURES = {
     "mol_delta_workspace_bytes": (_I64, [_I32, _I32, _I32, _I32]),
     "mol_lora_delta": (_I32, [_I32, _P, _I64, _I32, _P, _I32, _I32, _I32, _P, _I32, _P, _P,
                               _I32, _P, _P, _P, _I32, _I32, _I32, _P, _I64, _P, _SZ, _P]),
+    "mol_moe_combine": (_I32, [_I32, _P, _I64, _P, _P, _I32, _I32, _I32, _I32, _P, _I64, _P]),
+    "mol_lora_expand_combine": (_I32, [_I32, _P, _I32, _P, _I32, _P, _P, _P, _P, _P, _I32,
+                                       _I32, _I32, _I32, _P, _I64, _P, _I64, _P]),
 }
 
 
@@ -233,3 +236,46 @@ def mol_lora_delta(xin, row_div: int, A, slices: int, B, slot_scale, num_experts
         _ptr(num_post_padded), numel, num_virtual, block_m, _ptr(out), out.stride(0),
         _ptr(workspace), workspace.numel(), _stream(A)))
     return out
+
+
+def mol_moe_combine(rows, topk_ids, topk_weights, num_experts: int, y=None):
+    """y [M, N] = per token the router-weighted sum of its pair rows [M*topk, N]."""
+    _need(rows, "rows", contiguous=False)
+    _need(topk_ids, "topk_ids", torch.int32)
+    _need(topk_weights, "topk_weights", torch.float32)
+    if rows.stride(1) != 1:
+        raise ValueError("rows must have contiguous rows")
+    M, k = topk_ids.shape
+    N = rows.shape[1]
+    if y is None:
+        y = torch.empty((M, N), dtype=rows.dtype, device=rows.device)
+    _need(y, "y", rows.dtype, contiguous=False)
+    _check("mol_moe_combine", lib().mol_moe_combine(
+        _dtype_code(rows), _ptr(rows), rows.stride(0), _ptr(topk_ids), _ptr(topk_weights), M,
+        k, num_experts, N, _ptr(y), y.stride(0), _stream(rows)))
+    return y
+
+
+def mol_lora_expand_combine(s, B, slot_scale, topk_ids, lora_ids, topk_weights,
+                            num_experts: int, num_slots: int, base, y=None, slot_ranks=None):
+    """The down stage's expand fused with the combine: y [M, N] from s [M*topk, R], B
+    [E*S, N, R] and the pairs' base rows [M*topk, N]; the rows are not written."""
+    _need(B, "B")
+    _need(s, "s", torch.float32)
+    _need(slot_scale, "slot_scale", torch.float32)
+    _need(topk_ids, "topk_ids", torch.int32)
+    _need(lora_ids, "lora_ids", torch.int32)
+    _need(topk_weights, "topk_weights", torch.float32)
+    _need(base, "base", B.dtype, contiguous=False)
+    if base.stride(1) != 1:
+        raise ValueError("base must have contiguous rows")
+    V, N, R = B.shape
+    M, k = topk_ids.shape
+    if y is None:
+        y = torch.empty((M, N), dtype=B.dtype, device=B.device)
+    _need(y, "y", B.dtype, contiguous=False)
+    _check("mol_lora_expand_combine", lib().mol_lora_expand_combine(
+        _dtype_code(B), _ptr(s), R, _ptr(B), N, _ptr(slot_scale), _ranks(slot_ranks),
+        _ptr(topk_ids), _ptr(lora_ids), _ptr(topk_weights), M, k, num_experts, num_slots,
+        _ptr(base), base.stride(0), _ptr(y), y.stride(0), _stream(B)))
+    return y

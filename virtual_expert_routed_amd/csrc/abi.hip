@@ -145,7 +145,7 @@ MOL_API const char* mol_status_string(mol_status status) {
   }
 }
 
-MOL_API int32_t mol_abi_version(void) { return 2; }
+MOL_API int32_t mol_abi_version(void) { return 3; }
 
 MOL_API mol_status mol_virtual_topk(const int32_t* topk_ids, const int32_t* lora_ids,
                                     int32_t M, int32_t topk, int32_t num_experts,
@@ -396,6 +396,87 @@ MOL_API mol_status mol_lora_delta(int32_t dtype, const void* xin, int64_t ld_x,
   const hipError_t err = shrink_all(a, bf16, rpi, grid_s, mm_s, st);
   if (err != hipSuccess) return MOL_E_HIP;
   return hip_status(expand_all(a, bf16, grid_e, mm_e, st));
+}
+
+// ---- combine -----------------------------------------------------------------------
+
+MOL_API mol_status mol_moe_combine(int32_t dtype, const void* rows, int64_t ld_rows,
+                                   const int32_t* topk_ids, const float* topk_weights,
+                                   int32_t M, int32_t topk, int32_t num_experts, int32_t N,
+                                   void* y, int64_t ld_y, void* stream) {
+  if (dtype != MOL_F32 && dtype != MOL_BF16) return MOL_E_DTYPE;
+  if (M < 0 || topk < 1 || num_experts < 1 || N < 1 || ld_rows < N || ld_y < N)
+    return MOL_E_ARG;
+  if (M > 0 && (!rows || !topk_ids || !topk_weights || !y)) return MOL_E_ARG;
+  const bool bf16 = dtype == MOL_BF16;
+  const int ve = bf16 ? 8 : 4;  // elements of one 16-byte vector
+  if (N % ve || ld_rows % ve || ld_y % ve) return MOL_E_ALIGN;
+  if (M > 0 && (!aligned16(rows) || !aligned16(y))) return MOL_E_ALIGN;
+  if ((int64_t)M * topk > kI32Max) return MOL_E_LIMIT;
+  const int64_t grid = (int64_t)M * cdiv64(N, 64 * ve);
+  if (grid > kI32Max) return MOL_E_LIMIT;
+  if (M == 0) return MOL_OK;
+  mol::CombineArgs a{};
+  a.rows = rows;
+  a.ld_rows = ld_rows;
+  a.topk_ids = topk_ids;
+  a.weights = topk_weights;
+  a.M = M;
+  a.topk = topk;
+  a.E = num_experts;
+  a.N = N;
+  a.y = y;
+  a.ld_y = ld_y;
+  return hip_status(mol::launch_combine(a, bf16, (hipStream_t)stream));
+}
+
+MOL_API mol_status mol_lora_expand_combine(int32_t dtype, const float* s, int32_t R,
+                                           const void* B, int32_t N, const float* slot_scale,
+                                           const int32_t* slot_ranks, const int32_t* topk_ids,
+                                           const int32_t* lora_ids,
+                                           const float* topk_weights, int32_t M, int32_t topk,
+                                           int32_t num_experts, int32_t num_slots,
+                                           const void* base, int64_t ld_base, void* y,
+                                           int64_t ld_y, void* stream) {
+  if (dtype != MOL_F32 && dtype != MOL_BF16) return MOL_E_DTYPE;
+  if (M < 0 || topk < 1 || num_experts < 1 || num_slots < 1 || N < 1 || R < 1 ||
+      ld_base < N || ld_y < N)
+    return MOL_E_ARG;
+  if (M > 0 && (!s || !B || !slot_scale || !topk_ids || !lora_ids || !topk_weights || !base ||
+                !y))
+    return MOL_E_ARG;
+  const bool bf16 = dtype == MOL_BF16;
+  const int esz = bf16 ? 2 : 4;
+  if (((int64_t)R * esz) % 16) return MOL_E_ALIGN;
+  if (!mol::fused_rank_supported(R, bf16)) return MOL_E_LIMIT;
+  if ((int64_t)num_experts * num_slots + 1 > MOL_MAX_BUCKETS) return MOL_E_LIMIT;
+  if ((int64_t)N * R * esz >= (int64_t(1) << 31)) return MOL_E_LIMIT;  // one expert's B
+  if ((int64_t)M * topk > kI32Max) return MOL_E_LIMIT;
+  if (M > 0 && (!aligned16(s) || !aligned16(B) ||
+                reinterpret_cast<uintptr_t>(base) % esz || reinterpret_cast<uintptr_t>(y) % esz))
+    return MOL_E_ALIGN;
+  const int64_t grid = (int64_t)M * cdiv64(N, 64);
+  if (grid > kI32Max) return MOL_E_LIMIT;
+  if (M == 0) return MOL_OK;
+  mol::CombineArgs a{};
+  a.topk_ids = topk_ids;
+  a.weights = topk_weights;
+  a.lora = lora_ids;
+  a.M = M;
+  a.topk = topk;
+  a.E = num_experts;
+  a.S = num_slots;
+  a.N = N;
+  a.R = R;
+  a.s = s;
+  a.B = B;
+  a.scale = slot_scale;
+  a.ranks = slot_ranks;
+  a.base = base;
+  a.ld_base = ld_base;
+  a.y = y;
+  a.ld_y = ld_y;
+  return hip_status(mol::launch_expand_combine(a, bf16, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -68,6 +68,29 @@ struct DeltaArgs {
                          // kernels and the VALU kernels skip them; 0: VALU kernels only
 };
 
+// The combine after the down projection, and its form fused with the down-stage expand.
+struct CombineArgs {
+  const void* rows;        // combine: [M*topk, N] pair rows, ld_rows apart
+  int64_t ld_rows;
+  const int32_t* topk_ids; // [M, topk] base expert ids; pairs outside [0, E) have no row
+  const float* weights;    // [M, topk] router weights
+  const int32_t* lora;     // fused: [M] LoRA slot per token
+  int32_t M;
+  int32_t topk;
+  int32_t E;
+  int32_t S;
+  int32_t N;
+  int32_t R;               // fused: rank (one slice)
+  const float* s;          // fused: [M*topk, R]
+  const void* B;           // fused: [E*S, N, R]
+  const float* scale;      // fused: [S]
+  const int32_t* ranks;    // fused: [S] per-slot ranks or nullptr
+  const void* base;        // fused: [M*topk, N] base rows, ld_base apart
+  int64_t ld_base;
+  void* y;                 // [M, N], ld_y apart
+  int64_t ld_y;
+};
+
 // host-side launchers (return the launch status)
 hipError_t launch_virtual_topk(const int32_t* topk_ids, const int32_t* lora_ids, int32_t M,
                                int32_t topk, int32_t E, int32_t S, int32_t* out,
@@ -89,5 +112,10 @@ hipError_t launch_expand(const DeltaArgs& a, bool bf16, int grid, hipStream_t st
 int shrink_mfma_row_tile(int32_t R);
 hipError_t launch_shrink_mfma(const DeltaArgs& a, int grid, hipStream_t stream);
 hipError_t launch_expand_mfma(const DeltaArgs& a, int grid, hipStream_t stream);
+// combine: one wave per (token, 64 16-byte vectors of columns)
+hipError_t launch_combine(const CombineArgs& a, bool bf16, hipStream_t stream);
+// fused expand + combine: ranks it is built for (R/8 or R/4 a power of two up to 16)
+bool fused_rank_supported(int32_t R, bool bf16);
+hipError_t launch_expand_combine(const CombineArgs& a, bool bf16, hipStream_t stream);
 
 }  // namespace mol

@@ -21,7 +21,7 @@ def to_device(a: np.ndarray, device, bf16: bool) -> torch.Tensor:
 
 
 class DeviceLayer:
-    def __init__(self, inp: LayerInputs, device="cuda", outs=None):
+    def __init__(self, inp: LayerInputs, device="cuda", outs=None, topk_weights=None):
         cfg = inp.cfg
         self.cfg = cfg
         self.device = torch.device(device)
@@ -56,6 +56,12 @@ class DeviceLayer:
             self.out = [torch.zeros((numel, st.N), dtype=odt, device=dev) for st in cfg.stages]
         else:
             self.out = [to_device(o, dev, bf16) for o in outs]
+        # the combine after the last (down) stage: router weights and per-token output
+        self.topk_weights = self.y = None
+        if topk_weights is not None:
+            self.topk_weights = torch.from_numpy(
+                np.ascontiguousarray(topk_weights, dtype=np.float32)).to(dev)
+            self.y = torch.zeros((cfg.M, cfg.stages[-1].N), dtype=odt, device=dev)
 
     # ---------------------------------------------------------------------------- steps
     def align(self):
@@ -91,6 +97,26 @@ class DeviceLayer:
                           self.scale, c.E, *self.routing(), c.numel, c.V, c.block_m,
                           self.out[si], self.delta_ws[si], slot_ranks=self.slot_ranks)
         return self.out[si]
+
+    def combine(self, rows=None):
+        """y = per token the router-weighted sum of its rows of the down stage's out."""
+        c = self.cfg
+        rows = self.out[-1] if rows is None else rows
+        return mb.mol_moe_combine(rows, self.topk_ids, self.topk_weights, c.E, y=self.y)
+
+    def expand_combine(self, base=None):
+        """The down stage's expand fused with the combine: y from the down stage's s and
+        the pairs' base rows (default: the down stage's out, which is not written)."""
+        c = self.cfg
+        base = self.out[-1] if base is None else base
+        return mb.mol_lora_expand_combine(self.s[-1], self.B[-1], self.scale, self.topk_ids,
+                                          self.lora_ids, self.topk_weights, c.E, c.S, base,
+                                          y=self.y, slot_ranks=self.slot_ranks)
+
+    def y_host(self) -> np.ndarray:
+        if self.bf16:
+            return self.y.view(torch.int16).cpu().numpy().view(np.uint16)
+        return self.y.cpu().numpy()
 
     def run(self, fused: bool = True):
         """The whole path: align (remap inline), then every stage's shrink + expand."""
