@@ -383,8 +383,25 @@ hipError_t launch_shrink_mfma(const DeltaArgs& a, int grid, hipStream_t stream) 
   return hipGetLastError();
 }
 
+// Slices of s the widest item needs: an item's kExpandCols columns can straddle slice
+// boundaries. Only those columns of s are staged, so LDS is sized by them (at gate_up with
+// slice widths that are multiples of kExpandCols, one slice: half of R), which leaves room
+// for more workgroups per CU.
+int expand_mfma_span(const DeltaArgs& a) {
+  const int width = a.N / a.slices;
+  int span = 1;
+  for (int c0 = 0; c0 < a.N; c0 += kExpandCols) {
+    const int c1 = (c0 + kExpandCols < a.N ? c0 + kExpandCols : a.N) - 1;
+    const int sp = c1 / width - c0 / width + 1;
+    span = sp > span ? sp : span;
+  }
+  return span;
+}
+
 hipError_t launch_expand_mfma(const DeltaArgs& a, int grid, hipStream_t stream) {
-  const size_t lds = (size_t)kRowsPerPass * a.R * sizeof(float);  // s rows of one pass
+  // s rows of one pass, the columns of the slices one item spans
+  const size_t lds =
+      (size_t)kRowsPerPass * (a.R / a.slices) * expand_mfma_span(a) * sizeof(float);
   switch ((a.R / a.slices) / 32) {
     case 1: hipLaunchKernelGGL((expand_mfma_kernel<1>), dim3(grid), dim3(256), lds, stream, a); break;
     case 2: hipLaunchKernelGGL((expand_mfma_kernel<2>), dim3(grid), dim3(256), lds, stream, a); break;
