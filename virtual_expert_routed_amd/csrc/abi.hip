@@ -207,8 +207,10 @@ MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_
   const hipStream_t st = (hipStream_t)stream;
   const int nb = a.V + 1;
   if (numel <= mol::kAlignSmallMax) {
-    // counter rows + scan scratch + per pair a bucket id and a rank (uint16 each)
-    const int64_t fixed = 64 * (int64_t)sizeof(int) + ((numel + 1) & ~1LL) * 2 * 2;
+    // counter rows + bucket starts + scan scratch + per pair a bucket id and a rank
+    // (uint16 each)
+    const int64_t fixed =
+        ((int64_t)nb + 64) * (int64_t)sizeof(int) + ((numel + 1) & ~1LL) * 2 * 2;
     int64_t waves = (device_lds_bytes() - fixed) / ((int64_t)nb * (int64_t)sizeof(int));
     // walkers: one chunk of 64 pairs each for the smallest batches, two chunks each above
     // (more walkers shorten the walk but add counter rows to every bucket's sums)

@@ -120,29 +120,33 @@ __device__ __forceinline__ uint64_t match_key13(int key, bool valid) {
   return peers;
 }
 
-constexpr int kMaxBucketsPerThread = kMaxBuckets / 1024;  // 8
-
 // numel <= 4096: G workgroups of 1024 threads. Every workgroup builds the whole routing in
 // its own LDS (the ids are a few KiB, so the repeated reads hit L2), then writes only
 // its share of the outputs: the pairs p with p % G == g, and the expert ids and padding
 // of the buckets b with b % G == g. No workgroup waits for another.
-// LDS: `waves` counter rows of V+1 ints, 64 ints of scan scratch, then per pair its
-// bucket id and its rank among the earlier pairs of the same bucket in its wave's range
-// (uint16 each).
+// LDS: `waves` counter rows of V+1 ints, the V+1 bucket starts, 64 ints of scan scratch,
+// then per pair its bucket id and its rank among the earlier pairs of the same bucket in
+// its wave's range (uint16 each).
 //   A  every thread: bucket ids of its pairs (ids and slots loaded together) -> LDS;
 //      counter rows zeroed.
 //   B  wave w walks its contiguous range in chunks of 64, in order: ballot-matched peers
 //      give each pair's rank in the chunk, the group leader adds the group to row w and
 //      hands the row's previous value to its peers, so rank_in_range = old + rank.
-//   C  bucket totals, padded exclusive scan, expert ids; row w of bucket b becomes
-//      off_b + (pairs of b in ranges before w).
-//   D  sorted[row[w(p)][b(p)] + rank_in_range(p)] = p for this workgroup's pairs; each
-//      wave writes the padding of this workgroup's non-empty buckets its threads own.
+//   C  thread t owns BPT consecutive buckets. One pass over the rows, four at a time, with
+//      every owned bucket's reads of a round issued together: row w of bucket b becomes
+//      the pairs of b in ranges before w, and b's total stays in a register. After the
+//      padded exclusive scan, start[b] = off_b and the expert ids are written; nothing
+//      is read back from LDS.
+//   D  sorted[start[b(p)] + row[w(p)][b(p)] + rank_in_range(p)] = p for this workgroup's
+//      pairs; each wave writes the padding of this workgroup's non-empty buckets its
+//      threads own.
+template <int BPT>
 __global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a, int waves) {
   extern __shared__ int lds[];
   const int NB = a.V + 1;
   int* table = lds;                                   // [waves][NB]
-  int* sh = lds + waves * NB;                         // scan scratch
+  int* start = lds + waves * NB;                      // [NB] padded bucket starts
+  int* sh = start + NB;                               // scan scratch
   uint16_t* keys = reinterpret_cast<uint16_t*>(sh + 64);
   uint16_t* rel = keys + ((a.numel + 1) & ~1);
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
@@ -195,49 +199,48 @@ __global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a, int wave
   }
   __syncthreads();
 
-  // C: each thread owns a contiguous range of buckets. The counts of a bucket are read
-  // from every row before any is used (rows past `waves` read row 0 and count 0), so
-  // the reads of one bucket issue back to back.
-  const int bpt = (NB + (int)blockDim.x - 1) / (int)blockDim.x;
-  const int b0 = min(NB, tid * bpt), b1 = min(NB, b0 + bpt);
-  int mine = 0;
-  for (int b = b0; b < b1; ++b) {
-    int c = 0;
-    for (int w0 = 0; w0 < waves; w0 += 4) {  // four rows per round, read before use
-      int x[4];
+  // C
+  const int b0 = min(NB, tid * BPT);
+  const int nown = min(NB, b0 + BPT) - b0;  // buckets this thread owns (uniform bound BPT)
+  int run[BPT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = table[min(w0 + i, waves - 1) * NB + b];
+  for (int k = 0; k < BPT; ++k) run[k] = 0;
+  for (int w0 = 0; w0 < waves; w0 += 4) {
+    int x[BPT][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) c += w0 + i < waves ? x[i] : 0;
+    for (int k = 0; k < BPT; ++k) {
+      const int b = min(b0 + k, NB - 1);  // a valid address for buckets not owned
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[k][i] = table[min(w0 + i, waves - 1) * NB + b];
     }
-    mine += bm_round(a, c);
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (k < nown && w0 + i < waves) {
+          table[(w0 + i) * NB + b0 + k] = run[k];
+          run[k] += x[k][i];
+        }
+      }
+    }
   }
+  int mine = 0;
+#pragma unroll
+  for (int k = 0; k < BPT; ++k) mine += bm_round(a, run[k]);  // 0 past the owned buckets
   int total;
   int off = block_excl_scan(mine, sh, &total);
   // padding of this thread's buckets, kept as (first slot, count) per owned bucket
-  int pad_from[kMaxBucketsPerThread], pad_cnt[kMaxBucketsPerThread];
+  int pad_from[BPT], pad_cnt[BPT];
   int bmod = b0 % G;  // b % G for b = b0, b0 + 1, ...
 #pragma unroll
-  for (int k = 0; k < kMaxBucketsPerThread; ++k) {
+  for (int k = 0; k < BPT; ++k) {
     pad_cnt[k] = 0;
     pad_from[k] = 0;
-    const int b = b0 + k;
-    if (b < b1) {
-      int run = off;
-      for (int w0 = 0; w0 < waves; w0 += 4) {
-        int x[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = table[min(w0 + i, waves - 1) * NB + b];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (w0 + i < waves) {
-            table[(w0 + i) * NB + b] = run;
-            run += x[i];
-          }
-        }
-      }
-      const int c = run - off;
+    if (k < nown) {
+      const int b = b0 + k;
+      const int c = run[k];
       const int pc = bm_round(a, c);
+      start[b] = off;
       if (bmod == g) {
         const int eid = (b == a.V) ? -1 : b;
         const int blk0 = bm_div(a, off), nblk = bm_div(a, pc);
@@ -255,11 +258,12 @@ __global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a, int wave
   // D
   for (int p = g + tid * G; p < numel; p += (int)blockDim.x * G) {
     const int w = p / per;
-    a.sorted[table[w * NB + keys[p]] + rel[p]] = p;
+    const int key = keys[p];
+    a.sorted[start[key] + table[w * NB + key] + rel[p]] = p;
   }
   // padding: the wave's lanes fill one padded bucket after another
 #pragma unroll
-  for (int k = 0; k < kMaxBucketsPerThread; ++k) {
+  for (int k = 0; k < BPT; ++k) {
     uint64_t todo = wave_ballot(pad_cnt[k] > 0);
     while (todo) {
       const int src = __builtin_ctzll(todo);
@@ -402,8 +406,17 @@ hipError_t launch_virtual_topk(const int32_t* topk_ids, const int32_t* lora_ids,
 
 hipError_t launch_align_small(const AlignArgs& a, int waves, int groups, size_t lds_bytes,
                               hipStream_t stream) {
-  hipLaunchKernelGGL(align_small_kernel, dim3(groups), dim3(1024), lds_bytes, stream, a,
-                     waves);
+  // buckets per thread, rounded up to a power of two (V + 1 <= 8192 = 8 x 1024)
+  const int bpt = (a.V + 1 + 1023) / 1024;
+  const dim3 grid(groups), block(1024);
+  if (bpt <= 1)
+    hipLaunchKernelGGL(align_small_kernel<1>, grid, block, lds_bytes, stream, a, waves);
+  else if (bpt <= 2)
+    hipLaunchKernelGGL(align_small_kernel<2>, grid, block, lds_bytes, stream, a, waves);
+  else if (bpt <= 4)
+    hipLaunchKernelGGL(align_small_kernel<4>, grid, block, lds_bytes, stream, a, waves);
+  else
+    hipLaunchKernelGGL(align_small_kernel<8>, grid, block, lds_bytes, stream, a, waves);
   return hipGetLastError();
 }
 
