@@ -119,6 +119,35 @@ def fused_combine_bytes(cfg, st, stats, n_local):
             + cfg.M * st.N * esz + cfg.numel * 8 + cfg.M * 4)
 
 
+def shrink_rows_per_item(cfg, st):
+    """Rows of A_v per VALU shrink item: from 4, doubled while two such items' rows fit
+    32 KiB, at most 32."""
+    esz = 2 if cfg.dtype == "bf16" else 4
+    rpi = 4
+    while rpi < 32 and rpi * 2 * st.K * esz <= 32768:
+        rpi *= 2
+    return rpi
+
+
+def grid_report(cfg, max_blocks, stats):
+    """Workgroups each kernel launches (the grid follows the block bound, not padded rows)
+    and how many of them belong to live blocks with a virtual expert, per stage. Where the
+    MFMA kernels run, their grid is listed too (each block goes to one of the two)."""
+    vb = float(np.mean([s["valid_blocks"] for s in stats]))
+    rep = {}
+    for st in cfg.stages:
+        rg = -(-st.R // shrink_rows_per_item(cfg, st))
+        nch = -(-st.N // 256)
+        rep[f"shrink {st.name}"] = {"launched": max_blocks * rg, "live_blocks_items": vb * rg}
+        rep[f"expand {st.name}"] = {"launched": max_blocks * nch, "live_blocks_items": vb * nch}
+        if "mfma" in kernel_name(cfg, st, "shrink"):
+            rows = 128 if st.R > 64 else 64
+            rep[f"shrink {st.name}"]["mfma_launched"] = max_blocks * -(-st.R // rows)
+        if "mfma" in kernel_name(cfg, st, "expand"):
+            rep[f"expand {st.name}"]["mfma_launched"] = max_blocks * nch
+    return rep
+
+
 def kernel_name(cfg, st, kind):
     """The kernel instantiations libmol launches for this stage, as a profiler names them.
     Shrink: rows per work item start at 4 and double while two such items' A rows fit
@@ -132,9 +161,7 @@ def kernel_name(cfg, st, kind):
     mfma = (cfg.dtype == "bf16" and cfg.numel >= 4096 and cfg.numel >= 8 * (cfg.V + 1)
             and cfg.block_m >= 4)
     if kind == "shrink":
-        rpi = 4
-        while rpi < 32 and rpi * 2 * st.K * esz <= 32768:
-            rpi *= 2
+        rpi = shrink_rows_per_item(cfg, st)
         name = f"shrink_kernel<{b}, {256 // rpi}>"
         return name + " + shrink_mfma_kernel" if mfma else name
     name = f"expand_kernel<{b}, {st.r * esz // 16}>"
@@ -289,6 +316,22 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     gpu_elapsed = ev0.elapsed_time(ev1) * 1e-3
+    # spread of the layer time: HIP events around single replays of the rotation graph (or
+    # single eager steps), outside the timed region
+    dist = []
+    nd = max(1, min(64, K // L if graphs is not None else K))
+    for i in range(nd):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        if graphs is not None:
+            graph_all.replay()
+        else:
+            step_body(layers[i % L])
+        e1.record()
+        dist.append((e0, e1))
+    torch.cuda.synchronize()
+    per_layer = np.array([a.elapsed_time(b) * 1e3 / (L if graphs is not None else 1)
+                          for a, b in dist])
     # the layers each step used (the rotation restarts after the full-graph replays)
     step_layers = [i % L for i in range(L * (K // L))] + list(range(K % L)) \
         if graphs is not None else [i % L for i in range(K)]
@@ -382,12 +425,21 @@ def main():
         },
         "us_per_layer": ms_per_step * 1e3,
         "us_per_layer_gpu_events": gpu_elapsed / K * 1e6,
+        "us_per_layer_dist": {
+            "p10": float(np.percentile(per_layer, 10)),
+            "p50": float(np.percentile(per_layer, 50)),
+            "p90": float(np.percentile(per_layer, 90)),
+            "samples": int(per_layer.size),
+            "how": ("HIP events around single replays of the rotation graph, divided by the "
+                    "layers in it" if graphs is not None else "HIP events around single steps"),
+        },
         "align_us": align_us,
         "pairs_per_layer": float(np.mean([s["P"] for s in stats])),
         "touched_virtual_experts": float(np.mean([s["D"] for s in stats])),
         "kernels": [{"label": k["label"], "kernel": k["kernel"], "us": k["us"],
                      "GB/s": k["bytes"] / (k["us"] * 1e-6) / 1e9} for k in kernels],
         "delta_us": delta_us,
+        "grid_workgroups": grid_report(cfg, layers[0].max_blocks, stats),
         "reference_geometry_ctas": {
             f"{kind} {st.name}": reference_ctas(reference_grid_m(cfg), st.R if kind == "shrink"
                                                 else st.N // st.slices)
@@ -445,12 +497,32 @@ def main():
             if time.perf_counter() - t0 >= args.cpu_seconds:
                 break
         el = time.perf_counter() - t0
+        # the same passes on one thread, over a short sample
+        nt = oracle.num_threads()
+        oracle.set_num_threads(1)
+        t1 = time.perf_counter()
+        n1 = 0
+        while n1 < 1 or time.perf_counter() - t1 < min(3.0, args.cpu_seconds / 4):
+            oracle.run_layer(host_inputs[n1 % L])
+            n1 += 1
+        el1 = time.perf_counter() - t1
+        oracle.set_num_threads(nt)
+        cpu_model = ""
+        try:
+            for ln in open("/proc/cpuinfo"):
+                if ln.startswith("model name"):
+                    cpu_model = ln.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
         result["cpu_baseline"] = {
             "value": n_pairs / el, "unit": "pairs/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"{n_layers} whole layer passes of {cfg.name} (layers 0..{L - 1} "
                       f"cycled), fp64 C oracle, {el:.1f} s",
             "us_per_layer": el / n_layers * 1e6,
+            "single_thread_us_per_layer": el1 / n1 * 1e6,
+            "cpu_model": cpu_model,
         }
     print(json.dumps(result), flush=True)
 
