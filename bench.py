@@ -316,6 +316,34 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     gpu_elapsed = ev0.elapsed_time(ev1) * 1e-3
+    # the delta alone (both stages' mol_lora_delta, routing already in place) as graph replays
+    # of the rotation: the fused shrink + expand back to back, as a layer runs them
+    delta_graph_us = None
+    if graphs is not None:
+        for dl in layers:
+            dl.align()
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s2):
+            g_delta = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_delta, stream=s2):
+                for dl in layers:
+                    for si in range(len(cfg.stages)):
+                        dl.delta(si)
+        torch.cuda.current_stream().wait_stream(s2)
+        torch.cuda.synchronize()
+        g_delta.replay()
+        nrep = max(1, K // L)
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        d0.record()
+        for _ in range(nrep):
+            g_delta.replay()
+        d1.record()
+        torch.cuda.synchronize()
+        delta_graph_us = d0.elapsed_time(d1) * 1e3 / (nrep * L)
+        del g_delta
+
     # spread of the layer time: HIP events around single replays of the rotation graph (or
     # single eager steps), outside the timed region
     dist = []
@@ -445,6 +473,9 @@ def main():
                                                 else st.N // st.slices)
             for st in cfg.stages for kind in ("shrink", "expand")},
         "delta_hbm_frac": delta_bytes / (delta_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "delta_graph_us": delta_graph_us,
+        "delta_graph_hbm_frac": (delta_bytes / (delta_graph_us * 1e-6) / 1e9 / HBM_PEAK_GBS
+                                 if delta_graph_us else None),
         "kernel_timing": timing_src,
         "roofline": {
             "kernel": f"{dom['kernel']} ({dom['label']})",
