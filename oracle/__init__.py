@@ -59,6 +59,9 @@ def lib():
         L.oracle_lora_expand_combine.argtypes = [ctypes.c_int, P, I32, P, I32, P, P, P, P, P,
                                                  I64, I32, I32, I32, P, I64, P, I64]
         L.oracle_lora_expand_combine.restype = ctypes.c_int
+        L.oracle_moe_gemm.argtypes = [ctypes.c_int, P, I64, I32, P, I32, I32, P, I64, I32, I32,
+                                      P, I64, P, I32, I32, P, P, P, P, I32]
+        L.oracle_moe_gemm.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -210,6 +213,33 @@ def lora_expand_combine(s, B, scale, topk_ids, lora_ids, topk_weights, E: int, S
     if rc:
         raise ValueError(f"oracle_lora_expand_combine: {rc}")
     return y
+
+
+def moe_gemm(xin, row_div: int, W, topk_ids, E: int, out, s=None, slices: int = 1, B=None,
+             scale=None, lora_ids=None, S: int = 1, slot_ranks=None) -> np.ndarray:
+    """The base grouped GEMM of a stage into `out` [M*topk, N] (rows of pairs without a local
+    expert untouched); with s (float64 [M*topk, R]) and B, the LoRA delta is added before the
+    one rounding."""
+    xin = np.ascontiguousarray(xin)
+    W = np.ascontiguousarray(W)
+    Ew, N, K = W.shape
+    assert Ew == E and out.flags.c_contiguous and out.dtype == W.dtype
+    t = np.ascontiguousarray(topk_ids, dtype=np.int32)
+    M, k = t.shape
+    args = [None, 0, 1, None, None, None, None, 1]
+    if s is not None:
+        s = np.ascontiguousarray(s, dtype=np.float64)
+        B = np.ascontiguousarray(B)
+        assert B.dtype == W.dtype
+        args = [s, s.shape[1], slices, B, np.ascontiguousarray(scale, dtype=np.float32),
+                _ranks(slot_ranks), np.ascontiguousarray(lora_ids, dtype=np.int32), S]
+    rc = lib().oracle_moe_gemm(_dt(W), _ptr(xin), xin.shape[1], row_div, _ptr(W), K, N,
+                               _ptr(t), M, k, E, _ptr(out), out.shape[1], _ptr(args[0]),
+                               args[1], args[2], _ptr(args[3]), _ptr(args[4]), _ptr(args[5]),
+                               _ptr(args[6]), args[7])
+    if rc:
+        raise ValueError(f"oracle_moe_gemm: {rc}")
+    return out
 
 
 def run_layer(inp, outs=None, pair_mask=None):

@@ -27,6 +27,12 @@
  * Per-slot ranks (optional): a slot of rank rl < r uses rank dimensions [0, rl) of each
  * slice; s is 0 past it, and a slot of rank 0 gets no delta.
  *
+ *   base    - the base MoE grouped GEMM of a stage, which the pages run as the base
+ *             fused_moe_kernel launches the LoRA delta is added to: out[p, n] =
+ *             sum_k W[t_p, n, k] * xin[row(p), k] for a pair whose base expert t_p is local
+ *             (0 <= t_p < E), rounded once; with the LoRA delta fused in, out[p, n] = round(base
+ *             + delta) with the delta of the expand above (MindLab sglang PR 24, the PR body's
+ *             count of base and LoRA grouped-GEMM launches per layer).
  *   combine - the step after the down projection, which the pages leave implicit: each
  *             token's output is the router-weighted sum of its top-k pair rows,
  *             y[m, n] = sum_k w[m, k] * rows[m*topk + k, n], over the pairs whose base
@@ -372,6 +378,59 @@ int oracle_lora_expand_combine(int dtype, const double *s, int32_t R, const void
                 acc += (double)topk_weights[p] * row;
             }
             store_rounded(dtype, acc, y, m * ld_y + n);
+        }
+    }
+    return OR_OK;
+}
+
+/* ---- base grouped GEMM, alone or with the LoRA delta in its epilogue ------------------ */
+
+/* For every pair p with a local base expert t = topk_ids[p] (0 <= t < E):
+ *   acc = sum_k W[t][n][k] * xin[(p / row_div) * ld_x + k]              (k ascending)
+ *   if s != NULL and the token's slot l = lora_ids[p / topk] is in [0, S) and its rank
+ *   rl > 0:  acc += scale[l] * sum_{j < rl} B[t + l*E][n][j] * s[p*R + g(n)*r + j]
+ *   out[p][n] = round(acc)   (bf16 RNE from the double, or (float))
+ * with r = R / slices and g(n) = n / (N / slices). W is [E, N, K], B is [E*S, N, r]. Rows of
+ * pairs without a local expert are left untouched. */
+int oracle_moe_gemm(int dtype, const void *xin, int64_t ld_x, int32_t row_div, const void *W,
+                    int32_t K, int32_t N, const int32_t *topk_ids, int64_t M, int32_t topk,
+                    int32_t E, void *out, int64_t ld_out, const double *s, int32_t R,
+                    int32_t slices, const void *B, const float *scale,
+                    const int32_t *slot_ranks, const int32_t *lora_ids, int32_t S) {
+    if ((dtype != OR_F32 && dtype != OR_BF16) || K <= 0 || N <= 0 || M < 0 || topk <= 0 ||
+        E <= 0 || row_div <= 0 || ld_x < K || ld_out < N)
+        return OR_E_ARG;
+    if (s && (R <= 0 || slices <= 0 || R % slices || N % slices || !B || !scale ||
+              !lora_ids || S <= 0))
+        return OR_E_ARG;
+    const int64_t numel = M * topk;
+    const int32_t r = s ? R / slices : 0;
+    const int32_t width = s ? N / slices : N;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t p = 0; p < numel; ++p) {
+        const int32_t t = topk_ids[p];
+        if (t < 0 || t >= E) continue;  /* no local expert: row untouched */
+        const int64_t xrow = (p / row_div) * ld_x;
+        int32_t v = -1, rl = 0, l = -1;
+        if (s) {
+            l = lora_ids[p / topk];
+            v = virtual_id(t, l, E, S);
+            rl = v >= 0 ? slot_rank(slot_ranks, l, r) : 0;
+        }
+        for (int32_t n = 0; n < N; ++n) {
+            const int64_t wrow = ((int64_t)t * N + n) * K;
+            double acc = 0.0;
+            for (int32_t k = 0; k < K; ++k)
+                acc += load_elem(W, wrow + k, dtype) * load_elem(xin, xrow + k, dtype);
+            if (rl > 0) {
+                const int32_t g = n / width;
+                const int64_t brow = ((int64_t)v * N + n) * r;
+                double d = 0.0;
+                for (int32_t j = 0; j < rl; ++j)
+                    d += load_elem(B, brow + j, dtype) * s[p * R + (int64_t)g * r + j];
+                acc += (double)scale[l] * d;
+            }
+            store_rounded(dtype, acc, out, p * ld_out + n);
         }
     }
     return OR_OK;

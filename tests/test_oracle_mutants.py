@@ -21,11 +21,14 @@ MUTANTS = [
      "total += (count[b] / BM + 1) * BM;"),
     ("align_sentinel_tag", "(b == V) ? -1 : (int32_t)b", "(int32_t)b"),
     ("align_pad_value", "sorted_ids[i] = (int32_t)numel;", "sorted_ids[i] = -1;"),
-    ("shrink_drops_last_k", "for (int32_t k = 0; k < K; ++k)", "for (int32_t k = 0; k < K - 1; ++k)"),
+    ("shrink_drops_last_k", "for (int32_t k = 0; k < K; ++k)\n                    acc += load_elem(A",
+     "for (int32_t k = 0; k < K - 1; ++k)\n                    acc += load_elem(A"),
     ("shrink_transposed_A", "load_elem(A, arow + k, dtype)",
      "load_elem(A, (int64_t)e * R * K + (int64_t)k * R + i, dtype)"),
-    ("shrink_row_of_pair", "(p / row_div) * ld_x", "(p % row_div) * ld_x"),
-    ("expand_slice", "const int32_t g = n / width;", "const int32_t g = 0;"),
+    ("shrink_row_of_pair", "(p / row_div) * ld_x;\n            for (int32_t i = 0",
+     "(p % row_div) * ld_x;\n            for (int32_t i = 0"),
+    ("expand_slice", "const int32_t g = n / width;\n                const int64_t brow = ((int64_t)e",
+     "const int32_t g = 0;\n                const int64_t brow = ((int64_t)e"),
     ("expand_scale_slot", "(double)scale[e / E]", "(double)scale[0]"),
     ("expand_truncates", "nearbyint(ldexp(a, -q))", "trunc(ldexp(a, -q))"),
     ("expand_sign", "acc += load_elem(B, brow + jj, dtype) * s[",
@@ -44,6 +47,13 @@ MUTANTS = [
     ("fused_weight_dropped", "acc += (double)topk_weights[p] * row;", "acc += row;"),
     ("fused_rank_ignored", "for (int32_t j = 0; j < rl; ++j) d +=",
      "for (int32_t j = 0; j < R; ++j) d +="),
+    ("gemm_slot_ignored", "v = virtual_id(t, l, E, S);\n            rl",
+     "v = t;\n            rl"),
+    ("gemm_scale_dropped", "acc += (double)scale[l] * d;", "acc += d;"),
+    ("gemm_row_of_pair", "const int64_t xrow = (p / row_div) * ld_x;\n        int32_t v = -1",
+     "const int64_t xrow = (p % row_div) * ld_x;\n        int32_t v = -1"),
+    ("gemm_rank_ignored", "rl = v >= 0 ? slot_rank(slot_ranks, l, r) : 0;",
+     "rl = v >= 0 ? r : 0;"),
     ("fused_no_adapter_drops_base",
      "double row = load_elem(base, p * ld_base + n, dtype);\n"
      "                const int32_t v = virtual_id(t, lora_ids[m], E, S);",
@@ -85,6 +95,9 @@ def _battery(lib):
             lib, c) for c in P.FUSED]),
         ("fused_ranked", lambda: P.test_fused_combine_ranked_equals_full_rank_on_zeroed_weights(
             lib)),
+        ("gemm_matvec", lambda: [P.test_base_gemm_is_a_per_pair_matvec(lib, c)
+                                 for c in P.GEMM[:2]]),
+        ("gemm_fused", lambda: [P.test_fused_gemm_reduces_to_its_parts(lib, c) for c in P.GEMM]),
     ]
     for name, fn in cases:
         try:

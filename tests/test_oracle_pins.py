@@ -498,3 +498,80 @@ def test_fused_combine_ranked_equals_full_rank_on_zeroed_weights(oracle_lib):
     y0 = oracle_lib.lora_expand_combine(np.nan_to_num(s), z.stages[-1].B, inp.scale,
                                         inp.topk_ids, inp.lora_ids, w, cfg.E, cfg.S, base)
     assert np.array_equal(y, y0)
+
+
+# ------------------------------------------------------ base grouped GEMM (+ fused delta)
+# The base MoE GEMM of a stage: out[p] = W[t_p] x_row(p) for pairs with a local expert,
+# optionally with the LoRA delta added before the one rounding.
+
+GEMM = [
+    _small(configs.C0, name="gemm_f32"),
+    _small(SMALL_BF16, name="gemm_bf16"),
+    _small(SMALL_BF16, name="gemm_ranked", slot_ranks=(8, 3, 0)),
+]
+
+
+def _gemm_case(oracle_lib, cfg, seed, si=0):
+    inp = inputs.generate(cfg, seed=seed)
+    st, sin = cfg.stages[si], inp.stages[si]
+    W = inputs.base_weights(cfg, si, seed)
+    srt, eid, npp = oracle_lib.align_block_size(inp.topk_ids, inp.lora_ids, cfg.E, cfg.S,
+                                                cfg.block_m)
+    s = oracle_lib.lora_shrink(sin.xin, sin.row_div, sin.A, srt, eid, npp, cfg.numel,
+                               cfg.block_m, slices=st.slices, slot_ranks=inp.slot_ranks,
+                               E=cfg.E)
+    base = inputs.base_out(cfg, si, seed)
+    return inp, st, sin, W, (srt, eid, npp), s, base
+
+
+@pytest.mark.parametrize("cfg", GEMM[:2], ids=[c.name for c in GEMM[:2]])
+def test_base_gemm_is_a_per_pair_matvec(oracle_lib, cfg):
+    # numpy: each local pair's row is W[t] @ x, in double, rounded once; other rows untouched
+    inp, st, sin, W, _, _, start = _gemm_case(oracle_lib, cfg, seed=1)
+    out = oracle_lib.moe_gemm(sin.xin, sin.row_div, W, inp.topk_ids, cfg.E, start.copy())
+    t = inp.topk_ids.reshape(-1)
+    local = (t >= 0) & (t < cfg.E)
+    Wd, Xd = pins.to_f64(W), pins.to_f64(sin.xin)
+    rows = np.arange(cfg.numel) // sin.row_div
+    ref = np.einsum("pnk,pk->pn", Wd[np.where(local, t, 0)], Xd[rows])
+    got = pins.to_f64(out)
+    half = 2.0 ** -8 if cfg.dtype == "bf16" else 2.0 ** -23
+    assert np.all(np.abs(got[local] - ref[local]) <= half * np.abs(ref[local]) + 1e-30)
+    assert np.array_equal(out[~local], start[~local])
+    assert local.any() and (~local).any()
+
+
+@pytest.mark.parametrize("cfg", GEMM, ids=[c.name for c in GEMM])
+def test_fused_gemm_reduces_to_its_parts(oracle_lib, cfg):
+    inp, st, sin, W, (srt, eid, npp), s, start = _gemm_case(oracle_lib, cfg, seed=2)
+    inp.scale[:] = np.linspace(0.5, 2.0, cfg.S, dtype=np.float32)
+    s0 = np.nan_to_num(s)
+    kw = dict(s=s0, slices=st.slices, B=sin.B, scale=inp.scale, lora_ids=inp.lora_ids,
+              S=cfg.S, slot_ranks=inp.slot_ranks)
+    base_only = oracle_lib.moe_gemm(sin.xin, sin.row_div, W, inp.topk_ids, cfg.E, start.copy())
+    # zero scale: exactly the base GEMM
+    z = dict(kw, scale=np.zeros_like(inp.scale))
+    assert np.array_equal(
+        oracle_lib.moe_gemm(sin.xin, sin.row_div, W, inp.topk_ids, cfg.E, start.copy(), **z),
+        base_only)
+    # zero base weights: exactly the expand from zero rows, on the local pairs
+    fused0 = oracle_lib.moe_gemm(sin.xin, sin.row_div, np.zeros_like(W), inp.topk_ids, cfg.E,
+                                 start.copy(), **kw)
+    exp0 = oracle_lib.lora_expand(s, st.slices, sin.B, inp.scale, cfg.E, srt, eid, npp,
+                                  cfg.numel, cfg.block_m, np.zeros_like(start),
+                                  slot_ranks=inp.slot_ranks)
+    t = inp.topk_ids.reshape(-1)
+    local = (t >= 0) & (t < cfg.E)
+    assert np.array_equal(fused0[local], exp0[local])
+    # no adapters: the base GEMM
+    none = dict(kw, lora_ids=np.full(cfg.M, -1, np.int32))
+    assert np.array_equal(
+        oracle_lib.moe_gemm(sin.xin, sin.row_div, W, inp.topk_ids, cfg.E, start.copy(), **none),
+        base_only)
+    # the full fused row: base + delta within one rounding of the row (and of each part)
+    fused = oracle_lib.moe_gemm(sin.xin, sin.row_div, W, inp.topk_ids, cfg.E, start.copy(), **kw)
+    a, b, d = pins.to_f64(fused), pins.to_f64(base_only), pins.to_f64(exp0)
+    ulp = 2.0 ** -7 if cfg.dtype == "bf16" else 2.0 ** -22
+    tol = ulp * (np.abs(a) + np.abs(b) + np.abs(d)) + 1e-30
+    assert np.all(np.abs(a - (b + d))[local] <= tol[local])
+    assert np.array_equal(fused[~local], start[~local])

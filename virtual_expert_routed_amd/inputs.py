@@ -24,6 +24,8 @@ Recipe (one numpy PCG64 stream per (config, seed), drawn in this fixed order):
 Outside that stream (each from its own PCG64 stream keyed by (seed, tag), so the layer's
 draws above never move):
 * base_out: nonzero starting rows for an expand's output, N(0, 1);
+* base_weights [E, N, K]: a stage's base expert weights, N(0, w_sigma), for the base grouped
+  GEMM that the delta can be fused into;
 * topk_weights [M, topk] float32: the router's combine weights, a softmax over `topk`
   standard-normal logits per token (positive, summing to 1 per token, as a renormalised
   top-k softmax router gives).
@@ -176,3 +178,11 @@ def topk_weights(cfg: LayerConfig, seed: int) -> np.ndarray:
     z = rng.standard_normal((cfg.M, cfg.topk), dtype=np.float32)
     e = np.exp(z - z.max(axis=1, keepdims=True))
     return np.ascontiguousarray(e / e.sum(axis=1, keepdims=True), dtype=np.float32)
+
+
+def base_weights(cfg: LayerConfig, stage_index: int, seed: int) -> np.ndarray:
+    """A stage's base expert weights [E, N, K] ~ N(0, w_sigma) from their own stream
+    (seed, 3000 + stage)."""
+    st = cfg.stages[stage_index]
+    rng = np.random.default_rng([seed, 3000 + stage_index])
+    return _normals(rng, (cfg.E, st.N, st.K), cfg.w_sigma, cfg.dtype)
