@@ -71,7 +71,8 @@ enum { MOL_F32 = 0, MOL_BF16 = 1 };
 /* (host) Static description of a status code. Never NULL. */
 MOL_API const char *mol_status_string(mol_status status);
 
-/* (host) ABI version of this header, 3 (2 added the per-slot ranks, 3 the combine). */
+/* (host) ABI version of this header, 4 (2 added the per-slot ranks, 3 the combine, 4 the
+ * base grouped GEMM with the fused delta). */
 MOL_API int32_t mol_abi_version(void);
 
 /* ---------------------------------------------------------------------------------
@@ -207,6 +208,38 @@ MOL_API mol_status mol_lora_delta(int32_t dtype, const void *xin, int64_t ld_x,
                                   int32_t numel, int32_t num_virtual, int32_t block_m,
                                   void *out, int64_t ld_out, void *workspace,
                                   size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * mol_moe_gemm - the base MoE grouped GEMM of a stage, with the LoRA delta optionally fused
+ * into its epilogue. The pages' layer runs the base grouped-GEMM launches and then the LoRA
+ * launches that add the delta into the same rows (MindLab sglang PR 24, the PR body's count
+ * of base and LoRA launches per layer); fused, the rows are written once:
+ *   out[p, n] = round( sum_k W[t, n, k] * xin[p / row_div, k]
+ *                      + slot_scale[l] * sum_{j < rl} B[t + l*E, n, j] * s[p, (n / w) * r + j] )
+ * for every pair p with a local base expert t = topk id in [0, E) (other rows untouched),
+ * with l the token's slot (lora_ids[p / topk]; the delta term only for l in [0, S) and slot
+ * rank rl > 0), r = R / slices, w = N / slices. Summed in fp32, rounded once (bf16 RNE).
+ *   sorted_ids, expert_ids, num_post_padded
+ *                 the routing by BASE expert: mol_align_block_size over the top-k ids with
+ *                 lora_ids = NULL and num_slots = 1 (num_virtual = num_experts)
+ *   W             [E, N, K] base weights (dtype), 16-byte aligned, K * elem a multiple of 16
+ *   xin           rows of ld_x elements (16-byte multiple), row p / row_div for pair p
+ *   out           [numel, ld_out] (dtype), aligned to its element
+ *   s             NULL: the base GEMM alone. Else the fused delta: float32 [numel, R] from
+ *                 mol_lora_shrink of the same stage (16-byte aligned), B [E*S, N, r] (dtype,
+ *                 16-byte aligned), slot_scale [S], slot_ranks [S] or NULL, lora_ids [numel /
+ *                 topk]; r * elem a multiple of 16 and at most MOL_MAX_RANK_BYTES
+ * Built for decode-sized batches (a gather of matrix-vector products over the touched
+ * experts' weights, like the shrink). Errors as for mol_lora_shrink / mol_lora_expand.
+ * ------------------------------------------------------------------------------- */
+MOL_API mol_status mol_moe_gemm(int32_t dtype, const void *xin, int64_t ld_x, int32_t row_div,
+                                const void *W, int32_t K, int32_t N, int32_t num_experts,
+                                const int32_t *sorted_ids, const int32_t *expert_ids,
+                                const int32_t *num_post_padded, int32_t numel, int32_t block_m,
+                                void *out, int64_t ld_out, const float *s, int32_t R,
+                                int32_t slices, const void *B, const float *slot_scale,
+                                const int32_t *slot_ranks, const int32_t *lora_ids,
+                                int32_t topk, int32_t num_slots, void *stream);
 
 /* ---------------------------------------------------------------------------------
  * The combine after the down projection. The pages stop at the per-pair rows the down

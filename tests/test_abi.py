@@ -39,7 +39,7 @@ def test_only_mol_symbols_exported():
 
 def test_version_and_status_strings():
     L = mb.lib()
-    assert L.mol_abi_version() == 3
+    assert L.mol_abi_version() == 4
     for code in range(7):
         assert mb.status_string(code)
     assert mb.status_string(99) == "unknown status"
@@ -188,3 +188,28 @@ def test_combine_rejects_before_launch():
     assert fused(ldb=32) == mb.MOL_E_ARG
     assert fused(s=ctypes.c_void_p(0x1008)) == mb.MOL_E_ALIGN
     assert fused(M=0, s=None, B=None, t=None, l=None, w=None, base=None, y=None) == mb.MOL_OK
+
+
+def test_moe_gemm_rejects_before_launch():
+    L = mb.lib()
+
+    def gemm(dtype=mb.MOL_BF16, xin=FAKE, ldx=64, rd=1, W=FAKE, K=64, N=32, E=8, srt=FAKE,
+             eid=FAKE, npp=FAKE, numel=16, bm=16, out=FAKE, ldo=32, s=None, R=0, sl=1, B=None,
+             sc=None, rk=None, lora=None, topk=1, S=1):
+        return L.mol_moe_gemm(dtype, xin, ldx, rd, W, K, N, E, srt, eid, npp, numel, bm, out,
+                              ldo, s, R, sl, B, sc, rk, lora, topk, S, None)
+
+    assert gemm(dtype=4) == mb.MOL_E_DTYPE
+    assert gemm(ldx=32) == mb.MOL_E_ARG                      # ld_x < K
+    assert gemm(K=60, ldx=64) == mb.MOL_E_ALIGN              # 120-byte rows
+    assert gemm(W=ctypes.c_void_p(0x1008)) == mb.MOL_E_ALIGN
+    assert gemm(srt=None) == mb.MOL_E_ARG
+    assert gemm(E=8192) == mb.MOL_E_LIMIT                    # 8193 buckets
+    # fused delta: missing slots, rank bytes, misaligned s, token count
+    assert gemm(s=FAKE, R=16, B=FAKE, sc=FAKE, topk=2, S=2) == mb.MOL_E_ARG
+    assert gemm(s=FAKE, R=512, B=FAKE, sc=FAKE, lora=FAKE, topk=2, S=2) == mb.MOL_E_LIMIT
+    assert gemm(s=ctypes.c_void_p(0x1008), R=16, B=FAKE, sc=FAKE, lora=FAKE, topk=2,
+                S=2) == mb.MOL_E_ALIGN
+    assert gemm(s=FAKE, R=16, B=FAKE, sc=FAKE, lora=FAKE, topk=3, S=2) == mb.MOL_E_ARG
+    assert gemm(numel=0, xin=None, W=None, srt=None, eid=None, npp=None,
+                out=None) == mb.MOL_OK

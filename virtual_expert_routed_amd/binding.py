@@ -36,6 +36,8 @@ SIGNATURES = {
     "mol_delta_workspace_bytes": (_I64, [_I32, _I32, _I32, _I32]),
     "mol_lora_delta": (_I32, [_I32, _P, _I64, _I32, _P, _I32, _I32, _I32, _P, _I32, _P, _P,
                               _I32, _P, _P, _P, _I32, _I32, _I32, _P, _I64, _P, _SZ, _P]),
+    "mol_moe_gemm": (_I32, [_I32, _P, _I64, _I32, _P, _I32, _I32, _I32, _P, _P, _P, _I32, _I32,
+                            _P, _I64, _P, _I32, _I32, _P, _P, _P, _P, _I32, _I32, _P]),
     "mol_moe_combine": (_I32, [_I32, _P, _I64, _P, _P, _I32, _I32, _I32, _I32, _P, _I64, _P]),
     "mol_lora_expand_combine": (_I32, [_I32, _P, _I32, _P, _I32, _P, _P, _P, _P, _P, _I32,
                                        _I32, _I32, _I32, _P, _I64, _P, _I64, _P]),
@@ -279,3 +281,29 @@ def mol_lora_expand_combine(s, B, slot_scale, topk_ids, lora_ids, topk_weights,
         _ptr(topk_ids), _ptr(lora_ids), _ptr(topk_weights), M, k, num_experts, num_slots,
         _ptr(base), base.stride(0), _ptr(y), y.stride(0), _stream(B)))
     return y
+
+
+def mol_moe_gemm(xin, row_div: int, W, sorted_ids, expert_ids, num_post_padded, numel: int,
+                 block_m: int, out, s=None, slices: int = 1, B=None, slot_scale=None,
+                 lora_ids=None, topk: int = 1, num_slots: int = 1, slot_ranks=None):
+    """The base grouped GEMM of a stage into out [numel, N] (routing by base expert); with
+    s and B the LoRA delta is added before the one rounding."""
+    _need(xin, "xin", contiguous=False)
+    _need(W, "W")
+    _need(out, "out", W.dtype, contiguous=False)
+    if xin.stride(1) != 1 or out.stride(1) != 1:
+        raise ValueError("xin and out rows must be contiguous")
+    E, N, K = W.shape
+    R = 0
+    if s is not None:
+        _need(s, "s", torch.float32)
+        _need(B, "B", W.dtype)
+        _need(slot_scale, "slot_scale", torch.float32)
+        _need(lora_ids, "lora_ids", torch.int32)
+        R = s.shape[1]
+    _check("mol_moe_gemm", lib().mol_moe_gemm(
+        _dtype_code(W), _ptr(xin), xin.stride(0), row_div, _ptr(W), K, N, E, _ptr(sorted_ids),
+        _ptr(expert_ids), _ptr(num_post_padded), numel, block_m, _ptr(out), out.stride(0),
+        _ptr(s), R, slices, _ptr(B), _ptr(slot_scale), _ranks(slot_ranks), _ptr(lora_ids), topk,
+        num_slots, _stream(W)))
+    return out

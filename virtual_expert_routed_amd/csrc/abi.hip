@@ -145,7 +145,7 @@ MOL_API const char* mol_status_string(mol_status status) {
   }
 }
 
-MOL_API int32_t mol_abi_version(void) { return 3; }
+MOL_API int32_t mol_abi_version(void) { return 4; }
 
 MOL_API mol_status mol_virtual_topk(const int32_t* topk_ids, const int32_t* lora_ids,
                                     int32_t M, int32_t topk, int32_t num_experts,
@@ -398,6 +398,71 @@ MOL_API mol_status mol_lora_delta(int32_t dtype, const void* xin, int64_t ld_x,
   const hipError_t err = shrink_all(a, bf16, rpi, grid_s, mm_s, st);
   if (err != hipSuccess) return MOL_E_HIP;
   return hip_status(expand_all(a, bf16, grid_e, mm_e, st));
+}
+
+// ---- base grouped GEMM, alone or with the LoRA delta in its epilogue -----------------
+
+MOL_API mol_status mol_moe_gemm(int32_t dtype, const void* xin, int64_t ld_x, int32_t row_div,
+                                const void* W, int32_t K, int32_t N, int32_t num_experts,
+                                const int32_t* sorted_ids, const int32_t* expert_ids,
+                                const int32_t* num_post_padded, int32_t numel, int32_t block_m,
+                                void* out, int64_t ld_out, const float* s, int32_t R,
+                                int32_t slices, const void* B, const float* slot_scale,
+                                const int32_t* slot_ranks, const int32_t* lora_ids,
+                                int32_t topk, int32_t num_slots, void* stream) {
+  const StageCheck rc =
+      routing_check(sorted_ids, expert_ids, num_post_padded, numel, num_experts, block_m);
+  if (rc.st != MOL_OK) return rc.st;
+  if (dtype != MOL_F32 && dtype != MOL_BF16) return MOL_E_DTYPE;
+  if (K < 1 || N < 1 || row_div < 1 || ld_x < K || ld_out < N) return MOL_E_ARG;
+  if (numel > 0 && (!xin || !W || !out)) return MOL_E_ARG;
+  const bool bf16 = dtype == MOL_BF16;
+  const int esz = bf16 ? 2 : 4;
+  if (((int64_t)K * esz) % 16 || (ld_x * esz) % 16) return MOL_E_ALIGN;
+  if (numel > 0 && (!aligned16(xin) || !aligned16(W) || reinterpret_cast<uintptr_t>(out) % esz))
+    return MOL_E_ALIGN;
+  if ((int64_t)N * K * esz >= (int64_t(1) << 31)) return MOL_E_LIMIT;  // one expert's W
+  if (s) {  // the fused delta
+    if (R < 1 || slices < 1 || R % slices || N % slices || topk < 1 || num_slots < 1 ||
+        numel % topk)
+      return MOL_E_ARG;
+    if (numel > 0 && (!B || !slot_scale || !lora_ids)) return MOL_E_ARG;
+    const int64_t rbytes = (int64_t)(R / slices) * esz;
+    if (rbytes % 16) return MOL_E_ALIGN;
+    if (rbytes > MOL_MAX_RANK_BYTES) return MOL_E_LIMIT;
+    if ((int64_t)num_experts * num_slots + 1 > MOL_MAX_BUCKETS) return MOL_E_LIMIT;
+    if ((int64_t)N * rbytes >= (int64_t(1) << 31)) return MOL_E_LIMIT;  // one expert's B
+    if (numel > 0 && (!aligned16(s) || !aligned16(B))) return MOL_E_ALIGN;
+  }
+  if (numel == 0) return MOL_OK;
+  mol::GemmArgs g{};
+  g.route = make_delta_args(nullptr, 0, 1, nullptr, 1, 1, 1, nullptr, 1, nullptr, num_experts,
+                            sorted_ids, expert_ids, num_post_padded, numel, num_experts,
+                            block_m, nullptr, nullptr, 0, rc.max_blocks);
+  g.route.mfma_min = 0;
+  g.xin = xin;
+  g.ld_x = ld_x;
+  g.row_div = row_div;
+  g.W = W;
+  g.K = K;
+  g.N = N;
+  g.out = out;
+  g.ld_out = ld_out;
+  g.s = s;
+  g.R = s ? R : 0;
+  g.slices = s ? slices : 1;
+  g.B = B;
+  g.scale = slot_scale;
+  g.ranks = slot_ranks;
+  g.lora = lora_ids;
+  g.topk = s ? topk : 1;
+  g.E = num_experts;
+  g.S = s ? num_slots : 1;
+  const int rpi = mol::shrink_rows_per_item(K, esz);
+  g.rgroups = (int32_t)cdiv64(N, rpi);
+  const int64_t grid = rc.max_blocks * (int64_t)g.rgroups;
+  if (grid > kI32Max) return MOL_E_LIMIT;
+  return hip_status(mol::launch_moe_gemm(g, bf16, rpi, (int)grid, (hipStream_t)stream));
 }
 
 // ---- combine -----------------------------------------------------------------------

@@ -1,0 +1,202 @@
+// The base MoE grouped GEMM of a stage, with the LoRA delta optionally fused into its
+// epilogue. The pages' layer runs base grouped-GEMM launches and, after them, the LoRA
+// shrink/expand launches that add the delta into the same output rows (MindLab sglang
+// PR 24, the PR body's per-layer launch count). Here the delta can be added before the
+// base result is rounded, so the output rows are written once instead of written, read back
+// and written again.
+//
+//   out[p, n] = round( sum_k W[t_p, n, k] * xin[p / row_div, k]
+//                      + [fused, slot l valid, rank rl > 0]
+//                        scale[l] * sum_{j < rl} B[t_p + l*E, n, j] * s[p, g(n)*r + j] )
+//
+// for every pair whose base expert t_p is local (0 <= t_p < E); other rows are untouched.
+// The pairs come grouped by base expert (align_block_size over the base ids, one slot).
+//
+// At decode this is the same gather of matrix-vector products as the LoRA shrink, over
+// far larger weights (W_t is N x K), so it is built the same way: a work item is (block,
+// RPI consecutive output columns), each column's row of W_t read once with coalesced
+// 16-byte buffer loads by LPR lanes and reused for up to four pairs, the pairs' input
+// rows staged in LDS, the lanes' partial sums combined by a fixed xor tree. The fused
+// delta costs one more 16-byte B vector and two s vectors per lane and pair, loaded in
+// the same round trip as the weights, and each lane adds its part of the rank sum to its
+// partial before the tree: the delta needs no extra pass and no extra write.
+#include "delta_common.h"
+
+namespace mol {
+namespace {
+
+template <bool BF16, int LPR, bool FUSED>
+__device__ __forceinline__ void gemm_group(const GemmArgs& g, int e, int rg, const int* p,
+                                           int nq, uint4* xs) {
+  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int VE = BF16 ? 8 : 4;  // elements of one 16-byte vector
+  constexpr int RPI = kThreads / LPR;
+  constexpr int SEGV = kSeg * LPR;
+  constexpr int XPT = kPG * SEGV / kThreads;
+  static_assert(XPT >= 1 && kPG * SEGV % kThreads == 0, "x staging covers whole waves");
+  const int tid = threadIdx.x;
+  const int lr = tid % LPR;
+  const int n = rg * RPI + tid / LPR;  // this row group's output column
+  const bool n_ok = n < g.N;
+  const int nvec = g.K * ESZ / 16;
+  const int vpl = (nvec + LPR - 1) / LPR;
+  const int64_t wbytes = (int64_t)g.N * g.K * ESZ;
+  const __amdgpu_buffer_rsrc_t rw = expert_rsrc((const char*)g.W + (int64_t)e * wbytes, wbytes);
+  const uint32_t row_off = (uint32_t)(n_ok ? n : 0) * (uint32_t)(g.K * ESZ);
+  const char* xbase = (const char*)g.xin;
+  const int64_t xstride = g.ld_x * ESZ;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  float acc[kPG];
+#pragma unroll
+  for (int i = 0; i < kPG; ++i) acc[i] = 0.f;
+
+  // the fused delta's operands: lane lr holds 16-byte vector lr of the pair's B row (the
+  // rank slice of column n) and the matching 2 x 16 bytes of its s row, so its share of
+  // the rank sum goes into its partial before the xor tree
+  uint4 bq[kPG];
+  float4 s0[kPG], s1[kPG];
+  float scq[kPG];
+  int keepq[kPG];
+  if constexpr (FUSED) {
+    const int r = g.R / g.slices;
+    const int width = g.N / g.slices;
+    const int gs = n_ok ? n / width : 0;
+    const int64_t bbytes = (int64_t)g.N * r * ESZ;
+#pragma unroll
+    for (int i = 0; i < kPG; ++i) {
+      const int pq = i < nq ? (i == 0 ? p[0] : i == 1 ? p[1] : i == 2 ? p[2] : p[3]) : 0;
+      const int l = i < nq ? g.lora[pq / g.topk] : -1;
+      const bool lv = l >= 0 && l < g.S;
+      const int rl = lv ? (g.ranks ? min(max(g.ranks[l], 0), r) : r) : 0;
+      const int v = lv ? e + l * g.E : 0;
+      scq[i] = lv ? g.scale[l] : 0.f;
+      keepq[i] = rl - lr * VE;  // elements of this lane's vector inside the rank
+      const bool use = n_ok && rl > 0 && lr * VE < rl;
+      const __amdgpu_buffer_rsrc_t rb =
+          expert_rsrc((const char*)g.B + (int64_t)v * bbytes, bbytes);
+      bq[i] = buf16(rb, use ? (uint32_t)(n * r * ESZ + lr * 16) : kOutOfRange);
+      const float* sp = g.s + (int64_t)pq * g.R + gs * r + lr * VE;
+      const bool sok = use;
+      s0[i] = sok ? *reinterpret_cast<const float4*>(sp) : make_float4(0.f, 0.f, 0.f, 0.f);
+      s1[i] = (BF16 && sok) ? *reinterpret_cast<const float4*>(sp + 4)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);  // fp32 vectors hold 4
+    }
+  }
+
+  for (int m0 = 0; m0 < vpl; m0 += kSeg) {
+    uint4 wvec[kSeg];
+#pragma unroll
+    for (int sg = 0; sg < kSeg; ++sg) {
+      const int v = lr + (m0 + sg) * LPR;
+      wvec[sg] = buf16(rw, (n_ok && v < nvec) ? row_off + (uint32_t)v * 16u : kOutOfRange);
+    }
+    if (m0 > 0) __syncthreads();  // earlier readers of xs are done
+#pragma unroll
+    for (int t = 0; t < XPT; ++t) {
+      const int i = tid + t * kThreads;
+      const int q = i / SEGV;
+      const int v = m0 * LPR + (i - q * SEGV);
+      const bool ok = q < nq && v < nvec;
+      const int pq = !ok ? 0 : q == 0 ? p[0] : q == 1 ? p[1] : q == 2 ? p[2] : p[3];
+      lds_dma16(xbase + (ok ? (int64_t)(pq / g.row_div) * xstride + (int64_t)v * 16 : 0),
+                xs + wv * 64 + t * kThreads);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the x DMA, the weights (and the delta operands) landed
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kPG; ++i) {
+      if (i >= nq) break;
+#pragma unroll
+      for (int sg = 0; sg < kSeg; ++sg) {
+        const int v = lr + (m0 + sg) * LPR;
+        if (v < nvec) acc[i] = dot16<BF16>(wvec[sg], xs[i * SEGV + sg * LPR + lr], acc[i]);
+      }
+    }
+  }
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int i = 0; i < kPG; ++i) {
+      if (i >= nq) break;
+      const uint4 b = keepq[i] < VE ? keep_first<BF16>(bq[i], keepq[i]) : bq[i];
+      const float sv[8] = {s0[i].x, s0[i].y, s0[i].z, s0[i].w,
+                           s1[i].x, s1[i].y, s1[i].z, s1[i].w};
+      acc[i] = fmaf(scq[i], dot16_s<BF16>(b, sv, 0.f), acc[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kPG; ++i) {
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc[i] += __shfl_xor(acc[i], off, 64);
+  }
+  if (lr == 0 && n_ok) {
+#pragma unroll
+    for (int i = 0; i < kPG; ++i) {
+      if (i >= nq) break;
+      const int64_t o = (int64_t)p[i] * g.ld_out + n;
+      if constexpr (BF16)
+        ((uint16_t*)g.out)[o] = f32_to_bf16_rne(acc[i]);
+      else
+        ((float*)g.out)[o] = acc[i];
+    }
+  }
+}
+
+template <bool BF16, int LPR, bool FUSED>
+__global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs g) {
+  __shared__ int pid[kPidSlots];
+  __shared__ int nreal;
+  __shared__ uint4 xs[kPG * kSeg * LPR];
+  const DeltaArgs& a = g.route;
+  const int blk = blockIdx.x / g.rgroups, rg = blockIdx.x % g.rgroups;
+  int p[kPG];
+  bool all_here, mfma;
+  const int n4 = first_pairs(a, blk, p, &all_here, &mfma);
+  const int e = block_expert(a, blk);
+  if (e < 0) return;  // sentinel block (no local expert) or past the live blocks
+  if (all_here) {
+    if (n4 > 0) gemm_group<BF16, LPR, FUSED>(g, e, rg, p, n4, xs);
+    return;
+  }
+  for (int j0 = 0; j0 < a.BM; j0 += kPidSlots) {
+    const int pv = threadIdx.x < kPidSlots ? load_pid(a, blk, j0) : a.numel;
+    __syncthreads();
+    publish_pids(a, pv, pid, &nreal);
+    __syncthreads();
+    const int nr = nreal;
+    for (int q0 = 0; q0 < nr; q0 += kPG) {
+      int pq[kPG];
+#pragma unroll
+      for (int i = 0; i < kPG; ++i) pq[i] = q0 + i < nr ? pid[q0 + i] : a.numel;
+      __syncthreads();  // xs of the previous group is no longer read
+      gemm_group<BF16, LPR, FUSED>(g, e, rg, pq, min(kPG, nr - q0), xs);
+    }
+    if (nr < kPidSlots) return;  // the block's real entries ended in this pass
+  }
+}
+
+template <bool BF16, bool FUSED>
+hipError_t gemm_dispatch(const GemmArgs& g, int lpr, int grid, hipStream_t st) {
+  switch (lpr) {
+    case 8: hipLaunchKernelGGL((gemm_kernel<BF16, 8, FUSED>), dim3(grid), dim3(kThreads), 0, st, g); break;
+    case 16: hipLaunchKernelGGL((gemm_kernel<BF16, 16, FUSED>), dim3(grid), dim3(kThreads), 0, st, g); break;
+    case 32: hipLaunchKernelGGL((gemm_kernel<BF16, 32, FUSED>), dim3(grid), dim3(kThreads), 0, st, g); break;
+    case 64: hipLaunchKernelGGL((gemm_kernel<BF16, 64, FUSED>), dim3(grid), dim3(kThreads), 0, st, g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_moe_gemm(const GemmArgs& g, bool bf16, int rows_per_item, int grid,
+                           hipStream_t stream) {
+  const int lpr = kThreads / rows_per_item;
+  const bool fused = g.s != nullptr;
+  if (bf16)
+    return fused ? gemm_dispatch<true, true>(g, lpr, grid, stream)
+                 : gemm_dispatch<true, false>(g, lpr, grid, stream);
+  return fused ? gemm_dispatch<false, true>(g, lpr, grid, stream)
+               : gemm_dispatch<false, false>(g, lpr, grid, stream);
+}
+
+}  // namespace mol

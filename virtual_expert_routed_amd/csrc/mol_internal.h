@@ -91,6 +91,30 @@ struct CombineArgs {
   int64_t ld_y;
 };
 
+// The base MoE grouped GEMM of a stage, optionally with the LoRA delta in its epilogue.
+struct GemmArgs {
+  DeltaArgs route;         // routing of the base-expert blocks (V = E, mfma_min 0)
+  const void* xin;
+  int64_t ld_x;
+  int32_t row_div;
+  const void* W;           // [E, N, K]
+  int32_t K;
+  int32_t N;
+  int32_t rgroups;         // work items per block (groups of output columns)
+  void* out;               // [numel, ld_out]
+  int64_t ld_out;
+  const float* s;          // fused delta: [numel, R] from the LoRA shrink; nullptr: base only
+  int32_t R;
+  int32_t slices;
+  const void* B;           // [E*S, N, R/slices]
+  const float* scale;      // [S]
+  const int32_t* ranks;    // [S] or nullptr
+  const int32_t* lora;     // [numel / topk] slot per token
+  int32_t topk;
+  int32_t E;
+  int32_t S;
+};
+
 // host-side launchers (return the launch status)
 hipError_t launch_virtual_topk(const int32_t* topk_ids, const int32_t* lora_ids, int32_t M,
                                int32_t topk, int32_t E, int32_t S, int32_t* out,
@@ -112,6 +136,9 @@ hipError_t launch_expand(const DeltaArgs& a, bool bf16, int grid, hipStream_t st
 int shrink_mfma_row_tile(int32_t R);
 hipError_t launch_shrink_mfma(const DeltaArgs& a, int grid, hipStream_t stream);
 hipError_t launch_expand_mfma(const DeltaArgs& a, int grid, hipStream_t stream);
+// base grouped GEMM (+ fused delta when g.s is set): rows_per_item as for the shrink
+hipError_t launch_moe_gemm(const GemmArgs& g, bool bf16, int rows_per_item, int grid,
+                           hipStream_t stream);
 // combine: one wave per (token, 64 16-byte vectors of columns)
 hipError_t launch_combine(const CombineArgs& a, bool bf16, hipStream_t stream);
 // fused expand + combine: ranks it is built for (R/8 or R/4 a power of two up to 16)
