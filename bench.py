@@ -148,6 +148,70 @@ def grid_report(cfg, max_blocks, stats):
     return rep
 
 
+def base_gemm_leg(cfg, layers, host_inputs, torch, n_layers=2, rounds=8):
+    """The base grouped GEMM of each stage, alone and with the LoRA delta fused into its
+    epilogue, beside the unfused pair (base GEMM, then the LoRA expand into the same rows).
+    Two layers rotate (their touched base weights, ~0.9 GB each at the decode configs, are far
+    beyond the MALL); HIP events around runs of one call per layer, as for the path's
+    kernels. Reported beside the headline, not part of it."""
+    from virtual_expert_routed_amd import inputs
+    use = layers[:min(n_layers, len(layers))]
+    for l, dl in enumerate(use):
+        dl.attach_base([inputs.base_weights(cfg, si, l) for si in range(len(cfg.stages))])
+        dl.align()
+        dl.align_base()
+        for si in range(len(cfg.stages)):
+            dl.shrink(si)
+    torch.cuda.synchronize()
+    esz = 2 if cfg.dtype == "bf16" else 4
+    res = {}
+    for si, st in enumerate(cfg.stages):
+        fns = {"base": lambda dl: dl.base_gemm(si, False),
+               "expand": lambda dl: dl.expand(si),
+               "fused": lambda dl: dl.base_gemm(si, True)}
+        for fn in fns.values():  # warm
+            for dl in use:
+                fn(dl)
+        ev = {k: [] for k in fns}
+        for _ in range(rounds):
+            for k, fn in fns.items():
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for dl in use:
+                    fn(dl)
+                b.record()
+                ev[k].append((a, b))
+        torch.cuda.synchronize()
+        us = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) * 1e3 / len(use)
+              for k, v in ev.items()}
+        # algorithmic bytes: touched base experts' W, input rows, each local pair's out row
+        # written (the fused form adds the LoRA B of the touched virtual experts and s)
+        byt, fbyt = [], []
+        for h in host_inputs[:len(use)]:
+            t = h.topk_ids.reshape(-1)
+            loc = (t >= 0) & (t < cfg.E)
+            nexp = int(np.unique(t[loc]).size)
+            rows = int(np.unique(np.nonzero(loc)[0] // cfg.topk).size) if st.input == "x" \
+                else int(loc.sum())
+            b0 = nexp * st.N * st.K * esz + rows * st.K * esz + int(loc.sum()) * st.N * esz
+            v = t + np.repeat(h.lora_ids, cfg.topk) * cfg.E
+            lv = loc & (np.repeat(h.lora_ids, cfg.topk) >= 0) & (np.repeat(h.lora_ids, cfg.topk) < cfg.S)
+            d = int(np.unique(v[lv]).size)
+            byt.append(b0)
+            fbyt.append(b0 + d * st.N * st.r * esz + int(lv.sum()) * st.R * 4)
+        res[st.name] = {
+            "base_us": us["base"],
+            "base_GB/s": float(np.mean(byt)) / (us["base"] * 1e-6) / 1e9,
+            "base_then_expand_us": us["base"] + us["expand"],
+            "fused_us": us["fused"],
+            "fused_GB/s": float(np.mean(fbyt)) / (us["fused"] * 1e-6) / 1e9,
+            "saved_us": us["base"] + us["expand"] - us["fused"],
+        }
+    res["how"] = (f"HIP events around runs of one call per layer over {len(use)} rotated "
+                  f"layers, {rounds} runs each; LoRA s from the stage's shrink")
+    return res
+
+
 def kernel_name(cfg, st, kind):
     """The kernel instantiations libmol launches for this stage, as a profiler names them.
     Shrink: rows per work item start at 4 and double while two such items' A rows fit
@@ -490,6 +554,8 @@ def main():
             "us_per_launch": dom["us"],
         },
     }
+    result["base_gemm"] = base_gemm_leg(cfg, layers, host_inputs, torch) if cfg.M <= 1024 \
+        else None
     down = cfg.stages[-1]
     n_local = [int(((h.topk_ids >= 0) & (h.topk_ids < cfg.E)).sum()) for h in host_inputs]
     cb = float(np.mean([combine_bytes(cfg, down, n) for n in n_local]))

@@ -17,9 +17,12 @@
 // RPI consecutive output columns), each column's row of W_t read once with coalesced
 // 16-byte buffer loads by LPR lanes and reused for up to four pairs, the pairs' input
 // rows staged in LDS, the lanes' partial sums combined by a fixed xor tree. The fused
-// delta costs one more 16-byte B vector and two s vectors per lane and pair, loaded in
-// the same round trip as the weights, and each lane adds its part of the rank sum to its
-// partial before the tree: the delta needs no extra pass and no extra write.
+// delta costs one more 16-byte B vector and two s vectors per lane and pair, loaded after
+// the weight loop, and each lane adds its part of the rank sum to its partial before the
+// tree: the delta needs no extra pass over the output and no extra write. (Measured at
+// decode on MI355X, this extra round trip per item costs more than a separate expand
+// launch: the base GEMM alone streams its weights at about 5.8 TB/s in items of eight
+// columns, and any per-item latency shows.)
 #include "delta_common.h"
 
 namespace mol {
@@ -50,36 +53,24 @@ __device__ __forceinline__ void gemm_group(const GemmArgs& g, int e, int rg, con
 #pragma unroll
   for (int i = 0; i < kPG; ++i) acc[i] = 0.f;
 
-  // the fused delta's operands: lane lr holds 16-byte vector lr of the pair's B row (the
-  // rank slice of column n) and the matching 2 x 16 bytes of its s row, so its share of
-  // the rank sum goes into its partial before the xor tree
-  uint4 bq[kPG];
-  float4 s0[kPG], s1[kPG];
+  // The fused delta. Its per-pair slot, rank and scale are uniform over the workgroup and
+  // read up front; its vector operands (the B row slice and the s row slice a lane needs)
+  // are loaded after the weight loop, two pairs per round trip, so the loop keeps close to
+  // the register budget, and the occupancy, of the base GEMM alone. Lane lr takes 16-byte
+  // vector lr of its column's B row slice and the matching s values, and adds its share of
+  // the rank sum to its partial before the xor tree.
+  int rlq[kPG], vq[kPG];
   float scq[kPG];
-  int keepq[kPG];
   if constexpr (FUSED) {
     const int r = g.R / g.slices;
-    const int width = g.N / g.slices;
-    const int gs = n_ok ? n / width : 0;
-    const int64_t bbytes = (int64_t)g.N * r * ESZ;
 #pragma unroll
     for (int i = 0; i < kPG; ++i) {
       const int pq = i < nq ? (i == 0 ? p[0] : i == 1 ? p[1] : i == 2 ? p[2] : p[3]) : 0;
       const int l = i < nq ? g.lora[pq / g.topk] : -1;
       const bool lv = l >= 0 && l < g.S;
-      const int rl = lv ? (g.ranks ? min(max(g.ranks[l], 0), r) : r) : 0;
-      const int v = lv ? e + l * g.E : 0;
+      rlq[i] = lv ? (g.ranks ? min(max(g.ranks[l], 0), r) : r) : 0;
+      vq[i] = lv ? e + l * g.E : 0;
       scq[i] = lv ? g.scale[l] : 0.f;
-      keepq[i] = rl - lr * VE;  // elements of this lane's vector inside the rank
-      const bool use = n_ok && rl > 0 && lr * VE < rl;
-      const __amdgpu_buffer_rsrc_t rb =
-          expert_rsrc((const char*)g.B + (int64_t)v * bbytes, bbytes);
-      bq[i] = buf16(rb, use ? (uint32_t)(n * r * ESZ + lr * 16) : kOutOfRange);
-      const float* sp = g.s + (int64_t)pq * g.R + gs * r + lr * VE;
-      const bool sok = use;
-      s0[i] = sok ? *reinterpret_cast<const float4*>(sp) : make_float4(0.f, 0.f, 0.f, 0.f);
-      s1[i] = (BF16 && sok) ? *reinterpret_cast<const float4*>(sp + 4)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);  // fp32 vectors hold 4
     }
   }
 
@@ -101,7 +92,7 @@ __device__ __forceinline__ void gemm_group(const GemmArgs& g, int e, int rg, con
       lds_dma16(xbase + (ok ? (int64_t)(pq / g.row_div) * xstride + (int64_t)v * 16 : 0),
                 xs + wv * 64 + t * kThreads);
     }
-    __builtin_amdgcn_s_waitcnt(0);  // the x DMA, the weights (and the delta operands) landed
+    __builtin_amdgcn_s_waitcnt(0);  // the x DMA and the weights have landed
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kPG; ++i) {
@@ -114,13 +105,43 @@ __device__ __forceinline__ void gemm_group(const GemmArgs& g, int e, int rg, con
     }
   }
   if constexpr (FUSED) {
+    const int r = g.R / g.slices;
+    const bool lane_r = n_ok && lr * VE < r;  // this lane holds part of the rank
+    const int gs = n_ok ? n / (g.N / g.slices) : 0;
+    const int64_t bbytes = (int64_t)g.N * r * ESZ;
+    // two pairs per round trip: at decode a block rarely holds more, and holding four
+    // pairs' operands at once would cost the loop's occupancy
+    constexpr int kEP = 2;
 #pragma unroll
-    for (int i = 0; i < kPG; ++i) {
-      if (i >= nq) break;
-      const uint4 b = keepq[i] < VE ? keep_first<BF16>(bq[i], keepq[i]) : bq[i];
-      const float sv[8] = {s0[i].x, s0[i].y, s0[i].z, s0[i].w,
-                           s1[i].x, s1[i].y, s1[i].z, s1[i].w};
-      acc[i] = fmaf(scq[i], dot16_s<BF16>(b, sv, 0.f), acc[i]);
+    for (int h = 0; h < kPG; h += kEP) {
+      if (h >= nq) break;  // uniform
+      uint4 bq[kEP];
+      float4 s0[kEP], s1[kEP];
+#pragma unroll
+      for (int u = 0; u < kEP; ++u) {
+        const int i = h + u;
+        const bool use = i < nq && lane_r && lr * VE < rlq[i];
+        const __amdgpu_buffer_rsrc_t rb =
+            expert_rsrc((const char*)g.B + (int64_t)vq[i] * bbytes, bbytes);
+        bq[u] = buf16(rb, use ? (uint32_t)(n * r * ESZ + lr * 16) : kOutOfRange);
+        const int pq = i < nq ? (i == 0 ? p[0] : i == 1 ? p[1] : i == 2 ? p[2] : p[3]) : 0;
+        const float* sp = g.s + (int64_t)pq * g.R + gs * r + lr * VE;
+        s0[u] = use ? *reinterpret_cast<const float4*>(sp) : make_float4(0.f, 0.f, 0.f, 0.f);
+        s1[u] = BF16 && use ? *reinterpret_cast<const float4*>(sp + 4)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);  // fp32: 4 per vector
+      }
+#pragma unroll
+      for (int u = 0; u < kEP; ++u) {
+        const int i = h + u;
+        if (i < nq && rlq[i] > 0 && lane_r) {  // a slot with a delta; this lane holds a part
+          const float sv[8] = {s0[u].x, s0[u].y, s0[u].z, s0[u].w,
+                               s1[u].x, s1[u].y, s1[u].z, s1[u].w};
+          // B vectors past the slot's rank read as zero; the one that straddles it is trimmed
+          const uint4 b = rlq[i] < (lr + 1) * VE ? keep_first<BF16>(bq[u], rlq[i] - lr * VE)
+                                                 : bq[u];
+          acc[i] = fmaf(scq[i], dot16_s<BF16>(b, sv, 0.f), acc[i]);
+        }
+      }
     }
   }
 #pragma unroll

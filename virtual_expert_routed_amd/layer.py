@@ -63,6 +63,38 @@ class DeviceLayer:
                 np.ascontiguousarray(topk_weights, dtype=np.float32)).to(dev)
             self.y = torch.zeros((cfg.M, cfg.stages[-1].N), dtype=odt, device=dev)
 
+    def attach_base(self, weights):
+        """Base expert weights per stage ([E, N, K] each) for the base grouped GEMM, with its
+        own routing buffers (by base expert: one slot)."""
+        c = self.cfg
+        dev = self.device
+        self.W = [to_device(w, dev, self.bf16) for w in weights]
+        nblk = mb.mol_align_max_blocks(c.numel, c.E, c.block_m)
+        self.b_sorted = torch.empty(max(1, nblk * c.block_m), dtype=torch.int32, device=dev)
+        self.b_expert = torch.empty(max(1, nblk), dtype=torch.int32, device=dev)
+        self.b_npp = torch.empty(1, dtype=torch.int32, device=dev)
+        wsb = mb.mol_align_workspace_bytes(c.numel, c.E, c.block_m)
+        self.b_ws = torch.empty(max(256, wsb), dtype=torch.uint8, device=dev)
+
+    def align_base(self):
+        c = self.cfg
+        mb.mol_align_block_size(self.topk_ids, None, c.E, 1, c.block_m, self.b_sorted,
+                                self.b_expert, self.b_npp, self.b_ws)
+
+    def base_gemm(self, si: int, fused: bool):
+        """The stage's base grouped GEMM into out[si]; fused: with the LoRA delta (from this
+        stage's s, computed by shrink()) in its epilogue."""
+        c = self.cfg
+        st = c.stages[si]
+        kw = {}
+        if fused:
+            kw = dict(s=self.s[si], slices=st.slices, B=self.B[si], slot_scale=self.scale,
+                      lora_ids=self.lora_ids, topk=c.topk, num_slots=c.S,
+                      slot_ranks=self.slot_ranks)
+        mb.mol_moe_gemm(self.xin[si], self.row_div[si], self.W[si], self.b_sorted, self.b_expert,
+                        self.b_npp, c.numel, c.block_m, self.out[si], **kw)
+        return self.out[si]
+
     # ---------------------------------------------------------------------------- steps
     def align(self):
         c = self.cfg
