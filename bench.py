@@ -294,7 +294,7 @@ def copy_calibration(torch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for "
+        print(f"bench.py runs on one GPU: the path has no multi-GPU form (asked for "
               f"--gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     if os.environ.get("WORLD_SIZE", "1") not in ("", "1"):
