@@ -175,3 +175,42 @@ def test_combine_empty_batch():
     y = mb.mol_moe_combine(rows, ids, w, 8)
     assert y.shape == (0, 64)
     torch.cuda.synchronize()
+
+
+def test_combine_calls_replay_in_a_hip_graph():
+    """The layer, then the combine and the fused down expand + combine, captured in one
+    hipGraph: every replay (with eager work and syncs between) equals the eager result."""
+    cfg = configs.C1
+    inp = inputs.generate(cfg, seed=7)
+    w = inputs.topk_weights(cfg, 7)
+    dl = DeviceLayer(inp, topk_weights=w)
+    y_fused = torch.empty_like(dl.y)
+
+    def body():
+        dl.run()
+        dl.combine()
+        mb.mol_lora_expand_combine(dl.s[-1], dl.B[-1], dl.scale, dl.topk_ids, dl.lora_ids,
+                                   dl.topk_weights, cfg.E, cfg.S, dl.out[-1], y=y_fused)
+
+    for o in dl.out:
+        o.zero_()
+    body()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (*dl.out, dl.y, y_fused)]
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            body()
+    torch.cuda.current_stream().wait_stream(stream)
+    for rep in range(3):
+        for o in dl.out:
+            o.zero_()
+        dl.y.fill_(7.0)
+        y_fused.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((*dl.out, dl.y, y_fused), eager):
+            assert torch.equal(a, b), f"replay {rep}"

@@ -137,3 +137,57 @@ def test_fused_gemm_repeats_bit_identically():
         outs.append(out)
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1])
+
+
+def test_base_gemm_replays_in_a_hip_graph():
+    """The routing, the LoRA shrink and the fused base GEMM of a stage captured in one
+    hipGraph: every replay equals the eager result."""
+    cfg = _edge(name="graph", M=29)
+    dev = torch.device("cuda")
+    inp = inputs.generate(cfg, seed=8)
+    st, sin = cfg.stages[0], inp.stages[0]
+    topk = torch.from_numpy(inp.topk_ids).to(dev)
+    lora = torch.from_numpy(inp.lora_ids).to(dev)
+    scale = torch.from_numpy(inp.scale).to(dev)
+    nb = mb.mol_align_max_blocks(cfg.numel, cfg.V, cfg.block_m)
+    nbb = mb.mol_align_max_blocks(cfg.numel, cfg.E, cfg.block_m)
+    vrt = (torch.empty(nb * cfg.block_m, dtype=torch.int32, device=dev),
+           torch.empty(nb, dtype=torch.int32, device=dev),
+           torch.empty(1, dtype=torch.int32, device=dev))
+    brt = (torch.empty(nbb * cfg.block_m, dtype=torch.int32, device=dev),
+           torch.empty(nbb, dtype=torch.int32, device=dev),
+           torch.empty(1, dtype=torch.int32, device=dev))
+    xin = to_device(sin.xin, dev, True)
+    A = to_device(sin.A, dev, True)
+    B = to_device(sin.B, dev, True)
+    W = to_device(inputs.base_weights(cfg, 0, seed=8), dev, True)
+    s = torch.empty((cfg.numel, st.R), dtype=torch.float32, device=dev)
+    out = torch.zeros((cfg.numel, st.N), dtype=torch.bfloat16, device=dev)
+
+    def body():
+        mb.mol_align_block_size(topk, lora, cfg.E, cfg.S, cfg.block_m, *vrt)
+        mb.mol_align_block_size(topk, None, cfg.E, 1, cfg.block_m, *brt)
+        mb.mol_lora_shrink(xin, sin.row_div, A, *vrt, cfg.numel, cfg.V, cfg.block_m, s=s,
+                           slices=st.slices, num_experts=cfg.E)
+        mb.mol_moe_gemm(xin, sin.row_div, W, *brt, cfg.numel, cfg.block_m, out, s=s,
+                        slices=st.slices, B=B, slot_scale=scale, lora_ids=lora, topk=cfg.topk,
+                        num_slots=cfg.S)
+
+    out.fill_(3.0)  # rows of pairs without a local expert keep what they held
+    body()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            body()
+    torch.cuda.current_stream().wait_stream(stream)
+    for rep in range(3):
+        out.fill_(3.0)
+        s.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep}"
