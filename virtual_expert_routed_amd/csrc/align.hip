@@ -86,18 +86,6 @@ __device__ __forceinline__ int bm_round(const AlignArgs& a, int c) {
   return a.bm_shift >= 0 ? (c + a.BM - 1) & -a.BM : (c + a.BM - 1) / a.BM * a.BM;
 }
 
-// expert ids and padding entries of bucket b (c pairs at padded offset off), by `lanes`
-// cooperating threads starting at `first`.
-__device__ __forceinline__ void write_bucket_tail(const AlignArgs& a, int b, int c, int off,
-                                                  int first, int lanes) {
-  const int pc = bm_round(a, c);
-  const int eid = (b == a.V) ? -1 : b;
-  const int blk0 = bm_div(a, off);
-  const int nblk = bm_div(a, pc);
-  for (int j = first; j < nblk; j += lanes) a.expert_ids[blk0 + j] = eid;
-  for (int j = c + first; j < pc; j += lanes) a.sorted[off + j] = a.numel;
-}
-
 __global__ void __launch_bounds__(256) virtual_topk_kernel(const int32_t* __restrict__ topk,
                                                          const int32_t* __restrict__ lora,
                                                          int32_t numel, int32_t k, int32_t E,
@@ -369,8 +357,21 @@ __global__ void __launch_bounds__(256) align_scatter_kernel(AlignArgs a) {
   }
   if (t == 0 && tid == 0) *a.npp = total;
   __syncthreads();
+  // this tile's cursors: all of the thread's counter reads issued together
   const int32_t* row = a.counts + (int64_t)t * NB;
-  for (int b = tid; b < NB; b += 256) cur[b] = off[b] + row[b];
+  {
+    int rv[kScanBucketsPerThread];
+#pragma unroll
+    for (int k = 0; k < kScanBucketsPerThread; ++k) {
+      const int b = tid + 256 * k;
+      rv[k] = row[b < NB ? b : 0];
+    }
+#pragma unroll
+    for (int k = 0; k < kScanBucketsPerThread; ++k) {
+      const int b = tid + 256 * k;
+      if (b < NB) cur[b] = off[b] + rv[k];
+    }
+  }
   __syncthreads();
   if (wid == 0) {
     for (int c = begin; c < end; c += 64) {
@@ -386,9 +387,32 @@ __global__ void __launch_bounds__(256) align_scatter_kernel(AlignArgs a) {
       }
     }
   } else {
+    // expert ids and padding of this tile's share of the buckets: lane i of wave w takes
+    // bucket bb0 + 64 (w - 1) + i of each pass (its total read with the others, not one
+    // bucket after another), writes its expert ids, and the wave fills the padding of its
+    // buckets one after another with all lanes
     const int bb0 = (int)((int64_t)NB * t / a.ntiles);
     const int bb1 = (int)((int64_t)NB * (t + 1) / a.ntiles);
-    for (int b = bb0; b < bb1; ++b) write_bucket_tail(a, b, a.totals[b], off[b], tid - 64, 192);
+    for (int base = bb0 + 64 * (wid - 1); base < bb1; base += 192) {
+      const int b = base + lane;
+      const bool own = b < bb1;
+      const int c = own ? a.totals[b] : 0;
+      const int o = own ? off[b] : 0;
+      const int pc = bm_round(a, c);
+      if (own) {
+        const int eid = (b == a.V) ? -1 : b;
+        const int blk0 = bm_div(a, o), nblk = bm_div(a, pc);
+        for (int j = 0; j < nblk; ++j) a.expert_ids[blk0 + j] = eid;
+      }
+      uint64_t todo = wave_ballot(own && pc > c);
+      while (todo) {
+        const int src = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        const int from = __builtin_amdgcn_readlane(o + c, src);
+        const int cnt = __builtin_amdgcn_readlane(pc - c, src);
+        for (int j = lane; j < cnt; j += 64) a.sorted[from + j] = a.numel;
+      }
+    }
   }
 }
 
