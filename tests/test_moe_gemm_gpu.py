@@ -38,6 +38,18 @@ CASES = [
     _edge(name="ranked", slot_ranks=(16, 5, 0)),
     _edge(name="many_per_expert", M=200, E=4, topk=2, S=2, block_m=64),
     _edge(name="f32", dtype="f32", M=23, rank=4, E=5, S=2, stages=configs._two_stage(136, 40, 4)),
+    # the largest ranks the boundary accepts (256 bytes of one B row slice) at contraction
+    # lengths short enough that a column's lanes hold fewer rank vectors than the slice has:
+    # each lane must sum more than one vector of the rank (bf16 K = 256, r = 128; fp32 K =
+    # 128, r = 64), at full rank and with ranks that end inside a vector
+    _edge(name="rank128_bf16_k256", M=23, hidden=256, E=4, topk=2, S=2, rank=128,
+          stages=configs._two_stage(256, 256, 128)),
+    _edge(name="rank128_bf16_k256_ranked", M=23, hidden=256, E=4, topk=2, S=3, rank=128,
+          stages=configs._two_stage(256, 256, 128), slot_ranks=(128, 71, 0)),
+    _edge(name="rank64_f32_k128", dtype="f32", M=19, hidden=128, E=4, topk=2, S=2, rank=64,
+          stages=configs._two_stage(128, 128, 64)),
+    _edge(name="rank64_f32_k128_ranked", dtype="f32", M=19, hidden=128, E=4, topk=2, S=2,
+          rank=64, stages=configs._two_stage(128, 128, 64), slot_ranks=(37, 64)),
 ]
 
 

@@ -17,7 +17,7 @@
 // RPI consecutive output columns), each column's row of W_t read once with coalesced
 // 16-byte buffer loads by LPR lanes and reused for up to four pairs, the pairs' input
 // rows staged in LDS, the lanes' partial sums combined by a fixed xor tree. The fused
-// delta costs one more 16-byte B vector and two s vectors per lane and pair, loaded after
+// delta costs the B vectors and s values of each lane's share of the rank, loaded after
 // the weight loop, and each lane adds its part of the rank sum to its partial before the
 // tree: the delta needs no extra pass over the output and no extra write. (Measured at
 // decode on MI355X, this extra round trip per item costs more than a separate expand
@@ -57,8 +57,8 @@ __device__ __forceinline__ void gemm_group(const GemmArgs& g, int e, int rg, con
   // read up front; its vector operands (the B row slice and the s row slice a lane needs)
   // are loaded after the weight loop, two pairs per round trip, so the loop keeps close to
   // the register budget, and the occupancy, of the base GEMM alone. Lane lr takes 16-byte
-  // vector lr of its column's B row slice and the matching s values, and adds its share of
-  // the rank sum to its partial before the xor tree.
+  // vectors lr, lr + LPR, ... of its column's B row slice and the matching s values, and
+  // adds its share of the rank sum to its partial before the xor tree.
   int rlq[kPG], vq[kPG];
   float scq[kPG];
   if constexpr (FUSED) {
@@ -106,41 +106,53 @@ __device__ __forceinline__ void gemm_group(const GemmArgs& g, int e, int rg, con
   }
   if constexpr (FUSED) {
     const int r = g.R / g.slices;
-    const bool lane_r = n_ok && lr * VE < r;  // this lane holds part of the rank
     const int gs = n_ok ? n / (g.N / g.slices) : 0;
     const int64_t bbytes = (int64_t)g.N * r * ESZ;
+    // lane lr takes the 16-byte vectors lr, lr + LPR, ... of its column's B row slice (at
+    // most kMaxRankVecs of them, so NVL per lane) and the matching s values
+    constexpr int NVL = (kMaxRankVecs + LPR - 1) / LPR;
     // two pairs per round trip: at decode a block rarely holds more, and holding four
     // pairs' operands at once would cost the loop's occupancy
     constexpr int kEP = 2;
 #pragma unroll
     for (int h = 0; h < kPG; h += kEP) {
       if (h >= nq) break;  // uniform
-      uint4 bq[kEP];
-      float4 s0[kEP], s1[kEP];
+      uint4 bq[kEP][NVL];
+      float4 s0[kEP][NVL], s1[kEP][NVL];
 #pragma unroll
       for (int u = 0; u < kEP; ++u) {
         const int i = h + u;
-        const bool use = i < nq && lane_r && lr * VE < rlq[i];
         const __amdgpu_buffer_rsrc_t rb =
             expert_rsrc((const char*)g.B + (int64_t)vq[i] * bbytes, bbytes);
-        bq[u] = buf16(rb, use ? (uint32_t)(n * r * ESZ + lr * 16) : kOutOfRange);
         const int pq = i < nq ? (i == 0 ? p[0] : i == 1 ? p[1] : i == 2 ? p[2] : p[3]) : 0;
-        const float* sp = g.s + (int64_t)pq * g.R + gs * r + lr * VE;
-        s0[u] = use ? *reinterpret_cast<const float4*>(sp) : make_float4(0.f, 0.f, 0.f, 0.f);
-        s1[u] = BF16 && use ? *reinterpret_cast<const float4*>(sp + 4)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);  // fp32: 4 per vector
+#pragma unroll
+        for (int w = 0; w < NVL; ++w) {
+          const int vi = lr + w * LPR;  // vector of the B row slice
+          const bool use = i < nq && n_ok && vi * VE < rlq[i];
+          bq[u][w] = buf16(rb, use ? (uint32_t)(n * r * ESZ + vi * 16) : kOutOfRange);
+          const float* sp = g.s + (int64_t)pq * g.R + gs * r + vi * VE;
+          s0[u][w] = use ? *reinterpret_cast<const float4*>(sp) : make_float4(0.f, 0.f, 0.f, 0.f);
+          s1[u][w] = BF16 && use ? *reinterpret_cast<const float4*>(sp + 4)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);  // fp32: 4 per vector
+        }
       }
 #pragma unroll
       for (int u = 0; u < kEP; ++u) {
         const int i = h + u;
-        if (i < nq && rlq[i] > 0 && lane_r) {  // a slot with a delta; this lane holds a part
-          const float sv[8] = {s0[u].x, s0[u].y, s0[u].z, s0[u].w,
-                               s1[u].x, s1[u].y, s1[u].z, s1[u].w};
+        if (i >= nq || rlq[i] == 0 || !n_ok || lr * VE >= rlq[i]) continue;  // no part here
+        float d = 0.f;
+#pragma unroll
+        for (int w = 0; w < NVL; ++w) {
+          const int vi = lr + w * LPR;
+          if (vi * VE >= rlq[i]) break;
+          const float sv[8] = {s0[u][w].x, s0[u][w].y, s0[u][w].z, s0[u][w].w,
+                               s1[u][w].x, s1[u][w].y, s1[u][w].z, s1[u][w].w};
           // B vectors past the slot's rank read as zero; the one that straddles it is trimmed
-          const uint4 b = rlq[i] < (lr + 1) * VE ? keep_first<BF16>(bq[u], rlq[i] - lr * VE)
-                                                 : bq[u];
-          acc[i] = fmaf(scq[i], dot16_s<BF16>(b, sv, 0.f), acc[i]);
+          const uint4 b = rlq[i] < (vi + 1) * VE ? keep_first<BF16>(bq[u][w], rlq[i] - vi * VE)
+                                                 : bq[u][w];
+          d = dot16_s<BF16>(b, sv, d);
         }
+        acc[i] = fmaf(scq[i], d, acc[i]);
       }
     }
   }

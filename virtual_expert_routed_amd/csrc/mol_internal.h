@@ -11,6 +11,7 @@ constexpr int kAlignSmallMax = 4096;  // pairs the one-workgroup align handles
 constexpr int kShrinkItemBytes = 32768;  // target weight bytes per shrink work item
 constexpr int kMfmaMinPairs = 4;         // a block takes the MFMA path from this many pairs
 constexpr int kMfmaMinNumel = 4096;      // MFMA kernels are launched from this many pairs
+constexpr int kMaxRankVecs = 16;         // 16-byte vectors in one rank row slice (256 bytes)
 
 struct AlignArgs {
   const int32_t* ids;
