@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from tests import pins
+from tests import pins, shared
 from virtual_expert_routed_amd import binding as mb
 from virtual_expert_routed_amd import configs, inputs
 from virtual_expert_routed_amd.layer import DeviceLayer, to_device
@@ -157,6 +157,73 @@ def test_fused_and_chained_from_nonzero_base(cfg):
         assert np.all(np.isfinite(got)), what
         b = bound + (chain_extra if fn is None else 0.0)
         assert np.all(np.abs(got - ref) <= b), f"{cfg.name} {what}"
+
+
+FULL = [configs.C3, configs.C4]
+
+
+@pytest.mark.parametrize("cfg", FULL, ids=[c.name for c in FULL])
+def test_combine_full_size(cfg):
+    """mol_moe_combine over every token of a full-size prefill layer: within one unit of the
+    oracle everywhere, within half a unit of the exact weighted sum on a seeded sample of
+    tokens, and never reading the rows of pairs without a local expert (NaN here)."""
+    print(f"[combine full size] {cfg.name}", flush=True)
+    inp = inputs.generate(cfg, seed=0, tensors=False)
+    si = len(cfg.stages) - 1
+    rows = inputs.base_out(cfg, si, seed=3)
+    off = ~_local(cfg, inp.topk_ids)
+    rows[off] = np.uint16(0x7FC0)
+    w = inputs.topk_weights(cfg, 3)
+    ref = _f64(oracle.moe_combine(rows, inp.topk_ids, w, cfg.E), cfg)
+    dev = torch.device("cuda")
+    y = mb.mol_moe_combine(to_device(rows, dev, True), torch.from_numpy(inp.topk_ids).to(dev),
+                           torch.from_numpy(w).to(dev), cfg.E)
+    got = _f64(_host(y, cfg), cfg)
+    del y
+    assert np.all(np.isfinite(got))
+    half = 2.0 ** -8
+    assert np.all(np.abs(got - ref) <= 4 * half * np.abs(ref) + 1e-6)
+    tok = np.sort(np.random.default_rng(1).choice(cfg.M, size=512, replace=False))
+    r3 = rows.reshape(cfg.M, cfg.topk, -1)[tok]
+    o3 = off.reshape(cfg.M, cfg.topk)[tok]
+    exact = np.matmul(w[tok].astype(np.float64)[:, None, :],
+                      np.where(o3[:, :, None], 0.0, _f64(r3, cfg)))[:, 0]
+    assert np.all(np.abs(got[tok] - exact) <= half * np.abs(exact) + 1e-6)
+
+
+@pytest.mark.parametrize("cfg", FULL, ids=[c.name for c in FULL])
+def test_fused_and_chained_full_size_sampled(cfg):
+    """The down expand fused with the combine, and the unfused chain, on a full-size prefill
+    layer from zero base rows: the whole layer runs on the GPU, and a seeded sample of 256
+    tokens is compared with the oracle, which computes each token from its own pairs only."""
+    print(f"[expand_combine full size] {cfg.name}", flush=True)
+    inp = shared.generate(cfg, 0)
+    si = len(cfg.stages) - 1
+    st, sin = cfg.stages[si], inp.stages[si]
+    w = inputs.topk_weights(cfg, 0)
+    tok = np.sort(np.random.default_rng(2).choice(cfg.M, size=256, replace=False))
+    pairs = (tok[:, None] * cfg.topk + np.arange(cfg.topk)[None, :]).reshape(-1)
+    mask = np.zeros(cfg.numel, np.uint8)
+    mask[pairs] = 1
+    srt, eid, npp = oracle.align_block_size(inp.topk_ids, inp.lora_ids, cfg.E, cfg.S,
+                                            cfg.block_m)
+    s_ref = oracle.lora_shrink(sin.xin, sin.row_div, sin.A, srt, eid, npp, cfg.numel,
+                               cfg.block_m, pair_mask=mask, slot_ranks=inp.slot_ranks, E=cfg.E)
+    zero = np.zeros((tok.size * cfg.topk, st.N), dtype=np.uint16)
+    ref = _f64(oracle.lora_expand_combine(np.nan_to_num(s_ref[pairs]), sin.B, inp.scale,
+                                          inp.topk_ids[tok], inp.lora_ids[tok], w[tok], cfg.E,
+                                          cfg.S, zero, slot_ranks=inp.slot_ranks), cfg)
+    dl = DeviceLayer(inp, topk_weights=w)
+    dl.align()
+    dl.shrink(si)
+    fused = _f64(_host(dl.expand_combine(), cfg), cfg)[tok]
+    _check_tol(fused, ref, f"{cfg.name} fused (sampled tokens)")
+    assert not torch.any(dl.out[si]), "the fused call never writes the pair rows"
+    dl.expand(si)
+    chained = _f64(_host(dl.combine(), cfg), cfg)[tok]
+    _check_tol(chained, ref, f"{cfg.name} expand then combine (sampled tokens)")
+    del dl
+    torch.cuda.synchronize()
 
 
 def _check_tol(gpu, ref, what):

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from tests import pins
+from tests import pins, shared
 from virtual_expert_routed_amd import binding as mb
 from virtual_expert_routed_amd import configs, inputs
 from virtual_expert_routed_amd.layer import DeviceLayer
@@ -36,15 +36,31 @@ def as_f64(a, cfg):
     return pins.bf16_bits_to_f64(a) if cfg.dtype == "bf16" else np.asarray(a, np.float64)
 
 
-def sample_mask(cfg, routing, n=768, seed=0):
-    """Seeded sample of pairs plus every pair of the fullest block and the last block."""
+def sample_mask(cfg, routing, n=768, seed=0, hot=16):
+    """Pairs the oracle computes one by one at full size: a seeded sample of n pairs; one
+    pair, at a seeded position, of every block that holds real pairs (so every block of the
+    routing is compared); every pair of the first and the last block of each of the `hot`
+    fullest buckets (so every hot virtual expert's full tile and its ragged tail are
+    compared whole); and every pair of the last block."""
     srt, eid, npp = routing
     rng = np.random.default_rng(seed)
     mask = np.zeros(cfg.numel, np.uint8)
     mask[rng.choice(cfg.numel, size=min(n, cfg.numel), replace=False)] = 1
     blocks = srt.reshape(-1, cfg.block_m)
     fill = (blocks < cfg.numel).sum(1)
-    for b in (int(np.argmax(fill)), len(blocks) - 1):
+    nz = np.nonzero(fill)[0]
+    pick = np.minimum((rng.random(nz.size) * fill[nz]).astype(np.int64), fill[nz] - 1)
+    mask[blocks[nz, pick]] = 1
+    whole = [len(blocks) - 1]
+    valid = eid >= 0
+    if valid.any():
+        per_bucket = np.bincount(eid[valid], weights=fill[valid], minlength=cfg.V)
+        for b in np.argsort(-per_bucket, kind="stable")[:hot]:
+            if per_bucket[b] == 0:
+                break
+            idx = np.nonzero(eid == b)[0]
+            whole += [int(idx[0]), int(idx[-1])]
+    for b in whole:
         rows = blocks[b][blocks[b] < cfg.numel]
         mask[rows] = 1
     return mask
@@ -54,7 +70,7 @@ class Case:
     def __init__(self, cfg, seed=0, sampled=False):
         oracle.build()
         self.cfg = cfg
-        self.inp = inputs.generate(cfg, seed)
+        self.inp = shared.generate(cfg, seed)
         self.routing = oracle.align_block_size(self.inp.topk_ids, self.inp.lora_ids, cfg.E,
                                                cfg.S, cfg.block_m)
         self.mask = sample_mask(cfg, self.routing) if sampled else None
@@ -81,8 +97,11 @@ _cache = {}
 
 def get_case(cfg):
     if cfg.name not in _cache:
-        _cache.clear()   # keep one big case in host memory at a time
-        _cache[cfg.name] = Case(cfg, sampled=cfg.numel > 4096)
+        big = cfg.numel > 4096
+        if big:  # keep one big case in host memory at a time
+            for k in [k for k, c in _cache.items() if c.cfg.numel > 4096]:
+                del _cache[k]
+        _cache[cfg.name] = Case(cfg, sampled=big)
     return _cache[cfg.name]
 
 
@@ -153,9 +172,22 @@ def test_repeat_runs_are_bit_identical(cfg):
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("cfg", [configs.C0, configs.C1], ids=IDS[:2])
+def _nonzero_base_case(cfg):
+    return get_case(cfg) if cfg.name in IDS else Case(cfg)
+
+
+def _nonzero_base_cfgs():
+    by = {c.name: c for c in EDGE}
+    return [configs.C0, configs.C1, by["mfma_blocks"], by["ranked_mfma"], by["mfma_r64_zipf"],
+            configs.C4]
+
+
 def test_delta_adds_into_nonzero_output(cfg):
-    case = get_case(cfg)
+    """The delta added into nonzero output rows (out read, added to and rounded once), on
+    the VALU kernels (C0, C1) and on the MFMA expand's read-add-round of old values (the
+    MFMA edge shapes and the full-size C4 layer, sampled as in the parity test)."""
+    announce(f"[nonzero base] {cfg.name}")
+    case = _nonzero_base_case(cfg)
     base = [inputs.base_out(cfg, si, seed=5) for si in range(len(cfg.stages))]
     dl = DeviceLayer(case.inp, outs=base)
     dl.run()
@@ -164,15 +196,19 @@ def test_delta_adds_into_nonzero_output(cfg):
         sin = case.inp.stages[si]
         ref = base[si].copy()
         oracle.lora_expand(case.s[si], st.slices, sin.B, case.inp.scale, cfg.E, srt, eid, npp,
-                           cfg.numel, cfg.block_m, ref)
+                           cfg.numel, cfg.block_m, ref, pair_mask=case.mask,
+                           slot_ranks=case.inp.slot_ranks)
         got = dl.out_host(si)
         assert np.array_equal(got[case.no_delta], base[si][case.no_delta])
-        b64 = as_f64(base[si], cfg)[case.rows]
-        g64, r64 = as_f64(got, cfg)[case.rows], as_f64(ref, cfg)[case.rows]
+        b64 = as_f64(base[si][case.rows], cfg)
+        g64, r64 = as_f64(got[case.rows], cfg), as_f64(ref[case.rows], cfg)
+        del got, ref
         d_ref = r64 - b64
         ulp = np.abs(b64) * 2.0 ** -7 if cfg.dtype == "bf16" else np.abs(b64) * 2.0 ** -23
         bound = REL * np.max(np.abs(d_ref)) + ABS + ulp
         assert np.all(np.abs(g64 - r64) <= bound), f"{cfg.name}/{st.name}"
+    del dl
+    torch.cuda.synchronize()
 
 
 def _edge_cfg(**kw):
@@ -228,6 +264,11 @@ EDGE = [
               stages=configs._two_stage(264, 136, 32), block_m=64, sentinel_count=10,
               nolora_count=10),
 ]
+
+
+test_delta_adds_into_nonzero_output = pytest.mark.parametrize(
+    "cfg", _nonzero_base_cfgs(), ids=[c.name for c in _nonzero_base_cfgs()])(
+    test_delta_adds_into_nonzero_output)
 
 
 @pytest.mark.parametrize("cfg", EDGE, ids=[c.name for c in EDGE])
