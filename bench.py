@@ -47,7 +47,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle sample budget (0 = skip the CPU baseline)")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run a 1 GiB elementwise copy (counter calibration)")
+                    help="accepted for older profile commands: the 2 GiB copy that measures "
+                         "the achievable peak (and calibrates the counters) always runs")
+    ap.add_argument("--no-floor", action="store_true",
+                    help="skip the read-only streaming probe at the delta kernels' shapes")
     return ap.parse_args()
 
 
@@ -273,22 +276,114 @@ def measured_traffic(workload, kernel):
     return float(fields["traffic_bytes_per_launch"]), os.path.relpath(path, ROOT)
 
 
-def copy_calibration(torch):
-    """An elementwise copy (negation) of 1 GiB of fp32, three launches: the known-size
-    kernel the FETCH_SIZE and WRITE_SIZE counters are scaled by."""
-    n = (1 << 30) // 4
+def copy_calibration(torch, gib=2, launches=5):
+    """An elementwise copy (negation) of `gib` GiB of fp32 into another `gib` GiB, several
+    launches back to back: the measured peak for a kernel that reads and writes HBM, and
+    the known-size kernel the FETCH_SIZE and WRITE_SIZE counters are scaled by."""
+    n = (gib << 30) // 4
     src = torch.randn(n, device="cuda")
     dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(3):
+    times = []
+    for _ in range(launches):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
         torch.neg(src, out=dst)
-    b.record()
+        b.record()
+        times.append((a, b))
     torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1e3 / 3
-    return {"kernel": "torch.neg fp32 1 GiB -> 1 GiB", "bytes_read": n * 4,
-            "bytes_written": n * 4, "us": us, "GB/s": 2 * n * 4 / (us * 1e-6) / 1e9}
+    us = [a.elapsed_time(b) * 1e3 for a, b in times]
+    best = min(us)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"kernel": f"torch.neg fp32 {gib} GiB -> {gib} GiB", "bytes_read": n * 4,
+            "bytes_written": n * 4, "launches": launches, "us_best": best,
+            "us_median": float(np.median(us)), "GB/s": 2 * n * 4 / (best * 1e-6) / 1e9}
+
+
+def read_floor(cfg, kernels, grid, layers, torch, reps=20):
+    """The read-only streaming probe (libmolcalib.so) at the shapes of the delta's launches:
+    for each launch, as many 256-thread workgroups as the kernel has live work items, each
+    reading one chunk of (the launch's algorithmic bytes / items) after one dependent index
+    load, with no arithmetic and no stores. Every launch of a rotation of `layers` layers reads
+    its own random chunks of a 4 GiB buffer, so none is served from the memory-side cache.
+    Timed as graph replays: each shape alone (back to back over the layers), and the launches
+    of one layer in dependency order (the delta's chain of kernels), per layer."""
+    import ctypes
+    from virtual_expert_routed_amd import build as hb
+    lib = ctypes.CDLL(hb.CALIB_LIB)
+    fn = lib.molcal_read_chunks
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    shapes = []
+    for k in kernels:
+        items = max(1, int(round(grid[k["label"]]["live_blocks_items"])))
+        chunk = max(16, int(round(k["bytes"] / items / 16)) * 16)
+        shapes.append((k["label"], items, chunk))
+    buf_bytes = 4 << 30
+    per_layer = sum(n * c for _, n, c in shapes)
+    L = min(layers, int(buf_bytes / (1.5 * per_layer)))
+    if L < 1:
+        return {"skipped": f"one layer's launches read {per_layer / 1e9:.2f} GB, more than "
+                           f"the probe's {buf_bytes >> 30} GiB buffer holds with slack"}
+    dev = torch.device("cuda")
+    buf = torch.full((buf_bytes // 4,), 0x01010101, dtype=torch.int32, device=dev)
+    sink = torch.zeros(max(n for _, n, _ in shapes), dtype=torch.int32, device=dev)
+    rng = np.random.default_rng(12345)
+    idx = []  # idx[l][j]: chunk indices (in units of its chunk size) of launch j of layer l
+    off = 0
+    for l in range(L):
+        row = []
+        for _, n, c in shapes:
+            region = int(1.5 * n * c) // c  # chunk slots of this launch's own region
+            pick = rng.choice(region, size=n, replace=False) + off // c
+            row.append(torch.from_numpy(pick.astype(np.int32)).to(dev))
+            off += region * c
+        idx.append(row)
+
+    def launch(l, j):
+        _, n, c = shapes[j]
+        rc = fn(buf.data_ptr(), buf_bytes, idx[l][j].data_ptr(), n, c, sink.data_ptr(),
+                torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"molcal_read_chunks: {rc}")
+
+    def graph_time(body, per):
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=st):
+                body()
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (reps * per)
+
+    res = {"layers": L, "launches": []}
+    for j, (label, n, c) in enumerate(shapes):
+        us = graph_time(lambda j=j: [launch(l, j) for l in range(L)], L)
+        res["launches"].append({"label": label, "workgroups": n, "chunk_bytes": c,
+                                "us": us, "GB/s": n * c / (us * 1e-6) / 1e9})
+    res["chain_us_per_layer"] = graph_time(
+        lambda: [launch(l, j) for l in range(L) for j in range(len(shapes))], L)
+    res["chain_bytes"] = per_layer
+    res["how"] = ("read-only probe (libmolcalib.so): one 256-thread workgroup per live work "
+                  "item, one dependent index load, then its chunk with 16-byte loads; graph "
+                  f"replays over {L} layers' disjoint random chunks of a 4 GiB buffer")
+    del buf, sink
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -312,9 +407,10 @@ def main():
     L = max(1, args.layers)
 
     log(f"[bench] generating {L} layers of {cfg.name}")
-    host_inputs, layers = [], []
+    host_inputs, layers, input_hashes = [], [], []
     for l in range(L):
         inp = inputs.generate(cfg, seed=l)
+        input_hashes.append(inputs.sha256(inp))
         base = [inputs.base_out(cfg, si, seed=l) for si in range(len(cfg.stages))]
         layers.append(DeviceLayer(inp, device=dev, outs=base,
                                   topk_weights=inputs.topk_weights(cfg, l)))
@@ -411,7 +507,7 @@ def main():
     # spread of the layer time: HIP events around single replays of the rotation graph (or
     # single eager steps), outside the timed region
     dist = []
-    nd = max(1, min(64, K // L if graphs is not None else K))
+    nd = max(32, min(64, K // L if graphs is not None else K))
     for i in range(nd):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -515,6 +611,7 @@ def main():
             "block_m": cfg.block_m, "layers_rotated": L, "mode": args.mode,
             "accumulate": "fp32",
         },
+        "inputs_sha256": input_hashes,
         "us_per_layer": ms_per_step * 1e3,
         "us_per_layer_gpu_events": gpu_elapsed / K * 1e6,
         "us_per_layer_dist": {
@@ -577,8 +674,20 @@ def main():
         "fused_GB/s": fb / (fused_us * 1e-6) / 1e9 if fused_timed else None,
         "fused_hbm_frac": fb / (fused_us * 1e-6) / 1e9 / HBM_PEAK_GBS if fused_timed else None,
     }
-    if args.calibrate_copy:
-        result["copy_calibration"] = copy_calibration(torch)
+    # the achievable peak on this machine: a 2 GiB -> 2 GiB elementwise copy, beside the spec
+    cp = copy_calibration(torch)
+    result["copy_calibration"] = cp
+    result["roofline"]["measured_peak"] = cp["GB/s"]
+    result["roofline"]["measured_peak_source"] = cp["kernel"] + " (best of %d)" % cp["launches"]
+    result["roofline"]["frac_of_measured_peak"] = achieved / cp["GB/s"]
+    result["delta_graph_frac_of_measured_peak"] = (
+        delta_bytes / (delta_graph_us * 1e-6) / 1e9 / cp["GB/s"] if delta_graph_us else None)
+    if not args.no_floor:
+        log("[bench] read-only probe at the delta launches' shapes")
+        fl = read_floor(cfg, kernels, result["grid_workgroups"], L, torch)
+        if "chain_us_per_layer" in fl and delta_graph_us:
+            fl["delta_graph_us_over_chain"] = delta_graph_us / fl["chain_us_per_layer"]
+        result["read_floor"] = fl
 
     if args.cpu_seconds > 0:
         import oracle

@@ -3,7 +3,7 @@
     python -m virtual_expert_routed_amd.build
 
 Compiles every csrc/*.hip with hipcc in parallel, links the shared library next to this
-file, then lists the code objects embedded in it and fails unless a gfx950 one is there
+file (and, apart from it, the benchmark's read-only streaming probe libmolcalib.so), then lists the code objects embedded in it and fails unless a gfx950 one is there
 (a build that silently drops the target architecture still "succeeds" otherwise).
 """
 from __future__ import annotations
@@ -18,6 +18,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmol.so")
+# the benchmark's read-only streaming probe, a library of its own (not part of libmol)
+CALIB_SRC = os.path.join(PKG, "calib", "read_probe.hip")
+CALIB_LIB = os.path.join(PKG, "libmolcalib.so")
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -54,10 +57,16 @@ def code_objects(path: str = LIB) -> list:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
+    srcs = sources() + [CALIB_SRC]
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+    calib_obj = objs.pop()
+    _link([calib_obj], CALIB_LIB, verbose=False)
+    return _link(objs, LIB, verbose)
+
+
+def _link(objs: list, lib_path: str, verbose: bool) -> str:
+    tmp = lib_path + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -65,12 +74,12 @@ def build(verbose: bool = True) -> str:
     objs_listed = code_objects(tmp)
     if not any(ARCH in ln for ln in objs_listed):
         raise RuntimeError(f"{tmp} carries no {ARCH} code object: {objs_listed}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB} ({os.path.getsize(LIB)} bytes); code objects:")
+        print(f"built {lib_path} ({os.path.getsize(lib_path)} bytes); code objects:")
         for ln in objs_listed:
             print("   ", ln)
-    return LIB
+    return lib_path
 
 
 if __name__ == "__main__":

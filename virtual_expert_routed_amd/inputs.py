@@ -186,3 +186,24 @@ def base_weights(cfg: LayerConfig, stage_index: int, seed: int) -> np.ndarray:
     st = cfg.stages[stage_index]
     rng = np.random.default_rng([seed, 3000 + stage_index])
     return _normals(rng, (cfg.E, st.N, st.K), cfg.w_sigma, cfg.dtype)
+
+
+def sha256(inp: LayerInputs) -> str:
+    """SHA-256 over every array of one layer's inputs, in a fixed order (routing ids, slot
+    scales and ranks, x, then per stage its input rows, A and B), so a run's results can
+    name exactly the data they were measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    arrays = [inp.topk_ids, inp.lora_ids, inp.scale]
+    if inp.slot_ranks is not None:
+        arrays.append(inp.slot_ranks)
+    if inp.x is not None:
+        arrays.append(inp.x)
+    for st in inp.stages:
+        arrays += [st.xin, st.A, st.B]
+    for a in arrays:
+        a = np.ascontiguousarray(a)
+        h.update(str((a.dtype.str, a.shape)).encode())
+        h.update(memoryview(a).cast("B"))
+    return h.hexdigest()
+
