@@ -67,12 +67,14 @@ enum { MOL_F32 = 0, MOL_BF16 = 1 };
 #define MOL_MAX_BLOCK_M 1024
 /* expand: r * sizeof(elem) <= 256 bytes (rank <= 128 in bf16, <= 64 in fp32) */
 #define MOL_MAX_RANK_BYTES 256
+/* floats of the library's own per-GPU scratch behind mol_lora_delta_noalloc (16 MiB) */
+#define MOL_DELTA_SCRATCH_FLOATS (4 * 1024 * 1024)
 
 /* (host) Static description of a status code. Never NULL. */
 MOL_API const char *mol_status_string(mol_status status);
 
-/* (host) ABI version of this header, 4 (2 added the per-slot ranks, 3 the combine, 4 the
- * base grouped GEMM with the fused delta). */
+/* (host) ABI version of this header, 5 (2 added the per-slot ranks, 3 the combine, 4 the
+ * base grouped GEMM with the fused delta, 5 the allocation-free stage delta). */
 MOL_API int32_t mol_abi_version(void);
 
 /* ---------------------------------------------------------------------------------
@@ -208,6 +210,28 @@ MOL_API mol_status mol_lora_delta(int32_t dtype, const void *xin, int64_t ld_x,
                                   int32_t numel, int32_t num_virtual, int32_t block_m,
                                   void *out, int64_t ld_out, void *workspace,
                                   size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * mol_lora_delta_noalloc - mol_lora_delta for callers that cannot allocate device memory
+ * (code under hipGraph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same checks, kernels and results (bit-identical), but s lives in a scratch array that the
+ * library itself holds on each GPU, so no workspace is passed and nothing is allocated.
+ *   Limit: numel * R <= MOL_DELTA_SCRATCH_FLOATS (16 MiB of float32), else MOL_E_LIMIT
+ *          before anything is enqueued. The scratch needs no initial contents.
+ *   Every call on one GPU shares that GPU's scratch and leaves its contents behind: calls
+ *   that may overlap on one GPU (other streams, other threads) race and must not be made.
+ *   The first call on a device looks up the scratch's address there (no allocation); a
+ *   failure of that lookup returns MOL_E_HIP. Other errors as for mol_lora_delta.
+ * ------------------------------------------------------------------------------- */
+MOL_API mol_status mol_lora_delta_noalloc(int32_t dtype, const void *xin, int64_t ld_x,
+                                          int32_t row_div, const void *A, int32_t R,
+                                          int32_t K, int32_t slices, const void *B, int32_t N,
+                                          const float *slot_scale, const int32_t *slot_ranks,
+                                          int32_t num_experts, const int32_t *sorted_ids,
+                                          const int32_t *expert_ids,
+                                          const int32_t *num_post_padded, int32_t numel,
+                                          int32_t num_virtual, int32_t block_m, void *out,
+                                          int64_t ld_out, void *stream);
 
 /* ---------------------------------------------------------------------------------
  * mol_moe_gemm - the base MoE grouped GEMM of a stage, with the LoRA delta optionally fused

@@ -39,7 +39,7 @@ def test_only_mol_symbols_exported():
 
 def test_version_and_status_strings():
     L = mb.lib()
-    assert L.mol_abi_version() == 4
+    assert L.mol_abi_version() == 5
     for code in range(7):
         assert mb.status_string(code)
     assert mb.status_string(99) == "unknown status"
@@ -143,6 +143,24 @@ def test_shrink_expand_delta_reject_before_launch():
     # numel == 0 is a no-op
     assert L.mol_lora_delta(mb.MOL_BF16, None, 64, 1, None, 16, 64, 1, None, 32, None, None, 4,
                             None, None, None, 0, 8, 16, None, 32, None, 0, None) == mb.MOL_OK
+
+
+def test_noalloc_delta_rejects_before_launch():
+    L = mb.lib()
+
+    def noalloc(numel=16, R=16, K=64, out=FAKE, dtype=mb.MOL_BF16):
+        return L.mol_lora_delta_noalloc(dtype, FAKE, K, 1, FAKE, R, K, 1, FAKE, 32, FAKE, None,
+                                        4, FAKE, FAKE, FAKE, numel, 8, 16, out, 32, None)
+
+    # s of numel * R floats must fit the library's scratch
+    assert noalloc(numel=mb.MOL_DELTA_SCRATCH_FLOATS // 16 + 1) == mb.MOL_E_LIMIT
+    assert noalloc(dtype=6) == mb.MOL_E_DTYPE
+    assert noalloc(out=None) == mb.MOL_E_ARG
+    assert noalloc(K=60) == mb.MOL_E_ALIGN
+    assert noalloc(numel=0) == mb.MOL_OK  # a no-op: nothing looked up, nothing enqueued
+    text = open(HEADER).read()
+    assert f"#define MOL_DELTA_SCRATCH_FLOATS (4 * 1024 * 1024)" in text
+    assert mb.MOL_DELTA_SCRATCH_FLOATS == 4 * 1024 * 1024
 
 
 def test_library_is_built_for_gfx950():

@@ -36,6 +36,8 @@ SIGNATURES = {
     "mol_delta_workspace_bytes": (_I64, [_I32, _I32, _I32, _I32]),
     "mol_lora_delta": (_I32, [_I32, _P, _I64, _I32, _P, _I32, _I32, _I32, _P, _I32, _P, _P,
                               _I32, _P, _P, _P, _I32, _I32, _I32, _P, _I64, _P, _SZ, _P]),
+    "mol_lora_delta_noalloc": (_I32, [_I32, _P, _I64, _I32, _P, _I32, _I32, _I32, _P, _I32, _P,
+                                      _P, _I32, _P, _P, _P, _I32, _I32, _I32, _P, _I64, _P]),
     "mol_moe_gemm": (_I32, [_I32, _P, _I64, _I32, _P, _I32, _I32, _I32, _P, _P, _P, _I32, _I32,
                             _P, _I64, _P, _I32, _I32, _P, _P, _P, _P, _I32, _I32, _P]),
     "mol_moe_combine": (_I32, [_I32, _P, _I64, _P, _P, _I32, _I32, _I32, _I32, _P, _I64, _P]),
@@ -238,6 +240,32 @@ def mol_lora_delta(xin, row_div: int, A, slices: int, B, slot_scale, num_experts
         _ptr(num_post_padded), numel, num_virtual, block_m, _ptr(out), out.stride(0),
         _ptr(workspace), workspace.numel(), _stream(A)))
     return out
+
+
+def mol_lora_delta_noalloc(xin, row_div: int, A, slices: int, B, slot_scale, num_experts: int,
+                           sorted_ids, expert_ids, num_post_padded, numel: int,
+                           num_virtual: int, block_m: int, out, slot_ranks=None):
+    """mol_lora_delta with s in the library's own per-GPU scratch: no workspace argument and
+    nothing allocated (numel * R <= MOL_DELTA_SCRATCH_FLOATS; calls that overlap on one
+    GPU race)."""
+    _need(xin, "xin", contiguous=False)
+    _need(A, "A")
+    _need(B, "B")
+    _need(slot_scale, "slot_scale", torch.float32)
+    _need(out, "out", B.dtype, contiguous=False)
+    if xin.stride(1) != 1 or out.stride(1) != 1:
+        raise ValueError("xin and out rows must be contiguous")
+    V, R, K = A.shape
+    _, N, r = B.shape
+    _check("mol_lora_delta_noalloc", lib().mol_lora_delta_noalloc(
+        _dtype_code(A), _ptr(xin), xin.stride(0), row_div, _ptr(A), R, K, slices, _ptr(B), N,
+        _ptr(slot_scale), _ranks(slot_ranks), num_experts, _ptr(sorted_ids), _ptr(expert_ids),
+        _ptr(num_post_padded), numel, num_virtual, block_m, _ptr(out), out.stride(0),
+        _stream(A)))
+    return out
+
+
+MOL_DELTA_SCRATCH_FLOATS = 4 * 1024 * 1024
 
 
 def mol_moe_combine(rows, topk_ids, topk_weights, num_experts: int, y=None):

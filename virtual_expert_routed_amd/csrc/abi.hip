@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <atomic>
 #include <limits>
+#include <mutex>
 
 #include "mol_internal.h"
 
@@ -145,7 +146,7 @@ MOL_API const char* mol_status_string(mol_status status) {
   }
 }
 
-MOL_API int32_t mol_abi_version(void) { return 4; }
+MOL_API int32_t mol_abi_version(void) { return 5; }
 
 MOL_API mol_status mol_virtual_topk(const int32_t* topk_ids, const int32_t* lora_ids,
                                     int32_t M, int32_t topk, int32_t num_experts,
@@ -279,6 +280,88 @@ hipError_t expand_all(mol::DeltaArgs a, bool bf16, int64_t grid, int32_t mfma_mi
   return mol::launch_expand_mfma(a, (int)grid, st);
 }
 
+// Scratch of mol_lora_delta_noalloc: the fp32 rank-space rows s of one stage live here
+// instead of in a caller's workspace. Each GPU holds its own copy of this array, at its own
+// address, until the process ends. On the host its name stands for the symbol only: the
+// device address is taken with hipGetSymbolAddress once per device and kept below.
+__device__ __align__(256) float scratch[MOL_DELTA_SCRATCH_FLOATS];
+
+std::atomic<float*> g_scratch[64];  // device address of `scratch`, per device
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch` (looked up on the first call on a device).
+mol_status delta_scratch(float** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOL_E_HIP;
+  float* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* q = nullptr;
+      if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return MOL_E_HIP;
+      p = static_cast<float*>(q);
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MOL_OK;
+}
+
+// Host checks of a stage delta call (every argument but the workspace).
+mol_status delta_check(int32_t dtype, const void* xin, int64_t ld_x, int32_t row_div,
+                       const void* A, int32_t R, int32_t K, int32_t slices, const void* B,
+                       int32_t N, const float* slot_scale, int32_t num_experts,
+                       const int32_t* sorted_ids, const int32_t* expert_ids,
+                       const int32_t* num_post_padded, int32_t numel, int32_t num_virtual,
+                       int32_t block_m, const void* out, int64_t ld_out) {
+  const StageCheck rc =
+      routing_check(sorted_ids, expert_ids, num_post_padded, numel, num_virtual, block_m);
+  if (rc.st != MOL_OK) return rc.st;
+  alignas(16) float s_probe[4] = {};  // s is checked by the caller
+  mol_status c = shrink_check(dtype, xin, ld_x, row_div, A, R, K, numel, s_probe);
+  if (c != MOL_OK) return c;
+  c = expand_check(dtype, R, slices, B, N, slot_scale, num_experts, num_virtual, numel, out,
+                   ld_out);
+  if (c != MOL_OK) return c;
+  const bool bf16 = dtype == MOL_BF16;
+  const int esz = bf16 ? 2 : 4;
+  const int64_t mb = rc.max_blocks;
+  if (mb * cdiv64(R, mol::shrink_rows_per_item(K, esz)) > kI32Max ||
+      mb * cdiv64(N, mol::expand_cols_per_item(R, slices, esz)) > kI32Max)
+    return MOL_E_LIMIT;
+  if (shrink_mfma_min(bf16, numel, num_virtual, block_m) > 0 && mb * cdiv64(R, 64) > kI32Max)
+    return MOL_E_LIMIT;
+  return MOL_OK;
+}
+
+// Enqueue a checked stage delta with s at `s` (16-byte aligned, numel * R floats).
+mol_status delta_enqueue(int32_t dtype, const void* xin, int64_t ld_x, int32_t row_div,
+                         const void* A, int32_t R, int32_t K, int32_t slices, const void* B,
+                         int32_t N, const float* slot_scale, const int32_t* slot_ranks,
+                         int32_t num_experts, const int32_t* sorted_ids,
+                         const int32_t* expert_ids, const int32_t* num_post_padded,
+                         int32_t numel, int32_t num_virtual, int32_t block_m, void* out,
+                         int64_t ld_out, float* s, hipStream_t st) {
+  const bool bf16 = dtype == MOL_BF16;
+  const int esz = bf16 ? 2 : 4;
+  const int64_t mb = max_blocks_of(numel, num_virtual, block_m);
+  const int rpi = mol::shrink_rows_per_item(K, esz);
+  mol::DeltaArgs a = make_delta_args(xin, ld_x, row_div, A, R, K, slices, B, N, slot_scale,
+                                     num_experts, sorted_ids, expert_ids, num_post_padded,
+                                     numel, num_virtual, block_m, s, out, ld_out, mb);
+  a.ranks = slot_ranks;
+  a.rgroups = (int32_t)cdiv64(R, rpi);
+  a.nchunk = (int32_t)cdiv64(N, mol::expand_cols_per_item(R, slices, esz));
+  const int64_t grid_s = mb * (int64_t)a.rgroups;
+  const int64_t grid_e = mb * (int64_t)a.nchunk;
+  const int32_t mm_s = shrink_mfma_min(bf16, numel, num_virtual, block_m);
+  const int32_t mm_e =
+      expand_mfma_min(bf16, numel, num_virtual, block_m, R, slices, N, out, ld_out);
+  if (shrink_all(a, bf16, rpi, grid_s, mm_s, st) != hipSuccess) return MOL_E_HIP;
+  return hip_status(expand_all(a, bf16, grid_e, mm_e, st));
+}
+
 }  // namespace
 
 extern "C" {
@@ -362,42 +445,42 @@ MOL_API mol_status mol_lora_delta(int32_t dtype, const void* xin, int64_t ld_x,
                                   int32_t num_virtual, int32_t block_m, void* out,
                                   int64_t ld_out, void* workspace, size_t workspace_bytes,
                                   void* stream) {
-  const StageCheck rc =
-      routing_check(sorted_ids, expert_ids, num_post_padded, numel, num_virtual, block_m);
-  if (rc.st != MOL_OK) return rc.st;
-  alignas(16) float ws_probe[4] = {};  // s lives in the workspace, checked below
-  mol_status c = shrink_check(dtype, xin, ld_x, row_div, A, R, K, numel, ws_probe);
-  if (c != MOL_OK) return c;
-  c = expand_check(dtype, R, slices, B, N, slot_scale, num_experts, num_virtual, numel, out,
-                   ld_out);
-  if (c != MOL_OK) return c;
-  if (numel == 0) return MOL_OK;
+  const mol_status c =
+      delta_check(dtype, xin, ld_x, row_div, A, R, K, slices, B, N, slot_scale, num_experts,
+                  sorted_ids, expert_ids, num_post_padded, numel, num_virtual, block_m, out,
+                  ld_out);
+  if (c != MOL_OK || numel == 0) return c;
   const int64_t need = mol_delta_workspace_bytes(numel, R, num_virtual, block_m);
   if (need < 0) return (mol_status)(-need);
   if (!workspace || workspace_bytes < (size_t)need) return MOL_E_WORKSPACE;
   if (!aligned16(workspace)) return MOL_E_ALIGN;
-  const bool bf16 = dtype == MOL_BF16;
-  const int esz = bf16 ? 2 : 4;
-  const int rpi = mol::shrink_rows_per_item(K, esz);
-  float* s = static_cast<float*>(workspace);
-  mol::DeltaArgs a = make_delta_args(xin, ld_x, row_div, A, R, K, slices, B, N, slot_scale,
-                                     num_experts, sorted_ids, expert_ids, num_post_padded,
-                                     numel, num_virtual, block_m, s, out, ld_out,
-                                     rc.max_blocks);
-  a.ranks = slot_ranks;
-  a.rgroups = (int32_t)cdiv64(R, rpi);
-  a.nchunk = (int32_t)cdiv64(N, mol::expand_cols_per_item(R, slices, esz));
-  const int64_t grid_s = rc.max_blocks * (int64_t)a.rgroups;
-  const int64_t grid_e = rc.max_blocks * (int64_t)a.nchunk;
-  if (grid_s > kI32Max || grid_e > kI32Max) return MOL_E_LIMIT;
-  const int32_t mm_s = shrink_mfma_min(bf16, numel, num_virtual, block_m);
-  const int32_t mm_e =
-      expand_mfma_min(bf16, numel, num_virtual, block_m, R, slices, N, out, ld_out);
-  if (mm_s > 0 && rc.max_blocks * cdiv64(R, 64) > kI32Max) return MOL_E_LIMIT;
-  const hipStream_t st = (hipStream_t)stream;
-  const hipError_t err = shrink_all(a, bf16, rpi, grid_s, mm_s, st);
-  if (err != hipSuccess) return MOL_E_HIP;
-  return hip_status(expand_all(a, bf16, grid_e, mm_e, st));
+  return delta_enqueue(dtype, xin, ld_x, row_div, A, R, K, slices, B, N, slot_scale,
+                       slot_ranks, num_experts, sorted_ids, expert_ids, num_post_padded, numel,
+                       num_virtual, block_m, out, ld_out, static_cast<float*>(workspace),
+                       (hipStream_t)stream);
+}
+
+MOL_API mol_status mol_lora_delta_noalloc(int32_t dtype, const void* xin, int64_t ld_x,
+                                          int32_t row_div, const void* A, int32_t R, int32_t K,
+                                          int32_t slices, const void* B, int32_t N,
+                                          const float* slot_scale, const int32_t* slot_ranks,
+                                          int32_t num_experts, const int32_t* sorted_ids,
+                                          const int32_t* expert_ids,
+                                          const int32_t* num_post_padded, int32_t numel,
+                                          int32_t num_virtual, int32_t block_m, void* out,
+                                          int64_t ld_out, void* stream) {
+  const mol_status c =
+      delta_check(dtype, xin, ld_x, row_div, A, R, K, slices, B, N, slot_scale, num_experts,
+                  sorted_ids, expert_ids, num_post_padded, numel, num_virtual, block_m, out,
+                  ld_out);
+  if (c != MOL_OK || numel == 0) return c;
+  if ((int64_t)numel * R > MOL_DELTA_SCRATCH_FLOATS) return MOL_E_LIMIT;
+  float* s = nullptr;
+  const mol_status sc = delta_scratch(&s);
+  if (sc != MOL_OK) return sc;
+  return delta_enqueue(dtype, xin, ld_x, row_div, A, R, K, slices, B, N, slot_scale,
+                       slot_ranks, num_experts, sorted_ids, expert_ids, num_post_padded, numel,
+                       num_virtual, block_m, out, ld_out, s, (hipStream_t)stream);
 }
 
 // ---- base grouped GEMM, alone or with the LoRA delta in its epilogue -----------------
