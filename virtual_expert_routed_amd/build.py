@@ -29,6 +29,9 @@ CFLAGS = [
     "-Wall", "-Wno-unused-function",
     # packed fp32 instructions are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the first eight kernel parameters arrive preloaded in scalar registers (the delta
+    # kernels pass their routing arguments there)
+    "-mllvm", "-amdgpu-kernarg-preload-count=8",
 ]
 
 

@@ -266,6 +266,7 @@ int32_t expand_mfma_min(bool bf16, int32_t numel, int32_t num_virtual, int32_t b
 hipError_t shrink_all(mol::DeltaArgs a, bool bf16, int rpi, int64_t grid, int32_t mfma_min,
                       hipStream_t st) {
   a.mfma_min = mfma_min;
+  mol::with_divisors(a);
   hipError_t e = mol::launch_shrink(a, bf16, rpi, (int)grid, st);
   if (e != hipSuccess || mfma_min == 0) return e;
   return mol::launch_shrink_mfma(
@@ -275,6 +276,7 @@ hipError_t shrink_all(mol::DeltaArgs a, bool bf16, int rpi, int64_t grid, int32_
 hipError_t expand_all(mol::DeltaArgs a, bool bf16, int64_t grid, int32_t mfma_min,
                       hipStream_t st) {
   a.mfma_min = mfma_min;
+  mol::with_divisors(a);
   hipError_t e = mol::launch_expand(a, bf16, (int)grid, st);
   if (e != hipSuccess || mfma_min == 0) return e;
   return mol::launch_expand_mfma(a, (int)grid, st);
@@ -545,6 +547,12 @@ MOL_API mol_status mol_moe_gemm(int32_t dtype, const void* xin, int64_t ld_x, in
   g.rgroups = (int32_t)cdiv64(N, rpi);
   const int64_t grid = rc.max_blocks * (int64_t)g.rgroups;
   if (grid > kI32Max) return MOL_E_LIMIT;
+  // the kernel's fixed divisors: items per block, input rows, columns of a slice
+  g.route.rgroups = g.rgroups;
+  g.route.row_div = row_div;
+  g.route.N = N;
+  g.route.slices = g.slices;
+  mol::with_divisors(g.route);
   return hip_status(mol::launch_moe_gemm(g, bf16, rpi, (int)grid, (hipStream_t)stream));
 }
 

@@ -55,29 +55,100 @@ struct ShrinkLds {
   static constexpr int kVecs = kPG * kSeg * LPR;
 };
 
-// Rows [rg*RPI, rg*RPI+RPI) of s for the pairs p[0..nq) (nq <= kPG). The x segments of
-// the pairs go straight into xs (LDS); lane 0 of each row group stores the sums.
+// The x vectors [m0*LPR, m0*LPR + SEGV) of the rows of pairs p[0..nq) go straight into xs
+// (pair q at xs[q*SEGV]): pair by pair, each wave a run of 64 vectors. A wave whose run lies
+// past the segment or past the row issues nothing; masked lanes of the others read a valid
+// address, unused. Pair ids are indexed with compile-time indices only (a runtime index into
+// them would put them in scratch memory).
 template <bool BF16, int LPR>
-__device__ __forceinline__ void shrink_group(const DeltaArgs& a, int e, int rl, int rg,
-                                             const int* p, int nq, uint4* xs) {
+__device__ __forceinline__ void stage_x(const DeltaArgs& a, const int* p, int nq, int m0,
+                                        int nvec, uint4* xs) {
+  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int SEGV = kSeg * LPR;  // vectors of one x segment (a multiple of 64)
+  constexpr int RUNS = (SEGV + kThreads - 1) / kThreads;
+  static_assert(SEGV % 64 == 0, "x staging covers whole waves");
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const char* xbase = (const char*)a.xin;
+  const int64_t xstride = a.ld_x * ESZ;
+#pragma unroll
+  for (int q = 0; q < kPG; ++q) {
+    if (q >= nq) break;  // uniform
+    const int64_t xrow = (int64_t)fdiv(p[q], a.f_rd) * xstride;
+#pragma unroll
+    for (int t = 0; t < RUNS; ++t) {
+      const int i0 = t * kThreads + wv * 64;  // this wave's first vector of the segment
+      const int v0 = m0 * LPR + i0;
+      if (i0 >= SEGV || v0 >= nvec) continue;  // uniform: nothing to stage for this wave
+      const int v = v0 + lane;
+      const bool ok = v < nvec;
+      lds_dma16(xbase + (ok ? xrow + (int64_t)v * 16 : 0), xs + q * SEGV + i0);
+    }
+  }
+}
+
+// Row `row` of s for the pairs p[0..nq) (nq <= kPG) from the weight vectors av[] that this
+// lane holds (the lane's whole share of the row: vectors lr, lr+LPR, ... < nvec). Stages the
+// pairs' x rows, multiplies, reduces each row's LPR lanes by the fixed xor tree, and lane 0
+// of the row stores. The caller has issued the weight loads; every thread takes part.
+template <bool BF16, int LPR>
+__device__ __forceinline__ void shrink_pairs(const DeltaArgs& a, const uint4* av, int row,
+                                             bool row_in, const int* p, int nq, int nvec,
+                                             uint4* xs) {
+  constexpr int SEGV = kSeg * LPR;
+  const int lr = threadIdx.x % LPR;
+  stage_x<BF16, LPR>(a, p, nq, 0, nvec, xs);
+  __builtin_amdgcn_s_waitcnt(0);  // the x DMA (and the weights, the first time) have landed
+  __syncthreads();
+  float acc[kPG];
+#pragma unroll
+  for (int i = 0; i < kPG; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPG; ++i) {
+    if (i >= nq) break;
+#pragma unroll
+    for (int sg = 0; sg < kSeg; ++sg) {
+      const int v = lr + sg * LPR;
+      // keep the held weights packed: unpacked once for all groups, they would take twice
+      // the registers, and the unpacking would wait for the weight loads before the first
+      // group's x rows are even requested
+      uint4 w = av[sg];
+      asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+      if (v < nvec) acc[i] = dot16<BF16>(w, xs[i * SEGV + sg * LPR + lr], acc[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kPG; ++i) {
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc[i] += __shfl_xor(acc[i], off, 64);
+  }
+  if (lr == 0 && row_in) {
+#pragma unroll
+    for (int i = 0; i < kPG; ++i) {
+      if (i >= nq) break;
+      a.s[(int64_t)p[i] * a.R + row] = acc[i];
+    }
+  }
+}
+
+// Rows [rg*RPI, rg*RPI+RPI) of s for the pairs p[0..nq) (nq <= kPG) when a row is longer than
+// one register segment: the weights are loaded segment by segment, for every group of pairs.
+template <bool BF16, int LPR>
+__device__ __forceinline__ void shrink_group_long(const DeltaArgs& a, int e, int rl, int rg,
+                                                  const int* p, int nq, uint4* xs) {
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int RPI = kThreads / LPR;
-  constexpr int SEGV = kSeg * LPR;            // vectors of one x segment
-  constexpr int XPT = kPG * SEGV / kThreads;  // x vectors each thread stages
-  static_assert(XPT >= 1 && kPG * SEGV % kThreads == 0, "x staging covers whole waves");
+  constexpr int SEGV = kSeg * LPR;
   const int tid = threadIdx.x;
   const int lr = tid % LPR;
   const int row = rg * RPI + tid / LPR;
   const bool row_in = row < a.R;
-  const bool row_ok = row_in && row % (a.R / a.slices) < rl;  // past the rank: zero, unread
+  const bool row_ok = row_in && fmod(row, a.f_r) < rl;  // past the rank: zero, unread
   const int nvec = a.K * ESZ / 16;
   const int vpl = (nvec + LPR - 1) / LPR;
   const int64_t abytes = (int64_t)a.R * a.K * ESZ;
   const __amdgpu_buffer_rsrc_t ra = expert_rsrc((const char*)a.A + (int64_t)e * abytes, abytes);
   const uint32_t row_off = (uint32_t)(row_ok ? row : 0) * (uint32_t)(a.K * ESZ);
-  const char* xbase = (const char*)a.xin;
-  const int64_t xstride = a.ld_x * ESZ;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   float acc[kPG];
 #pragma unroll
   for (int i = 0; i < kPG; ++i) acc[i] = 0.f;
@@ -85,18 +156,7 @@ __device__ __forceinline__ void shrink_group(const DeltaArgs& a, int e, int rl, 
     uint4 av[kSeg];
     load_a_seg<LPR>(ra, row_off, row_ok, m0, nvec, av);
     if (m0 > 0) __syncthreads();  // earlier readers of xs are done
-    // x vectors of this segment: lane i of a wave writes 16 bytes at its wave's base;
-    // entries of pairs past nq or vectors past the row read a valid address, unused
-#pragma unroll
-    for (int t = 0; t < XPT; ++t) {
-      const int i = tid + t * kThreads;
-      const int q = i / SEGV;
-      const int v = m0 * LPR + (i - q * SEGV);
-      const bool ok = q < nq && v < nvec;
-      const int pq = !ok ? 0 : q == 0 ? p[0] : q == 1 ? p[1] : q == 2 ? p[2] : p[3];
-      lds_dma16(xbase + (ok ? (int64_t)(pq / a.row_div) * xstride + (int64_t)v * 16 : 0),
-                xs + wv * 64 + t * kThreads);
-    }
+    stage_x<BF16, LPR>(a, p, nq, m0, nvec, xs);
     __builtin_amdgcn_s_waitcnt(0);  // the x DMA and the weights have landed
     __syncthreads();
 #pragma unroll
@@ -123,23 +183,44 @@ __device__ __forceinline__ void shrink_group(const DeltaArgs& a, int e, int rl, 
   }
 }
 
-// Shrink work item (blk, rg): all real pairs of block blk.
-template <bool BF16, int LPR>
-__device__ __forceinline__ void shrink_block(const DeltaArgs& a, int blk, int rg, int* pid,
-                                             int& nreal, uint4* xs) {
-  int p[kPG];
-  bool all_here;
-  bool mfma;
-  const int n4 = first_pairs(a, blk, p, &all_here, &mfma);
-  const int e = block_expert(a, blk);
-  if (e < 0 || mfma) return;  // no delta, or the MFMA kernel's block
-  const int rl = slot_rank(a, e);
-  if (all_here) {  // the common decode case: no id staging at all
-    if (n4 > 0) shrink_group<BF16, LPR>(a, e, rl, rg, p, n4, xs);
-    return;
+// Shrink work item (blk, rg): all real pairs of block blk, kPG at a time. When a lane's share
+// of a row fits one register segment (every row up to 8*LPR vectors: K = 2048 at 8 rows per
+// item, K = 768 at 16), its weights are loaded once, together with the first group's x rows,
+// and held for every group of pairs of the block. A block whose real pairs are all among its
+// first kPG entries (nearly every block at decode) takes them from its head as scalars; a
+// larger one stages its pair ids through pid, 64 per pass (they form a prefix of the block).
+template <bool BF16, int LPR, bool HELD>
+__device__ __forceinline__ void shrink_block(const DeltaArgs& a, const RouteArgs& ra_, int blk,
+                                             int rg, int* pid, int& nreal, uint4* xs) {
+  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int RPI = kThreads / LPR;
+  const BlockHead h = block_head(a, ra_, blk);
+  if (h.e < 0 || h.nq == 0) return;  // no delta, or the MFMA kernel's block
+  const int rl = slot_rank(a, h.e);
+  const int nvec = a.K * ESZ / 16;  // HELD: nvec <= kSeg * LPR (chosen by the launcher)
+  const int tid = threadIdx.x;
+  const int row = rg * RPI + tid / LPR;
+  const bool row_in = row < a.R;
+  const bool row_ok = row_in && fmod(row, a.f_r) < rl;  // past the rank: zero, unread
+  uint4 av[kSeg];
+  if constexpr (HELD) {
+    const int64_t abytes = (int64_t)a.R * a.K * ESZ;
+    const __amdgpu_buffer_rsrc_t ra =
+        expert_rsrc((const char*)a.A + (int64_t)h.e * abytes, abytes);
+    load_a_seg<LPR>(ra, (uint32_t)(row_ok ? row : 0) * (uint32_t)(a.K * ESZ), row_ok, 0, nvec,
+                    av);
+    if (h.all_here) {  // the common decode case: the whole item is one straight run
+      shrink_pairs<BF16, LPR>(a, av, row, row_in, h.p, h.nq, nvec, xs);
+      return;
+    }
+  } else {
+    if (h.all_here) {
+      shrink_group_long<BF16, LPR>(a, h.e, rl, rg, h.p, h.nq, xs);
+      return;
+    }
   }
   for (int j0 = 0; j0 < a.BM; j0 += kPidSlots) {
-    const int pv = threadIdx.x < kPidSlots ? load_pid(a, blk, j0) : a.numel;
+    const int pv = tid < kPidSlots ? load_pid(a, blk, j0) : a.numel;
     __syncthreads();
     publish_pids(a, pv, pid, &nreal);
     __syncthreads();
@@ -148,19 +229,25 @@ __device__ __forceinline__ void shrink_block(const DeltaArgs& a, int blk, int rg
       int pq[kPG];
 #pragma unroll
       for (int i = 0; i < kPG; ++i) pq[i] = q0 + i < nr ? pid[q0 + i] : a.numel;
+      const int n = min(kPG, nr - q0);
       __syncthreads();  // xs of the previous group is no longer read
-      shrink_group<BF16, LPR>(a, e, rl, rg, pq, min(kPG, nr - q0), xs);
+      if constexpr (HELD)
+        shrink_pairs<BF16, LPR>(a, av, row, row_in, pq, n, nvec, xs);
+      else
+        shrink_group_long<BF16, LPR>(a, h.e, rl, rg, pq, n, xs);
     }
     if (nr < kPidSlots) return;  // the block's real entries ended in this pass
   }
 }
 
-template <bool BF16, int LPR>
-__global__ void __launch_bounds__(kThreads) shrink_kernel(DeltaArgs a) {
+template <bool BF16, int LPR, bool HELD>
+__global__ void __launch_bounds__(kThreads) shrink_kernel(MOL_ROUTE_PARAMS, DeltaArgs a) {
   __shared__ int pid[kPidSlots];
   __shared__ int nreal;
   __shared__ uint4 xs[ShrinkLds<LPR>::kVecs];
-  shrink_block<BF16, LPR>(a, blockIdx.x / a.rgroups, blockIdx.x % a.rgroups, pid, nreal, xs);
+  const RouteArgs r = MOL_ROUTE_MAKE;
+  const int blk = route_block(r);
+  shrink_block<BF16, LPR, HELD>(a, r, blk, (int)blockIdx.x - blk * r.per, pid, nreal, xs);
 }
 
 // ------------------------------------------------------------------------------ expand
@@ -259,28 +346,27 @@ __device__ __forceinline__ void expand_outputs(const DeltaArgs& a, const uint4 (
 
 // One expand work item: CPT*256 output columns for every real pair of block blk.
 template <bool BF16, int RV>
-__device__ __forceinline__ void expand_block(const DeltaArgs& a, int blk, int chunk, int* pid,
-                                             int& nreal, float* s_lds) {
+__device__ __forceinline__ void expand_block(const DeltaArgs& a, const RouteArgs& ra_, int blk,
+                                             int chunk, int* pid, int& nreal, float* s_lds) {
   constexpr int CPT = cols_per_thread(RV);
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int r = RV * 16 / ESZ;
   const int tid = threadIdx.x;
-  int p[kPG];
-  bool all_here;
-  bool mfma;
-  const int n4 = first_pairs(a, blk, p, &all_here, &mfma);
-  const int e = block_expert(a, blk);
-  if (e < 0 || mfma) return;  // no delta, or the MFMA kernel's block
+  const BlockHead h = block_head(a, ra_, blk);
+  const int e = h.e;
+  if (e < 0 || h.nq == 0) return;  // no delta, or the MFMA kernel's block
+  const int* p = h.p;
+  const int n4 = h.nq;
+  const bool all_here = h.all_here;
   const int rl = slot_rank(a, e);
   if (rl == 0) return;  // a slot of rank 0 adds nothing
-  const int width = a.N / a.slices;
   int n[CPT], soff[CPT];
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
     n[j] = chunk * (CPT * kThreads) + j * kThreads + tid;
-    soff[j] = (n[j] < a.N ? n[j] / width : 0) * r;
+    soff[j] = (n[j] < a.N ? fdiv(n[j], a.f_w) : 0) * r;
   }
-  const float sc = a.scale[e / a.E];
+  const float sc = a.scale[fdiv(e, a.f_e)];
   uint4 bv[CPT][RV];
   load_b_rows<BF16, RV, CPT>(a, e, rl, n, bv);
   if (all_here) {
@@ -290,9 +376,10 @@ __device__ __forceinline__ void expand_block(const DeltaArgs& a, int blk, int ch
     const int nvec = n4 * a.R / 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     for (int base = 0; base < nvec; base += kThreads) {
+      if (base + wv * 64 >= nvec) continue;  // uniform: nothing for this wave
       const int i = base + tid;
       const bool ok = i < nvec;
-      const int q = ok ? i / (a.R / 4) : 0;
+      const int q = ok ? fdiv(i, a.f_r4) : 0;
       const int c4 = ok ? i - q * (a.R / 4) : 0;
       const int pq = q == 0 ? p[0] : q == 1 ? p[1] : q == 2 ? p[2] : p[3];
       lds_dma16(a.s + (int64_t)pq * a.R + c4 * 4, s_lds + (base + wv * 64) * 4);
@@ -338,20 +425,22 @@ __device__ __forceinline__ void expand_block(const DeltaArgs& a, int blk, int ch
 }
 
 template <bool BF16, int RV>
-__global__ void __launch_bounds__(kThreads) expand_kernel(DeltaArgs a) {
+__global__ void __launch_bounds__(kThreads) expand_kernel(MOL_ROUTE_PARAMS, DeltaArgs a) {
   __shared__ int pid[kPidSlots];
   __shared__ int nreal;
   __shared__ __attribute__((aligned(16))) float s_lds[kSLdsFloats];
-  expand_block<BF16, RV>(a, blockIdx.x / a.nchunk, blockIdx.x % a.nchunk, pid, nreal, s_lds);
+  const RouteArgs r = MOL_ROUTE_MAKE;
+  const int blk = route_block(r);
+  expand_block<BF16, RV>(a, r, blk, (int)blockIdx.x - blk * r.per, pid, nreal, s_lds);
 }
 
-template <bool BF16>
+template <bool BF16, bool HELD>
 hipError_t shrink_dispatch(const DeltaArgs& a, int lpr, int grid, hipStream_t st) {
   switch (lpr) {
-    case 8: hipLaunchKernelGGL((shrink_kernel<BF16, 8>), dim3(grid), dim3(kThreads), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((shrink_kernel<BF16, 16>), dim3(grid), dim3(kThreads), 0, st, a); break;
-    case 32: hipLaunchKernelGGL((shrink_kernel<BF16, 32>), dim3(grid), dim3(kThreads), 0, st, a); break;
-    case 64: hipLaunchKernelGGL((shrink_kernel<BF16, 64>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((shrink_kernel<BF16, 8, HELD>), dim3(grid), dim3(kThreads), 0, st, MOL_ROUTE_ARGS(a, a.rgroups, a.f_rg), a); break;
+    case 16: hipLaunchKernelGGL((shrink_kernel<BF16, 16, HELD>), dim3(grid), dim3(kThreads), 0, st, MOL_ROUTE_ARGS(a, a.rgroups, a.f_rg), a); break;
+    case 32: hipLaunchKernelGGL((shrink_kernel<BF16, 32, HELD>), dim3(grid), dim3(kThreads), 0, st, MOL_ROUTE_ARGS(a, a.rgroups, a.f_rg), a); break;
+    case 64: hipLaunchKernelGGL((shrink_kernel<BF16, 64, HELD>), dim3(grid), dim3(kThreads), 0, st, MOL_ROUTE_ARGS(a, a.rgroups, a.f_rg), a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -360,11 +449,11 @@ hipError_t shrink_dispatch(const DeltaArgs& a, int lpr, int grid, hipStream_t st
 template <bool BF16>
 hipError_t expand_dispatch(const DeltaArgs& a, int rv, int grid, hipStream_t st) {
   switch (rv) {
-    case 1: hipLaunchKernelGGL((expand_kernel<BF16, 1>), dim3(grid), dim3(kThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((expand_kernel<BF16, 2>), dim3(grid), dim3(kThreads), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((expand_kernel<BF16, 4>), dim3(grid), dim3(kThreads), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((expand_kernel<BF16, 8>), dim3(grid), dim3(kThreads), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((expand_kernel<BF16, 16>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((expand_kernel<BF16, 1>), dim3(grid), dim3(kThreads), 0, st, MOL_ROUTE_ARGS(a, a.nchunk, a.f_nc), a); break;
+    case 2: hipLaunchKernelGGL((expand_kernel<BF16, 2>), dim3(grid), dim3(kThreads), 0, st, MOL_ROUTE_ARGS(a, a.nchunk, a.f_nc), a); break;
+    case 4: hipLaunchKernelGGL((expand_kernel<BF16, 4>), dim3(grid), dim3(kThreads), 0, st, MOL_ROUTE_ARGS(a, a.nchunk, a.f_nc), a); break;
+    case 8: hipLaunchKernelGGL((expand_kernel<BF16, 8>), dim3(grid), dim3(kThreads), 0, st, MOL_ROUTE_ARGS(a, a.nchunk, a.f_nc), a); break;
+    case 16: hipLaunchKernelGGL((expand_kernel<BF16, 16>), dim3(grid), dim3(kThreads), 0, st, MOL_ROUTE_ARGS(a, a.nchunk, a.f_nc), a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -387,8 +476,13 @@ int shrink_rows_per_item(int32_t K, int elem_bytes) {
 hipError_t launch_shrink(const DeltaArgs& a, bool bf16, int rows_per_item, int grid,
                          hipStream_t stream) {
   const int lpr = kThreads / rows_per_item;
-  return bf16 ? shrink_dispatch<true>(a, lpr, grid, stream)
-              : shrink_dispatch<false>(a, lpr, grid, stream);
+  // a lane's share of a row fits one register segment: held across the block's pairs
+  const bool held = (int64_t)a.K * (bf16 ? 2 : 4) / 16 <= (int64_t)kSeg * lpr;
+  if (bf16)
+    return held ? shrink_dispatch<true, true>(a, lpr, grid, stream)
+                : shrink_dispatch<true, false>(a, lpr, grid, stream);
+  return held ? shrink_dispatch<false, true>(a, lpr, grid, stream)
+              : shrink_dispatch<false, false>(a, lpr, grid, stream);
 }
 
 hipError_t launch_expand(const DeltaArgs& a, bool bf16, int grid, hipStream_t stream) {

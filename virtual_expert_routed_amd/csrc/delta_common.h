@@ -102,25 +102,90 @@ __device__ __forceinline__ bool block_has(const DeltaArgs& a, int blk, int t) {
   return t <= a.BM && real_pair(a.sorted[(int64_t)blk * a.BM + (t - 1)], a.numel);
 }
 
-// The first kPG entries of block blk as scalars (numel past the block); returns how many
-// are real pairs. *all_here tells whether they are all of the block's real pairs; *mfma
-// whether the block belongs to the MFMA kernels (entry mfma_min - 1 is real), read in the
-// same batch of loads.
-__device__ __forceinline__ int first_pairs(const DeltaArgs& a, int blk, int* p, bool* all_here,
-                                           bool* mfma) {
-  const int32_t* sp = a.sorted + (int64_t)blk * a.BM;
-  const bool use = a.mfma_min > 0 && a.mfma_min <= a.BM;
-  const int vm = sp[use ? a.mfma_min - 1 : 0];
-  int nr = 0;
+// What a work item needs to know of its block before its first weight load: the block's
+// virtual expert (e < 0: the item has nothing to do, because the block is past the live
+// blocks, in the sentinel bucket, or belongs to the MFMA kernels), its first kPG entries as
+// scalars (numel past the block) and how many of them are real pairs (a prefix).
+struct BlockHead {
+  int e;
+  int p[kPG];
+  int nq;
+  bool all_here;  // the block has no real pairs past its first kPG entries
+};
+
+// The routing arguments a delta item needs first. The kernels take them as their leading
+// scalar parameters (MOL_ROUTE_PARAMS), and the library is built with kernel-argument
+// preloading for the first eight parameters, so they arrive in scalar registers with the
+// wave and the item's routing reads can leave at its first instructions, with no fetch of
+// the argument buffer before them.
+struct RouteArgs {
+  const int32_t* sorted;
+  const int32_t* expert_ids;
+  const int32_t* npp;
+  int32_t BM;
+  int32_t mfma_min;
+  FastDiv per_div;  // work items per block, as a multiply-shift divisor (m, l)
+  int32_t per;      // work items per block
+};
+
+#define MOL_ROUTE_PARAMS                                                                    \
+  const int32_t *r_sorted, const int32_t *r_eids, const int32_t *r_npp, int32_t r_bm,      \
+      int32_t r_mm, uint32_t r_pm, uint32_t r_pl, int32_t r_per
+#define MOL_ROUTE_ARGS(a, per, div) \
+  (a).sorted, (a).expert_ids, (a).npp, (a).BM, (a).mfma_min, (div).m, (div).l, (per)
+#define MOL_ROUTE_MAKE \
+  RouteArgs{r_sorted, r_eids, r_npp, r_bm, r_mm, FastDiv{(uint32_t)r_per, r_pm, r_pl}, r_per}
+
+// The block and the item within it of this workgroup.
+__device__ __forceinline__ int route_block(const RouteArgs& r) {
+  return fdiv((int)blockIdx.x, r.per_div);
+}
+
+// The kernel arguments a delta item reads before its weight loads, all fetched at its start
+// in one batch. (Left to itself the compiler fetches each one where it is first used, and a
+// fetch that misses the scalar cache then costs one more round trip between the routing
+// reads and the weight loads.)
+__device__ __forceinline__ void fetch_args(const DeltaArgs& a) {
+  asm volatile("" ::"s"(a.xin), "s"(a.A), "s"(a.B), "s"(a.scale), "s"(a.s), "s"(a.out),
+               "s"(a.ranks), "s"(a.ld_x), "s"(a.ld_out));
+  asm volatile("" ::"s"(a.row_div), "s"(a.R), "s"(a.K), "s"(a.slices), "s"(a.N), "s"(a.E),
+               "s"(a.numel), "s"(a.V), "s"(a.max_blocks));
+  asm volatile("" ::"s"(a.f_bm.m), "s"(a.f_bm.l), "s"(a.f_e.m), "s"(a.f_e.l), "s"(a.f_r.m),
+               "s"(a.f_r.l), "s"(a.f_w.m), "s"(a.f_w.l), "s"(a.f_rd.m), "s"(a.f_rd.l),
+               "s"(a.f_r4.m), "s"(a.f_r4.l));
+}
+
+// Every routing read of the head leaves in one batch: the padded count, the expert id and
+// the entries are read from clamped indices with no branch between the loads, so an item
+// pays one round trip to the routing before it can issue its weight loads.
+__device__ __forceinline__ BlockHead block_head(const DeltaArgs& a, const RouteArgs& r,
+                                                int blk) {
+  const int32_t* sp = r.sorted + (int64_t)blk * r.BM;
+  const int last = r.BM - 1;
+  const bool use_m = r.mfma_min > 0 && r.mfma_min <= r.BM;
+  const int im = use_m ? r.mfma_min - 1 : 0;
+  int v[kPG];
+#pragma unroll
+  for (int i = 0; i < kPG; ++i) v[i] = sp[i < last ? i : last];
+  const int vm_raw = sp[im];
+  const int er = r.expert_ids[blk];
+  const int npp = *r.npp;
+  // after the routing reads, so that they stay scalar loads, and in their round trip
+  fetch_args(a);
+  const int vm = use_m ? vm_raw : a.numel;  // a select keeps its load unconditional
+  BlockHead h;
+  h.nq = 0;
 #pragma unroll
   for (int i = 0; i < kPG; ++i) {
-    const int v = sp[i < a.BM ? i : 0];
-    p[i] = i < a.BM ? v : a.numel;
-    nr += real_pair(p[i], a.numel) ? 1 : 0;
+    h.p[i] = i <= last ? v[i] : a.numel;
+    h.nq += real_pair(h.p[i], a.numel) ? 1 : 0;
   }
-  *all_here = nr < kPG || a.BM <= kPG;
-  *mfma = use && real_pair(vm, a.numel);
-  return nr;
+  h.all_here = h.nq < kPG || r.BM <= kPG;
+  const int nb = npp < 0 ? 0 : fdiv(npp, a.f_bm);
+  const int live = nb > a.max_blocks ? a.max_blocks : nb;
+  const bool mfma = real_pair(vm, a.numel);
+  h.e = (blk < live && real_expert(er, a.V) && !mfma) ? er : -1;
+  return h;
 }
 
 // Rank of the slot of virtual expert e: its slot_ranks entry clamped to [0, r], or r = R /
@@ -128,7 +193,7 @@ __device__ __forceinline__ int first_pairs(const DeltaArgs& a, int blk, int* p, 
 __device__ __forceinline__ int slot_rank(const DeltaArgs& a, int e) {
   const int r = a.R / a.slices;
   if (!a.ranks) return r;
-  const int v = a.ranks[e / a.E];
+  const int v = a.ranks[fdiv(e, a.f_e)];
   return v < 0 ? 0 : (v > r ? r : v);
 }
 

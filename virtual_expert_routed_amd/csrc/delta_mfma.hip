@@ -106,7 +106,7 @@ template <int NRT>
 __device__ __forceinline__ void load_x(const DeltaArgs& a, int p, bool real, int kc0,
                                        uint4* xf) {
   const int lane = threadIdx.x & 63;
-  const int64_t rowoff = real ? (int64_t)(p / a.row_div) * a.ld_x : 0;
+  const int64_t rowoff = real ? (int64_t)fdiv(p, a.f_rd) * a.ld_x : 0;
   const char* xb = (const char*)a.xin;
 #pragma unroll
   for (int st = 0; st < ShrinkGeom<NRT>::kSteps; ++st) {
@@ -259,7 +259,7 @@ __device__ __forceinline__ void expand_mfma_block(const DeltaArgs& a, int blk, i
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = a.R / a.slices, width = a.N / a.slices;
-  const float sc = a.scale[e / a.E];
+  const float sc = a.scale[fdiv(e, a.f_e)];
   // the slices this item's columns fall in: only their part of s is staged
   const int cfirst = chunk * kExpandCols;
   const int clast = min(a.N, cfirst + kExpandCols) - 1;
@@ -363,7 +363,7 @@ __global__ void __launch_bounds__(256) expand_mfma_kernel(DeltaArgs a) {
   __shared__ __attribute__((aligned(16))) float tile[16 * kTileStride];
   __shared__ int pid[kRowsPerPass];
   __shared__ int nrows_lds;
-  const int blk = blockIdx.x / a.nchunk, chunk = blockIdx.x % a.nchunk;
+  const int blk = fdiv((int)blockIdx.x, a.f_nc), chunk = (int)blockIdx.x - blk * a.nchunk;
   const int e = block_expert(a, blk);
   if (e < 0 || !block_has(a, blk, a.mfma_min)) return;
   const int rl = slot_rank(a, e);

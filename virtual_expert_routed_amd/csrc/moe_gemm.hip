@@ -89,7 +89,7 @@ __device__ __forceinline__ void gemm_group(const GemmArgs& g, int e, int rg, con
       const int v = m0 * LPR + (i - q * SEGV);
       const bool ok = q < nq && v < nvec;
       const int pq = !ok ? 0 : q == 0 ? p[0] : q == 1 ? p[1] : q == 2 ? p[2] : p[3];
-      lds_dma16(xbase + (ok ? (int64_t)(pq / g.row_div) * xstride + (int64_t)v * 16 : 0),
+      lds_dma16(xbase + (ok ? (int64_t)fdiv(pq, g.route.f_rd) * xstride + (int64_t)v * 16 : 0),
                 xs + wv * 64 + t * kThreads);
     }
     __builtin_amdgcn_s_waitcnt(0);  // the x DMA and the weights have landed
@@ -106,7 +106,7 @@ __device__ __forceinline__ void gemm_group(const GemmArgs& g, int e, int rg, con
   }
   if constexpr (FUSED) {
     const int r = g.R / g.slices;
-    const int gs = n_ok ? n / (g.N / g.slices) : 0;
+    const int gs = n_ok ? fdiv(n, g.route.f_w) : 0;
     const int64_t bbytes = (int64_t)g.N * r * ESZ;
     // lane lr takes the 16-byte vectors lr, lr + LPR, ... of its column's B row slice (at
     // most kMaxRankVecs of them, so NVL per lane) and the matching s values
@@ -175,19 +175,18 @@ __device__ __forceinline__ void gemm_group(const GemmArgs& g, int e, int rg, con
 }
 
 template <bool BF16, int LPR, bool FUSED>
-__global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs g) {
+__global__ void __launch_bounds__(kThreads) gemm_kernel(MOL_ROUTE_PARAMS, GemmArgs g) {
   __shared__ int pid[kPidSlots];
   __shared__ int nreal;
   __shared__ uint4 xs[kPG * kSeg * LPR];
   const DeltaArgs& a = g.route;
-  const int blk = blockIdx.x / g.rgroups, rg = blockIdx.x % g.rgroups;
-  int p[kPG];
-  bool all_here, mfma;
-  const int n4 = first_pairs(a, blk, p, &all_here, &mfma);
-  const int e = block_expert(a, blk);
+  const RouteArgs r = MOL_ROUTE_MAKE;
+  const int blk = route_block(r), rg = (int)blockIdx.x - blk * r.per;
+  const BlockHead h = block_head(a, r, blk);  // mfma_min is 0: no block is skipped for MFMA
+  const int e = h.e;
   if (e < 0) return;  // sentinel block (no local expert) or past the live blocks
-  if (all_here) {
-    if (n4 > 0) gemm_group<BF16, LPR, FUSED>(g, e, rg, p, n4, xs);
+  if (h.all_here) {
+    if (h.nq > 0) gemm_group<BF16, LPR, FUSED>(g, e, rg, h.p, h.nq, xs);
     return;
   }
   for (int j0 = 0; j0 < a.BM; j0 += kPidSlots) {
@@ -210,10 +209,10 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs g) {
 template <bool BF16, bool FUSED>
 hipError_t gemm_dispatch(const GemmArgs& g, int lpr, int grid, hipStream_t st) {
   switch (lpr) {
-    case 8: hipLaunchKernelGGL((gemm_kernel<BF16, 8, FUSED>), dim3(grid), dim3(kThreads), 0, st, g); break;
-    case 16: hipLaunchKernelGGL((gemm_kernel<BF16, 16, FUSED>), dim3(grid), dim3(kThreads), 0, st, g); break;
-    case 32: hipLaunchKernelGGL((gemm_kernel<BF16, 32, FUSED>), dim3(grid), dim3(kThreads), 0, st, g); break;
-    case 64: hipLaunchKernelGGL((gemm_kernel<BF16, 64, FUSED>), dim3(grid), dim3(kThreads), 0, st, g); break;
+    case 8: hipLaunchKernelGGL((gemm_kernel<BF16, 8, FUSED>), dim3(grid), dim3(kThreads), 0, st, MOL_ROUTE_ARGS(g.route, g.rgroups, g.route.f_rg), g); break;
+    case 16: hipLaunchKernelGGL((gemm_kernel<BF16, 16, FUSED>), dim3(grid), dim3(kThreads), 0, st, MOL_ROUTE_ARGS(g.route, g.rgroups, g.route.f_rg), g); break;
+    case 32: hipLaunchKernelGGL((gemm_kernel<BF16, 32, FUSED>), dim3(grid), dim3(kThreads), 0, st, MOL_ROUTE_ARGS(g.route, g.rgroups, g.route.f_rg), g); break;
+    case 64: hipLaunchKernelGGL((gemm_kernel<BF16, 64, FUSED>), dim3(grid), dim3(kThreads), 0, st, MOL_ROUTE_ARGS(g.route, g.rgroups, g.route.f_rg), g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fastdiv.h"
+
 namespace mol {
 
 constexpr int kMaxBuckets = 8192;     // V + 1 <= 8192
@@ -40,34 +42,59 @@ inline int64_t align_tile(int64_t numel) {
   return (t + 63) / 64 * 64;
 }
 
+// Arguments of the delta kernels. Laid out densely (pointers, then 64-bit strides, then
+// 32-bit fields, then the divisors) so that a kernel fetches all of it in a few wide scalar
+// loads, in the same round trip as its routing reads.
 struct DeltaArgs {
   const void* xin;
-  int64_t ld_x;
-  int32_t row_div;
   const void* A;
-  int32_t R;
-  int32_t K;
-  int32_t slices;
   const void* B;
-  int32_t N;
   const float* scale;
-  int32_t E;
   const int32_t* sorted;
   const int32_t* expert_ids;
   const int32_t* npp;
+  float* s;              // [numel, R]
+  void* out;
+  const int32_t* ranks;  // [S] per-slot ranks (clamped to [0, R/slices]) or nullptr
+  int64_t ld_x;
+  int64_t ld_out;
+  int32_t row_div;
+  int32_t R;
+  int32_t K;
+  int32_t slices;
+  int32_t N;
+  int32_t E;
   int32_t numel;
   int32_t V;             // virtual experts: expert ids outside [0, V) are skipped
   int32_t BM;
   int32_t rgroups;       // shrink work items per block (row groups of A)
   int32_t nchunk;        // expand work items per block (column chunks of B)
-  float* s;              // [numel, R]
-  void* out;
-  int64_t ld_out;
   int32_t max_blocks;
-  const int32_t* ranks;  // [S] per-slot ranks (clamped to [0, R/slices]) or nullptr
   int32_t mfma_min;      // > 0: blocks with at least this many real pairs go to the MFMA
                          // kernels and the VALU kernels skip them; 0: VALU kernels only
+  int32_t pad_;
+  // the launch's fixed divisors, as multiply-shift constants (set by with_divisors)
+  FastDiv f_rg;          // rgroups
+  FastDiv f_nc;          // nchunk
+  FastDiv f_bm;          // BM
+  FastDiv f_e;           // E
+  FastDiv f_r;           // R / slices (rank of one slice)
+  FastDiv f_w;           // N / slices (columns of one slice)
+  FastDiv f_rd;          // row_div
+  FastDiv f_r4;          // R / 4 (16-byte vectors of one s row)
 };
+
+// Host: fill the multiply-shift divisors of a from its fields (before every launch).
+inline void with_divisors(DeltaArgs& a) {
+  a.f_rg = make_fastdiv((uint32_t)(a.rgroups > 0 ? a.rgroups : 1));
+  a.f_nc = make_fastdiv((uint32_t)(a.nchunk > 0 ? a.nchunk : 1));
+  a.f_bm = make_fastdiv((uint32_t)a.BM);
+  a.f_e = make_fastdiv((uint32_t)a.E);
+  a.f_r = make_fastdiv((uint32_t)(a.slices > 0 ? a.R / a.slices : a.R));
+  a.f_w = make_fastdiv((uint32_t)(a.slices > 0 ? a.N / a.slices : a.N));
+  a.f_rd = make_fastdiv((uint32_t)a.row_div);
+  a.f_r4 = make_fastdiv((uint32_t)(a.R / 4 > 0 ? a.R / 4 : 1));
+}
 
 // The combine after the down projection, and its form fused with the down-stage expand.
 struct CombineArgs {
