@@ -202,6 +202,8 @@ MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_
   a.V = (int32_t)V64;
   a.BM = block_m;
   a.bm_shift = (block_m & (block_m - 1)) == 0 ? __builtin_ctz((unsigned)block_m) : -1;
+  a.f_topk = mol::make_fastdiv((uint32_t)topk);
+  a.f_bm = mol::make_fastdiv((uint32_t)block_m);
   a.sorted = sorted_ids;
   a.expert_ids = expert_ids;
   a.npp = num_post_padded;
@@ -223,6 +225,10 @@ MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_
     if ((int64_t)lds > device_lds_bytes()) return MOL_E_LIMIT;
     // workgroups that split the output writes (each one rebuilds the routing in LDS)
     const int groups = (int)std::max<int64_t>(1, std::min<int64_t>(16, cdiv64(numel, 16)));
+    // each walker's contiguous range of pairs: a multiple of 64
+    a.per = (int32_t)(cdiv64(cdiv64(numel, waves), 64) * 64);
+    a.f_per = mol::make_fastdiv((uint32_t)std::max<int64_t>(1, a.per));
+    a.f_groups = mol::make_fastdiv((uint32_t)groups);
     return hip_status(mol::launch_align_small(a, (int)waves, groups, lds, st));
   }
   a.tile = (int32_t)mol::align_tile(numel);

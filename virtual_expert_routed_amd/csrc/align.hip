@@ -42,7 +42,7 @@ __device__ __forceinline__ int remap_one(int32_t t, int32_t l, int32_t E, int32_
 
 __device__ __forceinline__ int bucket_of(const AlignArgs& a, int p) {
   const int32_t t = a.ids[p];
-  const int32_t v = a.lora ? remap_one(t, a.lora[p / a.topk], a.E, a.S) : t;
+  const int32_t v = a.lora ? remap_one(t, a.lora[fdiv(p, a.f_topk)], a.E, a.S) : t;
   return (v >= 0 && v < a.V) ? v : a.V;
 }
 
@@ -80,10 +80,10 @@ __device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
 
 // x / BLOCK_M and c rounded up to a multiple of BLOCK_M (shifts when BLOCK_M is a power of 2)
 __device__ __forceinline__ int bm_div(const AlignArgs& a, int x) {
-  return a.bm_shift >= 0 ? x >> a.bm_shift : x / a.BM;
+  return a.bm_shift >= 0 ? x >> a.bm_shift : fdiv(x, a.f_bm);
 }
 __device__ __forceinline__ int bm_round(const AlignArgs& a, int c) {
-  return a.bm_shift >= 0 ? (c + a.BM - 1) & -a.BM : (c + a.BM - 1) / a.BM * a.BM;
+  return a.bm_shift >= 0 ? (c + a.BM - 1) & -a.BM : fdiv(c + a.BM - 1, a.f_bm) * a.BM;
 }
 
 __global__ void __launch_bounds__(256) virtual_topk_kernel(const int32_t* __restrict__ topk,
@@ -128,35 +128,47 @@ __device__ __forceinline__ uint64_t match_key13(int key, bool valid) {
 //   D  sorted[start[b(p)] + row[w(p)][b(p)] + rank_in_range(p)] = p for this workgroup's
 //      pairs; each wave writes the padding of this workgroup's non-empty buckets its
 //      threads own.
+// The leading eight parameters (everything phase A needs: the ids, the slots, the pair
+// count, the token divisor, the key array's LDS offset and the remap's E and S) arrive
+// preloaded in scalar registers, so phase A's loads leave at the kernel's first
+// instructions, before the argument struct has been fetched.
 template <int BPT>
-__global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a, int waves) {
+__global__ void __launch_bounds__(1024)
+    align_small_kernel(const int32_t* ids, const int32_t* lora, int32_t numel_, uint32_t tk_m,
+                       uint32_t tk_l, int32_t keys_off, int32_t E, int32_t S, AlignArgs a,
+                       int waves) {
   extern __shared__ int lds[];
   const int NB = a.V + 1;
   int* table = lds;                                   // [waves][NB]
   int* start = lds + waves * NB;                      // [NB] padded bucket starts
-  int* sh = start + NB;                               // scan scratch
-  uint16_t* keys = reinterpret_cast<uint16_t*>(sh + 64);
-  uint16_t* rel = keys + ((a.numel + 1) & ~1);
+  int* sh = start + NB;                               // scan scratch (64 ints)
+  uint16_t* keys = reinterpret_cast<uint16_t*>(lds + keys_off);  // = sh + 64
+  uint16_t* rel = keys + ((numel_ + 1) & ~1);
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
-  const int numel = a.numel;
+  const int numel = numel_;
   const int g = blockIdx.x, G = gridDim.x;
+  const FastDiv f_topk{(uint32_t)a.topk, tk_m, tk_l};
 
-  // A: four pairs per thread per round, loads of ids and slots issued together
-  for (int base = 0; base < numel; base += 4 * 1024) {
+  // A: up to four pairs per thread (numel <= 4096 on this path), every load of ids and
+  // slots issued together from the preloaded leading parameters, at unconditional clamped
+  // addresses (an empty batch may come with no ids at all, so it loads nothing)
+  if (numel > 0) {
+    const int32_t* lsrc = lora ? lora : ids;  // a valid address either way
     int t[4], l[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int p = base + i * 1024 + tid;
+      const int p = i * 1024 + tid;
       const int pc = p < numel ? p : 0;
-      t[i] = a.ids[pc];
-      l[i] = a.lora ? a.lora[pc / a.topk] : 0;
+      t[i] = ids[pc];
+      l[i] = lsrc[lora ? fdiv(pc, f_topk) : pc];
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int p = base + i * 1024 + tid;
+      const int p = i * 1024 + tid;
       if (p < numel) {
-        const int v = a.lora ? remap_one(t[i], l[i], a.E, a.S) : t[i];
-        keys[p] = (uint16_t)((v >= 0 && v < a.V) ? v : a.V);
+        const int v = lora ? remap_one(t[i], l[i], E, S) : t[i];
+        const int V = E * S;
+        keys[p] = (uint16_t)((v >= 0 && v < V) ? v : V);
       }
     }
   }
@@ -164,7 +176,7 @@ __global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a, int wave
   __syncthreads();
 
   // B
-  const int per = ((numel + waves - 1) / waves + 63) / 64 * 64;
+  const int per = a.per;  // a multiple of 64, per * waves >= numel
   if (wid < waves) {
     int* row = table + wid * NB;
     const int begin = min(numel, wid * per);
@@ -219,7 +231,7 @@ __global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a, int wave
   int off = block_excl_scan(mine, sh, &total);
   // padding of this thread's buckets, kept as (first slot, count) per owned bucket
   int pad_from[BPT], pad_cnt[BPT];
-  int bmod = b0 % G;  // b % G for b = b0, b0 + 1, ...
+  int bmod = fmod(b0, a.f_groups);  // b % G for b = b0, b0 + 1, ...
 #pragma unroll
   for (int k = 0; k < BPT; ++k) {
     pad_cnt[k] = 0;
@@ -245,7 +257,7 @@ __global__ void __launch_bounds__(1024) align_small_kernel(AlignArgs a, int wave
 
   // D
   for (int p = g + tid * G; p < numel; p += (int)blockDim.x * G) {
-    const int w = p / per;
+    const int w = fdiv(p, a.f_per);
     const int key = keys[p];
     a.sorted[start[key] + table[w * NB + key] + rel[p]] = p;
   }
@@ -433,14 +445,20 @@ hipError_t launch_align_small(const AlignArgs& a, int waves, int groups, size_t 
   // buckets per thread, rounded up to a power of two (V + 1 <= 8192 = 8 x 1024)
   const int bpt = (a.V + 1 + 1023) / 1024;
   const dim3 grid(groups), block(1024);
+  const int keys_off = (waves + 1) * (a.V + 1) + 64;  // ints before the key array
+#define MOL_ALIGN_SMALL(BPT)                                                                \
+  hipLaunchKernelGGL(align_small_kernel<BPT>, grid, block, lds_bytes, stream, a.ids, a.lora, \
+                     a.numel, a.f_topk.m, a.f_topk.l, keys_off, a.lora ? a.E : a.V,       \
+                     a.lora ? a.S : 1, a, waves)
   if (bpt <= 1)
-    hipLaunchKernelGGL(align_small_kernel<1>, grid, block, lds_bytes, stream, a, waves);
+    MOL_ALIGN_SMALL(1);
   else if (bpt <= 2)
-    hipLaunchKernelGGL(align_small_kernel<2>, grid, block, lds_bytes, stream, a, waves);
+    MOL_ALIGN_SMALL(2);
   else if (bpt <= 4)
-    hipLaunchKernelGGL(align_small_kernel<4>, grid, block, lds_bytes, stream, a, waves);
+    MOL_ALIGN_SMALL(4);
   else
-    hipLaunchKernelGGL(align_small_kernel<8>, grid, block, lds_bytes, stream, a, waves);
+    MOL_ALIGN_SMALL(8);
+#undef MOL_ALIGN_SMALL
   return hipGetLastError();
 }
 

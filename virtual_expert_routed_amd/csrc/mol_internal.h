@@ -32,6 +32,11 @@ struct AlignArgs {
   int32_t* totals;       // three-kernel path: [V+1] pairs per bucket
   int32_t ntiles;
   int32_t tile;          // three-kernel path: pairs per tile
+  int32_t per;           // one-launch path: pairs of each walker's contiguous range
+  FastDiv f_topk;        // topk (token of a pair)
+  FastDiv f_per;         // per (walker of a pair)
+  FastDiv f_bm;          // BM
+  FastDiv f_groups;      // workgroups of the one-launch path
 };
 
 // Tiles of the three-kernel align: at most 64 of them up to 1M pairs (the column scan walks
