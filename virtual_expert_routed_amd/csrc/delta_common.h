@@ -22,18 +22,23 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// acc += <a, x> over one 16-byte vector of each
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// acc + a.lo * b.lo + a.hi * b.hi for two packed bf16 pairs, in one v_dot2c_f32_bf16 (the
+// bf16 products are exact in fp32; no unpacking of either operand)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// acc += <a, x> over one 16-byte vector of each (element pairs in ascending order)
 template <bool BF16>
 __device__ __forceinline__ float dot16(const uint4& a, const uint4& x, float acc) {
   if constexpr (BF16) {
-    acc = fmaf(bf16_lo(a.x), bf16_lo(x.x), acc);
-    acc = fmaf(bf16_hi(a.x), bf16_hi(x.x), acc);
-    acc = fmaf(bf16_lo(a.y), bf16_lo(x.y), acc);
-    acc = fmaf(bf16_hi(a.y), bf16_hi(x.y), acc);
-    acc = fmaf(bf16_lo(a.z), bf16_lo(x.z), acc);
-    acc = fmaf(bf16_hi(a.z), bf16_hi(x.z), acc);
-    acc = fmaf(bf16_lo(a.w), bf16_lo(x.w), acc);
-    acc = fmaf(bf16_hi(a.w), bf16_hi(x.w), acc);
+    acc = dot2_bf16(a.x, x.x, acc);
+    acc = dot2_bf16(a.y, x.y, acc);
+    acc = dot2_bf16(a.z, x.z, acc);
+    acc = dot2_bf16(a.w, x.w, acc);
   } else {
     acc = fmaf(__uint_as_float(a.x), __uint_as_float(x.x), acc);
     acc = fmaf(__uint_as_float(a.y), __uint_as_float(x.y), acc);
