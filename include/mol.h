@@ -73,8 +73,9 @@ enum { MOL_F32 = 0, MOL_BF16 = 1 };
 /* (host) Static description of a status code. Never NULL. */
 MOL_API const char *mol_status_string(mol_status status);
 
-/* (host) ABI version of this header, 5 (2 added the per-slot ranks, 3 the combine, 4 the
- * base grouped GEMM with the fused delta, 5 the allocation-free stage delta). */
+/* (host) ABI version of this header, 6 (2 added the per-slot ranks, 3 the combine, 4 the
+ * base grouped GEMM with the fused delta, 5 the allocation-free stage delta, 6 the work
+ * plan). */
 MOL_API int32_t mol_abi_version(void);
 
 /* ---------------------------------------------------------------------------------
@@ -104,6 +105,25 @@ MOL_API int64_t mol_align_max_blocks(int64_t numel, int32_t num_virtual, int32_t
 MOL_API int64_t mol_align_workspace_bytes(int64_t numel, int32_t num_virtual, int32_t block_m);
 
 /* ---------------------------------------------------------------------------------
+ * The work plan (optional). A batch with split = 4 (numel >= 4096, numel >= 8 (V + 1) and
+ * block_m >= 4; else split = 0) divides its blocks between two kinds of kernels: a block
+ * with at least `split` real pairs is dense, the rest (a bucket's ragged last block) are
+ * few and small. For such a batch, mol_align_block_size can write beside the routing a plan
+ * of the delta's work: the dense blocks in runs of consecutive blocks of one bucket, and the
+ * real pairs of every other block of a real bucket cut into groups of at most four. The
+ * shrink and expand calls then take the small blocks' work from the group entries instead
+ * of launching over every possible block. With split = 0 nothing is written and the calls
+ * ignore a plan (every block then takes the same kernels, whose grid over the possible
+ * blocks is then the cheaper schedule). Layout (int32 words): [0] group count, [1]
+ * dense-run count, [2] split, [3..7] 0; from word 8, numel group entries of 8 words {block,
+ * virtual expert, pairs (1..4), 0, four pair ids (numel past the count)}; then dense runs
+ * of 4 words {first block, blocks (1..4), virtual expert, 0}, at most min(max_blocks,
+ * numel / split). Entries follow bucket and block order; the sentinel bucket gets none.
+ *   mol_plan_bytes: bytes of a plan buffer (a multiple of 256), or -mol_status.
+ * ------------------------------------------------------------------------------- */
+MOL_API int64_t mol_plan_bytes(int64_t numel, int32_t num_virtual, int32_t block_m);
+
+/* ---------------------------------------------------------------------------------
  * mol_align_block_size - bucket the numel = M * topk pairs by virtual expert (PR 24262
  * page: histogram, padded prefix sum, per-block expert ids, token scatter; PR 24171
  * page: the extra sentinel bucket whose blocks are -1).
@@ -120,6 +140,9 @@ MOL_API int64_t mol_align_workspace_bytes(int64_t numel, int32_t num_virtual, in
  *                    gets b, or -1 for the sentinel bucket.
  *   num_post_padded  int32 [1] out: sum_b pc_b.
  *   Entries past num_post_padded (resp. num_post_padded / block_m) are left undefined.
+ *   plan, plan_bytes the work plan out (see above; 16-byte aligned, at least
+ *                    mol_plan_bytes()), or NULL (0). Written only when split > 0; the
+ *                    buffer is left untouched otherwise.
  *   workspace        device scratch of mol_align_workspace_bytes(), or NULL when that is 0.
  * No atomics are used; results are bit-for-bit reproducible. M == 0 writes
  * num_post_padded = 0 (sorted_ids and expert_ids may then be NULL).
@@ -130,7 +153,8 @@ MOL_API mol_status mol_align_block_size(const int32_t *ids, const int32_t *lora_
                                         int32_t M, int32_t topk, int32_t num_experts,
                                         int32_t num_slots, int32_t block_m,
                                         int32_t *sorted_ids, int32_t *expert_ids,
-                                        int32_t *num_post_padded, void *workspace,
+                                        int32_t *num_post_padded, int32_t *plan,
+                                        size_t plan_bytes, void *workspace,
                                         size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------
@@ -154,6 +178,11 @@ MOL_API mol_status mol_align_block_size(const int32_t *ids, const int32_t *lora_
  *                s[p, g r + i] = 0 for i >= rl
  *   sorted_ids, expert_ids, num_post_padded: the outputs of mol_align_block_size for
  *                `numel` pairs, V = num_virtual virtual experts and this block_m
+ *   plan         the work plan the same align call wrote, or NULL. For a batch with
+ *                split > 0 whose dense blocks take the matrix-core kernels, the other
+ *                kernels take their work items from it (same results); otherwise, and
+ *                without one, their grid spans every possible block. (The expand, and the
+ *                shrink and expand of mol_lora_delta, take the same argument.)
  *   s            float32 [numel, R] out, 16-byte aligned; rows of pairs that get no delta are
  *                untouched
  * Requires K * elem and ld_x * elem to be multiples of 16 bytes, R % slices == 0, and xin,
@@ -164,8 +193,8 @@ MOL_API mol_status mol_lora_shrink(int32_t dtype, const void *xin, int64_t ld_x,
                                    int32_t slices, const int32_t *slot_ranks,
                                    int32_t num_experts, const int32_t *sorted_ids,
                                    const int32_t *expert_ids, const int32_t *num_post_padded,
-                                   int32_t numel, int32_t num_virtual, int32_t block_m,
-                                   float *s, void *stream);
+                                   const int32_t *plan, int32_t numel, int32_t num_virtual,
+                                   int32_t block_m, float *s, void *stream);
 
 /* ---------------------------------------------------------------------------------
  * mol_lora_expand - for the same pairs, with r = R / slices, w = N / slices and rl the
@@ -187,9 +216,9 @@ MOL_API mol_status mol_lora_expand(int32_t dtype, const float *s, int32_t R, int
                                    const void *B, int32_t N, const float *slot_scale,
                                    const int32_t *slot_ranks, int32_t num_experts,
                                    const int32_t *sorted_ids, const int32_t *expert_ids,
-                                   const int32_t *num_post_padded, int32_t numel,
-                                   int32_t num_virtual, int32_t block_m, void *out,
-                                   int64_t ld_out, void *stream);
+                                   const int32_t *num_post_padded, const int32_t *plan,
+                                   int32_t numel, int32_t num_virtual, int32_t block_m,
+                                   void *out, int64_t ld_out, void *stream);
 
 /* ---------------------------------------------------------------------------------
  * mol_lora_delta - one stage: shrink then expand, with s kept in the caller's workspace.
@@ -207,8 +236,8 @@ MOL_API mol_status mol_lora_delta(int32_t dtype, const void *xin, int64_t ld_x,
                                   const float *slot_scale, const int32_t *slot_ranks,
                                   int32_t num_experts, const int32_t *sorted_ids,
                                   const int32_t *expert_ids, const int32_t *num_post_padded,
-                                  int32_t numel, int32_t num_virtual, int32_t block_m,
-                                  void *out, int64_t ld_out, void *workspace,
+                                  const int32_t *plan, int32_t numel, int32_t num_virtual,
+                                  int32_t block_m, void *out, int64_t ld_out, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------
@@ -229,7 +258,8 @@ MOL_API mol_status mol_lora_delta_noalloc(int32_t dtype, const void *xin, int64_
                                           const float *slot_scale, const int32_t *slot_ranks,
                                           int32_t num_experts, const int32_t *sorted_ids,
                                           const int32_t *expert_ids,
-                                          const int32_t *num_post_padded, int32_t numel,
+                                          const int32_t *num_post_padded,
+                                          const int32_t *plan, int32_t numel,
                                           int32_t num_virtual, int32_t block_m, void *out,
                                           int64_t ld_out, void *stream);
 

@@ -39,7 +39,7 @@ def test_only_mol_symbols_exported():
 
 def test_version_and_status_strings():
     L = mb.lib()
-    assert L.mol_abi_version() == 5
+    assert L.mol_abi_version() == 6
     for code in range(7):
         assert mb.status_string(code)
     assert mb.status_string(99) == "unknown status"
@@ -83,21 +83,40 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails va
 def test_align_rejects_before_launch():
     L = mb.lib()
     # too many buckets
-    assert L.mol_align_block_size(FAKE, FAKE, 4, 2, 4096, 2, 64, FAKE, FAKE, FAKE, None, 0,
+    assert L.mol_align_block_size(FAKE, FAKE, 4, 2, 4096, 2, 64, FAKE, FAKE, FAKE, None, 0, None, 0,
                                   None) == mb.MOL_E_LIMIT
     # null outputs
-    assert L.mol_align_block_size(FAKE, None, 4, 2, 8, 2, 16, None, FAKE, FAKE, None, 0,
+    assert L.mol_align_block_size(FAKE, None, 4, 2, 8, 2, 16, None, FAKE, FAKE, None, 0, None, 0,
                                   None) == mb.MOL_E_ARG
-    assert L.mol_align_block_size(FAKE, None, 4, 2, 8, 2, 16, FAKE, FAKE, None, None, 0,
+    assert L.mol_align_block_size(FAKE, None, 4, 2, 8, 2, 16, FAKE, FAKE, None, None, 0, None, 0,
                                   None) == mb.MOL_E_ARG
     # bad sizes
-    assert L.mol_align_block_size(FAKE, None, -1, 2, 8, 2, 16, FAKE, FAKE, FAKE, None, 0,
+    assert L.mol_align_block_size(FAKE, None, -1, 2, 8, 2, 16, FAKE, FAKE, FAKE, None, 0, None, 0,
                                   None) == mb.MOL_E_ARG
-    assert L.mol_align_block_size(FAKE, None, 4, 2, 8, 2, 2048, FAKE, FAKE, FAKE, None, 0,
+    assert L.mol_align_block_size(FAKE, None, 4, 2, 8, 2, 2048, FAKE, FAKE, FAKE, None, 0, None, 0,
                                   None) == mb.MOL_E_LIMIT
     # large path without workspace
-    assert L.mol_align_block_size(FAKE, None, 5000, 1, 8, 2, 16, FAKE, FAKE, FAKE, None, 0,
+    assert L.mol_align_block_size(FAKE, None, 5000, 1, 8, 2, 16, FAKE, FAKE, FAKE, None, 0, None, 0,
                                   None) == mb.MOL_E_WORKSPACE
+
+
+def test_align_plan_sizing_and_checks():
+    L = mb.lib()
+    # the plan's room: header, numel group entries of 8 words, dense runs of 4 words
+    for numel, V, bm in ((184, 1024, 64), (1024, 2048, 64), (32768, 8064, 64),
+                         (131072, 2048, 64), (16, 8, 16), (0, 8, 16)):
+        split = 4 if (numel >= 4096 and numel >= 8 * (V + 1) and bm >= 4) else 0
+        mb_ = mb.mol_align_max_blocks(numel, V, bm)
+        dense = min(mb_, numel // split) if split else 0
+        words = 8 + 8 * numel + 4 * dense
+        assert mb.mol_plan_bytes(numel, V, bm) == -(-words * 4 // 256) * 256
+    # a plan buffer that is too small, or misaligned
+    need = mb.mol_plan_bytes(16, 16, 16)
+    assert L.mol_align_block_size(FAKE, None, 8, 2, 8, 2, 16, FAKE, FAKE, FAKE, FAKE, need - 4,
+                                  None, 0, None) == mb.MOL_E_WORKSPACE
+    assert L.mol_align_block_size(FAKE, None, 8, 2, 8, 2, 16, FAKE, FAKE, FAKE,
+                                  ctypes.c_void_p(0x1004), need, None, 0,
+                                  None) == mb.MOL_E_ALIGN
 
 
 def test_remap_rejects_before_launch():
@@ -110,39 +129,39 @@ def test_remap_rejects_before_launch():
 def test_shrink_expand_delta_reject_before_launch():
     L = mb.lib()
     # shrink: unknown dtype, K not a multiple of 16 bytes, misaligned pointer
-    assert L.mol_lora_shrink(7, FAKE, 64, 1, FAKE, 8, 64, 1, None, 8, FAKE, FAKE, FAKE, 16, 8,
+    assert L.mol_lora_shrink(7, FAKE, 64, 1, FAKE, 8, 64, 1, None, 8, FAKE, FAKE, FAKE, None, 16, 8,
                              16, FAKE, None) == mb.MOL_E_DTYPE
     assert L.mol_lora_shrink(mb.MOL_BF16, FAKE, 68, 1, FAKE, 8, 60, 1, None, 8, FAKE, FAKE,
-                             FAKE, 16, 8, 16, FAKE, None) == mb.MOL_E_ALIGN
+                             FAKE, None, 16, 8, 16, FAKE, None) == mb.MOL_E_ALIGN
     assert L.mol_lora_shrink(mb.MOL_F32, ctypes.c_void_p(0x1004), 64, 1, FAKE, 8, 64, 1, None,
-                             8, FAKE, FAKE, FAKE, 16, 8, 16, FAKE, None) == mb.MOL_E_ALIGN
+                             8, FAKE, FAKE, FAKE, None, 16, 8, 16, FAKE, None) == mb.MOL_E_ALIGN
     assert L.mol_lora_shrink(mb.MOL_F32, FAKE, 32, 1, FAKE, 8, 64, 1, None, 8, FAKE, FAKE,
-                             FAKE, 16, 8, 16, FAKE, None) == mb.MOL_E_ARG           # ld_x < K
+                             FAKE, None, 16, 8, 16, FAKE, None) == mb.MOL_E_ARG           # ld_x < K
     assert L.mol_lora_shrink(mb.MOL_BF16, FAKE, 64, 1, FAKE, 8, 64, 1, None, 8, FAKE, FAKE,
-                             FAKE, 16, 8, 16, ctypes.c_void_p(0x1008), None) == mb.MOL_E_ALIGN
+                             FAKE, None, 16, 8, 16, ctypes.c_void_p(0x1008), None) == mb.MOL_E_ALIGN
     assert L.mol_lora_shrink(mb.MOL_BF16, FAKE, 64, 1, FAKE, 8, 64, 3, None, 8, FAKE, FAKE,
-                             FAKE, 16, 8, 16, FAKE, None) == mb.MOL_E_ARG     # R % slices
+                             FAKE, None, 16, 8, 16, FAKE, None) == mb.MOL_E_ARG     # R % slices
     assert L.mol_lora_shrink(mb.MOL_BF16, FAKE, 64, 1, FAKE, 8, 64, 1, None, 3, FAKE, FAKE,
-                             FAKE, 16, 8, 16, FAKE, None) == mb.MOL_E_ARG     # V % E
+                             FAKE, None, 16, 8, 16, FAKE, None) == mb.MOL_E_ARG     # V % E
     # expand: R % slices, rank too large, V not a multiple of E
     assert L.mol_lora_expand(mb.MOL_BF16, FAKE, 63, 2, FAKE, 32, FAKE, None, 4, FAKE, FAKE,
-                             FAKE, 16, 8, 16, FAKE, 32, None) == mb.MOL_E_ARG
+                             FAKE, None, 16, 8, 16, FAKE, 32, None) == mb.MOL_E_ARG
     assert L.mol_lora_expand(mb.MOL_BF16, FAKE, 512, 2, FAKE, 32, FAKE, None, 4, FAKE, FAKE,
-                             FAKE, 16, 8, 16, FAKE, 32, None) == mb.MOL_E_LIMIT
+                             FAKE, None, 16, 8, 16, FAKE, 32, None) == mb.MOL_E_LIMIT
     assert L.mol_lora_expand(mb.MOL_BF16, FAKE, 16, 1, FAKE, 32, FAKE, None, 3, FAKE, FAKE,
-                             FAKE, 16, 8, 16, FAKE, 32, None) == mb.MOL_E_ARG
+                             FAKE, None, 16, 8, 16, FAKE, 32, None) == mb.MOL_E_ARG
     assert L.mol_lora_expand(mb.MOL_BF16, ctypes.c_void_p(0x1008), 16, 1, FAKE, 32, FAKE, None,
-                             4, FAKE, FAKE, FAKE, 16, 8, 16, FAKE, 32, None) == mb.MOL_E_ALIGN
+                             4, FAKE, FAKE, FAKE, None, 16, 8, 16, FAKE, 32, None) == mb.MOL_E_ALIGN
     # delta: workspace missing or too small
     assert L.mol_lora_delta(mb.MOL_BF16, FAKE, 64, 1, FAKE, 16, 64, 1, FAKE, 32, FAKE, None, 4,
-                            FAKE, FAKE, FAKE, 16, 8, 16, FAKE, 32, None, 0,
+                            FAKE, FAKE, FAKE, None, 16, 8, 16, FAKE, 32, None, 0,
                             None) == mb.MOL_E_WORKSPACE
     assert L.mol_lora_delta(mb.MOL_BF16, FAKE, 64, 1, FAKE, 16, 64, 1, FAKE, 32, FAKE, None, 4,
-                            FAKE, FAKE, FAKE, 16, 8, 16, FAKE, 32, FAKE, 64,
+                            FAKE, FAKE, FAKE, None, 16, 8, 16, FAKE, 32, FAKE, 64,
                             None) == mb.MOL_E_WORKSPACE
     # numel == 0 is a no-op
     assert L.mol_lora_delta(mb.MOL_BF16, None, 64, 1, None, 16, 64, 1, None, 32, None, None, 4,
-                            None, None, None, 0, 8, 16, None, 32, None, 0, None) == mb.MOL_OK
+                            None, None, None, None, 0, 8, 16, None, 32, None, 0, None) == mb.MOL_OK
 
 
 def test_noalloc_delta_rejects_before_launch():
@@ -150,7 +169,7 @@ def test_noalloc_delta_rejects_before_launch():
 
     def noalloc(numel=16, R=16, K=64, out=FAKE, dtype=mb.MOL_BF16):
         return L.mol_lora_delta_noalloc(dtype, FAKE, K, 1, FAKE, R, K, 1, FAKE, 32, FAKE, None,
-                                        4, FAKE, FAKE, FAKE, numel, 8, 16, out, 32, None)
+                                        4, FAKE, FAKE, FAKE, None, numel, 8, 16, out, 32, None)
 
     # s of numel * R floats must fit the library's scratch
     assert noalloc(numel=mb.MOL_DELTA_SCRATCH_FLOATS // 16 + 1) == mb.MOL_E_LIMIT

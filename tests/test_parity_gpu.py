@@ -136,6 +136,40 @@ def test_remap_and_align_bit_exact(cfg):
     torch.cuda.synchronize()
 
 
+PLAN_MARK = -7  # what the tests fill a plan buffer with before the align
+
+
+def check_plan(cfg, plan_t, routing):
+    """The align's work plan on the device equals its rebuild from the oracle's routing;
+    without a dense split the align leaves the buffer (filled with PLAN_MARK) untouched."""
+    srt, eid, npp = routing
+    split, groups, dense = pins.expected_plan(cfg.numel, cfg.V, cfg.block_m, srt, eid, npp)
+    plan = plan_t.cpu().numpy()
+    if split == 0:
+        assert np.all(plan == PLAN_MARK), f"{cfg.name}: plan written without a split"
+        return
+    assert tuple(plan[:3]) == (len(groups), len(dense), split), cfg.name
+    g = plan[8:8 + 8 * len(groups)].reshape(-1, 8)
+    if groups:
+        want = np.array(groups, dtype=np.int64)
+        assert np.array_equal(g[:, [0, 1, 2, 4, 5, 6, 7]], want), f"{cfg.name}: group entries"
+    d0 = 8 + 8 * cfg.numel
+    d = plan[d0:d0 + 4 * len(dense)].reshape(-1, 4)
+    if dense:
+        assert np.array_equal(d[:, :3], np.array(dense, dtype=np.int64)), f"{cfg.name}: runs"
+
+
+@pytest.mark.parametrize("cfg", ALL, ids=IDS)
+def test_align_work_plan(cfg):
+    announce(f"[plan] {cfg.name}")
+    case = get_case(cfg)
+    dl = DeviceLayer(case.inp)
+    dl.plan.fill_(PLAN_MARK)
+    dl.align()
+    check_plan(cfg, dl.plan, case.routing)
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("cfg", ALL, ids=IDS)
 def test_shrink_expand_and_fused_delta_parity(cfg):
     announce(f"[delta] {cfg.name}")
@@ -276,14 +310,21 @@ def test_edge_cases(cfg):
     announce(f"[edge] {cfg.name}")
     case = Case(cfg)
     dl = DeviceLayer(case.inp)
+    dl.plan.fill_(PLAN_MARK)
     dl.align()
     srt, eid, npp = dl.routing_host()
     assert npp == case.routing[2]
     assert np.array_equal(srt, case.routing[0]) and np.array_equal(eid, case.routing[1])
     assert npp // cfg.block_m <= dl.max_blocks
+    check_plan(cfg, dl.plan, case.routing)
+    blockwise = DeviceLayer(case.inp, use_plan=False)  # the same calls without the plan
+    blockwise.align()
     for si, st in enumerate(cfg.stages):
         dl.delta(si)
+        blockwise.delta(si)
         got = as_f64(dl.out_host(si), cfg)
+        within_tol(as_f64(blockwise.out_host(si), cfg)[case.rows],
+                   as_f64(case.out[si], cfg)[case.rows], f"{cfg.name}/{st.name} (no plan)")
         within_tol(got[case.rows], as_f64(case.out[si], cfg)[case.rows],
                    f"{cfg.name}/{st.name}")
         assert np.all(got[case.no_delta] == 0)
@@ -311,12 +352,15 @@ def test_align_sizes_at_kernel_bounds(M, k, E, S, bm):
     ids = rng.integers(-2, E + 2, size=(M, k)).astype(np.int32)
     lora = rng.integers(-1, S + 1, size=M).astype(np.int32)
     srt, eid, npp = oracle.align_block_size(ids, lora, E, S, bm)
+    plan = mb.new_plan(M * k, E * S, bm, "cuda").fill_(PLAN_MARK)
     s2, e2, n2 = mb.mol_align_block_size(torch.from_numpy(ids).cuda(),
-                                         torch.from_numpy(lora).cuda(), E, S, bm)
+                                         torch.from_numpy(lora).cuda(), E, S, bm, plan=plan)
     n2 = int(n2.item())
     assert n2 == npp
     assert np.array_equal(s2[:n2].cpu().numpy(), srt)
     assert np.array_equal(e2[: n2 // bm].cpu().numpy(), eid)
+    cfg = configs.scaled(configs.C1, name="bounds", M=M, topk=k, E=E, S=S, block_m=bm)
+    check_plan(cfg, plan, (srt, eid, npp))
 
 
 def test_empty_batch():

@@ -27,17 +27,19 @@ SIGNATURES = {
     "mol_virtual_topk": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _P, _P]),
     "mol_align_max_blocks": (_I64, [_I64, _I32, _I32]),
     "mol_align_workspace_bytes": (_I64, [_I64, _I32, _I32]),
+    "mol_plan_bytes": (_I64, [_I64, _I32, _I32]),
     "mol_align_block_size": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _SZ,
-                                    _P]),
+                                    _P, _SZ, _P]),
     "mol_lora_shrink": (_I32, [_I32, _P, _I64, _I32, _P, _I32, _I32, _I32, _P, _I32, _P, _P,
-                               _P, _I32, _I32, _I32, _P, _P]),
-    "mol_lora_expand": (_I32, [_I32, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _P, _P, _I32,
-                               _I32, _I32, _P, _I64, _P]),
+                               _P, _P, _I32, _I32, _I32, _P, _P]),
+    "mol_lora_expand": (_I32, [_I32, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _P, _P, _P,
+                               _I32, _I32, _I32, _P, _I64, _P]),
     "mol_delta_workspace_bytes": (_I64, [_I32, _I32, _I32, _I32]),
     "mol_lora_delta": (_I32, [_I32, _P, _I64, _I32, _P, _I32, _I32, _I32, _P, _I32, _P, _P,
-                              _I32, _P, _P, _P, _I32, _I32, _I32, _P, _I64, _P, _SZ, _P]),
+                              _I32, _P, _P, _P, _P, _I32, _I32, _I32, _P, _I64, _P, _SZ, _P]),
     "mol_lora_delta_noalloc": (_I32, [_I32, _P, _I64, _I32, _P, _I32, _I32, _I32, _P, _I32, _P,
-                                      _P, _I32, _P, _P, _P, _I32, _I32, _I32, _P, _I64, _P]),
+                                      _P, _I32, _P, _P, _P, _P, _I32, _I32, _I32, _P, _I64,
+                                      _P]),
     "mol_moe_gemm": (_I32, [_I32, _P, _I64, _I32, _P, _I32, _I32, _I32, _P, _P, _P, _I32, _I32,
                             _P, _I64, _P, _I32, _I32, _P, _P, _P, _P, _I32, _I32, _P]),
     "mol_moe_combine": (_I32, [_I32, _P, _I64, _P, _P, _I32, _I32, _I32, _I32, _P, _I64, _P]),
@@ -122,6 +124,19 @@ def mol_align_workspace_bytes(numel: int, num_virtual: int, block_m: int) -> int
     return int(v)
 
 
+def mol_plan_bytes(numel: int, num_virtual: int, block_m: int) -> int:
+    v = lib().mol_plan_bytes(numel, num_virtual, block_m)
+    if v < 0:
+        raise MolError("mol_plan_bytes", -v)
+    return int(v)
+
+
+def new_plan(numel: int, num_virtual: int, block_m: int, device):
+    """A buffer for the align's work plan (int32; written by mol_align_block_size)."""
+    n = mol_plan_bytes(numel, num_virtual, block_m)
+    return torch.empty(max(64, n // 4), dtype=torch.int32, device=device)
+
+
 def mol_delta_workspace_bytes(numel: int, R: int, num_virtual: int, block_m: int) -> int:
     v = lib().mol_delta_workspace_bytes(numel, R, num_virtual, block_m)
     if v < 0:
@@ -147,8 +162,9 @@ def mol_virtual_topk(topk_ids, lora_ids, num_experts: int, num_slots: int, out=N
 
 def mol_align_block_size(ids, lora_ids, num_experts: int, num_slots: int, block_m: int,
                          sorted_ids=None, expert_ids=None, num_post_padded=None,
-                         workspace=None):
-    """Returns (sorted_ids, expert_ids, num_post_padded) sized by mol_align_max_blocks."""
+                         workspace=None, plan=None):
+    """Returns (sorted_ids, expert_ids, num_post_padded) sized by mol_align_max_blocks. With
+    plan (an int32 tensor of mol_plan_bytes), the work plan is written there as well."""
     _need(ids, "ids", torch.int32)
     if lora_ids is not None:
         _need(lora_ids, "lora_ids", torch.int32)
@@ -165,9 +181,12 @@ def mol_align_block_size(ids, lora_ids, num_experts: int, num_slots: int, block_
     wsb = mol_align_workspace_bytes(M * k, V, block_m)
     if wsb and workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    if plan is not None:
+        _need(plan, "plan", torch.int32)
     _check("mol_align_block_size", lib().mol_align_block_size(
         _ptr(ids), _ptr(lora_ids), M, k, num_experts, num_slots, block_m, _ptr(sorted_ids),
-        _ptr(expert_ids), _ptr(num_post_padded), _ptr(workspace) if wsb else None,
+        _ptr(expert_ids), _ptr(num_post_padded), _ptr(plan),
+        plan.numel() * 4 if plan is not None else 0, _ptr(workspace) if wsb else None,
         workspace.numel() if (wsb and workspace is not None) else 0, _stream(ids)))
     return sorted_ids, expert_ids, num_post_padded
 
@@ -180,7 +199,7 @@ def _ranks(slot_ranks):
 
 def mol_lora_shrink(xin, row_div: int, A, sorted_ids, expert_ids, num_post_padded,
                     numel: int, num_virtual: int, block_m: int, s=None, slices: int = 1,
-                    slot_ranks=None, num_experts: int = None):
+                    slot_ranks=None, num_experts: int = None, plan=None):
     _need(xin, "xin", contiguous=False)
     _need(A, "A")
     if xin.stride(1) != 1:
@@ -193,13 +212,13 @@ def mol_lora_shrink(xin, row_div: int, A, sorted_ids, expert_ids, num_post_padde
     _check("mol_lora_shrink", lib().mol_lora_shrink(
         _dtype_code(A), _ptr(xin), xin.stride(0), row_div, _ptr(A), R, K, slices,
         _ranks(slot_ranks), E, _ptr(sorted_ids), _ptr(expert_ids), _ptr(num_post_padded),
-        numel, num_virtual, block_m, _ptr(s), _stream(A)))
+        _ptr(plan), numel, num_virtual, block_m, _ptr(s), _stream(A)))
     return s
 
 
 def mol_lora_expand(s, slices: int, B, slot_scale, num_experts: int, sorted_ids, expert_ids,
                     num_post_padded, numel: int, num_virtual: int, block_m: int, out,
-                    slot_ranks=None):
+                    slot_ranks=None, plan=None):
     _need(B, "B")
     _need(s, "s", torch.float32)
     _need(slot_scale, "slot_scale", torch.float32)
@@ -210,8 +229,8 @@ def mol_lora_expand(s, slices: int, B, slot_scale, num_experts: int, sorted_ids,
     _check("mol_lora_expand", lib().mol_lora_expand(
         _dtype_code(B), _ptr(s), s.shape[1], slices, _ptr(B), N, _ptr(slot_scale),
         _ranks(slot_ranks), num_experts, _ptr(sorted_ids), _ptr(expert_ids),
-        _ptr(num_post_padded), numel, num_virtual, block_m, _ptr(out), out.stride(0),
-        _stream(B)))
+        _ptr(num_post_padded), _ptr(plan), numel, num_virtual, block_m, _ptr(out),
+        out.stride(0), _stream(B)))
     return out
 
 
@@ -223,7 +242,7 @@ def new_delta_workspace(numel: int, R: int, num_virtual: int, block_m: int, devi
 
 def mol_lora_delta(xin, row_div: int, A, slices: int, B, slot_scale, num_experts: int,
                    sorted_ids, expert_ids, num_post_padded, numel: int, num_virtual: int,
-                   block_m: int, out, workspace, slot_ranks=None):
+                   block_m: int, out, workspace, slot_ranks=None, plan=None):
     _need(xin, "xin", contiguous=False)
     _need(A, "A")
     _need(B, "B")
@@ -237,14 +256,14 @@ def mol_lora_delta(xin, row_div: int, A, slices: int, B, slot_scale, num_experts
     _check("mol_lora_delta", lib().mol_lora_delta(
         _dtype_code(A), _ptr(xin), xin.stride(0), row_div, _ptr(A), R, K, slices, _ptr(B), N,
         _ptr(slot_scale), _ranks(slot_ranks), num_experts, _ptr(sorted_ids), _ptr(expert_ids),
-        _ptr(num_post_padded), numel, num_virtual, block_m, _ptr(out), out.stride(0),
+        _ptr(num_post_padded), _ptr(plan), numel, num_virtual, block_m, _ptr(out), out.stride(0),
         _ptr(workspace), workspace.numel(), _stream(A)))
     return out
 
 
 def mol_lora_delta_noalloc(xin, row_div: int, A, slices: int, B, slot_scale, num_experts: int,
                            sorted_ids, expert_ids, num_post_padded, numel: int,
-                           num_virtual: int, block_m: int, out, slot_ranks=None):
+                           num_virtual: int, block_m: int, out, slot_ranks=None, plan=None):
     """mol_lora_delta with s in the library's own per-GPU scratch: no workspace argument and
     nothing allocated (numel * R <= MOL_DELTA_SCRATCH_FLOATS; calls that overlap on one
     GPU race)."""
@@ -260,7 +279,7 @@ def mol_lora_delta_noalloc(xin, row_div: int, A, slices: int, B, slot_scale, num
     _check("mol_lora_delta_noalloc", lib().mol_lora_delta_noalloc(
         _dtype_code(A), _ptr(xin), xin.stride(0), row_div, _ptr(A), R, K, slices, _ptr(B), N,
         _ptr(slot_scale), _ranks(slot_ranks), num_experts, _ptr(sorted_ids), _ptr(expert_ids),
-        _ptr(num_post_padded), numel, num_virtual, block_m, _ptr(out), out.stride(0),
+        _ptr(num_post_padded), _ptr(plan), numel, num_virtual, block_m, _ptr(out), out.stride(0),
         _stream(A)))
     return out
 

@@ -37,6 +37,29 @@ int device_lds_bytes() {
 }
 
 
+// Compute units of the current device, cached per device (the plan-driven grids are at
+// most what the chip holds at once).
+std::atomic<int> g_cus[64];
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = g_cus[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int attr = 0;
+    if (hipDeviceGetAttribute(&attr, hipDeviceAttributeMultiprocessorCount, dev) !=
+            hipSuccess ||
+        attr <= 0)
+      attr = 256;
+    v = attr;
+    g_cus[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// Workgroups the plan-driven kernels keep resident per compute unit.
+constexpr int64_t kPlanGroupsPerCU = 8;
+
 mol_status hip_status(hipError_t e) { return e == hipSuccess ? MOL_OK : MOL_E_HIP; }
 
 // number of blocks any routing of numel pairs over V virtual experts can produce
@@ -146,7 +169,7 @@ MOL_API const char* mol_status_string(mol_status status) {
   }
 }
 
-MOL_API int32_t mol_abi_version(void) { return 5; }
+MOL_API int32_t mol_abi_version(void) { return 6; }
 
 MOL_API mol_status mol_virtual_topk(const int32_t* topk_ids, const int32_t* lora_ids,
                                     int32_t M, int32_t topk, int32_t num_experts,
@@ -174,11 +197,19 @@ MOL_API int64_t mol_align_workspace_bytes(int64_t numel, int32_t num_virtual,
   return round256((ntiles * nb + nb) * (int64_t)sizeof(int32_t));
 }
 
+MOL_API int64_t mol_plan_bytes(int64_t numel, int32_t num_virtual, int32_t block_m) {
+  const int64_t mb = align_check(numel, num_virtual, block_m);
+  if (mb < 0) return mb;
+  const int32_t split = mol::plan_split(numel, num_virtual, block_m);
+  return round256(mol::plan_words(numel, mb, split) * (int64_t)sizeof(int32_t));
+}
+
 MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_ids,
                                         int32_t M, int32_t topk, int32_t num_experts,
                                         int32_t num_slots, int32_t block_m,
                                         int32_t* sorted_ids, int32_t* expert_ids,
-                                        int32_t* num_post_padded, void* workspace,
+                                        int32_t* num_post_padded, int32_t* plan,
+                                        size_t plan_bytes, void* workspace,
                                         size_t workspace_bytes, void* stream) {
   if (M < 0 || topk < 1 || num_experts < 1 || num_slots < 1 || block_m < 1)
     return MOL_E_ARG;
@@ -191,8 +222,18 @@ MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_
   if (numel > 0 && (!ids || !sorted_ids || !expert_ids)) return MOL_E_ARG;
   const int64_t need = mol_align_workspace_bytes(numel, (int32_t)V64, block_m);
   if (need > 0 && (!workspace || workspace_bytes < (size_t)need)) return MOL_E_WORKSPACE;
+  if (plan) {
+    const int64_t pneed = mol_plan_bytes(numel, (int32_t)V64, block_m);
+    if (pneed < 0) return (mol_status)(-pneed);
+    if (plan_bytes < (size_t)pneed) return MOL_E_WORKSPACE;
+    if (!aligned16(plan)) return MOL_E_ALIGN;
+  }
 
   mol::AlignArgs a{};
+  a.split = mol::plan_split(numel, V64, block_m);
+  a.plan = a.split > 0 ? plan : nullptr;  // no dense split: nothing to plan
+  a.gmax = (int32_t)mol::plan_max_groups(numel);
+  a.max_blocks = (int32_t)mb;
   a.ids = ids;
   a.lora = lora_ids;
   a.topk = topk;
@@ -212,8 +253,8 @@ MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_
   if (numel <= mol::kAlignSmallMax) {
     // counter rows + bucket starts + scan scratch + per pair a bucket id and a rank
     // (uint16 each)
-    const int64_t fixed =
-        ((int64_t)nb + 64) * (int64_t)sizeof(int) + ((numel + 1) & ~1LL) * 2 * 2;
+    const int64_t fixed = ((int64_t)nb * (plan ? 2 : 1) + 64) * (int64_t)sizeof(int) +
+                          ((numel + 1) & ~1LL) * 2 * 2;
     int64_t waves = (device_lds_bytes() - fixed) / ((int64_t)nb * (int64_t)sizeof(int));
     // walkers: one chunk of 64 pairs each for the smallest batches, two chunks each above
     // (more walkers shorten the walk but add counter rows to every bucket's sums)
@@ -269,21 +310,42 @@ int32_t expand_mfma_min(bool bf16, int32_t numel, int32_t num_virtual, int32_t b
 }
 
 // VALU shrink over every block (skipping the MFMA ones), then the MFMA shrink if enabled.
+// When the MFMA kernels take the dense blocks (those with at least `split` pairs) and a plan
+// is given, the VALU kernels take the remaining small blocks from the plan's group entries;
+// otherwise (and without a plan) their grid spans every possible block.
 hipError_t shrink_all(mol::DeltaArgs a, bool bf16, int rpi, int64_t grid, int32_t mfma_min,
-                      hipStream_t st) {
+                      const int32_t* plan, hipStream_t st) {
   a.mfma_min = mfma_min;
   mol::with_divisors(a);
-  hipError_t e = mol::launch_shrink(a, bf16, rpi, (int)grid, st);
+  const int32_t split = mol::plan_split(a.numel, a.V, a.BM);
+  hipError_t e;
+  if (plan && split > 0 && mfma_min == split) {
+    const int64_t items =
+        std::min<int64_t>(mol::plan_max_groups(a.numel) * a.rgroups, int64_t(1) << 30);
+    const int64_t g = std::min<int64_t>(items, device_cus() * kPlanGroupsPerCU);
+    e = mol::launch_shrink_plan(a, plan, (int)items, bf16, rpi, (int)g, st);
+  } else {
+    e = mol::launch_shrink(a, bf16, rpi, (int)grid, st);
+  }
   if (e != hipSuccess || mfma_min == 0) return e;
   return mol::launch_shrink_mfma(
       a, (int)(a.max_blocks * cdiv64(a.R, mol::shrink_mfma_row_tile(a.R))), st);
 }
 
 hipError_t expand_all(mol::DeltaArgs a, bool bf16, int64_t grid, int32_t mfma_min,
-                      hipStream_t st) {
+                      const int32_t* plan, hipStream_t st) {
   a.mfma_min = mfma_min;
   mol::with_divisors(a);
-  hipError_t e = mol::launch_expand(a, bf16, (int)grid, st);
+  const int32_t split = mol::plan_split(a.numel, a.V, a.BM);
+  hipError_t e;
+  if (plan && split > 0 && mfma_min == split) {
+    const int64_t items =
+        std::min<int64_t>(mol::plan_max_groups(a.numel) * a.nchunk, int64_t(1) << 30);
+    const int64_t g = std::min<int64_t>(items, device_cus() * kPlanGroupsPerCU);
+    e = mol::launch_expand_plan(a, plan, (int)items, bf16, (int)g, st);
+  } else {
+    e = mol::launch_expand(a, bf16, (int)grid, st);
+  }
   if (e != hipSuccess || mfma_min == 0) return e;
   return mol::launch_expand_mfma(a, (int)grid, st);
 }
@@ -350,7 +412,7 @@ mol_status delta_enqueue(int32_t dtype, const void* xin, int64_t ld_x, int32_t r
                          int32_t num_experts, const int32_t* sorted_ids,
                          const int32_t* expert_ids, const int32_t* num_post_padded,
                          int32_t numel, int32_t num_virtual, int32_t block_m, void* out,
-                         int64_t ld_out, float* s, hipStream_t st) {
+                         int64_t ld_out, float* s, const int32_t* plan, hipStream_t st) {
   const bool bf16 = dtype == MOL_BF16;
   const int esz = bf16 ? 2 : 4;
   const int64_t mb = max_blocks_of(numel, num_virtual, block_m);
@@ -366,8 +428,8 @@ mol_status delta_enqueue(int32_t dtype, const void* xin, int64_t ld_x, int32_t r
   const int32_t mm_s = shrink_mfma_min(bf16, numel, num_virtual, block_m);
   const int32_t mm_e =
       expand_mfma_min(bf16, numel, num_virtual, block_m, R, slices, N, out, ld_out);
-  if (shrink_all(a, bf16, rpi, grid_s, mm_s, st) != hipSuccess) return MOL_E_HIP;
-  return hip_status(expand_all(a, bf16, grid_e, mm_e, st));
+  if (shrink_all(a, bf16, rpi, grid_s, mm_s, plan, st) != hipSuccess) return MOL_E_HIP;
+  return hip_status(expand_all(a, bf16, grid_e, mm_e, plan, st));
 }
 
 }  // namespace
@@ -379,7 +441,7 @@ MOL_API mol_status mol_lora_shrink(int32_t dtype, const void* xin, int64_t ld_x,
                                    int32_t slices, const int32_t* slot_ranks,
                                    int32_t num_experts, const int32_t* sorted_ids,
                                    const int32_t* expert_ids, const int32_t* num_post_padded,
-                                   int32_t numel, int32_t num_virtual, int32_t block_m,
+                                   const int32_t* plan, int32_t numel, int32_t num_virtual, int32_t block_m,
                                    float* s, void* stream) {
   const StageCheck rc =
       routing_check(sorted_ids, expert_ids, num_post_padded, numel, num_virtual, block_m);
@@ -401,7 +463,7 @@ MOL_API mol_status mol_lora_shrink(int32_t dtype, const void* xin, int64_t ld_x,
   a.rgroups = (int32_t)rgroups;
   const int32_t mm = shrink_mfma_min(bf16, numel, num_virtual, block_m);
   if (mm > 0 && rc.max_blocks * cdiv64(R, 64) > kI32Max) return MOL_E_LIMIT;
-  return hip_status(shrink_all(a, bf16, rpi, grid, mm, (hipStream_t)stream));
+  return hip_status(shrink_all(a, bf16, rpi, grid, mm, plan, (hipStream_t)stream));
 }
 
 MOL_API mol_status mol_lora_expand(int32_t dtype, const float* s, int32_t R, int32_t slices,
@@ -409,9 +471,9 @@ MOL_API mol_status mol_lora_expand(int32_t dtype, const float* s, int32_t R, int
                                    const int32_t* slot_ranks, int32_t num_experts,
                                    const int32_t* sorted_ids,
                                    const int32_t* expert_ids,
-                                   const int32_t* num_post_padded, int32_t numel,
-                                   int32_t num_virtual, int32_t block_m, void* out,
-                                   int64_t ld_out, void* stream) {
+                                   const int32_t* num_post_padded, const int32_t* plan,
+                                   int32_t numel, int32_t num_virtual, int32_t block_m,
+                                   void* out, int64_t ld_out, void* stream) {
   const StageCheck rc =
       routing_check(sorted_ids, expert_ids, num_post_padded, numel, num_virtual, block_m);
   if (rc.st != MOL_OK) return rc.st;
@@ -432,7 +494,7 @@ MOL_API mol_status mol_lora_expand(int32_t dtype, const float* s, int32_t R, int
   if (grid > kI32Max) return MOL_E_LIMIT;
   const int32_t mm =
       expand_mfma_min(bf16, numel, num_virtual, block_m, R, slices, N, out, ld_out);
-  return hip_status(expand_all(a, bf16, grid, mm, (hipStream_t)stream));
+  return hip_status(expand_all(a, bf16, grid, mm, plan, (hipStream_t)stream));
 }
 
 MOL_API int64_t mol_delta_workspace_bytes(int32_t numel, int32_t R, int32_t num_virtual,
@@ -449,10 +511,10 @@ MOL_API mol_status mol_lora_delta(int32_t dtype, const void* xin, int64_t ld_x,
                                   const float* slot_scale, const int32_t* slot_ranks,
                                   int32_t num_experts,
                                   const int32_t* sorted_ids, const int32_t* expert_ids,
-                                  const int32_t* num_post_padded, int32_t numel,
-                                  int32_t num_virtual, int32_t block_m, void* out,
-                                  int64_t ld_out, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
+                                  const int32_t* num_post_padded, const int32_t* plan,
+                                  int32_t numel, int32_t num_virtual, int32_t block_m,
+                                  void* out, int64_t ld_out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
   const mol_status c =
       delta_check(dtype, xin, ld_x, row_div, A, R, K, slices, B, N, slot_scale, num_experts,
                   sorted_ids, expert_ids, num_post_padded, numel, num_virtual, block_m, out,
@@ -464,7 +526,7 @@ MOL_API mol_status mol_lora_delta(int32_t dtype, const void* xin, int64_t ld_x,
   if (!aligned16(workspace)) return MOL_E_ALIGN;
   return delta_enqueue(dtype, xin, ld_x, row_div, A, R, K, slices, B, N, slot_scale,
                        slot_ranks, num_experts, sorted_ids, expert_ids, num_post_padded, numel,
-                       num_virtual, block_m, out, ld_out, static_cast<float*>(workspace),
+                       num_virtual, block_m, out, ld_out, static_cast<float*>(workspace), plan,
                        (hipStream_t)stream);
 }
 
@@ -474,9 +536,9 @@ MOL_API mol_status mol_lora_delta_noalloc(int32_t dtype, const void* xin, int64_
                                           const float* slot_scale, const int32_t* slot_ranks,
                                           int32_t num_experts, const int32_t* sorted_ids,
                                           const int32_t* expert_ids,
-                                          const int32_t* num_post_padded, int32_t numel,
-                                          int32_t num_virtual, int32_t block_m, void* out,
-                                          int64_t ld_out, void* stream) {
+                                          const int32_t* num_post_padded, const int32_t* plan,
+                                          int32_t numel, int32_t num_virtual, int32_t block_m,
+                                          void* out, int64_t ld_out, void* stream) {
   const mol_status c =
       delta_check(dtype, xin, ld_x, row_div, A, R, K, slices, B, N, slot_scale, num_experts,
                   sorted_ids, expert_ids, num_post_padded, numel, num_virtual, block_m, out,
@@ -488,7 +550,7 @@ MOL_API mol_status mol_lora_delta_noalloc(int32_t dtype, const void* xin, int64_
   if (sc != MOL_OK) return sc;
   return delta_enqueue(dtype, xin, ld_x, row_div, A, R, K, slices, B, N, slot_scale,
                        slot_ranks, num_experts, sorted_ids, expert_ids, num_post_padded, numel,
-                       num_virtual, block_m, out, ld_out, s, (hipStream_t)stream);
+                       num_virtual, block_m, out, ld_out, s, plan, (hipStream_t)stream);
 }
 
 // ---- base grouped GEMM, alone or with the LoRA delta in its epilogue -----------------

@@ -39,6 +39,21 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRowsPerPass = 64;  // pairs of a block per pass (4 waves x 16)
 constexpr int kKChunk = 128;      // shrink: k elements staged per chunk at 64 rows
+constexpr int kXcds = 8;          // accelerator dies (XCDs), each with its own L2
+
+// Workgroups are handed to the XCDs in turn (workgroup i to XCD i % 8). The shrink's item
+// of workgroup i is remapped so that each XCD works through one contiguous eighth of the
+// items in order: the workgroups resident on an XCD at one time then take neighbouring
+// blocks, mostly of the same virtual expert, and share its weight tiles through that XCD's
+// L2. The grid is n_items rounded up to a multiple of 8; items past n_items are empty.
+// (The expand's items vary more in cost, with the pairs a block holds; grouping them by
+// XCD unbalanced the dies and made it slower, so it keeps the plain order.)
+__device__ __forceinline__ int xcd_item(int n_items) {
+  const int per = (n_items + kXcds - 1) / kXcds;
+  const int wg = (int)blockIdx.x;
+  return (wg % kXcds) * per + wg / kXcds;
+}
+inline int xcd_grid(int n_items) { return (n_items + kXcds - 1) / kXcds * kXcds; }
 
 __device__ __forceinline__ floatx4_t mfma16(const uint4& a, const uint4& b, floatx4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8_t*>(&a),
@@ -117,14 +132,16 @@ __device__ __forceinline__ void load_x(const DeltaArgs& a, int p, bool real, int
 }
 
 template <int NRT>
-__global__ void __launch_bounds__(256) shrink_mfma_kernel(DeltaArgs a) {
+__global__ void __launch_bounds__(256) shrink_mfma_kernel(DeltaArgs a, int n_items) {
   using G = ShrinkGeom<NRT>;
   constexpr int NT = 4 * NRT;  // 16-row tiles of A_v per wave
   __shared__ __attribute__((aligned(16))) uint4 wt[2][1024];  // 2 x 16 KiB
   __shared__ int pid[kRowsPerPass];
   __shared__ int nrows_lds;
   const int nrt = (a.R + G::kRows - 1) / G::kRows;
-  const int blk = blockIdx.x / nrt, r0 = (blockIdx.x % nrt) * G::kRows;
+  const int item = xcd_item(n_items);
+  if (item >= n_items) return;
+  const int blk = item / nrt, r0 = (item % nrt) * G::kRows;
   const int e = block_expert(a, blk);
   if (e < 0 || !block_has(a, blk, a.mfma_min)) return;
   const int rl = slot_rank(a, e), r = a.R / a.slices;  // rows past the rank store 0
@@ -375,11 +392,12 @@ __global__ void __launch_bounds__(256) expand_mfma_kernel(DeltaArgs a) {
 
 int shrink_mfma_row_tile(int32_t R) { return R > 64 ? 128 : 64; }
 
-hipError_t launch_shrink_mfma(const DeltaArgs& a, int grid, hipStream_t stream) {
+hipError_t launch_shrink_mfma(const DeltaArgs& a, int items, hipStream_t stream) {
+  const dim3 grid(xcd_grid(items));
   if (shrink_mfma_row_tile(a.R) == 128)
-    hipLaunchKernelGGL((shrink_mfma_kernel<2>), dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((shrink_mfma_kernel<2>), grid, dim3(256), 0, stream, a, items);
   else
-    hipLaunchKernelGGL((shrink_mfma_kernel<1>), dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((shrink_mfma_kernel<1>), grid, dim3(256), 0, stream, a, items);
   return hipGetLastError();
 }
 

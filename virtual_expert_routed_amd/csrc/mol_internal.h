@@ -15,6 +15,41 @@ constexpr int kMfmaMinPairs = 4;         // a block takes the MFMA path from thi
 constexpr int kMfmaMinNumel = 4096;      // MFMA kernels are launched from this many pairs
 constexpr int kMaxRankVecs = 16;         // 16-byte vectors in one rank row slice (256 bytes)
 
+// The work plan the align writes beside the routing when asked (int32 words):
+//   [0] number of group entries G, [1] number of dense entries D, [2] the split, [3..7] 0;
+//   group entries from word kPlanHeader, kPlanGroupInts each, for at most gmax = numel:
+//     {block, virtual expert, nq (1..4), 0, p0, p1, p2, p3}: up to four consecutive real
+//     pairs of one block (numel in the slots past nq), in bucket and block order;
+//   dense entries after the gmax group entries, kPlanDenseInts each:
+//     {first block, blocks (1..kPlanDenseBlocks), virtual expert, 0}: consecutive blocks
+//     of one bucket that each hold at least `split` real pairs, in bucket order.
+// A block with at least `split` real pairs (split > 0) goes to the dense entries, any other
+// block of a real bucket to the group entries; the sentinel bucket gets no entries.
+constexpr int kPlanHeader = 8;
+constexpr int kPlanGroupInts = 8;
+constexpr int kPlanDenseInts = 4;
+constexpr int kPlanDenseBlocks = 4;
+
+// The split: blocks with at least this many real pairs are dense (0: none are). Dense
+// blocks are worth their own kernels only for batches large enough to hold them in
+// numbers: from 4096 pairs and 8 pairs per bucket on average, and BLOCK_M >= 4.
+static_assert(kMfmaMinPairs <= 4, "a ragged block below the split fits one group entry");
+inline int32_t plan_split(int64_t numel, int64_t V, int32_t BM) {
+  return (numel >= kMfmaMinNumel && numel >= 8 * (V + 1) && BM >= kMfmaMinPairs)
+             ? kMfmaMinPairs
+             : 0;
+}
+inline int64_t plan_max_groups(int64_t numel) { return numel; }
+inline int64_t plan_max_dense(int64_t numel, int64_t max_blocks, int32_t split) {
+  if (split <= 0) return 0;
+  const int64_t d = numel / split;
+  return d < max_blocks ? d : max_blocks;
+}
+inline int64_t plan_words(int64_t numel, int64_t max_blocks, int32_t split) {
+  return kPlanHeader + kPlanGroupInts * plan_max_groups(numel) +
+         kPlanDenseInts * plan_max_dense(numel, max_blocks, split);
+}
+
 struct AlignArgs {
   const int32_t* ids;
   const int32_t* lora;   // nullptr: ids are virtual ids
@@ -37,6 +72,10 @@ struct AlignArgs {
   FastDiv f_per;         // per (walker of a pair)
   FastDiv f_bm;          // BM
   FastDiv f_groups;      // workgroups of the one-launch path
+  int32_t* plan;         // the work plan (nullptr: none is written)
+  int32_t split;         // the plan's dense threshold
+  int32_t gmax;          // group entries the plan has room for (dense entries follow)
+  int32_t max_blocks;    // the routing's block bound
 };
 
 // Tiles of the three-kernel align: at most 64 of them up to 1M pairs (the column scan walks
@@ -164,10 +203,16 @@ int expand_cols_per_item(int32_t R, int32_t slices, int elem_bytes);
 hipError_t launch_shrink(const DeltaArgs& a, bool bf16, int rows_per_item, int grid,
                          hipStream_t stream);
 hipError_t launch_expand(const DeltaArgs& a, bool bf16, int grid, hipStream_t stream);
+// the same kernels' work driven by an align work plan: `items` = group entries the plan has
+// room for times the work items per entry; grid <= items
+hipError_t launch_shrink_plan(const DeltaArgs& a, const int32_t* plan, int items, bool bf16,
+                              int rows_per_item, int grid, hipStream_t stream);
+hipError_t launch_expand_plan(const DeltaArgs& a, const int32_t* plan, int items, bool bf16,
+                              int grid, hipStream_t stream);
 // bf16 MFMA kernels for the blocks with at least a.mfma_min real pairs
 // rows of A_v per MFMA shrink work item (the grid is max_blocks * cdiv(R, this))
 int shrink_mfma_row_tile(int32_t R);
-hipError_t launch_shrink_mfma(const DeltaArgs& a, int grid, hipStream_t stream);
+hipError_t launch_shrink_mfma(const DeltaArgs& a, int items, hipStream_t stream);
 hipError_t launch_expand_mfma(const DeltaArgs& a, int grid, hipStream_t stream);
 // base grouped GEMM (+ fused delta when g.s is set): rows_per_item as for the shrink
 hipError_t launch_moe_gemm(const GemmArgs& g, bool bf16, int rows_per_item, int grid,

@@ -21,7 +21,8 @@ def to_device(a: np.ndarray, device, bf16: bool) -> torch.Tensor:
 
 
 class DeviceLayer:
-    def __init__(self, inp: LayerInputs, device="cuda", outs=None, topk_weights=None):
+    def __init__(self, inp: LayerInputs, device="cuda", outs=None, topk_weights=None,
+                 use_plan=True):
         cfg = inp.cfg
         self.cfg = cfg
         self.device = torch.device(device)
@@ -48,6 +49,8 @@ class DeviceLayer:
         self.npp = torch.empty(1, dtype=torch.int32, device=dev)
         wsb = mb.mol_align_workspace_bytes(numel, V, BM)
         self.align_ws = torch.empty(max(256, wsb), dtype=torch.uint8, device=dev)
+        # the align's work plan, which the shrink and expand calls then take their work from
+        self.plan = mb.new_plan(numel, V, BM, dev) if use_plan else None
         self.delta_ws = [mb.new_delta_workspace(numel, st.R, V, BM, dev) for st in cfg.stages]
         self.s = [torch.empty((max(1, numel), st.R), dtype=torch.float32, device=dev)
                   for st in cfg.stages]
@@ -99,7 +102,8 @@ class DeviceLayer:
     def align(self):
         c = self.cfg
         mb.mol_align_block_size(self.topk_ids, self.lora_ids, c.E, c.S, c.block_m,
-                                self.sorted_ids, self.expert_ids, self.npp, self.align_ws)
+                                self.sorted_ids, self.expert_ids, self.npp, self.align_ws,
+                                plan=self.plan)
 
     def remap(self):
         c = self.cfg
@@ -112,14 +116,15 @@ class DeviceLayer:
         c = self.cfg
         mb.mol_lora_shrink(self.xin[si], self.row_div[si], self.A[si], *self.routing(),
                            c.numel, c.V, c.block_m, s=self.s[si], slices=c.stages[si].slices,
-                           slot_ranks=self.slot_ranks, num_experts=c.E)
+                           slot_ranks=self.slot_ranks, num_experts=c.E, plan=self.plan)
         return self.s[si]
 
     def expand(self, si: int):
         c = self.cfg
         st = c.stages[si]
         mb.mol_lora_expand(self.s[si], st.slices, self.B[si], self.scale, c.E, *self.routing(),
-                           c.numel, c.V, c.block_m, self.out[si], slot_ranks=self.slot_ranks)
+                           c.numel, c.V, c.block_m, self.out[si], slot_ranks=self.slot_ranks,
+                           plan=self.plan)
         return self.out[si]
 
     def delta(self, si: int):
@@ -127,7 +132,8 @@ class DeviceLayer:
         st = c.stages[si]
         mb.mol_lora_delta(self.xin[si], self.row_div[si], self.A[si], st.slices, self.B[si],
                           self.scale, c.E, *self.routing(), c.numel, c.V, c.block_m,
-                          self.out[si], self.delta_ws[si], slot_ranks=self.slot_ranks)
+                          self.out[si], self.delta_ws[si], slot_ranks=self.slot_ranks,
+                          plan=self.plan)
         return self.out[si]
 
     def combine(self, rows=None):
