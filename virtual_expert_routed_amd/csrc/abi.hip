@@ -311,8 +311,9 @@ int32_t expand_mfma_min(bool bf16, int32_t numel, int32_t num_virtual, int32_t b
 
 // VALU shrink over every block (skipping the MFMA ones), then the MFMA shrink if enabled.
 // When the MFMA kernels take the dense blocks (those with at least `split` pairs) and a plan
-// is given, the VALU kernels take the remaining small blocks from the plan's group entries;
-// otherwise (and without a plan) their grid spans every possible block.
+// is given, the VALU kernels take the remaining small blocks from the plan's group entries
+// (and the MFMA expand takes the dense runs); otherwise (and without a plan) the grids span
+// every possible block.
 hipError_t shrink_all(mol::DeltaArgs a, bool bf16, int rpi, int64_t grid, int32_t mfma_min,
                       const int32_t* plan, hipStream_t st) {
   a.mfma_min = mfma_min;
@@ -343,9 +344,11 @@ hipError_t expand_all(mol::DeltaArgs a, bool bf16, int64_t grid, int32_t mfma_mi
         std::min<int64_t>(mol::plan_max_groups(a.numel) * a.nchunk, int64_t(1) << 30);
     const int64_t g = std::min<int64_t>(items, device_cus() * kPlanGroupsPerCU);
     e = mol::launch_expand_plan(a, plan, (int)items, bf16, (int)g, st);
-  } else {
-    e = mol::launch_expand(a, bf16, (int)grid, st);
+    if (e != hipSuccess) return e;
+    const int64_t dmax = mol::plan_max_dense(a.numel, a.max_blocks, split);
+    return mol::launch_expand_mfma_runs(a, plan, (int)(dmax * a.nchunk), st);
   }
+  e = mol::launch_expand(a, bf16, (int)grid, st);
   if (e != hipSuccess || mfma_min == 0) return e;
   return mol::launch_expand_mfma(a, (int)grid, st);
 }

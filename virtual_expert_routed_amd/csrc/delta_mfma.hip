@@ -41,17 +41,18 @@ constexpr int kRowsPerPass = 64;  // pairs of a block per pass (4 waves x 16)
 constexpr int kKChunk = 128;      // shrink: k elements staged per chunk at 64 rows
 constexpr int kXcds = 8;          // accelerator dies (XCDs), each with its own L2
 
-// Workgroups are handed to the XCDs in turn (workgroup i to XCD i % 8). The shrink's item
-// of workgroup i is remapped so that each XCD works through one contiguous eighth of the
+// Workgroups are handed to the XCDs in turn (workgroup i to XCD i % 8). The item of
+// workgroup i is remapped so that each XCD works through one contiguous eighth of the live
 // items in order: the workgroups resident on an XCD at one time then take neighbouring
-// blocks, mostly of the same virtual expert, and share its weight tiles through that XCD's
-// L2. The grid is n_items rounded up to a multiple of 8; items past n_items are empty.
-// (The expand's items vary more in cost, with the pairs a block holds; grouping them by
-// XCD unbalanced the dies and made it slower, so it keeps the plain order.)
-__device__ __forceinline__ int xcd_item(int n_items) {
-  const int per = (n_items + kXcds - 1) / kXcds;
-  const int wg = (int)blockIdx.x;
-  return (wg % kXcds) * per + wg / kXcds;
+// blocks, mostly of the same virtual expert, and share its weight tiles (and, in the
+// expand, a block's s rows across its column chunks) through that XCD's L2. The eighths
+// are of the live items (a prefix of the launched ones, counted on the device), so every
+// XCD gets its share of the work. The grid covers every possible item, rounded up to a
+// multiple of 8; a workgroup past the live items gets n_live, which is empty.
+__device__ __forceinline__ int xcd_item(int n_live) {
+  const int per = (n_live + kXcds - 1) / kXcds;
+  const int wg = (int)blockIdx.x, local = wg / kXcds;
+  return local < per ? (wg % kXcds) * per + local : n_live;
 }
 inline int xcd_grid(int n_items) { return (n_items + kXcds - 1) / kXcds * kXcds; }
 
@@ -131,81 +132,118 @@ __device__ __forceinline__ void load_x(const DeltaArgs& a, int p, bool real, int
   }
 }
 
+// One pass: wave w's 16 entries pid[16w..16w+15] (numel: not a real pair) times rows
+// r0..r0+kRows-1 of A_v, which the workgroup's four waves stream through LDS one k chunk at
+// a time (double buffered: the next chunk and the next x fragments are in flight while the
+// current one is multiplied). A wave with no real pair skips the loads and products but
+// takes part in the staging. Results go to s (rows past the slot's rank store 0).
 template <int NRT>
-__global__ void __launch_bounds__(256) shrink_mfma_kernel(DeltaArgs a, int n_items) {
+__device__ __forceinline__ void shrink_mfma_pass(const DeltaArgs& a, const char* av, int r0,
+                                                 int rl, const int* pid, uint4 (*wt)[1024]) {
   using G = ShrinkGeom<NRT>;
   constexpr int NT = 4 * NRT;  // 16-row tiles of A_v per wave
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = a.R / a.slices;
+  const int nchunks = (a.K + G::kChunk - 1) / G::kChunk;
+  const int p = pid[16 * w + (lane & 15)];
+  const bool real = real_pair(p, a.numel);
+  const bool live = __builtin_amdgcn_ballot_w64(real) != 0;  // uniform over the wave
+  floatx4_t acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  uint4 xf[G::kSteps], xn[G::kSteps];
+  stage_w<NRT>(a, av, r0, 0, wt[0]);
+  if (live) load_x<NRT>(a, p, real, 0, xf);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nchunks) {  // next chunk in flight while this one is multiplied
+      stage_w<NRT>(a, av, r0, (c + 1) * G::kChunk, wt[buf ^ 1]);
+      if (live) load_x<NRT>(a, p, real, (c + 1) * G::kChunk, xn);
+    }
+    if (live) {
+#pragma unroll
+      for (int st = 0; st < G::kSteps; ++st) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int rr = nt * 16 + (lane & 15);
+          const int slot = (4 * st + (lane >> 4)) ^ (rr & (G::kSlots - 1));
+          const uint4 wf = wt[buf][rr * G::kSlots + slot];
+          acc[nt] = mfma16(xf[st], wf, acc[nt]);
+        }
+      }
+    }
+    if (c + 1 < nchunks) {
+#pragma unroll
+      for (int st = 0; st < G::kSteps; ++st) xf[st] = xn[st];
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // chunk c+1 has landed and chunk c is no longer read
+  }
+  if (live) {
+    // result rows 4 (l/16) + i of this wave's tile = pairs, column l % 16 = row of A_v
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pi = pid[16 * w + 4 * (lane >> 4) + i];
+      if (real_pair(pi, a.numel)) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int row = r0 + nt * 16 + (lane & 15);
+          if (row < a.R) a.s[(int64_t)pi * a.R + row] = row % r < rl ? acc[nt][i] : 0.f;
+        }
+      }
+    }
+  }
+}
+
+// Registers for four workgroups per CU.
+template <int NRT>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+    shrink_mfma_kernel(DeltaArgs a, int n_items) {
+  using G = ShrinkGeom<NRT>;
   __shared__ __attribute__((aligned(16))) uint4 wt[2][1024];  // 2 x 16 KiB
   __shared__ int pid[kRowsPerPass];
   __shared__ int nrows_lds;
   const int nrt = (a.R + G::kRows - 1) / G::kRows;
-  const int item = xcd_item(n_items);
-  if (item >= n_items) return;
+  const int n_live = min(n_items, live_blocks(a, *a.npp) * nrt);
+  const int item = xcd_item(n_live);
+  if (item >= n_live) return;
   const int blk = item / nrt, r0 = (item % nrt) * G::kRows;
   const int e = block_expert(a, blk);
   if (e < 0 || !block_has(a, blk, a.mfma_min)) return;
-  const int rl = slot_rank(a, e), r = a.R / a.slices;  // rows past the rank store 0
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rl = slot_rank(a, e);
   const char* av = (const char*)a.A + (int64_t)e * a.R * a.K * 2;
-  const int nchunks = (a.K + G::kChunk - 1) / G::kChunk;
   for (int j0 = 0; j0 < a.BM; j0 += kRowsPerPass) {
     const int nrows = stage_rows(a, blk, j0, pid, &nrows_lds);
     if (nrows == 0) break;
-    const bool live = 16 * w < nrows;  // uniform over the wave
-    const int m = 16 * w + (lane & 15);
-    const int p = pid[m];
-    const bool real = m < nrows;
-    floatx4_t acc[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    uint4 xf[G::kSteps], xn[G::kSteps];
-    stage_w<NRT>(a, av, r0, 0, wt[0]);
-    if (live) load_x<NRT>(a, p, real, 0, xf);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int c = 0; c < nchunks; ++c) {
-      const int buf = c & 1;
-      if (c + 1 < nchunks) {  // next chunk in flight while this one is multiplied
-        stage_w<NRT>(a, av, r0, (c + 1) * G::kChunk, wt[buf ^ 1]);
-        if (live) load_x<NRT>(a, p, real, (c + 1) * G::kChunk, xn);
-      }
-      if (live) {
-#pragma unroll
-        for (int st = 0; st < G::kSteps; ++st) {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const int rr = nt * 16 + (lane & 15);
-            const int slot = (4 * st + (lane >> 4)) ^ (rr & (G::kSlots - 1));
-            const uint4 wf = wt[buf][rr * G::kSlots + slot];
-            acc[nt] = mfma16(xf[st], wf, acc[nt]);
-          }
-        }
-      }
-      if (c + 1 < nchunks) {
-#pragma unroll
-        for (int st = 0; st < G::kSteps; ++st) xf[st] = xn[st];
-      }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();  // chunk c+1 has landed and chunk c is no longer read
-    }
-    if (live) {
-      // result rows 4 (l/16) + i of this wave's tile = pairs, column l % 16 = row of A_v
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int mi = 16 * w + 4 * (lane >> 4) + i;
-        const int pi = pid[mi];
-        if (mi < nrows) {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const int row = r0 + nt * 16 + (lane & 15);
-            if (row < a.R) a.s[(int64_t)pi * a.R + row] = row % r < rl ? acc[nt][i] : 0.f;
-          }
-        }
-      }
-    }
+    shrink_mfma_pass<NRT>(a, av, r0, rl, pid, wt);
     if (nrows < kRowsPerPass) break;
   }
+}
+
+// ----------------------------------------------------------------- plan-driven dense runs
+// With the align's work plan the MFMA expand takes the plan's dense runs instead of single
+// blocks: up to kPlanDenseBlocks consecutive blocks of one virtual expert, each with at
+// least `split` real pairs. A run item holds its weight columns for all of its blocks,
+// where a block item loads them once per block (a hot expert's bucket of many blocks is
+// read about a quarter as often). The shrink keeps its block items: a run there needs the
+// accumulators of every block at once, and at the occupancy that leaves it measured
+// slower than block items ordered by XCD, which share A_v through L2 instead.
+
+// Dense entry `run` of the plan: {first block, blocks, virtual expert}; nb = 0 past the
+// plan's count (the entry read is then entry 0, a valid address).
+struct DenseRun {
+  int blk0, nb, e;
+};
+__device__ __forceinline__ DenseRun dense_run(const int32_t* plan, int numel, int run) {
+  const int count = plan[1];
+  const int rc = run < count ? run : 0;
+  const int4 d = *reinterpret_cast<const int4*>(plan + kPlanHeader +
+                                                (int64_t)numel * kPlanGroupInts +
+                                                (int64_t)rc * kPlanDenseInts);
+  return DenseRun{d.x, run < count ? d.y : 0, d.z};
 }
 
 // ------------------------------------------------------------------------------ expand
@@ -268,10 +306,12 @@ __device__ __forceinline__ void load_out_tile(const DeltaArgs& a, const int* pid
   }
 }
 
+// Blocks blk0..blk0+nb-1 (of virtual expert e) for output columns chunk: the weights are
+// loaded once and held for every block.
 template <int KS>
-__device__ __forceinline__ void expand_mfma_block(const DeltaArgs& a, int blk, int chunk,
-                                                  int e, int rl, int* pid, int* nrows_lds,
-                                                  uint4* s_lds, float* tile) {
+__device__ __forceinline__ void expand_mfma_blocks(const DeltaArgs& a, int blk0, int nb,
+                                                   int chunk, int e, int rl, int* pid,
+                                                   int* nrows_lds, uint4* s_lds, float* tile) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -298,8 +338,9 @@ __device__ __forceinline__ void expand_mfma_block(const DeltaArgs& a, int blk, i
       bf[nt][st] = buf16(rb, n < a.N && k < rl ? (uint32_t)((n * r + k) * 2) : kOutOfRange);
     }
   }
+  for (int b = 0; b < nb; ++b)
   for (int j0 = 0; j0 < a.BM; j0 += kRowsPerPass) {
-    const int nrows = stage_rows(a, blk, j0, pid, nrows_lds);
+    const int nrows = stage_rows(a, blk0 + b, j0, pid, nrows_lds);
     if (nrows == 0) break;
     stage_s(a, pid, nrows, cb, rs, mask, s_lds);
     uint4 ov[2];
@@ -385,7 +426,26 @@ __global__ void __launch_bounds__(256) expand_mfma_kernel(DeltaArgs a) {
   if (e < 0 || !block_has(a, blk, a.mfma_min)) return;
   const int rl = slot_rank(a, e);
   if (rl == 0) return;  // a slot of rank 0 adds nothing
-  expand_mfma_block<KS>(a, blk, chunk, e, rl, pid, &nrows_lds, s_lds, tile);
+  expand_mfma_blocks<KS>(a, blk, 1, chunk, e, rl, pid, &nrows_lds, s_lds, tile);
+}
+
+// Expand over the plan's dense runs: item = (run, 256 output columns).
+template <int KS>
+__global__ void __launch_bounds__(256) expand_mfma_run_kernel(const int32_t* plan,
+                                                              int n_items, DeltaArgs a) {
+  extern __shared__ uint4 s_lds[];
+  __shared__ __attribute__((aligned(16))) float tile[16 * kTileStride];
+  __shared__ int pid[kRowsPerPass];
+  __shared__ int nrows_lds;
+  const int n_live = min(n_items, plan[1] * a.nchunk);
+  const int item = xcd_item(n_live);
+  if (item >= n_live) return;
+  const int run = fdiv(item, a.f_nc), chunk = item - run * a.nchunk;
+  const DenseRun d = dense_run(plan, a.numel, run);
+  if (d.nb == 0) return;
+  const int rl = slot_rank(a, d.e);
+  if (rl == 0) return;  // a slot of rank 0 adds nothing
+  expand_mfma_blocks<KS>(a, d.blk0, d.nb, chunk, d.e, rl, pid, &nrows_lds, s_lds, tile);
 }
 
 }  // namespace
@@ -425,6 +485,22 @@ hipError_t launch_expand_mfma(const DeltaArgs& a, int grid, hipStream_t stream) 
     case 2: hipLaunchKernelGGL((expand_mfma_kernel<2>), dim3(grid), dim3(256), lds, stream, a); break;
     case 3: hipLaunchKernelGGL((expand_mfma_kernel<3>), dim3(grid), dim3(256), lds, stream, a); break;
     case 4: hipLaunchKernelGGL((expand_mfma_kernel<4>), dim3(grid), dim3(256), lds, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_expand_mfma_runs(const DeltaArgs& a, const int32_t* plan, int items,
+                                   hipStream_t stream) {
+  const dim3 grid(xcd_grid(items));
+  // s rows of one pass, the columns of the slices one item spans
+  const size_t lds =
+      (size_t)kRowsPerPass * (a.R / a.slices) * expand_mfma_span(a) * sizeof(float);
+  switch ((a.R / a.slices) / 32) {
+    case 1: hipLaunchKernelGGL((expand_mfma_run_kernel<1>), grid, dim3(256), lds, stream, plan, items, a); break;
+    case 2: hipLaunchKernelGGL((expand_mfma_run_kernel<2>), grid, dim3(256), lds, stream, plan, items, a); break;
+    case 3: hipLaunchKernelGGL((expand_mfma_run_kernel<3>), grid, dim3(256), lds, stream, plan, items, a); break;
+    case 4: hipLaunchKernelGGL((expand_mfma_run_kernel<4>), grid, dim3(256), lds, stream, plan, items, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -214,6 +214,10 @@ hipError_t launch_expand_plan(const DeltaArgs& a, const int32_t* plan, int items
 int shrink_mfma_row_tile(int32_t R);
 hipError_t launch_shrink_mfma(const DeltaArgs& a, int items, hipStream_t stream);
 hipError_t launch_expand_mfma(const DeltaArgs& a, int grid, hipStream_t stream);
+// the expand over the plan's dense runs: items = dense-entry room x column chunks; entries
+// past the plan's count are empty
+hipError_t launch_expand_mfma_runs(const DeltaArgs& a, const int32_t* plan, int items,
+                                   hipStream_t stream);
 // base grouped GEMM (+ fused delta when g.s is set): rows_per_item as for the shrink
 hipError_t launch_moe_gemm(const GemmArgs& g, bool bf16, int rows_per_item, int grid,
                            hipStream_t stream);
