@@ -55,11 +55,15 @@ struct ShrinkLds {
   static constexpr int kVecs = kPG * kSeg * LPR;
 };
 
+// Sixteen zero bytes in device memory: the source of the x slots past a row.
+__device__ const uint4 kZero16 = {0, 0, 0, 0};
+
 // The x vectors [m0*LPR, m0*LPR + SEGV) of the rows of pairs p[0..nq) go straight into xs
 // (pair q at xs[q*SEGV]): pair by pair, each wave a run of 64 vectors. A wave whose run lies
-// past the segment or past the row issues nothing; masked lanes of the others read a valid
-// address, unused. Pair ids are indexed with compile-time indices only (a runtime index into
-// them would put them in scratch memory).
+// past the segment issues nothing; slots past the row are filled with zeros, so every slot
+// of the segment holds a finite value and the products need no mask. Pair ids are indexed
+// with compile-time indices only (a runtime index into them would put them in scratch
+// memory).
 template <bool BF16, int LPR>
 __device__ __forceinline__ void stage_x(const DeltaArgs& a, const int* p, int nq, int m0,
                                         int nvec, uint4* xs) {
@@ -78,11 +82,11 @@ __device__ __forceinline__ void stage_x(const DeltaArgs& a, const int* p, int nq
 #pragma unroll
     for (int t = 0; t < RUNS; ++t) {
       const int i0 = t * kThreads + wv * 64;  // this wave's first vector of the segment
-      const int v0 = m0 * LPR + i0;
-      if (i0 >= SEGV || v0 >= nvec) continue;  // uniform: nothing to stage for this wave
-      const int v = v0 + lane;
-      const bool ok = v < nvec;
-      lds_dma16(xbase + (ok ? xrow + (int64_t)v * 16 : 0), xs + q * SEGV + i0);
+      if (i0 >= SEGV) continue;  // uniform: past the segment
+      const int v = m0 * LPR + i0 + lane;
+      const void* src = v < nvec ? (const void*)(xbase + xrow + (int64_t)v * 16)
+                                 : (const void*)&kZero16;
+      lds_dma16(src, xs + q * SEGV + i0);
     }
   }
 }
@@ -100,22 +104,22 @@ __device__ __forceinline__ void shrink_pairs(const DeltaArgs& a, const uint4* av
   stage_x<BF16, LPR>(a, p, nq, 0, nvec, xs);
   __builtin_amdgcn_s_waitcnt(0);  // the x DMA (and the weights, the first time) have landed
   __syncthreads();
+  // Branch-free products: every pair slot of the group and every segment vector is
+  // multiplied, each weight vector against the four pairs' x vectors read together, so the
+  // LDS reads go out four at a time instead of one round trip each behind its own branch.
+  // Past the row both the held weights and the staged x are zero; pair slots past nq read
+  // stale LDS and are never stored. (The bf16 products take the packed pairs as they are,
+  // so the held weights are never unpacked.)
   float acc[kPG];
 #pragma unroll
   for (int i = 0; i < kPG; ++i) acc[i] = 0.f;
 #pragma unroll
-  for (int i = 0; i < kPG; ++i) {
-    if (i >= nq) break;
+  for (int sg = 0; sg < kSeg; ++sg) {
+    uint4 xv[kPG];
 #pragma unroll
-    for (int sg = 0; sg < kSeg; ++sg) {
-      const int v = lr + sg * LPR;
-      // keep the held weights packed: unpacked once for all groups, they would take twice
-      // the registers, and the unpacking would wait for the weight loads before the first
-      // group's x rows are even requested
-      uint4 w = av[sg];
-      asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
-      if (v < nvec) acc[i] = dot16<BF16>(w, xs[i * SEGV + sg * LPR + lr], acc[i]);
-    }
+    for (int i = 0; i < kPG; ++i) xv[i] = xs[i * SEGV + sg * LPR + lr];
+#pragma unroll
+    for (int i = 0; i < kPG; ++i) acc[i] = dot16<BF16>(av[sg], xv[i], acc[i]);
   }
 #pragma unroll
   for (int i = 0; i < kPG; ++i) {
