@@ -218,23 +218,30 @@ def base_gemm_leg(cfg, layers, host_inputs, torch, n_layers=2, rounds=8):
 def kernel_name(cfg, st, kind):
     """The kernel instantiations libmol launches for this stage, as a profiler names them.
     Shrink: rows per work item start at 4 and double while two such items' A rows fit
-    32 KiB (at most 32); lanes per row = 256 / rows per item. Expand: 16-byte vectors
-    per B row = r * element size / 16."""
+    32 KiB (at most 32); lanes per row = 256 / rows per item; the weights are held in
+    registers when a lane's share of a row fits 8 vectors of 16 bytes. Expand: 16-byte
+    vectors per B row = r * element size / 16."""
     esz = 2 if cfg.dtype == "bf16" else 4
     b = "true" if cfg.dtype == "bf16" else "false"
     # from 4096 pairs and 8 pairs per bucket on average (bf16, BLOCK_M >= 4) blocks of >= 4
     # pairs go to the MFMA kernels, launched after the VALU kernel of the same call; the
-    # expand also needs r % 32 == 0, r <= 128 and a slice width that is a multiple of 64
+    # expand also needs r % 32 == 0, r <= 128 and a slice width that is a multiple of 64.
+    # The layer passes the align's work plan, which the calls take exactly then: the VALU
+    # kernels walk its group entries, and the MFMA expand its dense runs.
     mfma = (cfg.dtype == "bf16" and cfg.numel >= 4096 and cfg.numel >= 8 * (cfg.V + 1)
             and cfg.block_m >= 4)
     if kind == "shrink":
-        rpi = shrink_rows_per_item(cfg, st)
-        name = f"shrink_kernel<{b}, {256 // rpi}>"
-        return name + " + shrink_mfma_kernel" if mfma else name
-    name = f"expand_kernel<{b}, {st.r * esz // 16}>"
-    if mfma and st.r % 32 == 0 and st.r <= 128 and (st.N // st.slices) % 64 == 0:
-        name += f" + expand_mfma_kernel<{st.r // 32}>"
-    return name
+        lpr = 256 // shrink_rows_per_item(cfg, st)
+        held = "true" if st.K * esz // 16 <= 8 * lpr else "false"
+        valu = "shrink_plan_kernel" if mfma else "shrink_kernel"
+        name = f"{valu}<{b}, {lpr}, {held}>"
+        return name + f" + shrink_mfma_kernel<{2 if st.R > 64 else 1}>" if mfma else name
+    rv = st.r * esz // 16
+    emfma = (mfma and st.r % 32 == 0 and st.r <= 128 and st.R <= 256
+             and (st.N // st.slices) % 64 == 0)
+    if emfma:
+        return f"expand_plan_kernel<{b}, {rv}> + expand_mfma_run_kernel<{st.r // 32}>"
+    return f"expand_kernel<{b}, {rv}>"
 
 
 def reference_ctas(grid_m, n, block_n=64):
@@ -250,10 +257,10 @@ def reference_grid_m(cfg):
 
 
 def delta_source_sha256():
-    """Hash of the VALU delta kernels' sources (the kernels and their device helpers)."""
+    """Hash of the delta kernels' sources (VALU and MFMA kernels and their device helpers)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("delta.hip", "delta_common.h"):
+    for f in ("delta.hip", "delta_mfma.hip", "delta_common.h"):
         h.update(open(os.path.join(ROOT, "virtual_expert_routed_amd", "csrc", f), "rb").read())
     return h.hexdigest()
 
