@@ -13,7 +13,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmol.so")
+# MOL_LIBRARY names another build of the same library (the host-sanitizer build of the CPU
+# tests); by default, the one built in-tree
+LIB_PATH = os.environ.get("MOL_LIBRARY") or os.path.join(_PKG, "libmol.so")
 
 MOL_OK, MOL_E_ARG, MOL_E_LIMIT, MOL_E_DTYPE, MOL_E_ALIGN, MOL_E_WORKSPACE, MOL_E_HIP = range(7)
 MOL_F32, MOL_BF16 = 0, 1
