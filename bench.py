@@ -69,8 +69,12 @@ def layer_stats(dl):
     P = int(pairs.size)
     D = int(np.unique(eid[valid_blocks]).size)
     T = int(np.unique(pairs // cfg.topk).size)
+    # runs of up to four consecutive blocks of one virtual expert (the align's work plan)
+    v = eid[valid_blocks]
+    runs = int(sum(-(-int(c) // 4) for c in np.unique(v, return_counts=True)[1])) if v.size \
+        else 0
     return {"P": P, "D": D, "T": T, "npp": npp, "blocks": int(eid.size),
-            "valid_blocks": int(valid_blocks.sum())}
+            "valid_blocks": int(valid_blocks.sum()), "runs": runs}
 
 
 def _sizes(cfg, st, stats):
@@ -135,19 +139,29 @@ def shrink_rows_per_item(cfg, st):
 def grid_report(cfg, max_blocks, stats):
     """Workgroups each kernel launches (the grid follows the block bound, not padded rows)
     and how many of them belong to live blocks with a virtual expert, per stage. Where the
-    MFMA kernels run, their grid is listed too (each block goes to one of the two)."""
+    MFMA kernels take the batch, theirs are listed instead (items: blocks times row tiles
+    for the shrink, the plan's run room times column chunks for the expand; the grids are
+    rounded up to a multiple of 8)."""
     vb = float(np.mean([s["valid_blocks"] for s in stats]))
     rep = {}
     for st in cfg.stages:
         rg = -(-st.R // shrink_rows_per_item(cfg, st))
         nch = -(-st.N // 256)
-        rep[f"shrink {st.name}"] = {"launched": max_blocks * rg, "live_blocks_items": vb * rg}
-        rep[f"expand {st.name}"] = {"launched": max_blocks * nch, "live_blocks_items": vb * nch}
         if "mfma" in kernel_name(cfg, st, "shrink"):
-            rows = 128 if st.R > 64 else 64
-            rep[f"shrink {st.name}"]["mfma_launched"] = max_blocks * -(-st.R // rows)
+            rt = -(-st.R // (128 if st.R > 64 else 64))
+            rep[f"shrink {st.name}"] = {"launched": -(-max_blocks * rt // 8) * 8,
+                                        "live_blocks_items": vb * rt}
+        else:
+            rep[f"shrink {st.name}"] = {"launched": max_blocks * rg,
+                                        "live_blocks_items": vb * rg}
         if "mfma" in kernel_name(cfg, st, "expand"):
-            rep[f"expand {st.name}"]["mfma_launched"] = max_blocks * nch
+            runs = min(max_blocks, cfg.numel)
+            rep[f"expand {st.name}"] = {"launched": -(-runs * nch // 8) * 8,
+                                        "live_runs_items": float(np.mean(
+                                            [s["runs"] for s in stats])) * nch}
+        else:
+            rep[f"expand {st.name}"] = {"launched": max_blocks * nch,
+                                        "live_blocks_items": vb * nch}
     return rep
 
 
@@ -223,25 +237,21 @@ def kernel_name(cfg, st, kind):
     vectors per B row = r * element size / 16."""
     esz = 2 if cfg.dtype == "bf16" else 4
     b = "true" if cfg.dtype == "bf16" else "false"
-    # from 4096 pairs and 8 pairs per bucket on average (bf16, BLOCK_M >= 4) blocks of >= 4
-    # pairs go to the MFMA kernels, launched after the VALU kernel of the same call; the
-    # expand also needs r % 32 == 0, r <= 128 and a slice width that is a multiple of 64.
-    # The layer passes the align's work plan, which the calls take exactly then: the VALU
-    # kernels walk its group entries, and the MFMA expand its dense runs.
-    mfma = (cfg.dtype == "bf16" and cfg.numel >= 4096 and cfg.numel >= 8 * (cfg.V + 1)
-            and cfg.block_m >= 4)
+    # from 4096 pairs and 8 pairs per bucket on average (bf16) every block goes to the MFMA
+    # kernels and no VALU kernel is launched; the expand also needs r % 32 == 0, r <= 128,
+    # R <= 256 and a slice width that is a multiple of 64, and takes the align's plan (the
+    # layer passes one) as runs of blocks
+    mfma = cfg.dtype == "bf16" and cfg.numel >= 4096 and cfg.numel >= 8 * (cfg.V + 1)
     if kind == "shrink":
+        if mfma:
+            return f"shrink_mfma_kernel<{2 if st.R > 64 else 1}>"
         lpr = 256 // shrink_rows_per_item(cfg, st)
         held = "true" if st.K * esz // 16 <= 8 * lpr else "false"
-        valu = "shrink_plan_kernel" if mfma else "shrink_kernel"
-        name = f"{valu}<{b}, {lpr}, {held}>"
-        return name + f" + shrink_mfma_kernel<{2 if st.R > 64 else 1}>" if mfma else name
-    rv = st.r * esz // 16
-    emfma = (mfma and st.r % 32 == 0 and st.r <= 128 and st.R <= 256
-             and (st.N // st.slices) % 64 == 0)
-    if emfma:
-        return f"expand_plan_kernel<{b}, {rv}> + expand_mfma_run_kernel<{st.r // 32}>"
-    return f"expand_kernel<{b}, {rv}>"
+        return f"shrink_kernel<{b}, {lpr}, {held}>"
+    if (mfma and st.r % 32 == 0 and st.r <= 128 and st.R <= 256
+            and (st.N // st.slices) % 64 == 0):
+        return f"expand_mfma_run_kernel<{st.r // 32}>"
+    return f"expand_kernel<{b}, {st.r * esz // 16}>"
 
 
 def reference_ctas(grid_m, n, block_n=64):

@@ -73,9 +73,9 @@ enum { MOL_F32 = 0, MOL_BF16 = 1 };
 /* (host) Static description of a status code. Never NULL. */
 MOL_API const char *mol_status_string(mol_status status);
 
-/* (host) ABI version of this header, 6 (2 added the per-slot ranks, 3 the combine, 4 the
+/* (host) ABI version of this header, 7 (2 added the per-slot ranks, 3 the combine, 4 the
  * base grouped GEMM with the fused delta, 5 the allocation-free stage delta, 6 the work
- * plan). */
+ * plan, 7 the plan as runs of blocks only, read by the expand). */
 MOL_API int32_t mol_abi_version(void);
 
 /* ---------------------------------------------------------------------------------
@@ -105,20 +105,16 @@ MOL_API int64_t mol_align_max_blocks(int64_t numel, int32_t num_virtual, int32_t
 MOL_API int64_t mol_align_workspace_bytes(int64_t numel, int32_t num_virtual, int32_t block_m);
 
 /* ---------------------------------------------------------------------------------
- * The work plan (optional). A batch with split = 4 (numel >= 4096, numel >= 8 (V + 1) and
- * block_m >= 4; else split = 0) divides its blocks between two kinds of kernels: a block
- * with at least `split` real pairs is dense, the rest (a bucket's ragged last block) are
- * few and small. For such a batch, mol_align_block_size can write beside the routing a plan
- * of the delta's work: the dense blocks in runs of consecutive blocks of one bucket, and the
- * real pairs of every other block of a real bucket cut into groups of at most four. The
- * shrink and expand calls then take the small blocks' work from the group entries instead
- * of launching over every possible block. With split = 0 nothing is written and the calls
- * ignore a plan (every block then takes the same kernels, whose grid over the possible
- * blocks is then the cheaper schedule). Layout (int32 words): [0] group count, [1]
- * dense-run count, [2] split, [3..7] 0; from word 8, numel group entries of 8 words {block,
- * virtual expert, pairs (1..4), 0, four pair ids (numel past the count)}; then dense runs
- * of 4 words {first block, blocks (1..4), virtual expert, 0}, at most min(max_blocks,
- * numel / split). Entries follow bucket and block order; the sentinel bucket gets none.
+ * The work plan (optional). A batch of at least 4096 pairs and 8 pairs per bucket on average
+ * (numel >= 8 (V + 1)) is dense enough for the bf16 matrix-core kernels, which then take
+ * every block (no VALU kernel is launched). For such a batch, mol_align_block_size can write
+ * beside the routing a plan of its blocks: runs of up to four consecutive blocks of one
+ * virtual expert, every block of a real bucket in exactly one run. The expand then takes
+ * whole runs as work items and loads each weight column once per run instead of once per
+ * block. For other batches nothing is written and the calls ignore a plan. Layout (int32
+ * words): [0] the number of runs, [1..7] 0; from word 8, runs of 4 words {first block,
+ * blocks (1..4), virtual expert, 0} in bucket order, at most min(max_blocks, numel). The
+ * sentinel bucket has none.
  *   mol_plan_bytes: bytes of a plan buffer (a multiple of 256), or -mol_status.
  * ------------------------------------------------------------------------------- */
 MOL_API int64_t mol_plan_bytes(int64_t numel, int32_t num_virtual, int32_t block_m);
@@ -141,8 +137,8 @@ MOL_API int64_t mol_plan_bytes(int64_t numel, int32_t num_virtual, int32_t block
  *   num_post_padded  int32 [1] out: sum_b pc_b.
  *   Entries past num_post_padded (resp. num_post_padded / block_m) are left undefined.
  *   plan, plan_bytes the work plan out (see above; 16-byte aligned, at least
- *                    mol_plan_bytes()), or NULL (0). Written only when split > 0; the
- *                    buffer is left untouched otherwise.
+ *                    mol_plan_bytes()), or NULL (0). Written only for a batch that takes
+ *                    the matrix-core kernels; the buffer is left untouched otherwise.
  *   workspace        device scratch of mol_align_workspace_bytes(), or NULL when that is 0.
  * No atomics are used; results are bit-for-bit reproducible. M == 0 writes
  * num_post_padded = 0 (sorted_ids and expert_ids may then be NULL).
@@ -178,11 +174,6 @@ MOL_API mol_status mol_align_block_size(const int32_t *ids, const int32_t *lora_
  *                s[p, g r + i] = 0 for i >= rl
  *   sorted_ids, expert_ids, num_post_padded: the outputs of mol_align_block_size for
  *                `numel` pairs, V = num_virtual virtual experts and this block_m
- *   plan         the work plan the same align call wrote, or NULL. For a batch with
- *                split > 0 whose dense blocks take the matrix-core kernels, the other
- *                kernels take their work items from it (same results); otherwise, and
- *                without one, their grid spans every possible block. (The expand, and the
- *                shrink and expand of mol_lora_delta, take the same argument.)
  *   s            float32 [numel, R] out, 16-byte aligned; rows of pairs that get no delta are
  *                untouched
  * Requires K * elem and ld_x * elem to be multiples of 16 bytes, R % slices == 0, and xin,
@@ -193,8 +184,8 @@ MOL_API mol_status mol_lora_shrink(int32_t dtype, const void *xin, int64_t ld_x,
                                    int32_t slices, const int32_t *slot_ranks,
                                    int32_t num_experts, const int32_t *sorted_ids,
                                    const int32_t *expert_ids, const int32_t *num_post_padded,
-                                   const int32_t *plan, int32_t numel, int32_t num_virtual,
-                                   int32_t block_m, float *s, void *stream);
+                                   int32_t numel, int32_t num_virtual, int32_t block_m,
+                                   float *s, void *stream);
 
 /* ---------------------------------------------------------------------------------
  * mol_lora_expand - for the same pairs, with r = R / slices, w = N / slices and rl the
@@ -209,6 +200,10 @@ MOL_API mol_status mol_lora_shrink(int32_t dtype, const void *xin, int64_t ld_x,
  *   slot_ranks   int32 [num_virtual / num_experts] or NULL (see above)
  *   out          [numel, ld_out] read and written in place; rows of pairs without a
  *                delta are left bit-for-bit untouched
+ *   plan         the work plan the same align call wrote, or NULL. When the matrix-core
+ *                kernels take the batch, their items are then the plan's runs (same
+ *                results); otherwise it is not read. (mol_lora_delta and
+ *                mol_lora_delta_noalloc take the same argument for their expand.)
  * Requires R % slices == 0, N % slices == 0, r * elem a multiple of 16 bytes and at most
  * MOL_MAX_RANK_BYTES, B and s 16-byte aligned (MOL_E_ALIGN), out aligned to its element.
  * ------------------------------------------------------------------------------- */

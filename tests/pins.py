@@ -113,43 +113,24 @@ def delta_per_pair(cfg_E, cfg_S, topk, vids, stage, xin, row_div, A, B, scale):
 
 def expected_plan(numel, V, block_m, sorted_ids, expert_ids, npp):
     """The work plan the align writes, rebuilt on the host from a routing (sorted_ids and
-    expert_ids over [0, npp)): (split, group entries, dense runs). A plan is only written
-    for a batch with a dense split (split = 4 from 4096 pairs and 8 pairs per bucket on
-    average, with block_m >= 4; split = 0 returns no entries: nothing is written). A block
-    of a real bucket with at least `split` real pairs is dense, listed in runs of up to four
-    consecutive blocks of one bucket; any other block of a real bucket is cut into groups of
-    up to four consecutive pairs, each entry (block, virtual expert, pair count, the pair
-    ids padded with numel). Entries follow bucket and block order; the sentinel bucket has
-    none."""
-    split = 4 if (numel >= 4096 and numel >= 8 * (V + 1) and block_m >= 4) else 0
-    if split == 0:
-        return 0, [], []
+    expert_ids over [0, npp)): (written, runs). A plan is only written for a batch of at
+    least 4096 pairs and 8 pairs per bucket on average (otherwise written is False and there
+    are no runs). Every block of a real bucket lies in exactly one run of up to four
+    consecutive blocks of that bucket, (first block, blocks, virtual expert), in bucket
+    order; the sentinel bucket has none."""
+    if not (numel >= 4096 and numel >= 8 * (V + 1)):
+        return False, []
     nblk = npp // block_m
-    blocks = np.asarray(sorted_ids[:npp]).reshape(nblk, block_m) if nblk else \
-        np.zeros((0, block_m), np.int64)
     eid = np.asarray(expert_ids[:nblk])
-    groups, dense = [], []
+    runs = []
     i = 0
     while i < nblk:
         e = int(eid[i])
         j = i
-        while j < nblk and int(eid[j]) == e:
+        while j < nblk and int(eid[j]) == e:  # the bucket's blocks
             j += 1
         if e >= 0:
-            fills = [int((blocks[k] < numel).sum()) for k in range(i, j)]
-            run = []
-            for k, f in zip(range(i, j), fills):
-                if split and f >= split:
-                    run.append(k)
-                    if len(run) == 4:
-                        dense.append((run[0], len(run), e))
-                        run = []
-                else:
-                    for q in range(0, f, 4):
-                        nq = min(4, f - q)
-                        ps = [int(x) for x in blocks[k, q:q + nq]] + [numel] * (4 - nq)
-                        groups.append((k, e, nq, *ps))
-            if run:
-                dense.append((run[0], len(run), e))
+            for k in range(i, j, 4):
+                runs.append((k, min(4, j - k), e))
         i = j
-    return split, groups, dense
+    return True, runs

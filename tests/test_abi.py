@@ -39,7 +39,7 @@ def test_only_mol_symbols_exported():
 
 def test_version_and_status_strings():
     L = mb.lib()
-    assert L.mol_abi_version() == 6
+    assert L.mol_abi_version() == 7
     for code in range(7):
         assert mb.status_string(code)
     assert mb.status_string(99) == "unknown status"
@@ -102,13 +102,12 @@ def test_align_rejects_before_launch():
 
 def test_align_plan_sizing_and_checks():
     L = mb.lib()
-    # the plan's room: header, numel group entries of 8 words, dense runs of 4 words
+    # the plan's room: a header of 8 words, then runs of 4 words, at most one per block of a
+    # real bucket (every such block holds a pair): min(max_blocks, numel)
     for numel, V, bm in ((184, 1024, 64), (1024, 2048, 64), (32768, 8064, 64),
-                         (131072, 2048, 64), (16, 8, 16), (0, 8, 16)):
-        split = 4 if (numel >= 4096 and numel >= 8 * (V + 1) and bm >= 4) else 0
+                         (131072, 2048, 64), (16, 8, 16), (0, 8, 16), (5000, 7, 1)):
         mb_ = mb.mol_align_max_blocks(numel, V, bm)
-        dense = min(mb_, numel // split) if split else 0
-        words = 8 + 8 * numel + 4 * dense
+        words = 8 + 4 * min(mb_, numel)
         assert mb.mol_plan_bytes(numel, V, bm) == -(-words * 4 // 256) * 256
     # a plan buffer that is too small, or misaligned
     need = mb.mol_plan_bytes(16, 16, 16)
@@ -129,20 +128,20 @@ def test_remap_rejects_before_launch():
 def test_shrink_expand_delta_reject_before_launch():
     L = mb.lib()
     # shrink: unknown dtype, K not a multiple of 16 bytes, misaligned pointer
-    assert L.mol_lora_shrink(7, FAKE, 64, 1, FAKE, 8, 64, 1, None, 8, FAKE, FAKE, FAKE, None, 16, 8,
+    assert L.mol_lora_shrink(7, FAKE, 64, 1, FAKE, 8, 64, 1, None, 8, FAKE, FAKE, FAKE, 16, 8,
                              16, FAKE, None) == mb.MOL_E_DTYPE
     assert L.mol_lora_shrink(mb.MOL_BF16, FAKE, 68, 1, FAKE, 8, 60, 1, None, 8, FAKE, FAKE,
-                             FAKE, None, 16, 8, 16, FAKE, None) == mb.MOL_E_ALIGN
+                             FAKE, 16, 8, 16, FAKE, None) == mb.MOL_E_ALIGN
     assert L.mol_lora_shrink(mb.MOL_F32, ctypes.c_void_p(0x1004), 64, 1, FAKE, 8, 64, 1, None,
-                             8, FAKE, FAKE, FAKE, None, 16, 8, 16, FAKE, None) == mb.MOL_E_ALIGN
+                             8, FAKE, FAKE, FAKE, 16, 8, 16, FAKE, None) == mb.MOL_E_ALIGN
     assert L.mol_lora_shrink(mb.MOL_F32, FAKE, 32, 1, FAKE, 8, 64, 1, None, 8, FAKE, FAKE,
-                             FAKE, None, 16, 8, 16, FAKE, None) == mb.MOL_E_ARG           # ld_x < K
+                             FAKE, 16, 8, 16, FAKE, None) == mb.MOL_E_ARG           # ld_x < K
     assert L.mol_lora_shrink(mb.MOL_BF16, FAKE, 64, 1, FAKE, 8, 64, 1, None, 8, FAKE, FAKE,
-                             FAKE, None, 16, 8, 16, ctypes.c_void_p(0x1008), None) == mb.MOL_E_ALIGN
+                             FAKE, 16, 8, 16, ctypes.c_void_p(0x1008), None) == mb.MOL_E_ALIGN
     assert L.mol_lora_shrink(mb.MOL_BF16, FAKE, 64, 1, FAKE, 8, 64, 3, None, 8, FAKE, FAKE,
-                             FAKE, None, 16, 8, 16, FAKE, None) == mb.MOL_E_ARG     # R % slices
+                             FAKE, 16, 8, 16, FAKE, None) == mb.MOL_E_ARG     # R % slices
     assert L.mol_lora_shrink(mb.MOL_BF16, FAKE, 64, 1, FAKE, 8, 64, 1, None, 3, FAKE, FAKE,
-                             FAKE, None, 16, 8, 16, FAKE, None) == mb.MOL_E_ARG     # V % E
+                             FAKE, 16, 8, 16, FAKE, None) == mb.MOL_E_ARG     # V % E
     # expand: R % slices, rank too large, V not a multiple of E
     assert L.mol_lora_expand(mb.MOL_BF16, FAKE, 63, 2, FAKE, 32, FAKE, None, 4, FAKE, FAKE,
                              FAKE, None, 16, 8, 16, FAKE, 32, None) == mb.MOL_E_ARG

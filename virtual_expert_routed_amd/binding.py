@@ -33,7 +33,7 @@ SIGNATURES = {
     "mol_align_block_size": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _SZ,
                                     _P, _SZ, _P]),
     "mol_lora_shrink": (_I32, [_I32, _P, _I64, _I32, _P, _I32, _I32, _I32, _P, _I32, _P, _P,
-                               _P, _P, _I32, _I32, _I32, _P, _P]),
+                               _P, _I32, _I32, _I32, _P, _P]),
     "mol_lora_expand": (_I32, [_I32, _P, _I32, _I32, _P, _I32, _P, _P, _I32, _P, _P, _P, _P,
                                _I32, _I32, _I32, _P, _I64, _P]),
     "mol_delta_workspace_bytes": (_I64, [_I32, _I32, _I32, _I32]),
@@ -201,7 +201,7 @@ def _ranks(slot_ranks):
 
 def mol_lora_shrink(xin, row_div: int, A, sorted_ids, expert_ids, num_post_padded,
                     numel: int, num_virtual: int, block_m: int, s=None, slices: int = 1,
-                    slot_ranks=None, num_experts: int = None, plan=None):
+                    slot_ranks=None, num_experts: int = None):
     _need(xin, "xin", contiguous=False)
     _need(A, "A")
     if xin.stride(1) != 1:
@@ -214,7 +214,7 @@ def mol_lora_shrink(xin, row_div: int, A, sorted_ids, expert_ids, num_post_padde
     _check("mol_lora_shrink", lib().mol_lora_shrink(
         _dtype_code(A), _ptr(xin), xin.stride(0), row_div, _ptr(A), R, K, slices,
         _ranks(slot_ranks), E, _ptr(sorted_ids), _ptr(expert_ids), _ptr(num_post_padded),
-        _ptr(plan), numel, num_virtual, block_m, _ptr(s), _stream(A)))
+        numel, num_virtual, block_m, _ptr(s), _stream(A)))
     return s
 
 

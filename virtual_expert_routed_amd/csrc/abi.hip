@@ -37,29 +37,6 @@ int device_lds_bytes() {
 }
 
 
-// Compute units of the current device, cached per device (the plan-driven grids are at
-// most what the chip holds at once).
-std::atomic<int> g_cus[64];
-
-int device_cus() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int v = g_cus[dev].load(std::memory_order_relaxed);
-  if (v == 0) {
-    int attr = 0;
-    if (hipDeviceGetAttribute(&attr, hipDeviceAttributeMultiprocessorCount, dev) !=
-            hipSuccess ||
-        attr <= 0)
-      attr = 256;
-    v = attr;
-    g_cus[dev].store(v, std::memory_order_relaxed);
-  }
-  return v;
-}
-
-// Workgroups the plan-driven kernels keep resident per compute unit.
-constexpr int64_t kPlanGroupsPerCU = 8;
-
 mol_status hip_status(hipError_t e) { return e == hipSuccess ? MOL_OK : MOL_E_HIP; }
 
 // number of blocks any routing of numel pairs over V virtual experts can produce
@@ -169,7 +146,7 @@ MOL_API const char* mol_status_string(mol_status status) {
   }
 }
 
-MOL_API int32_t mol_abi_version(void) { return 6; }
+MOL_API int32_t mol_abi_version(void) { return 7; }
 
 MOL_API mol_status mol_virtual_topk(const int32_t* topk_ids, const int32_t* lora_ids,
                                     int32_t M, int32_t topk, int32_t num_experts,
@@ -200,8 +177,7 @@ MOL_API int64_t mol_align_workspace_bytes(int64_t numel, int32_t num_virtual,
 MOL_API int64_t mol_plan_bytes(int64_t numel, int32_t num_virtual, int32_t block_m) {
   const int64_t mb = align_check(numel, num_virtual, block_m);
   if (mb < 0) return mb;
-  const int32_t split = mol::plan_split(numel, num_virtual, block_m);
-  return round256(mol::plan_words(numel, mb, split) * (int64_t)sizeof(int32_t));
+  return round256(mol::plan_words(numel, mb) * (int64_t)sizeof(int32_t));
 }
 
 MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_ids,
@@ -230,9 +206,8 @@ MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_
   }
 
   mol::AlignArgs a{};
-  a.split = mol::plan_split(numel, V64, block_m);
-  a.plan = a.split > 0 ? plan : nullptr;  // no dense split: nothing to plan
-  a.gmax = (int32_t)mol::plan_max_groups(numel);
+  a.plan = mol::mfma_batch(numel, V64) ? plan : nullptr;  // otherwise nothing to plan
+  a.dmax = (int32_t)mol::plan_max_runs(numel, mb);
   a.max_blocks = (int32_t)mb;
   a.ids = ids;
   a.lora = lora_ids;
@@ -253,7 +228,7 @@ MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_
   if (numel <= mol::kAlignSmallMax) {
     // counter rows + bucket starts + scan scratch + per pair a bucket id and a rank
     // (uint16 each)
-    const int64_t fixed = ((int64_t)nb * (plan ? 2 : 1) + 64) * (int64_t)sizeof(int) +
+    const int64_t fixed = ((int64_t)nb + 64) * (int64_t)sizeof(int) +
                           ((numel + 1) & ~1LL) * 2 * 2;
     int64_t waves = (device_lds_bytes() - fixed) / ((int64_t)nb * (int64_t)sizeof(int));
     // walkers: one chunk of 64 pairs each for the smallest batches, two chunks each above
@@ -287,69 +262,47 @@ MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_
 
 namespace {
 
-// Blocks with at least this many real pairs take the bf16 MFMA kernels (0: none do). The
-// MFMA kernels are only launched for batches large enough to hold such blocks in numbers:
-// from 4096 pairs and 8 pairs per bucket on average. Their grid spans every possible
-// block, so a launch whose blocks are all small would only cost its empty workgroups.
-int32_t shrink_mfma_min(bool bf16, int32_t numel, int32_t num_virtual, int32_t block_m) {
-  return (bf16 && numel >= mol::kMfmaMinNumel &&
-          (int64_t)numel >= 8 * ((int64_t)num_virtual + 1) && block_m >= mol::kMfmaMinPairs)
-             ? mol::kMfmaMinPairs
-             : 0;
+// Whether the bf16 MFMA kernels take every block (and no VALU kernel is launched), else the
+// VALU kernels take every block. The MFMA kernels serve batches large enough to hold dense
+// blocks in numbers (mol::mfma_batch): their grid spans every possible block, so a batch of
+// small blocks would pay for empty workgroups, and a block of one or two pairs is a mostly
+// empty tile.
+bool shrink_uses_mfma(bool bf16, int32_t numel, int32_t num_virtual) {
+  return bf16 && mol::mfma_batch(numel, num_virtual);
 }
 
 // The MFMA expand also needs whole 32-wide rank steps, s rows of at most 256 floats (they
 // are staged in LDS), 64-column groups inside one slice, and 16-byte aligned groups of
 // eight out elements.
-int32_t expand_mfma_min(bool bf16, int32_t numel, int32_t num_virtual, int32_t block_m,
-                        int32_t R, int32_t slices, int32_t N, const void* out, int64_t ld_out) {
+bool expand_uses_mfma(bool bf16, int32_t numel, int32_t num_virtual, int32_t R, int32_t slices,
+                      int32_t N, const void* out, int64_t ld_out) {
   const int32_t r = R / slices;
   const bool shape_ok = r % 32 == 0 && r <= 128 && R <= 256 && (N / slices) % 64 == 0 &&
                         ld_out % 8 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0;
-  return shape_ok ? shrink_mfma_min(bf16, numel, num_virtual, block_m) : 0;
+  return shape_ok && shrink_uses_mfma(bf16, numel, num_virtual);
 }
 
-// VALU shrink over every block (skipping the MFMA ones), then the MFMA shrink if enabled.
-// When the MFMA kernels take the dense blocks (those with at least `split` pairs) and a plan
-// is given, the VALU kernels take the remaining small blocks from the plan's group entries
-// (and the MFMA expand takes the dense runs); otherwise (and without a plan) the grids span
-// every possible block.
-hipError_t shrink_all(mol::DeltaArgs a, bool bf16, int rpi, int64_t grid, int32_t mfma_min,
-                      const int32_t* plan, hipStream_t st) {
-  a.mfma_min = mfma_min;
+// The shrink of a stage: the MFMA kernel over every block when the batch takes it (items
+// ordered by XCD), else the VALU kernel over every block.
+hipError_t shrink_all(mol::DeltaArgs a, bool bf16, int rpi, int64_t grid, bool mfma,
+                      hipStream_t st) {
   mol::with_divisors(a);
-  const int32_t split = mol::plan_split(a.numel, a.V, a.BM);
-  hipError_t e;
-  if (plan && split > 0 && mfma_min == split) {
-    const int64_t items =
-        std::min<int64_t>(mol::plan_max_groups(a.numel) * a.rgroups, int64_t(1) << 30);
-    const int64_t g = std::min<int64_t>(items, device_cus() * kPlanGroupsPerCU);
-    e = mol::launch_shrink_plan(a, plan, (int)items, bf16, rpi, (int)g, st);
-  } else {
-    e = mol::launch_shrink(a, bf16, rpi, (int)grid, st);
-  }
-  if (e != hipSuccess || mfma_min == 0) return e;
+  if (!mfma) return mol::launch_shrink(a, bf16, rpi, (int)grid, st);
   return mol::launch_shrink_mfma(
       a, (int)(a.max_blocks * cdiv64(a.R, mol::shrink_mfma_row_tile(a.R))), st);
 }
 
-hipError_t expand_all(mol::DeltaArgs a, bool bf16, int64_t grid, int32_t mfma_min,
+// The expand of a stage: the MFMA kernel when the batch and the shape allow it, over the
+// align's dense runs when a plan is given and over every block otherwise; else the VALU
+// kernel over every block.
+hipError_t expand_all(mol::DeltaArgs a, bool bf16, int64_t grid, bool mfma,
                       const int32_t* plan, hipStream_t st) {
-  a.mfma_min = mfma_min;
   mol::with_divisors(a);
-  const int32_t split = mol::plan_split(a.numel, a.V, a.BM);
-  hipError_t e;
-  if (plan && split > 0 && mfma_min == split) {
-    const int64_t items =
-        std::min<int64_t>(mol::plan_max_groups(a.numel) * a.nchunk, int64_t(1) << 30);
-    const int64_t g = std::min<int64_t>(items, device_cus() * kPlanGroupsPerCU);
-    e = mol::launch_expand_plan(a, plan, (int)items, bf16, (int)g, st);
-    if (e != hipSuccess) return e;
-    const int64_t dmax = mol::plan_max_dense(a.numel, a.max_blocks, split);
-    return mol::launch_expand_mfma_runs(a, plan, (int)(dmax * a.nchunk), st);
+  if (!mfma) return mol::launch_expand(a, bf16, (int)grid, st);
+  if (plan) {
+    const int64_t runs = mol::plan_max_runs(a.numel, a.max_blocks);
+    return mol::launch_expand_mfma_runs(a, plan, (int)(runs * a.nchunk), st);
   }
-  e = mol::launch_expand(a, bf16, (int)grid, st);
-  if (e != hipSuccess || mfma_min == 0) return e;
   return mol::launch_expand_mfma(a, (int)grid, st);
 }
 
@@ -403,7 +356,7 @@ mol_status delta_check(int32_t dtype, const void* xin, int64_t ld_x, int32_t row
   if (mb * cdiv64(R, mol::shrink_rows_per_item(K, esz)) > kI32Max ||
       mb * cdiv64(N, mol::expand_cols_per_item(R, slices, esz)) > kI32Max)
     return MOL_E_LIMIT;
-  if (shrink_mfma_min(bf16, numel, num_virtual, block_m) > 0 && mb * cdiv64(R, 64) > kI32Max)
+  if (shrink_uses_mfma(bf16, numel, num_virtual) && mb * cdiv64(R, 64) > kI32Max)
     return MOL_E_LIMIT;
   return MOL_OK;
 }
@@ -428,10 +381,9 @@ mol_status delta_enqueue(int32_t dtype, const void* xin, int64_t ld_x, int32_t r
   a.nchunk = (int32_t)cdiv64(N, mol::expand_cols_per_item(R, slices, esz));
   const int64_t grid_s = mb * (int64_t)a.rgroups;
   const int64_t grid_e = mb * (int64_t)a.nchunk;
-  const int32_t mm_s = shrink_mfma_min(bf16, numel, num_virtual, block_m);
-  const int32_t mm_e =
-      expand_mfma_min(bf16, numel, num_virtual, block_m, R, slices, N, out, ld_out);
-  if (shrink_all(a, bf16, rpi, grid_s, mm_s, plan, st) != hipSuccess) return MOL_E_HIP;
+  const bool mm_s = shrink_uses_mfma(bf16, numel, num_virtual);
+  const bool mm_e = expand_uses_mfma(bf16, numel, num_virtual, R, slices, N, out, ld_out);
+  if (shrink_all(a, bf16, rpi, grid_s, mm_s, st) != hipSuccess) return MOL_E_HIP;
   return hip_status(expand_all(a, bf16, grid_e, mm_e, plan, st));
 }
 
@@ -444,7 +396,7 @@ MOL_API mol_status mol_lora_shrink(int32_t dtype, const void* xin, int64_t ld_x,
                                    int32_t slices, const int32_t* slot_ranks,
                                    int32_t num_experts, const int32_t* sorted_ids,
                                    const int32_t* expert_ids, const int32_t* num_post_padded,
-                                   const int32_t* plan, int32_t numel, int32_t num_virtual, int32_t block_m,
+                                   int32_t numel, int32_t num_virtual, int32_t block_m,
                                    float* s, void* stream) {
   const StageCheck rc =
       routing_check(sorted_ids, expert_ids, num_post_padded, numel, num_virtual, block_m);
@@ -464,9 +416,9 @@ MOL_API mol_status mol_lora_shrink(int32_t dtype, const void* xin, int64_t ld_x,
                                      numel, num_virtual, block_m, s, nullptr, 0, rc.max_blocks);
   a.ranks = slot_ranks;
   a.rgroups = (int32_t)rgroups;
-  const int32_t mm = shrink_mfma_min(bf16, numel, num_virtual, block_m);
-  if (mm > 0 && rc.max_blocks * cdiv64(R, 64) > kI32Max) return MOL_E_LIMIT;
-  return hip_status(shrink_all(a, bf16, rpi, grid, mm, plan, (hipStream_t)stream));
+  const bool mm = shrink_uses_mfma(bf16, numel, num_virtual);
+  if (mm && rc.max_blocks * cdiv64(R, 64) > kI32Max) return MOL_E_LIMIT;
+  return hip_status(shrink_all(a, bf16, rpi, grid, mm, (hipStream_t)stream));
 }
 
 MOL_API mol_status mol_lora_expand(int32_t dtype, const float* s, int32_t R, int32_t slices,
@@ -495,8 +447,7 @@ MOL_API mol_status mol_lora_expand(int32_t dtype, const float* s, int32_t R, int
   a.nchunk = (int32_t)cdiv64(N, mol::expand_cols_per_item(R, slices, bf16 ? 2 : 4));
   const int64_t grid = rc.max_blocks * a.nchunk;
   if (grid > kI32Max) return MOL_E_LIMIT;
-  const int32_t mm =
-      expand_mfma_min(bf16, numel, num_virtual, block_m, R, slices, N, out, ld_out);
+  const bool mm = expand_uses_mfma(bf16, numel, num_virtual, R, slices, N, out, ld_out);
   return hip_status(expand_all(a, bf16, grid, mm, plan, (hipStream_t)stream));
 }
 
@@ -595,7 +546,6 @@ MOL_API mol_status mol_moe_gemm(int32_t dtype, const void* xin, int64_t ld_x, in
   g.route = make_delta_args(nullptr, 0, 1, nullptr, 1, 1, 1, nullptr, 1, nullptr, num_experts,
                             sorted_ids, expert_ids, num_post_padded, numel, num_experts,
                             block_m, nullptr, nullptr, 0, rc.max_blocks);
-  g.route.mfma_min = 0;
   g.xin = xin;
   g.ld_x = ld_x;
   g.row_div = row_div;

@@ -87,64 +87,25 @@ __device__ __forceinline__ int bm_round(const AlignArgs& a, int c) {
 }
 
 // ---------------------------------------------------------------------- the work plan
-// What a bucket b with c real pairs contributes to the plan (layout in mol_internal.h). A
-// plan is only written with a dense split (0 < split <= 4 <= BM), so every full block is
-// dense and only a ragged last block below the split has group entries.
-struct BucketPlan {
-  int full;           // full blocks
-  int rem;            // real pairs of the ragged last block (0: none)
-  int dense_blocks;   // its first dense_blocks blocks are dense
-  int groups;         // group entries of the ragged block when it is not dense
-  int dense_entries;  // dense entries: runs of up to kPlanDenseBlocks dense blocks
-};
-
-__device__ __forceinline__ BucketPlan bucket_plan(const AlignArgs& a, int b, int c) {
-  BucketPlan r{0, 0, 0, 0, 0};
-  if (b >= a.V || c <= 0) return r;  // the sentinel bucket and empty buckets: nothing
-  r.full = bm_div(a, c);
-  r.rem = c - r.full * a.BM;
-  const bool ragged_dense = r.rem >= a.split;
-  r.dense_blocks = r.full + (ragged_dense ? 1 : 0);
-  r.groups = (!ragged_dense && r.rem > 0) ? (r.rem + 3) >> 2 : 0;
-  r.dense_entries = (r.dense_blocks + kPlanDenseBlocks - 1) / kPlanDenseBlocks;
-  return r;
+// A bucket of c real pairs has cdiv(c, BM) blocks, listed in the plan as runs of up to
+// kPlanDenseBlocks consecutive blocks (layout in mol_internal.h); the sentinel bucket and
+// empty buckets have none.
+__device__ __forceinline__ int bucket_runs(const AlignArgs& a, int b, int c) {
+  if (b >= a.V || c <= 0) return 0;
+  return (bm_div(a, c + a.BM - 1) + kPlanDenseBlocks - 1) / kPlanDenseBlocks;
 }
 
-__device__ __forceinline__ int32_t* plan_group(const AlignArgs& a, int i) {
-  return a.plan + kPlanHeader + (int64_t)i * kPlanGroupInts;
-}
-__device__ __forceinline__ int32_t* plan_dense(const AlignArgs& a, int j) {
-  return a.plan + kPlanHeader + (int64_t)a.gmax * kPlanGroupInts + (int64_t)j * kPlanDenseInts;
+__device__ __forceinline__ int32_t* plan_run(const AlignArgs& a, int j) {
+  return a.plan + kPlanHeader + (int64_t)j * kPlanDenseInts;
 }
 
-
-// The bucket's dense entries and the headers of its group entries (block, expert, pair
-// count, and numel in the pair slots past the count); the pair slots themselves are
-// written by whoever places the pairs. off_b is the bucket's first slot.
-__device__ __forceinline__ void write_bucket_plan(const AlignArgs& a, int b, int off_b,
-                                                  const BucketPlan& bp, int goff, int doff) {
-  const int blk0 = bm_div(a, off_b);
-  for (int j = 0; j < bp.dense_entries; ++j) {
-    int32_t* d = plan_dense(a, doff + j);
-    const int first = j * kPlanDenseBlocks;
-    const int n = min(kPlanDenseBlocks, bp.dense_blocks - first);
-    *reinterpret_cast<int4*>(d) = make_int4(blk0 + first, n, b, 0);
-  }
-  for (int gi = 0; gi < bp.groups; ++gi) {  // the ragged block's pairs, four at a time
-    const int nq = min(4, bp.rem - 4 * gi);
-    int32_t* g = plan_group(a, goff + gi);
-    *reinterpret_cast<int4*>(g) = make_int4(blk0 + bp.dense_blocks, b, nq, 0);
-    for (int i = nq; i < 4; ++i) g[4 + i] = a.numel;
-  }
-}
-
-// Where pair p, the r-th pair of its bucket, goes in the plan: its group entry's pair slot
-// (nullptr for a pair of a dense block).
-__device__ __forceinline__ int32_t* plan_pair_slot(const AlignArgs& a, int r, int goff,
-                                                   int dense_blocks) {
-  const int jb = bm_div(a, r), o = r - jb * a.BM;
-  if (jb < dense_blocks) return nullptr;  // otherwise jb is the ragged block
-  return plan_group(a, goff + (o >> 2)) + 4 + (o & 3);
+// Run jj of bucket b (first slot off_b, c real pairs) into plan entry j.
+__device__ __forceinline__ void write_run(const AlignArgs& a, int b, int off_b, int c, int jj,
+                                          int j) {
+  const int nblk = bm_div(a, c + a.BM - 1);
+  const int first = jj * kPlanDenseBlocks;
+  *reinterpret_cast<int4*>(plan_run(a, j)) =
+      make_int4(bm_div(a, off_b) + first, min(kPlanDenseBlocks, nblk - first), b, 0);
 }
 
 __global__ void __launch_bounds__(256) virtual_topk_kernel(const int32_t* __restrict__ topk,
@@ -200,12 +161,9 @@ __global__ void __launch_bounds__(1024)
                        int waves) {
   extern __shared__ int lds[];
   const int NB = a.V + 1;
-  const bool planned = a.plan != nullptr;
   int* table = lds;                                   // [waves][NB]
   int* start = lds + waves * NB;                      // [NB] padded bucket starts
-  int* gsd = start + NB;                              // [NB] with a plan: group offset << 16
-                                                      //      | dense blocks, per bucket
-  int* sh = gsd + (planned ? NB : 0);                 // scan scratch (64 ints)
+  int* sh = start + NB;                               // scan scratch (64 ints)
   uint16_t* keys = reinterpret_cast<uint16_t*>(lds + keys_off);  // = sh + 64
   uint16_t* rel = keys + ((numel_ + 1) & ~1);
   const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
@@ -317,32 +275,30 @@ __global__ void __launch_bounds__(1024)
     }
   }
   if (tid == 0 && g == 0) *a.npp = total;
-  if (planned) {
-    // the plan: group and dense entries per owned bucket (at most numel of each here, so
-    // both offsets fit 16 bits and one packed scan gives them), headers and dense entries
-    // written by the bucket's owning workgroup
-    BucketPlan bp[BPT];
-    int packed = 0;
+  if (a.plan) {
+    // the plan: each owned bucket's runs, at offsets from one more block scan, written by
+    // the bucket's owning workgroup
+    int nr = 0;
 #pragma unroll
-    for (int k = 0; k < BPT; ++k) {
-      bp[k] = bucket_plan(a, k < nown ? b0 + k : a.V, k < nown ? run[k] : 0);
-      packed += (bp[k].groups << 16) + bp[k].dense_entries;
-    }
-    int ptotal;
-    int pre = block_excl_scan(packed, sh, &ptotal);
+    for (int k = 0; k < BPT; ++k) nr += k < nown ? bucket_runs(a, b0 + k, run[k]) : 0;
+    int rtotal;
+    int pre = block_excl_scan(nr, sh, &rtotal);
     int bm2 = fmod(b0, a.f_groups);
 #pragma unroll
     for (int k = 0; k < BPT; ++k) {
       if (k < nown) {
         const int b = b0 + k;
-        gsd[b] = ((pre >> 16) << 16) | bp[k].dense_blocks;
-        if (bm2 == g) write_bucket_plan(a, b, start[b], bp[k], pre >> 16, pre & 0xffff);
-        pre += (bp[k].groups << 16) + bp[k].dense_entries;
+        const int nk = bucket_runs(a, b, run[k]);
+        if (bm2 == g)
+          for (int jj = 0; jj < nk; ++jj) write_run(a, b, start[b], run[k], jj, pre + jj);
+        pre += nk;
         bm2 = bm2 + 1 == G ? 0 : bm2 + 1;
       }
     }
-    if (tid == 0 && g == 0)
-      *reinterpret_cast<int4*>(a.plan) = make_int4(ptotal >> 16, ptotal & 0xffff, a.split, 0);
+    if (tid == 0 && g == 0) {
+      reinterpret_cast<int4*>(a.plan)[0] = make_int4(rtotal, 0, 0, 0);
+      reinterpret_cast<int4*>(a.plan)[1] = make_int4(0, 0, 0, 0);
+    }
   }
   __syncthreads();
 
@@ -352,11 +308,6 @@ __global__ void __launch_bounds__(1024)
     const int key = keys[p];
     const int r = table[w * NB + key] + rel[p];  // the pair's rank within its bucket
     a.sorted[start[key] + r] = p;
-    if (planned && key < a.V) {
-      const int v = gsd[key];
-      int32_t* slot = plan_pair_slot(a, r, v >> 16, v & 0xffff);
-      if (slot) *slot = p;
-    }
   }
   // padding: the wave's lanes fill one padded bucket after another
 #pragma unroll
@@ -525,87 +476,36 @@ __global__ void __launch_bounds__(256) align_scatter_kernel(AlignArgs a) {
   }
 }
 
-// numel > 4096, after the scatter: the work plan, one thread per entry. Every workgroup
-// scans the per-bucket entry counts (from the totals) into LDS prefix arrays; a thread then
-// finds its entry's bucket by binary search and writes the entry, taking a group entry's
-// pairs from the sorted ids the scatter has written.
-constexpr int kPlanEntriesPerThread = 4;
-
-__device__ __forceinline__ int bucket_of_entry(const int* incl, int nb, int i) {
-  // the bucket b with incl[b - 1] <= i < incl[b] (incl: inclusive prefix sums, ascending)
-  int lo = 0, hi = nb - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (incl[mid] > i) hi = mid; else lo = mid + 1;
-  }
-  return lo;
-}
-
-__global__ void __launch_bounds__(256) align_plan_kernel(AlignArgs a, int32_t gcap,
-                                                         int32_t dmax) {
-  extern __shared__ int lds[];
+// numel > 4096, after the column scan: the work plan, by one 1024-thread workgroup. Thread t
+// owns consecutive buckets, reads their totals, and two block scans (padded sizes and run
+// counts) give each owned bucket its first slot and its first run; the thread then writes
+// the bucket's runs.
+__global__ void __launch_bounds__(1024) align_plan_kernel(AlignArgs a) {
+  __shared__ int sh[64];
   const int NB = a.V + 1;
-  int* gin = lds;            // [NB] inclusive prefix of group entries
-  int* din = lds + NB;       // [NB] inclusive prefix of dense entries
-  int* offs = lds + 2 * NB;  // [NB] first slot of each bucket
-  int* sh = lds + 3 * NB;    // scan scratch (64)
   const int tid = threadIdx.x;
-  const int bpt = (NB + 255) / 256;
+  const int bpt = (NB + 1023) / 1024;
   const int b0 = min(NB, tid * bpt), b1 = min(NB, b0 + bpt);
-  int pc = 0, ng = 0, nd = 0;
+  int pc = 0, nr = 0;
   for (int b = b0; b < b1; ++b) {
     const int c = a.totals[b];
-    const BucketPlan bp = bucket_plan(a, b, c);
     pc += bm_round(a, c);
-    ng += bp.groups;
-    nd += bp.dense_entries;
+    nr += bucket_runs(a, b, c);
   }
-  int tp, tg, td;
+  int tp, tr;
   int po = block_excl_scan(pc, sh, &tp);
   __syncthreads();
-  int go = block_excl_scan(ng, sh, &tg);
-  __syncthreads();
-  int dd = block_excl_scan(nd, sh, &td);
+  int ro = block_excl_scan(nr, sh, &tr);
   for (int b = b0; b < b1; ++b) {
     const int c = a.totals[b];
-    const BucketPlan bp = bucket_plan(a, b, c);
-    offs[b] = po;
+    const int nk = bucket_runs(a, b, c);
+    for (int jj = 0; jj < nk; ++jj) write_run(a, b, po, c, jj, ro + jj);
     po += bm_round(a, c);
-    go += bp.groups;
-    dd += bp.dense_entries;
-    gin[b] = go;
-    din[b] = dd;
+    ro += nk;
   }
-  if (blockIdx.x == 0 && tid == 0)
-    *reinterpret_cast<int4*>(a.plan) = make_int4(tg, td, a.split, 0);
-  __syncthreads();
-  const int base = (blockIdx.x * 256 + tid) * kPlanEntriesPerThread;
-  for (int k = 0; k < kPlanEntriesPerThread; ++k) {
-    const int i = base + k;
-    if (i < tg) {  // group entry i
-      const int b = bucket_of_entry(gin, NB, i);
-      const int gi = i - (b > 0 ? gin[b - 1] : 0);
-      const BucketPlan bp = bucket_plan(a, b, a.totals[b]);
-      const int jb = bp.dense_blocks, q0 = 4 * gi;  // the ragged block's pairs q0..
-      const int nq = min(4, bp.rem - q0);
-      const int slot = offs[b] + jb * a.BM + q0;
-      int pv[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) pv[q] = q < nq ? a.sorted[slot + q] : a.numel;
-      int32_t* g = plan_group(a, i);
-      *reinterpret_cast<int4*>(g) = make_int4(bm_div(a, offs[b]) + jb, b, nq, 0);
-      *reinterpret_cast<int4*>(g + 4) = make_int4(pv[0], pv[1], pv[2], pv[3]);
-    }
-    const int j = i - gcap;  // dense entries take the indices after the groups' room
-    if (j >= 0 && j < td && j < dmax) {
-      const int b = bucket_of_entry(din, NB, j);
-      const int jj = j - (b > 0 ? din[b - 1] : 0);
-      const BucketPlan bp = bucket_plan(a, b, a.totals[b]);
-      const int first = jj * kPlanDenseBlocks;
-      *reinterpret_cast<int4*>(plan_dense(a, j)) =
-          make_int4(bm_div(a, offs[b]) + first, min(kPlanDenseBlocks, bp.dense_blocks - first),
-                    b, 0);
-    }
+  if (tid == 0) {
+    reinterpret_cast<int4*>(a.plan)[0] = make_int4(tr, 0, 0, 0);
+    reinterpret_cast<int4*>(a.plan)[1] = make_int4(0, 0, 0, 0);
   }
 }
 
@@ -626,8 +526,8 @@ hipError_t launch_align_small(const AlignArgs& a, int waves, int groups, size_t 
   // buckets per thread, rounded up to a power of two (V + 1 <= 8192 = 8 x 1024)
   const int bpt = (a.V + 1 + 1023) / 1024;
   const dim3 grid(groups), block(1024);
-  // ints before the key array: counter rows, bucket starts, the plan's per-bucket offsets
-  const int keys_off = (waves + 1 + (a.plan ? 1 : 0)) * (a.V + 1) + 64;
+  // ints before the key array: counter rows, bucket starts, scan scratch
+  const int keys_off = (waves + 1) * (a.V + 1) + 64;
 #define MOL_ALIGN_SMALL(BPT)                                                                \
   hipLaunchKernelGGL(align_small_kernel<BPT>, grid, block, lds_bytes, stream, a.ids, a.lora, \
                      a.numel, a.f_topk.m, a.f_topk.l, keys_off, a.lora ? a.E : a.V,       \
@@ -657,16 +557,7 @@ hipError_t launch_align_large(const AlignArgs& a, size_t scatter_lds_bytes,
                      stream, a);
   e = hipGetLastError();
   if (e != hipSuccess || !a.plan) return e;
-  const int64_t dmax = plan_max_dense(a.numel, a.max_blocks, a.split);
-  // at most one group entry per bucket: only a ragged block below the split (< 4 pairs) has
-  // any
-  const int64_t gcap = std::min<int64_t>(a.gmax, a.V);
-  const int64_t slots = gcap + dmax;
-  const unsigned grid = (unsigned)((slots + 256 * kPlanEntriesPerThread - 1) /
-                                   (256 * kPlanEntriesPerThread));
-  const size_t lds = (size_t)(3 * (a.V + 1) + 64) * sizeof(int);
-  hipLaunchKernelGGL(align_plan_kernel, dim3(grid), dim3(256), lds, stream, a, (int32_t)gcap,
-                     (int32_t)dmax);
+  hipLaunchKernelGGL(align_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -199,7 +199,7 @@ __device__ __forceinline__ void shrink_block(const DeltaArgs& a, const RouteArgs
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int RPI = kThreads / LPR;
   const BlockHead h = block_head(a, ra_, blk);
-  if (h.e < 0 || h.nq == 0) return;  // no delta, or the MFMA kernel's block
+  if (h.e < 0 || h.nq == 0) return;  // no delta
   const int rl = slot_rank(a, h.e);
   const int nvec = a.K * ESZ / 16;  // HELD: nvec <= kSeg * LPR (chosen by the launcher)
   const int tid = threadIdx.x;
@@ -393,7 +393,7 @@ __device__ __forceinline__ void expand_block(const DeltaArgs& a, const RouteArgs
   const int tid = threadIdx.x;
   const BlockHead h = block_head(a, ra_, blk);
   const int e = h.e;
-  if (e < 0 || h.nq == 0) return;  // no delta, or the MFMA kernel's block
+  if (e < 0 || h.nq == 0) return;  // no delta
   const int rl = slot_rank(a, e);
   if (rl == 0) return;  // a slot of rank 0 adds nothing
   int n[CPT], soff[CPT];
@@ -445,126 +445,6 @@ __global__ void __launch_bounds__(kThreads) expand_kernel(MOL_ROUTE_PARAMS, Delt
   expand_block<BF16, RV>(a, r, blk, (int)blockIdx.x - blk * r.per, pid, nreal, s_lds);
 }
 
-// ------------------------------------------------------------------- plan-driven items
-// With a work plan from the align, a work item is (group entry, row group) for the shrink
-// and (group entry, column chunk) for the expand: at most kPG pairs of one block, so every
-// item is one straight pass, a block of many pairs is spread over several items instead of
-// walking its groups one after another, and the grid follows the entries instead of every
-// possible block. The grid is at most what the chip holds at once; each workgroup takes
-// items gridDim apart until the plan's count is reached. The plan's count and the item's
-// entry are read in one batch, from the preloaded plan pointer.
-struct PlanItem {
-  int idx;     // group entry
-  int sub;     // row group (shrink) or column chunk (expand)
-  int e;       // virtual expert
-  int nq;      // real pairs (1..kPG)
-  int p[kPG];  // their ids (numel past nq)
-  int count;   // group entries in the plan
-  bool live;   // false: past the plan's entries, the workgroup is done
-};
-
-__device__ __forceinline__ PlanItem plan_item(const int32_t* plan, int item, const FastDiv& per) {
-  PlanItem it;
-  it.idx = fdiv(item, per);
-  it.sub = item - it.idx * (int)per.d;
-  const int count = plan[0];
-  const int32_t* g = plan + kPlanHeader + (int64_t)it.idx * kPlanGroupInts;
-  const int4 h = *reinterpret_cast<const int4*>(g);
-  const int4 q = *reinterpret_cast<const int4*>(g + 4);
-  it.count = count;
-  it.live = it.idx < count;
-  it.e = h.y;
-  it.nq = h.z;
-  it.p[0] = q.x;
-  it.p[1] = q.y;
-  it.p[2] = q.z;
-  it.p[3] = q.w;
-  return it;
-}
-
-// Pin the first entry's words (and the count) where the caller needs them: otherwise the
-// compiler moves the entry's loads below the count check, a second round trip.
-__device__ __forceinline__ void pin_item(const PlanItem& it) {
-  asm volatile("" ::"s"(it.e), "s"(it.nq), "s"(it.p[0]), "s"(it.p[1]), "s"(it.p[2]),
-               "s"(it.p[3]), "s"(it.count));
-}
-
-#define MOL_PLAN_PARAMS \
-  const int32_t *plan, int32_t items, int32_t per, uint32_t per_m, uint32_t per_l
-
-template <bool BF16, int LPR, bool HELD>
-__global__ void __launch_bounds__(kThreads) shrink_plan_kernel(MOL_PLAN_PARAMS, DeltaArgs a) {
-  constexpr int ESZ = BF16 ? 2 : 4;
-  constexpr int RPI = kThreads / LPR;
-  __shared__ uint4 xs[ShrinkLds<LPR>::kVecs];
-  const FastDiv fper{(uint32_t)per, per_m, per_l};
-  int item = blockIdx.x;
-  // the first item's entry is read before anything else (scalar loads from the preloaded
-  // plan pointer at a clamped, always valid index, in one round trip with the argument
-  // fetch); later items' entries are read at the end of the previous item
-  PlanItem it = plan_item(plan, item < items ? item : 0, fper);
-  fetch_args(a);
-  pin_item(it);
-  if (item >= items) return;
-  const int nvec = a.K * ESZ / 16;
-  for (;; it = plan_item(plan, item, fper)) {
-    if (!it.live) return;  // entries come in order: every later item is past the count too
-    const int rl = slot_rank(a, it.e);
-    const int row = it.sub * RPI + (int)threadIdx.x / LPR;
-    const bool row_in = row < a.R;
-    if (item != (int)blockIdx.x) __syncthreads();  // the previous item is done with xs
-    if constexpr (HELD) {
-      const bool row_ok = row_in && fmod(row, a.f_r) < rl;  // past the rank: zero, unread
-      const int64_t abytes = (int64_t)a.R * a.K * ESZ;
-      const __amdgpu_buffer_rsrc_t ra =
-          expert_rsrc((const char*)a.A + (int64_t)it.e * abytes, abytes);
-      uint4 av[kSeg];
-      load_a_seg<LPR>(ra, (uint32_t)(row_ok ? row : 0) * (uint32_t)(a.K * ESZ), row_ok, 0,
-                      nvec, av);
-      shrink_pairs<BF16, LPR>(a, av, row, row_in, it.p, it.nq, nvec, xs);
-    } else {
-      shrink_group_long<BF16, LPR>(a, it.e, rl, it.sub, it.p, it.nq, xs);
-    }
-    item += gridDim.x;
-    if (item >= items) return;
-  }
-}
-
-template <bool BF16, int RV>
-__global__ void __launch_bounds__(kThreads) expand_plan_kernel(MOL_PLAN_PARAMS, DeltaArgs a) {
-  constexpr int CPT = cols_per_thread(RV);
-  constexpr int ESZ = BF16 ? 2 : 4;
-  constexpr int r = RV * 16 / ESZ;
-  __shared__ int pid[kPidSlots];
-  __shared__ __attribute__((aligned(16))) float s_lds[kSLdsFloats];
-  const FastDiv fper{(uint32_t)per, per_m, per_l};
-  const int tid = threadIdx.x;
-  int item = blockIdx.x;
-  PlanItem it = plan_item(plan, item < items ? item : 0, fper);  // as in the shrink
-  fetch_args(a);
-  pin_item(it);
-  if (item >= items) return;
-  for (;; it = plan_item(plan, item, fper)) {
-    if (!it.live) return;
-    const int rl = slot_rank(a, it.e);
-    if (item != (int)blockIdx.x) __syncthreads();  // the previous item is done with LDS
-    if (rl > 0) {  // a slot of rank 0 adds nothing (uniform over the workgroup)
-    int n[CPT], soff[CPT];
-#pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      n[j] = it.sub * (CPT * kThreads) + j * kThreads + tid;
-      soff[j] = (n[j] < a.N ? fdiv(n[j], a.f_w) : 0) * r;
-    }
-    const float sc = a.scale[fdiv(it.e, a.f_e)];
-    uint4 bv[CPT][RV];
-    load_b_rows<BF16, RV, CPT>(a, it.e, rl, n, bv);
-    expand_pairs<BF16, RV>(a, rl, n, soff, sc, bv, it.p, it.nq, pid, s_lds);
-    }
-    item += gridDim.x;
-    if (item >= items) return;
-  }
-}
-
 template <bool BF16, bool HELD>
 hipError_t shrink_dispatch(const DeltaArgs& a, int lpr, int grid, hipStream_t st) {
   switch (lpr) {
@@ -585,47 +465,6 @@ hipError_t expand_dispatch(const DeltaArgs& a, int rv, int grid, hipStream_t st)
     case 4: hipLaunchKernelGGL((expand_kernel<BF16, 4>), dim3(grid), dim3(kThreads), 0, st, MOL_ROUTE_ARGS(a, a.nchunk, a.f_nc), a); break;
     case 8: hipLaunchKernelGGL((expand_kernel<BF16, 8>), dim3(grid), dim3(kThreads), 0, st, MOL_ROUTE_ARGS(a, a.nchunk, a.f_nc), a); break;
     case 16: hipLaunchKernelGGL((expand_kernel<BF16, 16>), dim3(grid), dim3(kThreads), 0, st, MOL_ROUTE_ARGS(a, a.nchunk, a.f_nc), a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-template <bool BF16, bool HELD>
-hipError_t shrink_plan_dispatch(const DeltaArgs& a, const int32_t* plan, int items, int lpr,
-                                int grid, hipStream_t st) {
-  const FastDiv& f = a.f_rg;
-  switch (lpr) {
-#define MOL_SP(L)                                                                              \
-  case L:                                                                                      \
-    hipLaunchKernelGGL((shrink_plan_kernel<BF16, L, HELD>), dim3(grid), dim3(kThreads), 0, st, \
-                       plan, items, a.rgroups, f.m, f.l, a);                                   \
-    break;
-    MOL_SP(8)
-    MOL_SP(16)
-    MOL_SP(32)
-    MOL_SP(64)
-#undef MOL_SP
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-template <bool BF16>
-hipError_t expand_plan_dispatch(const DeltaArgs& a, const int32_t* plan, int items, int rv,
-                                int grid, hipStream_t st) {
-  const FastDiv& f = a.f_nc;
-  switch (rv) {
-#define MOL_EP(R)                                                                               \
-  case R:                                                                                       \
-    hipLaunchKernelGGL((expand_plan_kernel<BF16, R>), dim3(grid), dim3(kThreads), 0, st, plan, \
-                       items, a.nchunk, f.m, f.l, a);                                           \
-    break;
-    MOL_EP(1)
-    MOL_EP(2)
-    MOL_EP(4)
-    MOL_EP(8)
-    MOL_EP(16)
-#undef MOL_EP
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -661,24 +500,6 @@ hipError_t launch_expand(const DeltaArgs& a, bool bf16, int grid, hipStream_t st
   const int rv = (a.R / a.slices) * (bf16 ? 2 : 4) / 16;
   return bf16 ? expand_dispatch<true>(a, rv, grid, stream)
               : expand_dispatch<false>(a, rv, grid, stream);
-}
-
-hipError_t launch_shrink_plan(const DeltaArgs& a, const int32_t* plan, int items, bool bf16,
-                              int rows_per_item, int grid, hipStream_t stream) {
-  const int lpr = kThreads / rows_per_item;
-  const bool held = (int64_t)a.K * (bf16 ? 2 : 4) / 16 <= (int64_t)kSeg * lpr;
-  if (bf16)
-    return held ? shrink_plan_dispatch<true, true>(a, plan, items, lpr, grid, stream)
-                : shrink_plan_dispatch<true, false>(a, plan, items, lpr, grid, stream);
-  return held ? shrink_plan_dispatch<false, true>(a, plan, items, lpr, grid, stream)
-              : shrink_plan_dispatch<false, false>(a, plan, items, lpr, grid, stream);
-}
-
-hipError_t launch_expand_plan(const DeltaArgs& a, const int32_t* plan, int items, bool bf16,
-                              int grid, hipStream_t stream) {
-  const int rv = (a.R / a.slices) * (bf16 ? 2 : 4) / 16;
-  return bf16 ? expand_plan_dispatch<true>(a, plan, items, rv, grid, stream)
-              : expand_plan_dispatch<false>(a, plan, items, rv, grid, stream);
 }
 
 }  // namespace mol

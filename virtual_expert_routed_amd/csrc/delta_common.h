@@ -102,15 +102,11 @@ __device__ __forceinline__ int block_expert(const DeltaArgs& a, int blk) {
   return (blk < live_blocks(a, npp) && real_expert(e, a.V)) ? e : -1;
 }
 
-// Whether block blk holds at least t >= 1 real pairs (its real entries form a prefix).
-__device__ __forceinline__ bool block_has(const DeltaArgs& a, int blk, int t) {
-  return t <= a.BM && real_pair(a.sorted[(int64_t)blk * a.BM + (t - 1)], a.numel);
-}
 
 // What a work item needs to know of its block before its first weight load: the block's
 // virtual expert (e < 0: the item has nothing to do, because the block is past the live
-// blocks, in the sentinel bucket, or belongs to the MFMA kernels), its first kPG entries as
-// scalars (numel past the block) and how many of them are real pairs (a prefix).
+// blocks or in the sentinel bucket), its first kPG entries as scalars (numel past the
+// block) and how many of them are real pairs (a prefix).
 struct BlockHead {
   int e;
   int p[kPG];
@@ -128,18 +124,17 @@ struct RouteArgs {
   const int32_t* expert_ids;
   const int32_t* npp;
   int32_t BM;
-  int32_t mfma_min;
   FastDiv per_div;  // work items per block, as a multiply-shift divisor (m, l)
   int32_t per;      // work items per block
 };
 
-#define MOL_ROUTE_PARAMS                                                                    \
-  const int32_t *r_sorted, const int32_t *r_eids, const int32_t *r_npp, int32_t r_bm,      \
-      int32_t r_mm, uint32_t r_pm, uint32_t r_pl, int32_t r_per
+#define MOL_ROUTE_PARAMS                                                               \
+  const int32_t *r_sorted, const int32_t *r_eids, const int32_t *r_npp, int32_t r_bm, \
+      uint32_t r_pm, uint32_t r_pl, int32_t r_per
 #define MOL_ROUTE_ARGS(a, per, div) \
-  (a).sorted, (a).expert_ids, (a).npp, (a).BM, (a).mfma_min, (div).m, (div).l, (per)
+  (a).sorted, (a).expert_ids, (a).npp, (a).BM, (div).m, (div).l, (per)
 #define MOL_ROUTE_MAKE \
-  RouteArgs{r_sorted, r_eids, r_npp, r_bm, r_mm, FastDiv{(uint32_t)r_per, r_pm, r_pl}, r_per}
+  RouteArgs{r_sorted, r_eids, r_npp, r_bm, FastDiv{(uint32_t)r_per, r_pm, r_pl}, r_per}
 
 // The block and the item within it of this workgroup.
 __device__ __forceinline__ int route_block(const RouteArgs& r) {
@@ -167,17 +162,13 @@ __device__ __forceinline__ BlockHead block_head(const DeltaArgs& a, const RouteA
                                                 int blk) {
   const int32_t* sp = r.sorted + (int64_t)blk * r.BM;
   const int last = r.BM - 1;
-  const bool use_m = r.mfma_min > 0 && r.mfma_min <= r.BM;
-  const int im = use_m ? r.mfma_min - 1 : 0;
   int v[kPG];
 #pragma unroll
   for (int i = 0; i < kPG; ++i) v[i] = sp[i < last ? i : last];
-  const int vm_raw = sp[im];
   const int er = r.expert_ids[blk];
   const int npp = *r.npp;
   // after the routing reads, so that they stay scalar loads, and in their round trip
   fetch_args(a);
-  const int vm = use_m ? vm_raw : a.numel;  // a select keeps its load unconditional
   BlockHead h;
   h.nq = 0;
 #pragma unroll
@@ -188,8 +179,7 @@ __device__ __forceinline__ BlockHead block_head(const DeltaArgs& a, const RouteA
   h.all_here = h.nq < kPG || r.BM <= kPG;
   const int nb = npp < 0 ? 0 : fdiv(npp, a.f_bm);
   const int live = nb > a.max_blocks ? a.max_blocks : nb;
-  const bool mfma = real_pair(vm, a.numel);
-  h.e = (blk < live && real_expert(er, a.V) && !mfma) ? er : -1;
+  h.e = (blk < live && real_expert(er, a.V)) ? er : -1;
   return h;
 }
 

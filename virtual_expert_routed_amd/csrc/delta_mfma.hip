@@ -7,8 +7,9 @@
 //
 // At prefill a hot virtual expert's block carries up to BLOCK_M real pairs, so a block is a
 // real dense tile and the products run on v_mfma_f32_16x16x32_bf16 (fp32 accumulation).
-// These kernels take only blocks with at least mfma_min real pairs; the VALU kernels of the
-// same launch skip exactly those blocks, so every block is computed once.
+// A batch large enough for them (from 4096 pairs and 8 per bucket on average) gives every
+// block to these kernels and launches no VALU kernel: a block of one or two pairs still
+// costs less as a mostly empty tile than a VALU launch over every possible block.
 //
 // MFMA 16x16x32 operand layout (lane l of a wave): A holds row l % 16, k = 8*(l/16)..+8;
 // B holds column l % 16, k = 8*(l/16)..+8; the 16x16 fp32 result holds column l % 16,
@@ -212,7 +213,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
   if (item >= n_live) return;
   const int blk = item / nrt, r0 = (item % nrt) * G::kRows;
   const int e = block_expert(a, blk);
-  if (e < 0 || !block_has(a, blk, a.mfma_min)) return;
+  if (e < 0) return;  // past the live blocks or the sentinel bucket
   const int rl = slot_rank(a, e);
   const char* av = (const char*)a.A + (int64_t)e * a.R * a.K * 2;
   for (int j0 = 0; j0 < a.BM; j0 += kRowsPerPass) {
@@ -224,25 +225,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 }
 
 // ----------------------------------------------------------------- plan-driven dense runs
-// With the align's work plan the MFMA expand takes the plan's dense runs instead of single
-// blocks: up to kPlanDenseBlocks consecutive blocks of one virtual expert, each with at
-// least `split` real pairs. A run item holds its weight columns for all of its blocks,
+// With the align's work plan the MFMA expand takes the plan's runs instead of single
+// blocks: up to kPlanDenseBlocks consecutive blocks of one virtual expert. A run item holds its weight columns for all of its blocks,
 // where a block item loads them once per block (a hot expert's bucket of many blocks is
 // read about a quarter as often). The shrink keeps its block items: a run there needs the
 // accumulators of every block at once, and at the occupancy that leaves it measured
 // slower than block items ordered by XCD, which share A_v through L2 instead.
 
-// Dense entry `run` of the plan: {first block, blocks, virtual expert}; nb = 0 past the
-// plan's count (the entry read is then entry 0, a valid address).
+// Run `run` of the plan: {first block, blocks, virtual expert}; nb = 0 past the plan's
+// count (the entry read is then entry 0, a valid address).
 struct DenseRun {
   int blk0, nb, e;
 };
-__device__ __forceinline__ DenseRun dense_run(const int32_t* plan, int numel, int run) {
-  const int count = plan[1];
+__device__ __forceinline__ DenseRun dense_run(const int32_t* plan, int run) {
+  const int count = plan[0];
   const int rc = run < count ? run : 0;
-  const int4 d = *reinterpret_cast<const int4*>(plan + kPlanHeader +
-                                                (int64_t)numel * kPlanGroupInts +
-                                                (int64_t)rc * kPlanDenseInts);
+  const int4 d =
+      *reinterpret_cast<const int4*>(plan + kPlanHeader + (int64_t)rc * kPlanDenseInts);
   return DenseRun{d.x, run < count ? d.y : 0, d.z};
 }
 
@@ -423,7 +422,7 @@ __global__ void __launch_bounds__(256) expand_mfma_kernel(DeltaArgs a) {
   __shared__ int nrows_lds;
   const int blk = fdiv((int)blockIdx.x, a.f_nc), chunk = (int)blockIdx.x - blk * a.nchunk;
   const int e = block_expert(a, blk);
-  if (e < 0 || !block_has(a, blk, a.mfma_min)) return;
+  if (e < 0) return;  // past the live blocks or the sentinel bucket
   const int rl = slot_rank(a, e);
   if (rl == 0) return;  // a slot of rank 0 adds nothing
   expand_mfma_blocks<KS>(a, blk, 1, chunk, e, rl, pid, &nrows_lds, s_lds, tile);
@@ -437,11 +436,11 @@ __global__ void __launch_bounds__(256) expand_mfma_run_kernel(const int32_t* pla
   __shared__ __attribute__((aligned(16))) float tile[16 * kTileStride];
   __shared__ int pid[kRowsPerPass];
   __shared__ int nrows_lds;
-  const int n_live = min(n_items, plan[1] * a.nchunk);
+  const int n_live = min(n_items, plan[0] * a.nchunk);  // the plan's runs x column chunks
   const int item = xcd_item(n_live);
   if (item >= n_live) return;
   const int run = fdiv(item, a.f_nc), chunk = item - run * a.nchunk;
-  const DenseRun d = dense_run(plan, a.numel, run);
+  const DenseRun d = dense_run(plan, run);
   if (d.nb == 0) return;
   const int rl = slot_rank(a, d.e);
   if (rl == 0) return;  // a slot of rank 0 adds nothing

@@ -182,7 +182,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(MOL_ROUTE_PARAMS, GemmAr
   const DeltaArgs& a = g.route;
   const RouteArgs r = MOL_ROUTE_MAKE;
   const int blk = route_block(r), rg = (int)blockIdx.x - blk * r.per;
-  const BlockHead h = block_head(a, r, blk);  // mfma_min is 0: no block is skipped for MFMA
+  const BlockHead h = block_head(a, r, blk);
   const int e = h.e;
   if (e < 0) return;  // sentinel block (no local expert) or past the live blocks
   if (h.all_here) {

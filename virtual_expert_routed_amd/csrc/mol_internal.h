@@ -11,43 +11,32 @@ namespace mol {
 constexpr int kMaxBuckets = 8192;     // V + 1 <= 8192
 constexpr int kAlignSmallMax = 4096;  // pairs the one-workgroup align handles
 constexpr int kShrinkItemBytes = 32768;  // target weight bytes per shrink work item
-constexpr int kMfmaMinPairs = 4;         // a block takes the MFMA path from this many pairs
 constexpr int kMfmaMinNumel = 4096;      // MFMA kernels are launched from this many pairs
 constexpr int kMaxRankVecs = 16;         // 16-byte vectors in one rank row slice (256 bytes)
 
-// The work plan the align writes beside the routing when asked (int32 words):
-//   [0] number of group entries G, [1] number of dense entries D, [2] the split, [3..7] 0;
-//   group entries from word kPlanHeader, kPlanGroupInts each, for at most gmax = numel:
-//     {block, virtual expert, nq (1..4), 0, p0, p1, p2, p3}: up to four consecutive real
-//     pairs of one block (numel in the slots past nq), in bucket and block order;
-//   dense entries after the gmax group entries, kPlanDenseInts each:
-//     {first block, blocks (1..kPlanDenseBlocks), virtual expert, 0}: consecutive blocks
-//     of one bucket that each hold at least `split` real pairs, in bucket order.
-// A block with at least `split` real pairs (split > 0) goes to the dense entries, any other
-// block of a real bucket to the group entries; the sentinel bucket gets no entries.
+// A batch takes the bf16 MFMA kernels for all of its blocks when it is large enough to hold
+// dense blocks in numbers: from kMfmaMinNumel pairs and 8 pairs per bucket on average. Its
+// VALU kernels are then not launched at all; a block of few pairs still costs less as a
+// mostly empty MFMA tile than as a VALU item.
+inline bool mfma_batch(int64_t numel, int64_t V) {
+  return numel >= kMfmaMinNumel && numel >= 8 * (V + 1);
+}
+
+// The work plan the align writes beside the routing when asked, for such a batch (int32
+// words): [0] the number of runs D, [1..7] 0; from word kPlanHeader, D runs of
+// kPlanDenseInts words {first block, blocks (1..kPlanDenseBlocks), virtual expert, 0}:
+// consecutive blocks of one real bucket, in bucket order, every block of a real bucket in
+// exactly one run (the sentinel bucket has none). A block holds at least one real pair, so
+// there are at most min(max_blocks, numel) runs.
 constexpr int kPlanHeader = 8;
-constexpr int kPlanGroupInts = 8;
 constexpr int kPlanDenseInts = 4;
 constexpr int kPlanDenseBlocks = 4;
 
-// The split: blocks with at least this many real pairs are dense (0: none are). Dense
-// blocks are worth their own kernels only for batches large enough to hold them in
-// numbers: from 4096 pairs and 8 pairs per bucket on average, and BLOCK_M >= 4.
-static_assert(kMfmaMinPairs <= 4, "a ragged block below the split fits one group entry");
-inline int32_t plan_split(int64_t numel, int64_t V, int32_t BM) {
-  return (numel >= kMfmaMinNumel && numel >= 8 * (V + 1) && BM >= kMfmaMinPairs)
-             ? kMfmaMinPairs
-             : 0;
+inline int64_t plan_max_runs(int64_t numel, int64_t max_blocks) {
+  return numel < max_blocks ? numel : max_blocks;
 }
-inline int64_t plan_max_groups(int64_t numel) { return numel; }
-inline int64_t plan_max_dense(int64_t numel, int64_t max_blocks, int32_t split) {
-  if (split <= 0) return 0;
-  const int64_t d = numel / split;
-  return d < max_blocks ? d : max_blocks;
-}
-inline int64_t plan_words(int64_t numel, int64_t max_blocks, int32_t split) {
-  return kPlanHeader + kPlanGroupInts * plan_max_groups(numel) +
-         kPlanDenseInts * plan_max_dense(numel, max_blocks, split);
+inline int64_t plan_words(int64_t numel, int64_t max_blocks) {
+  return kPlanHeader + kPlanDenseInts * plan_max_runs(numel, max_blocks);
 }
 
 struct AlignArgs {
@@ -73,8 +62,7 @@ struct AlignArgs {
   FastDiv f_bm;          // BM
   FastDiv f_groups;      // workgroups of the one-launch path
   int32_t* plan;         // the work plan (nullptr: none is written)
-  int32_t split;         // the plan's dense threshold
-  int32_t gmax;          // group entries the plan has room for (dense entries follow)
+  int32_t dmax;          // runs the plan has room for
   int32_t max_blocks;    // the routing's block bound
 };
 
@@ -114,9 +102,6 @@ struct DeltaArgs {
   int32_t rgroups;       // shrink work items per block (row groups of A)
   int32_t nchunk;        // expand work items per block (column chunks of B)
   int32_t max_blocks;
-  int32_t mfma_min;      // > 0: blocks with at least this many real pairs go to the MFMA
-                         // kernels and the VALU kernels skip them; 0: VALU kernels only
-  int32_t pad_;
   // the launch's fixed divisors, as multiply-shift constants (set by with_divisors)
   FastDiv f_rg;          // rgroups
   FastDiv f_nc;          // nchunk
@@ -165,7 +150,7 @@ struct CombineArgs {
 
 // The base MoE grouped GEMM of a stage, optionally with the LoRA delta in its epilogue.
 struct GemmArgs {
-  DeltaArgs route;         // routing of the base-expert blocks (V = E, mfma_min 0)
+  DeltaArgs route;         // routing of the base-expert blocks (V = E)
   const void* xin;
   int64_t ld_x;
   int32_t row_div;
@@ -203,13 +188,7 @@ int expand_cols_per_item(int32_t R, int32_t slices, int elem_bytes);
 hipError_t launch_shrink(const DeltaArgs& a, bool bf16, int rows_per_item, int grid,
                          hipStream_t stream);
 hipError_t launch_expand(const DeltaArgs& a, bool bf16, int grid, hipStream_t stream);
-// the same kernels' work driven by an align work plan: `items` = group entries the plan has
-// room for times the work items per entry; grid <= items
-hipError_t launch_shrink_plan(const DeltaArgs& a, const int32_t* plan, int items, bool bf16,
-                              int rows_per_item, int grid, hipStream_t stream);
-hipError_t launch_expand_plan(const DeltaArgs& a, const int32_t* plan, int items, bool bf16,
-                              int grid, hipStream_t stream);
-// bf16 MFMA kernels for the blocks with at least a.mfma_min real pairs
+// bf16 MFMA kernels, for every block of a batch that takes them (mfma_batch)
 // rows of A_v per MFMA shrink work item (the grid is max_blocks * cdiv(R, this))
 int shrink_mfma_row_tile(int32_t R);
 hipError_t launch_shrink_mfma(const DeltaArgs& a, int items, hipStream_t stream);

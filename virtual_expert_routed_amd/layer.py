@@ -49,7 +49,7 @@ class DeviceLayer:
         self.npp = torch.empty(1, dtype=torch.int32, device=dev)
         wsb = mb.mol_align_workspace_bytes(numel, V, BM)
         self.align_ws = torch.empty(max(256, wsb), dtype=torch.uint8, device=dev)
-        # the align's work plan, which the shrink and expand calls then take their work from
+        # the align's work plan, which the expand then takes its work items from
         self.plan = mb.new_plan(numel, V, BM, dev) if use_plan else None
         self.delta_ws = [mb.new_delta_workspace(numel, st.R, V, BM, dev) for st in cfg.stages]
         self.s = [torch.empty((max(1, numel), st.R), dtype=torch.float32, device=dev)
@@ -116,7 +116,7 @@ class DeviceLayer:
         c = self.cfg
         mb.mol_lora_shrink(self.xin[si], self.row_div[si], self.A[si], *self.routing(),
                            c.numel, c.V, c.block_m, s=self.s[si], slices=c.stages[si].slices,
-                           slot_ranks=self.slot_ranks, num_experts=c.E, plan=self.plan)
+                           slot_ranks=self.slot_ranks, num_experts=c.E)
         return self.s[si]
 
     def expand(self, si: int):
