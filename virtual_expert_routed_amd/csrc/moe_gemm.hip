@@ -17,20 +17,26 @@
 // RPI consecutive output columns), each column's row of W_t read once with coalesced
 // 16-byte buffer loads by LPR lanes and reused for up to four pairs, the pairs' input
 // rows staged in LDS, the lanes' partial sums combined by a fixed xor tree. The fused
-// delta costs the B vectors and s values of each lane's share of the rank, loaded after
-// the weight loop, and each lane adds its part of the rank sum to its partial before the
-// tree: the delta needs no extra pass over the output and no extra write. (Measured at
-// decode on MI355X, this extra round trip per item costs more than a separate expand
-// launch: the base GEMM alone streams its weights at about 5.8 TB/s in items of eight
-// columns, and any per-item latency shows.)
+// delta costs, per pair, the B row slices of the item's columns and the s row, moved into
+// LDS by direct-to-LDS loads in the last weight segment's round trip, and each lane adds its
+// part of the rank sum to its partial before the tree: the delta needs no extra pass over
+// the output and no extra write. (Measured at decode on MI355X it is still slower than the
+// base GEMM followed by a separate expand: the base GEMM streams its weights at about
+// 6 TB/s in items of eight columns, and the delta's extra bytes per item show.)
 #include "delta_common.h"
 
 namespace mol {
 namespace {
 
+// The fused delta's operands in (dynamic) LDS: per pair, the B row slices of the item's
+// columns and the s row (R <= 256 floats).
+constexpr int kSRowBytes = 1024;
+__host__ __device__ inline int gemm_bslice_bytes(int rpi, int rbytes) { return rpi * rbytes; }
+static_assert(kThreads / 64 == kPG, "wave q stages pair q's delta operands");
+
 template <bool BF16, int LPR, bool FUSED>
 __device__ __forceinline__ void gemm_group(const GemmArgs& g, int e, int rg, const int* p,
-                                           int nq, uint4* xs) {
+                                           int nq, uint4* xs, char* dl) {
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int VE = BF16 ? 8 : 4;  // elements of one 16-byte vector
   constexpr int RPI = kThreads / LPR;
@@ -54,11 +60,12 @@ __device__ __forceinline__ void gemm_group(const GemmArgs& g, int e, int rg, con
   for (int i = 0; i < kPG; ++i) acc[i] = 0.f;
 
   // The fused delta. Its per-pair slot, rank and scale are uniform over the workgroup and
-  // read up front; its vector operands (the B row slice and the s row slice a lane needs)
-  // are loaded after the weight loop, two pairs per round trip, so the loop keeps close to
-  // the register budget, and the occupancy, of the base GEMM alone. Lane lr takes 16-byte
-  // vectors lr, lr + LPR, ... of its column's B row slice and the matching s values, and
-  // adds its share of the rank sum to its partial before the xor tree.
+  // read up front. Its vector operands go straight to LDS in the last weight segment's round
+  // trip (wave q: pair q's B row slices for the item's columns, one contiguous run, and its
+  // s row), so the delta adds neither a dependent round trip nor registers to the weight
+  // loop. After the products, lane lr takes 16-byte vectors lr, lr + LPR, ... of its
+  // column's B row slice and the matching s values, and adds its share of the rank sum to
+  // its partial before the xor tree.
   int rlq[kPG], vq[kPG];
   float scq[kPG];
   if constexpr (FUSED) {
@@ -92,6 +99,26 @@ __device__ __forceinline__ void gemm_group(const GemmArgs& g, int e, int rg, con
       lds_dma16(xbase + (ok ? (int64_t)fdiv(pq, g.route.f_rd) * xstride + (int64_t)v * 16 : 0),
                 xs + wv * 64 + t * kThreads);
     }
+    if constexpr (FUSED) {
+      if (m0 + kSeg >= vpl && wv < nq) {  // wave q takes pair q (uniform)
+        const int r = g.R / g.slices, rb = r * ESZ;
+        const int bsz = gemm_bslice_bytes(RPI, rb);
+        const int lane = tid & 63;
+        const int v = wv == 0 ? vq[0] : wv == 1 ? vq[1] : wv == 2 ? vq[2] : vq[3];
+        const int pq = wv == 0 ? p[0] : wv == 1 ? p[1] : wv == 2 ? p[2] : p[3];
+        // the item's columns n0.. are consecutive rows of B_v: one contiguous slice (the
+        // columns past N are not loaded; their lanes never read them)
+        const int64_t mat = (int64_t)g.N * rb;
+        const char* bsrc = (const char*)g.B + (int64_t)v * mat;
+        const int64_t first = (int64_t)rg * RPI * rb;
+        const int nv = (int)(min<int64_t>(mat - first, bsz) / 16);
+        char* bdst = dl + wv * bsz;
+        for (int t0 = 0; t0 < nv; t0 += 64)
+          if (t0 + lane < nv) lds_dma16(bsrc + first + (int64_t)(t0 + lane) * 16, bdst + t0 * 16);
+        const float* srow = g.s + (int64_t)pq * g.R;
+        if (lane < g.R / 4) lds_dma16(srow + lane * 4, dl + kPG * bsz + wv * kSRowBytes);
+      }
+    }
     __builtin_amdgcn_s_waitcnt(0);  // the x DMA and the weights have landed
     __syncthreads();
 #pragma unroll
@@ -105,55 +132,31 @@ __device__ __forceinline__ void gemm_group(const GemmArgs& g, int e, int rg, con
     }
   }
   if constexpr (FUSED) {
-    const int r = g.R / g.slices;
+    const int r = g.R / g.slices, rb = r * ESZ;
+    const int bsz = gemm_bslice_bytes(RPI, rb);
     const int gs = n_ok ? fdiv(n, g.route.f_w) : 0;
-    const int64_t bbytes = (int64_t)g.N * r * ESZ;
-    // lane lr takes the 16-byte vectors lr, lr + LPR, ... of its column's B row slice (at
-    // most kMaxRankVecs of them, so NVL per lane) and the matching s values
+    const int c = tid / LPR;  // this lane's column within the item
     constexpr int NVL = (kMaxRankVecs + LPR - 1) / LPR;
-    // two pairs per round trip: at decode a block rarely holds more, and holding four
-    // pairs' operands at once would cost the loop's occupancy
-    constexpr int kEP = 2;
 #pragma unroll
-    for (int h = 0; h < kPG; h += kEP) {
-      if (h >= nq) break;  // uniform
-      uint4 bq[kEP][NVL];
-      float4 s0[kEP][NVL], s1[kEP][NVL];
+    for (int i = 0; i < kPG; ++i) {
+      if (i >= nq || rlq[i] == 0 || !n_ok || lr * VE >= rlq[i]) continue;  // no part here
+      const char* bsl = dl + i * bsz + c * rb;
+      const float* sp0 = reinterpret_cast<const float*>(dl + kPG * bsz + i * kSRowBytes) + gs * r;
+      float d = 0.f;
 #pragma unroll
-      for (int u = 0; u < kEP; ++u) {
-        const int i = h + u;
-        const __amdgpu_buffer_rsrc_t rb =
-            expert_rsrc((const char*)g.B + (int64_t)vq[i] * bbytes, bbytes);
-        const int pq = i < nq ? (i == 0 ? p[0] : i == 1 ? p[1] : i == 2 ? p[2] : p[3]) : 0;
-#pragma unroll
-        for (int w = 0; w < NVL; ++w) {
-          const int vi = lr + w * LPR;  // vector of the B row slice
-          const bool use = i < nq && n_ok && vi * VE < rlq[i];
-          bq[u][w] = buf16(rb, use ? (uint32_t)(n * r * ESZ + vi * 16) : kOutOfRange);
-          const float* sp = g.s + (int64_t)pq * g.R + gs * r + vi * VE;
-          s0[u][w] = use ? *reinterpret_cast<const float4*>(sp) : make_float4(0.f, 0.f, 0.f, 0.f);
-          s1[u][w] = BF16 && use ? *reinterpret_cast<const float4*>(sp + 4)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);  // fp32: 4 per vector
-        }
+      for (int w = 0; w < NVL; ++w) {
+        const int vi = lr + w * LPR;
+        if (vi * VE >= rlq[i]) break;
+        const uint4 braw = *reinterpret_cast<const uint4*>(bsl + vi * 16);
+        const float4 s0 = *reinterpret_cast<const float4*>(sp0 + vi * VE);
+        const float4 s1 = BF16 ? *reinterpret_cast<const float4*>(sp0 + vi * VE + 4)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);  // fp32: 4 per vector
+        const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        // the vector that straddles the slot's rank is trimmed
+        const uint4 b = rlq[i] < (vi + 1) * VE ? keep_first<BF16>(braw, rlq[i] - vi * VE) : braw;
+        d = dot16_s<BF16>(b, sv, d);
       }
-#pragma unroll
-      for (int u = 0; u < kEP; ++u) {
-        const int i = h + u;
-        if (i >= nq || rlq[i] == 0 || !n_ok || lr * VE >= rlq[i]) continue;  // no part here
-        float d = 0.f;
-#pragma unroll
-        for (int w = 0; w < NVL; ++w) {
-          const int vi = lr + w * LPR;
-          if (vi * VE >= rlq[i]) break;
-          const float sv[8] = {s0[u][w].x, s0[u][w].y, s0[u][w].z, s0[u][w].w,
-                               s1[u][w].x, s1[u][w].y, s1[u][w].z, s1[u][w].w};
-          // B vectors past the slot's rank read as zero; the one that straddles it is trimmed
-          const uint4 b = rlq[i] < (vi + 1) * VE ? keep_first<BF16>(bq[u][w], rlq[i] - vi * VE)
-                                                 : bq[u][w];
-          d = dot16_s<BF16>(b, sv, d);
-        }
-        acc[i] = fmaf(scq[i], d, acc[i]);
-      }
+      acc[i] = fmaf(scq[i], d, acc[i]);
     }
   }
 #pragma unroll
@@ -179,6 +182,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(MOL_ROUTE_PARAMS, GemmAr
   __shared__ int pid[kPidSlots];
   __shared__ int nreal;
   __shared__ uint4 xs[kPG * kSeg * LPR];
+  extern __shared__ __attribute__((aligned(16))) char dl[];  // the fused delta's operands
   const DeltaArgs& a = g.route;
   const RouteArgs r = MOL_ROUTE_MAKE;
   const int blk = route_block(r), rg = (int)blockIdx.x - blk * r.per;
@@ -186,7 +190,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(MOL_ROUTE_PARAMS, GemmAr
   const int e = h.e;
   if (e < 0) return;  // sentinel block (no local expert) or past the live blocks
   if (h.all_here) {
-    if (h.nq > 0) gemm_group<BF16, LPR, FUSED>(g, e, rg, h.p, h.nq, xs);
+    if (h.nq > 0) gemm_group<BF16, LPR, FUSED>(g, e, rg, h.p, h.nq, xs, dl);
     return;
   }
   for (int j0 = 0; j0 < a.BM; j0 += kPidSlots) {
@@ -200,7 +204,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(MOL_ROUTE_PARAMS, GemmAr
 #pragma unroll
       for (int i = 0; i < kPG; ++i) pq[i] = q0 + i < nr ? pid[q0 + i] : a.numel;
       __syncthreads();  // xs of the previous group is no longer read
-      gemm_group<BF16, LPR, FUSED>(g, e, rg, pq, min(kPG, nr - q0), xs);
+      gemm_group<BF16, LPR, FUSED>(g, e, rg, pq, min(kPG, nr - q0), xs, dl);
     }
     if (nr < kPidSlots) return;  // the block's real entries ended in this pass
   }
@@ -208,11 +212,15 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(MOL_ROUTE_PARAMS, GemmAr
 
 template <bool BF16, bool FUSED>
 hipError_t gemm_dispatch(const GemmArgs& g, int lpr, int grid, hipStream_t st) {
+  const size_t dyn =
+      FUSED ? (size_t)kPG * (gemm_bslice_bytes(kThreads / lpr, (g.R / g.slices) * (BF16 ? 2 : 4)) +
+                             kSRowBytes)
+            : 0;
   switch (lpr) {
-    case 8: hipLaunchKernelGGL((gemm_kernel<BF16, 8, FUSED>), dim3(grid), dim3(kThreads), 0, st, MOL_ROUTE_ARGS(g.route, g.rgroups, g.route.f_rg), g); break;
-    case 16: hipLaunchKernelGGL((gemm_kernel<BF16, 16, FUSED>), dim3(grid), dim3(kThreads), 0, st, MOL_ROUTE_ARGS(g.route, g.rgroups, g.route.f_rg), g); break;
-    case 32: hipLaunchKernelGGL((gemm_kernel<BF16, 32, FUSED>), dim3(grid), dim3(kThreads), 0, st, MOL_ROUTE_ARGS(g.route, g.rgroups, g.route.f_rg), g); break;
-    case 64: hipLaunchKernelGGL((gemm_kernel<BF16, 64, FUSED>), dim3(grid), dim3(kThreads), 0, st, MOL_ROUTE_ARGS(g.route, g.rgroups, g.route.f_rg), g); break;
+    case 8: hipLaunchKernelGGL((gemm_kernel<BF16, 8, FUSED>), dim3(grid), dim3(kThreads), dyn, st, MOL_ROUTE_ARGS(g.route, g.rgroups, g.route.f_rg), g); break;
+    case 16: hipLaunchKernelGGL((gemm_kernel<BF16, 16, FUSED>), dim3(grid), dim3(kThreads), dyn, st, MOL_ROUTE_ARGS(g.route, g.rgroups, g.route.f_rg), g); break;
+    case 32: hipLaunchKernelGGL((gemm_kernel<BF16, 32, FUSED>), dim3(grid), dim3(kThreads), dyn, st, MOL_ROUTE_ARGS(g.route, g.rgroups, g.route.f_rg), g); break;
+    case 64: hipLaunchKernelGGL((gemm_kernel<BF16, 64, FUSED>), dim3(grid), dim3(kThreads), dyn, st, MOL_ROUTE_ARGS(g.route, g.rgroups, g.route.f_rg), g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
