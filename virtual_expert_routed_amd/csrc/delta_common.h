@@ -216,6 +216,21 @@ __device__ __forceinline__ uint4 ld16_if(const char* base, int64_t off, bool ok)
   return ok ? v : make_uint4(0, 0, 0, 0);
 }
 
+// Non-temporal 16-byte load and store, for a stream that is read once and written once
+// (the out rows a kernel updates in place): the hint keeps those lines from evicting data
+// that other workgroups re-read from L2, such as an expert's weight tile.
+typedef unsigned int nt_u4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld16_nt_if(const char* base, int64_t off, bool ok) {
+  const nt_u4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u4*>(base + (ok ? off : 0)));
+  return ok ? make_uint4(v.x, v.y, v.z, v.w) : make_uint4(0, 0, 0, 0);
+}
+
+__device__ __forceinline__ void st16_nt(char* p, uint4 v) {
+  const nt_u4 t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<nt_u4*>(p));
+}
+
 // Raw buffer loads over one expert's weight matrix: the resource covers exactly that
 // matrix, offsets are 32-bit, and an offset past its end reads as zero in hardware, so
 // masked lanes need neither a branch nor a select nor a 64-bit address of their own.

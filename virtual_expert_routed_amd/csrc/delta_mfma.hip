@@ -291,6 +291,8 @@ constexpr int kTileStride = kExpandCols + 4;  // fp32 result tile row, padded ag
 // The out rows of pair tile pt as the epilogue reads them: thread t holds the 16-byte
 // vectors t and t + 256 of the tile's 16 rows x 32 vectors (8 bf16 each), so every wave
 // reads two rows' 512 contiguous bytes. Vectors of rows that are not real pairs read zero.
+// The rows are read and written non-temporally: each is touched once by this workgroup,
+// while the weight tile of a virtual expert is re-read by its other column chunks' blocks.
 __device__ __forceinline__ void load_out_tile(const DeltaArgs& a, const int* pid, int nrows,
                                               int pt, int chunk, uint4* ov) {
   const int t = threadIdx.x;
@@ -301,7 +303,7 @@ __device__ __forceinline__ void load_out_tile(const DeltaArgs& a, const int* pid
     const int n = chunk * kExpandCols + (v % 32) * 8;
     const bool ok = m < nrows && n < a.N;
     const int64_t off = ok ? ((int64_t)pid[m] * a.ld_out + n) * 2 : 0;
-    ov[h] = ld16_if((const char*)a.out, off, ok);
+    ov[h] = ld16_nt_if((const char*)a.out, off, ok);
   }
 }
 
@@ -400,8 +402,8 @@ __device__ __forceinline__ void expand_mfma_blocks(const DeltaArgs& a, int blk0,
             const float hi = fmaf(sc, d[2 * i + 1], bf16_hi(ow[i]));
             res[i] = (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
           }
-          *reinterpret_cast<uint4*>((char*)a.out + ((int64_t)pid[mq] * a.ld_out + n) * 2) =
-              make_uint4(res[0], res[1], res[2], res[3]);
+          st16_nt((char*)a.out + ((int64_t)pid[mq] * a.ld_out + n) * 2,
+                  make_uint4(res[0], res[1], res[2], res[3]));
         }
       }
       __syncthreads();  // the tile is rewritten by the next pair tile
