@@ -50,9 +50,14 @@ __device__ __forceinline__ void load_a_seg(__amdgpu_buffer_rsrc_t ra, uint32_t r
   }
 }
 
+// Pairs whose x segments one LDS stage holds: eight where a segment is at most 2 KiB (rows
+// of up to 1024 bf16, the down projection's), so a block of up to eight pairs fetches its x
+// in one round trip, and four for longer segments, which keeps the stage at 16 KiB where
+// the registers allow six workgroups per CU.
 template <int LPR>
 struct ShrinkLds {
-  static constexpr int kVecs = kPG * kSeg * LPR;
+  static constexpr int kPairs = LPR <= 16 ? 8 : 4;
+  static constexpr int kVecs = kPairs * kSeg * LPR;
 };
 
 // Sixteen zero bytes in device memory: the source of the x slots past a row.
@@ -64,7 +69,7 @@ __device__ const uint4 kZero16 = {0, 0, 0, 0};
 // of the segment holds a finite value and the products need no mask. Pair ids are indexed
 // with compile-time indices only (a runtime index into them would put them in scratch
 // memory).
-template <bool BF16, int LPR>
+template <bool BF16, int LPR, int NQ>
 __device__ __forceinline__ void stage_x(const DeltaArgs& a, const int* p, int nq, int m0,
                                         int nvec, uint4* xs) {
   constexpr int ESZ = BF16 ? 2 : 4;
@@ -76,7 +81,7 @@ __device__ __forceinline__ void stage_x(const DeltaArgs& a, const int* p, int nq
   const char* xbase = (const char*)a.xin;
   const int64_t xstride = a.ld_x * ESZ;
 #pragma unroll
-  for (int q = 0; q < kPG; ++q) {
+  for (int q = 0; q < NQ; ++q) {
     if (q >= nq) break;  // uniform
     const int64_t xrow = (int64_t)fdiv(p[q], a.f_rd) * xstride;
 #pragma unroll
@@ -91,46 +96,51 @@ __device__ __forceinline__ void stage_x(const DeltaArgs& a, const int* p, int nq
   }
 }
 
-// Row `row` of s for the pairs p[0..nq) (nq <= kPG) from the weight vectors av[] that this
+// Row `row` of s for the pairs p[0..nq) (nq <= NQ) from the weight vectors av[] that this
 // lane holds (the lane's whole share of the row: vectors lr, lr+LPR, ... < nvec). Stages the
-// pairs' x rows, multiplies, reduces each row's LPR lanes by the fixed xor tree, and lane 0
-// of the row stores. The caller has issued the weight loads; every thread takes part.
-template <bool BF16, int LPR>
+// pairs' x rows in one round trip, multiplies, reduces each row's LPR lanes by the fixed
+// xor tree, and lane 0 of the row stores. The caller has issued the weight loads; every
+// thread takes part.
+template <bool BF16, int LPR, int NQ>
 __device__ __forceinline__ void shrink_pairs(const DeltaArgs& a, const uint4* av, int row,
                                              bool row_in, const int* p, int nq, int nvec,
                                              uint4* xs) {
   constexpr int SEGV = kSeg * LPR;
   const int lr = threadIdx.x % LPR;
-  stage_x<BF16, LPR>(a, p, nq, 0, nvec, xs);
+  stage_x<BF16, LPR, NQ>(a, p, nq, 0, nvec, xs);
   __builtin_amdgcn_s_waitcnt(0);  // the x DMA (and the weights, the first time) have landed
   __syncthreads();
-  // Branch-free products: every pair slot of the group and every segment vector is
-  // multiplied, each weight vector against the four pairs' x vectors read together, so the
-  // LDS reads go out four at a time instead of one round trip each behind its own branch.
-  // Past the row both the held weights and the staged x are zero; pair slots past nq read
-  // stale LDS and are never stored. (The bf16 products take the packed pairs as they are,
-  // so the held weights are never unpacked.)
-  float acc[kPG];
+  // Branch-free products, kPG pairs at a time: every pair slot of the group and every
+  // segment vector is multiplied, each weight vector against the pairs' x vectors read
+  // together, so the LDS reads go out kPG at a time instead of one round trip each behind
+  // its own branch. Past the row both the held weights and the staged x are zero; pair
+  // slots past nq read stale LDS and are never stored. (The bf16 products take the packed
+  // pairs as they are, so the held weights are never unpacked.)
 #pragma unroll
-  for (int i = 0; i < kPG; ++i) acc[i] = 0.f;
+  for (int q0 = 0; q0 < NQ; q0 += kPG) {
+    if (q0 >= nq) break;  // uniform
+    float acc[kPG];
 #pragma unroll
-  for (int sg = 0; sg < kSeg; ++sg) {
-    uint4 xv[kPG];
+    for (int i = 0; i < kPG; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int i = 0; i < kPG; ++i) xv[i] = xs[i * SEGV + sg * LPR + lr];
+    for (int sg = 0; sg < kSeg; ++sg) {
+      uint4 xv[kPG];
 #pragma unroll
-    for (int i = 0; i < kPG; ++i) acc[i] = dot16<BF16>(av[sg], xv[i], acc[i]);
-  }
+      for (int i = 0; i < kPG; ++i) xv[i] = xs[(q0 + i) * SEGV + sg * LPR + lr];
 #pragma unroll
-  for (int i = 0; i < kPG; ++i) {
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) acc[i] += __shfl_xor(acc[i], off, 64);
-  }
-  if (lr == 0 && row_in) {
+      for (int i = 0; i < kPG; ++i) acc[i] = dot16<BF16>(av[sg], xv[i], acc[i]);
+    }
 #pragma unroll
     for (int i = 0; i < kPG; ++i) {
-      if (i >= nq) break;
-      a.s[(int64_t)p[i] * a.R + row] = acc[i];
+#pragma unroll
+      for (int off = LPR / 2; off > 0; off >>= 1) acc[i] += __shfl_xor(acc[i], off, 64);
+    }
+    if (lr == 0 && row_in) {
+#pragma unroll
+      for (int i = 0; i < kPG; ++i) {
+        if (q0 + i >= nq) break;
+        a.s[(int64_t)p[q0 + i] * a.R + row] = acc[i];
+      }
     }
   }
 }
@@ -160,7 +170,7 @@ __device__ __forceinline__ void shrink_group_long(const DeltaArgs& a, int e, int
     uint4 av[kSeg];
     load_a_seg<LPR>(ra, row_off, row_ok, m0, nvec, av);
     if (m0 > 0) __syncthreads();  // earlier readers of xs are done
-    stage_x<BF16, LPR>(a, p, nq, m0, nvec, xs);
+    stage_x<BF16, LPR, kPG>(a, p, nq, m0, nvec, xs);
     __builtin_amdgcn_s_waitcnt(0);  // the x DMA and the weights have landed
     __syncthreads();
 #pragma unroll
@@ -187,18 +197,19 @@ __device__ __forceinline__ void shrink_group_long(const DeltaArgs& a, int e, int
   }
 }
 
-// Shrink work item (blk, rg): all real pairs of block blk, kPG at a time. When a lane's share
+// Shrink work item (blk, rg): all real pairs of block blk, NQ at a time. When a lane's share
 // of a row fits one register segment (every row up to 8*LPR vectors: K = 2048 at 8 rows per
 // item, K = 768 at 16), its weights are loaded once, together with the first group's x rows,
 // and held for every group of pairs of the block. A block whose real pairs are all among its
-// first kPG entries (nearly every block at decode) takes them from its head as scalars; a
+// first NQ entries (nearly every block at decode) takes them from its head as scalars; a
 // larger one stages its pair ids through pid, 64 per pass (they form a prefix of the block).
 template <bool BF16, int LPR, bool HELD>
 __device__ __forceinline__ void shrink_block(const DeltaArgs& a, const RouteArgs& ra_, int blk,
                                              int rg, int* pid, int& nreal, uint4* xs) {
   constexpr int ESZ = BF16 ? 2 : 4;
   constexpr int RPI = kThreads / LPR;
-  const BlockHead h = block_head(a, ra_, blk);
+  constexpr int NQ = HELD ? ShrinkLds<LPR>::kPairs : kPG;  // pairs per x stage
+  const BlockHeadN<NQ> h = block_head<NQ>(a, ra_, blk);
   if (h.e < 0 || h.nq == 0) return;  // no delta
   const int rl = slot_rank(a, h.e);
   const int nvec = a.K * ESZ / 16;  // HELD: nvec <= kSeg * LPR (chosen by the launcher)
@@ -214,7 +225,7 @@ __device__ __forceinline__ void shrink_block(const DeltaArgs& a, const RouteArgs
     load_a_seg<LPR>(ra, (uint32_t)(row_ok ? row : 0) * (uint32_t)(a.K * ESZ), row_ok, 0, nvec,
                     av);
     if (h.all_here) {  // the common decode case: the whole item is one straight run
-      shrink_pairs<BF16, LPR>(a, av, row, row_in, h.p, h.nq, nvec, xs);
+      shrink_pairs<BF16, LPR, NQ>(a, av, row, row_in, h.p, h.nq, nvec, xs);
       return;
     }
   } else {
@@ -229,14 +240,14 @@ __device__ __forceinline__ void shrink_block(const DeltaArgs& a, const RouteArgs
     publish_pids(a, pv, pid, &nreal);
     __syncthreads();
     const int nr = nreal;
-    for (int q0 = 0; q0 < nr; q0 += kPG) {
-      int pq[kPG];
+    for (int q0 = 0; q0 < nr; q0 += NQ) {
+      int pq[NQ];
 #pragma unroll
-      for (int i = 0; i < kPG; ++i) pq[i] = q0 + i < nr ? pid[q0 + i] : a.numel;
-      const int n = min(kPG, nr - q0);
+      for (int i = 0; i < NQ; ++i) pq[i] = q0 + i < nr ? pid[q0 + i] : a.numel;
+      const int n = min(NQ, nr - q0);
       __syncthreads();  // xs of the previous group is no longer read
       if constexpr (HELD)
-        shrink_pairs<BF16, LPR>(a, av, row, row_in, pq, n, nvec, xs);
+        shrink_pairs<BF16, LPR, NQ>(a, av, row, row_in, pq, n, nvec, xs);
       else
         shrink_group_long<BF16, LPR>(a, h.e, rl, rg, pq, n, xs);
     }

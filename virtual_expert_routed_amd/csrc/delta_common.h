@@ -105,14 +105,16 @@ __device__ __forceinline__ int block_expert(const DeltaArgs& a, int blk) {
 
 // What a work item needs to know of its block before its first weight load: the block's
 // virtual expert (e < 0: the item has nothing to do, because the block is past the live
-// blocks or in the sentinel bucket), its first kPG entries as scalars (numel past the
+// blocks or in the sentinel bucket), its first NH entries as scalars (numel past the
 // block) and how many of them are real pairs (a prefix).
-struct BlockHead {
+template <int NH>
+struct BlockHeadN {
   int e;
-  int p[kPG];
+  int p[NH];
   int nq;
-  bool all_here;  // the block has no real pairs past its first kPG entries
+  bool all_here;  // the block has no real pairs past its first NH entries
 };
+using BlockHead = BlockHeadN<kPG>;
 
 // The routing arguments a delta item needs first. The kernels take them as their leading
 // scalar parameters (MOL_ROUTE_PARAMS), and the library is built with kernel-argument
@@ -158,25 +160,26 @@ __device__ __forceinline__ void fetch_args(const DeltaArgs& a) {
 // Every routing read of the head leaves in one batch: the padded count, the expert id and
 // the entries are read from clamped indices with no branch between the loads, so an item
 // pays one round trip to the routing before it can issue its weight loads.
-__device__ __forceinline__ BlockHead block_head(const DeltaArgs& a, const RouteArgs& r,
-                                                int blk) {
+template <int NH = kPG>
+__device__ __forceinline__ BlockHeadN<NH> block_head(const DeltaArgs& a, const RouteArgs& r,
+                                                     int blk) {
   const int32_t* sp = r.sorted + (int64_t)blk * r.BM;
   const int last = r.BM - 1;
-  int v[kPG];
+  int v[NH];
 #pragma unroll
-  for (int i = 0; i < kPG; ++i) v[i] = sp[i < last ? i : last];
+  for (int i = 0; i < NH; ++i) v[i] = sp[i < last ? i : last];
   const int er = r.expert_ids[blk];
   const int npp = *r.npp;
   // after the routing reads, so that they stay scalar loads, and in their round trip
   fetch_args(a);
-  BlockHead h;
+  BlockHeadN<NH> h;
   h.nq = 0;
 #pragma unroll
-  for (int i = 0; i < kPG; ++i) {
+  for (int i = 0; i < NH; ++i) {
     h.p[i] = i <= last ? v[i] : a.numel;
     h.nq += real_pair(h.p[i], a.numel) ? 1 : 0;
   }
-  h.all_here = h.nq < kPG || r.BM <= kPG;
+  h.all_here = h.nq < NH || r.BM <= NH;
   const int nb = npp < 0 ? 0 : fdiv(npp, a.f_bm);
   const int live = nb > a.max_blocks ? a.max_blocks : nb;
   h.e = (blk < live && real_expert(er, a.V)) ? er : -1;
