@@ -229,6 +229,58 @@ def base_gemm_leg(cfg, layers, host_inputs, torch, n_layers=2, rounds=8):
     return res
 
 
+def prefill_base_leg(cfg, host_inputs, delta_graph_us, torch, rounds=5):
+    """Context at prefill, beside the headline and not part of it: the base grouped GEMM of
+    each stage, one hipBLASLt GEMM (torch.mm) per base expert over that expert's rows already
+    gathered (the gather is not timed), on random weights of the stage's shape. This library
+    does not build a prefill base GEMM; the leg shows what share of a layer the delta is."""
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    g.manual_seed(20240601)
+    t = host_inputs[0].topk_ids.reshape(-1)
+    loc = (t >= 0) & (t < cfg.E)
+    counts = np.bincount(t[loc], minlength=cfg.E)
+    starts = np.concatenate([[0], np.cumsum(counts)])
+    P = int(counts.sum())
+    res = {"what": "base grouped GEMM for context: one torch.mm (hipBLASLt) per base expert "
+                   "over its gathered rows, bf16, random weights; not this library's code and "
+                   "not part of us_per_layer", "local_pairs": P}
+    total = 0.0
+    for si, st in enumerate(cfg.stages):
+        W = torch.randn(cfg.E, st.N, st.K, device=dev, dtype=torch.bfloat16, generator=g)
+        X = torch.randn(P, st.K, device=dev, dtype=torch.bfloat16, generator=g)
+        Y = torch.empty(P, st.N, device=dev, dtype=torch.bfloat16)
+        # each expert's weight as its own contiguous [K, N] operand (no transposed view)
+        Wt = [W[e].t().contiguous() if counts[e] else None for e in range(cfg.E)]
+        del W
+
+        def run():
+            for e in range(cfg.E):
+                if counts[e]:
+                    torch.mm(X[starts[e]:starts[e + 1]], Wt[e], out=Y[starts[e]:starts[e + 1]])
+        run()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(rounds):
+            run()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / rounds
+        flop = 2.0 * P * st.N * st.K
+        res[st.name] = {"us": us, "TFLOP/s": flop / (us * 1e-6) / 1e12,
+                        "frac_of_bf16_dense_peak": flop / (us * 1e-6) / 1e12 / 2500.0}
+        total += us
+        del X, Y, Wt
+        torch.cuda.empty_cache()
+    res["base_us"] = total
+    if delta_graph_us:
+        res["delta_us"] = delta_graph_us
+        res["base_plus_delta_us"] = total + delta_graph_us
+        res["delta_share"] = delta_graph_us / (total + delta_graph_us)
+    return res
+
+
 def kernel_name(cfg, st, kind):
     """The kernel instantiations libmol launches for this stage, as a profiler names them.
     Shrink: rows per work item start at 4 and double while two such items' A rows fit
@@ -668,8 +720,28 @@ def main():
             "us_per_launch": dom["us"],
         },
     }
-    result["base_gemm"] = base_gemm_leg(cfg, layers, host_inputs, torch) if cfg.M <= 1024 \
-        else None
+    if cfg.name == configs.N2.name:
+        # the pages' own numbers for these stages on this shape (MindLab sglang PR 24: the
+        # root-cause passage and the PR body's background): B300, one real model's routing,
+        # before their grid fix, which they estimate takes the down expand to ~40 us
+        by_label = {k["label"]: k["us"] for k in kernels}
+        pages = {"expand down": 160.6, "expand gate_up": 7.5 + 6.8}
+        result["pages_comparison"] = {
+            "what": ("this library's launch per stage on the pages' decode shape against the "
+                     "pages' B300 time for the same stage before their fix (their gate and up "
+                     "expands are two launches, 7.5 + 6.8 us; here one two-slice launch); other "
+                     "hardware and routing: context, not a target"),
+            "pages_down_expand_estimate_after_fix_us": 40.0,
+            **{lab: {"pages_us": p, "us": by_label[lab], "pages_over_ours": p / by_label[lab]}
+               for lab, p in pages.items()},
+        }
+    if cfg.M <= 1024:
+        result["base_gemm"] = base_gemm_leg(cfg, layers, host_inputs, torch)
+    elif cfg.dtype == "bf16":
+        log("[bench] base grouped GEMM for context (hipBLASLt per base expert)")
+        result["base_gemm"] = prefill_base_leg(cfg, host_inputs, delta_graph_us, torch)
+    else:
+        result["base_gemm"] = None
     down = cfg.stages[-1]
     n_local = [int(((h.topk_ids >= 0) & (h.topk_ids < cfg.E)).sum()) for h in host_inputs]
     cb = float(np.mean([combine_bytes(cfg, down, n) for n in n_local]))

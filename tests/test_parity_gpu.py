@@ -105,7 +105,7 @@ def get_case(cfg):
     return _cache[cfg.name]
 
 
-ALL = [configs.C0, configs.C1, configs.C2, configs.C3, configs.C4]
+ALL = [configs.C0, configs.C1, configs.C2, configs.C3, configs.C4, configs.N2]
 IDS = [c.name for c in ALL]
 
 

@@ -38,3 +38,17 @@ def test_reference_grid_m_vs_real_block_bound():
         assert ours <= ref
     assert bench.reference_grid_m(configs.C1) == 1012
     assert mb.mol_align_max_blocks(configs.C1.numel, configs.C1.V, configs.C1.block_m) == 184
+
+
+def test_n2_config_has_the_pages_decode_shape():
+    # MindLab PR 24 page: down expand N = 6144 and gate/up expands N = 256 at r = 32 and
+    # BLOCK_M = 64, ~1.1 k routed pairs, and a worst-case buffer of 1604 blocks
+    c = configs.N2
+    gate_up, down = c.stages
+    assert (down.N, down.r, c.block_m) == (6144, 32, 64)
+    assert gate_up.N // gate_up.slices == 256 and gate_up.r == 32
+    assert 1000 <= c.numel - c.sentinel_count <= 1200
+    grid_m = bench.reference_grid_m(c)
+    assert abs(grid_m - 1604) <= 0.01 * 1604
+    assert abs(bench.reference_ctas(grid_m, 6144) - 153984) <= 0.01 * 153984
+    assert abs(bench.reference_ctas(grid_m, 256) - 6416) <= 0.01 * 6416

@@ -1,4 +1,5 @@
-"""Shapes of the five synthetic MoL (multi-LoRA MoE) layers the path is exercised on.
+"""Shapes of the synthetic MoL (multi-LoRA MoE) layers the path is exercised on: the five
+workloads C0-C4 and N2, the pages' own decode shape.
 
 A layer routes M tokens to `topk` of E base experts and gives every token one LoRA
 slot out of S, so a (token, slot) pair lands on virtual expert  v = e + slot * E,
@@ -105,7 +106,20 @@ C4 = LayerConfig(
     sentinel_count=_round_half_up(0.02, 16384 * 8), nolora_count=0, lora_dist="uniform",
     note="large prefill, rank 64, Zipf(1.1) experts")
 
-CONFIGS = (C0, C1, C2, C3, C4)
+# The decode shape the MindLab sglang PR 24 page measures (its root-cause passage and the PR
+# body's background section): a speculative-verify step of 23 requests with about 1.1 k routed
+# (token, virtual expert) pairs, BLOCK_M = 64, rank 32; the LoRA gate and up expands have
+# N = 256 each (one two-slice stage here, N = 512) and the down expand N = 6144, so the
+# hidden size is 6144 and the per-GPU intermediate 256. The pages give neither the token
+# count nor E and S: 138 tokens (23 x 6) at top-8 give 1104 pair slots, and E = 160, S = 10
+# put the worst-case routing buffer at 1594 blocks of 64 against the page's 1604.
+N2 = LayerConfig(
+    name="n2_verify_h6144", dtype="bf16", M=138, hidden=6144, E=160, topk=8, S=10, rank=32,
+    block_m=64, stages=_two_stage(6144, 256, 32), expert_dist="uniform",
+    sentinel_count=_round_half_up(0.02, 138 * 8), nolora_count=0, lora_dist="uniform",
+    note="the pages' decode shape: ~1.1 k pairs, down expand N = 6144, r = 32")
+
+CONFIGS = (C0, C1, C2, C3, C4, N2)
 BY_NAME = {c.name: c for c in CONFIGS}
 
 
