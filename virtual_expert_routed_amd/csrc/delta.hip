@@ -13,7 +13,7 @@
 //    read once with coalesced 16-byte buffer loads (LPR = 256/RPI lanes per row, each
 //    row's lanes reading consecutive vectors), held in registers and reused for up to
 //    four pairs at a time. The pairs' x segments go straight into LDS (direct-to-LDS
-//    loads) once per item. The LPR partial sums are combined by a fixed xor tree, so s
+//    loads) once per item. The LPR partial sums are combined by a fixed butterfly, so s
 //    is bit-reproducible and needs no split-K partials.
 //  * expand item = (block, 256 output columns): one thread per column holds the
 //    column's r weights in registers; the block's s rows are staged in LDS; out is read,
@@ -37,7 +37,7 @@ namespace {
 // ------------------------------------------------------------------------------ shrink
 // Lane lr of a row's LPR-lane group owns the 16-byte vectors lr, lr+LPR, lr+2*LPR, ...
 // of the row, sums their products in ascending order, and the lanes are combined by a
-// fixed xor tree: the result depends only on (K, LPR).
+// fixed butterfly (group_sum): the result depends only on (K, LPR).
 
 template <int LPR>
 __device__ __forceinline__ void load_a_seg(__amdgpu_buffer_rsrc_t ra, uint32_t row_off, bool row_ok,
@@ -99,7 +99,7 @@ __device__ __forceinline__ void stage_x(const DeltaArgs& a, const int* p, int nq
 // Row `row` of s for the pairs p[0..nq) (nq <= NQ) from the weight vectors av[] that this
 // lane holds (the lane's whole share of the row: vectors lr, lr+LPR, ... < nvec). Stages the
 // pairs' x rows in one round trip, multiplies, reduces each row's LPR lanes by the fixed
-// xor tree, and lane 0 of the row stores. The caller has issued the weight loads; every
+// butterfly, and lane 0 of the row stores. The caller has issued the weight loads; every
 // thread takes part.
 template <bool BF16, int LPR, int NQ>
 __device__ __forceinline__ void shrink_pairs(const DeltaArgs& a, const uint4* av, int row,
@@ -131,10 +131,7 @@ __device__ __forceinline__ void shrink_pairs(const DeltaArgs& a, const uint4* av
       for (int i = 0; i < kPG; ++i) acc[i] = dot16<BF16>(av[sg], xv[i], acc[i]);
     }
 #pragma unroll
-    for (int i = 0; i < kPG; ++i) {
-#pragma unroll
-      for (int off = LPR / 2; off > 0; off >>= 1) acc[i] += __shfl_xor(acc[i], off, 64);
-    }
+    for (int i = 0; i < kPG; ++i) acc[i] = group_sum<LPR>(acc[i]);
     if (lr == 0 && row_in) {
 #pragma unroll
       for (int i = 0; i < kPG; ++i) {
@@ -184,10 +181,7 @@ __device__ __forceinline__ void shrink_group_long(const DeltaArgs& a, int e, int
     }
   }
 #pragma unroll
-  for (int i = 0; i < kPG; ++i) {
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) acc[i] += __shfl_xor(acc[i], off, 64);
-  }
+  for (int i = 0; i < kPG; ++i) acc[i] = group_sum<LPR>(acc[i]);
   if (lr == 0 && row_in) {
 #pragma unroll
     for (int i = 0; i < kPG; ++i) {

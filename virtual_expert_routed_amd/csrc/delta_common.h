@@ -212,6 +212,28 @@ __device__ __forceinline__ uint4 keep_first(uint4 v, int keep) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// The sum over each group of LPR consecutive lanes (LPR a power of two up to 64), left in
+// every lane of the group, by a butterfly in ascending distance: cross-lane moves inside a
+// row of 16 for distances 1 to 8, a swizzle for 16, a permute for 32. From distance 4 on,
+// every lane of a quad (of an 8-lane half row) already holds the same value, so the row
+// mirrors pair the same values as an xor would; each lane then adds the same two values in
+// the same order, and the result depends only on LPR.
+template <int CTRL>
+__device__ __forceinline__ float from_lane(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (LPR >= 2) v += from_lane<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  if constexpr (LPR >= 4) v += from_lane<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  if constexpr (LPR >= 8) v += from_lane<0x141>(v);  // row_half_mirror
+  if constexpr (LPR >= 16) v += from_lane<0x140>(v); // row_mirror
+  if constexpr (LPR >= 32)                            // lanes i and i ^ 16
+    v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+  if constexpr (LPR >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
 // Branch-free 16-byte load: a masked address is clamped to the array's first element
 // and its value replaced by zero.
 __device__ __forceinline__ uint4 ld16_if(const char* base, int64_t off, bool ok) {

@@ -16,7 +16,7 @@
 // far larger weights (W_t is N x K), so it is built the same way: a work item is (block,
 // RPI consecutive output columns), each column's row of W_t read once with coalesced
 // 16-byte buffer loads by LPR lanes and reused for up to four pairs, the pairs' input
-// rows staged in LDS, the lanes' partial sums combined by a fixed xor tree. The fused
+// rows staged in LDS, the lanes' partial sums combined by a fixed butterfly. The fused
 // delta costs, per pair, the B row slices of the item's columns and the s row, moved into
 // LDS by direct-to-LDS loads in the last weight segment's round trip, and each lane adds its
 // part of the rank sum to its partial before the tree: the delta needs no extra pass over
@@ -65,7 +65,7 @@ __device__ __forceinline__ void gemm_group(const GemmArgs& g, int e, int rg, con
   // s row), so the delta adds neither a dependent round trip nor registers to the weight
   // loop. After the products, lane lr takes 16-byte vectors lr, lr + LPR, ... of its
   // column's B row slice and the matching s values, and adds its share of the rank sum to
-  // its partial before the xor tree.
+  // its partial before the butterfly.
   int rlq[kPG], vq[kPG];
   float scq[kPG];
   if constexpr (FUSED) {
@@ -160,10 +160,7 @@ __device__ __forceinline__ void gemm_group(const GemmArgs& g, int e, int rg, con
     }
   }
 #pragma unroll
-  for (int i = 0; i < kPG; ++i) {
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) acc[i] += __shfl_xor(acc[i], off, 64);
-  }
+  for (int i = 0; i < kPG; ++i) acc[i] = group_sum<LPR>(acc[i]);
   if (lr == 0 && n_ok) {
 #pragma unroll
     for (int i = 0; i < kPG; ++i) {
