@@ -318,13 +318,24 @@ def reference_grid_m(cfg):
     return -(-(cfg.numel + (cfg.V + 1) * (cfg.block_m - 1)) // cfg.block_m)
 
 
-def delta_source_sha256():
-    """Hash of the delta kernels' sources (VALU and MFMA kernels and their device helpers)."""
+def code_sha256(sources):
+    """SHA-256 of C/HIP source texts with the comments and the layout of whitespace left out:
+    a change of wording keeps the hash, any change of the code itself does not."""
     import hashlib
+    import re
     h = hashlib.sha256()
-    for f in ("delta.hip", "delta_mfma.hip", "delta_common.h"):
-        h.update(open(os.path.join(ROOT, "virtual_expert_routed_amd", "csrc", f), "rb").read())
+    for src in sources:
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)  # block comments
+        src = re.sub(r"//[^\n]*", " ", src)                # line comments
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()
+
+
+def delta_source_sha256():
+    """Hash of the delta kernels' code (VALU and MFMA kernels and their device helpers), as
+    recorded in the counter summaries."""
+    return code_sha256(open(os.path.join(ROOT, "virtual_expert_routed_amd", "csrc", f)).read()
+                       for f in ("delta.hip", "delta_mfma.hip", "delta_common.h"))
 
 
 def measured_traffic(workload, kernel):

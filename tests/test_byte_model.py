@@ -56,3 +56,26 @@ def test_terms_scale_with_pairs_tokens_and_experts():
     est = stats(P=159, D=146, T=23, blocks=147)
     total = sum(bench.stage_bytes(cfg, st, est) for st in cfg.stages)
     assert 81.0e6 < total < 82.0e6
+
+
+def test_code_hash_ignores_comments_and_layout_only():
+    # the counter summaries stay valid across a rewording, and only then
+    base = "int f(int a) {\n  return a + 1;  // one more\n}\n/* note */\n"
+    reworded = "int f(int a) {   // the successor\n  return a + 1;\n}\n/* other\n note */"
+    changed = "int f(int a) {\n  return a + 2;  // one more\n}\n/* note */\n"
+    assert bench.code_sha256([base]) == bench.code_sha256([reworded])
+    assert bench.code_sha256([base]) != bench.code_sha256([changed])
+    assert bench.code_sha256([base, base]) != bench.code_sha256([base])
+
+
+def test_counter_summaries_name_their_kernel_and_code():
+    # every committed counter summary carries the lines bench reads back
+    import glob
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    files = glob.glob(os.path.join(root, "profiles", "pmc_traffic_*.md"))
+    assert files
+    for f in files:
+        text = open(f).read()
+        for key in ("kernel: ", "kernel_source_sha256: ", "traffic_bytes_per_launch: "):
+            assert key in text, (f, key)

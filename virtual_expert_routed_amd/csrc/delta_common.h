@@ -213,11 +213,12 @@ __device__ __forceinline__ uint4 keep_first(uint4 v, int keep) {
 }
 
 // The sum over each group of LPR consecutive lanes (LPR a power of two up to 64), left in
-// every lane of the group, by a butterfly in ascending distance: cross-lane moves inside a
-// row of 16 for distances 1 to 8, a swizzle for 16, a permute for 32. From distance 4 on,
-// every lane of a quad (of an 8-lane half row) already holds the same value, so the row
-// mirrors pair the same values as an xor would; each lane then adds the same two values in
-// the same order, and the result depends only on LPR.
+// every lane of the group, by a butterfly in ascending distance d: cross-lane moves inside a
+// row of 16 lanes for d = 1 to 8, a swizzle for 16, a permute for 32. Before the step of
+// distance d >= 4 every aligned run of d lanes holds one value, and a half-row (d = 4) or row
+// (d = 8) mirror maps each run onto its neighbour, so it adds the same two values an xor
+// would; the two lanes of a pair add them in either order, which gives the same sum. The
+// result depends only on LPR.
 template <int CTRL>
 __device__ __forceinline__ float from_lane(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
