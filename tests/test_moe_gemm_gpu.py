@@ -34,6 +34,7 @@ CASES = [
     configs.C0,
     configs.C1,
     configs.C2,
+    configs.N2,  # the pages' decode shape: K = 6144 on the gate_up stage, N = 6144 on the down
     _edge(name="ragged"),
     _edge(name="ranked", slot_ranks=(16, 5, 0)),
     _edge(name="many_per_expert", M=200, E=4, topk=2, S=2, block_m=64),
