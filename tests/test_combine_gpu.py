@@ -37,6 +37,7 @@ CASES = [
     configs.C0,
     configs.C1,
     configs.C2,
+    configs.N2,  # the pages' decode shape: the down rows are 6144 wide
     _edge(name="topk1", topk=1, sentinel_count=5),
     _edge(name="ranked", slot_ranks=(16, 5, 0)),
     _edge(name="all_nolora", M=20, nolora_count=20),
@@ -129,7 +130,8 @@ def test_fused_and_chained_from_zero_base(cfg):
     _check_tol(chained, ref, f"{cfg.name} expand then combine")
 
 
-@pytest.mark.parametrize("cfg", [configs.C1, CASES[4], CASES[-1]], ids=["c1", "ranked", "f32"])
+@pytest.mark.parametrize("cfg", [configs.C1, CASES[IDS.index("ranked")], CASES[-1]],
+                         ids=["c1", "ranked", "f32"])
 def test_fused_and_chained_from_nonzero_base(cfg):
     print(f"[expand_combine base] {cfg.name}", flush=True)
     si = len(cfg.stages) - 1
