@@ -96,6 +96,33 @@ __device__ __forceinline__ void stage_x(const DeltaArgs& a, const int* p, int nq
   }
 }
 
+// The products of NP pairs (their x staged at xs[i*SEGV]) with the held weight vectors,
+// each weight vector against the pairs' x vectors read together, the rows' lanes reduced by
+// the butterfly, and lane 0 of each row storing.
+template <bool BF16, int LPR, int NP>
+__device__ __forceinline__ void shrink_products(const DeltaArgs& a, const uint4* av, int row,
+                                                bool row_in, const int* p, const uint4* xs) {
+  constexpr int SEGV = kSeg * LPR;
+  const int lr = threadIdx.x % LPR;
+  float acc[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int sg = 0; sg < kSeg; ++sg) {
+    uint4 xv[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) xv[i] = xs[i * SEGV + sg * LPR + lr];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) acc[i] = dot16<BF16>(av[sg], xv[i], acc[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < NP; ++i) acc[i] = group_sum<LPR>(acc[i]);
+  if (lr == 0 && row_in) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) a.s[(int64_t)p[i] * a.R + row] = acc[i];
+  }
+}
+
 // Row `row` of s for the pairs p[0..nq) (nq <= NQ) from the weight vectors av[] that this
 // lane holds (the lane's whole share of the row: vectors lr, lr+LPR, ... < nvec). Stages the
 // pairs' x rows in one round trip, multiplies, reduces each row's LPR lanes by the fixed
@@ -106,39 +133,28 @@ __device__ __forceinline__ void shrink_pairs(const DeltaArgs& a, const uint4* av
                                              bool row_in, const int* p, int nq, int nvec,
                                              uint4* xs) {
   constexpr int SEGV = kSeg * LPR;
-  const int lr = threadIdx.x % LPR;
   stage_x<BF16, LPR, NQ>(a, p, nq, 0, nvec, xs);
   __builtin_amdgcn_s_waitcnt(0);  // the x DMA (and the weights, the first time) have landed
   __syncthreads();
-  // Branch-free products, kPG pairs at a time: every pair slot of the group and every
-  // segment vector is multiplied, each weight vector against the pairs' x vectors read
-  // together, so the LDS reads go out kPG at a time instead of one round trip each behind
-  // its own branch. Past the row both the held weights and the staged x are zero; pair
-  // slots past nq read stale LDS and are never stored. (The bf16 products take the packed
-  // pairs as they are, so the held weights are never unpacked.)
+  // The products, kPG pairs at a time, with the group's pair count chosen by one uniform
+  // switch: inside, every segment vector of every pair is multiplied with no branch, each
+  // weight vector against the pairs' x vectors read together, so the LDS reads go out
+  // together instead of one round trip each behind its own branch. Past the row both the
+  // held weights and the staged x are zero. (The bf16 products take the packed pairs as they
+  // are, so the held weights are never unpacked.) A block of one pair, the common case at
+  // decode, then computes one pair's products and reduction, not four.
 #pragma unroll
   for (int q0 = 0; q0 < NQ; q0 += kPG) {
     if (q0 >= nq) break;  // uniform
-    float acc[kPG];
-#pragma unroll
-    for (int i = 0; i < kPG; ++i) acc[i] = 0.f;
-#pragma unroll
-    for (int sg = 0; sg < kSeg; ++sg) {
-      uint4 xv[kPG];
-#pragma unroll
-      for (int i = 0; i < kPG; ++i) xv[i] = xs[(q0 + i) * SEGV + sg * LPR + lr];
-#pragma unroll
-      for (int i = 0; i < kPG; ++i) acc[i] = dot16<BF16>(av[sg], xv[i], acc[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < kPG; ++i) acc[i] = group_sum<LPR>(acc[i]);
-    if (lr == 0 && row_in) {
-#pragma unroll
-      for (int i = 0; i < kPG; ++i) {
-        if (q0 + i >= nq) break;
-        a.s[(int64_t)p[q0 + i] * a.R + row] = acc[i];
-      }
-    }
+    const int m = nq - q0;  // uniform: pairs in this group (the last may hold fewer)
+    if (m == 1)
+      shrink_products<BF16, LPR, 1>(a, av, row, row_in, p + q0, xs + q0 * SEGV);
+    else if (m == 2)
+      shrink_products<BF16, LPR, 2>(a, av, row, row_in, p + q0, xs + q0 * SEGV);
+    else if (m == 3)
+      shrink_products<BF16, LPR, 3>(a, av, row, row_in, p + q0, xs + q0 * SEGV);
+    else
+      shrink_products<BF16, LPR, kPG>(a, av, row, row_in, p + q0, xs + q0 * SEGV);
   }
 }
 
