@@ -230,14 +230,15 @@ MOL_API mol_status mol_align_block_size(const int32_t* ids, const int32_t* lora_
     // (uint16 each)
     const int64_t fixed = ((int64_t)nb + 64) * (int64_t)sizeof(int) +
                           ((numel + 1) & ~1LL) * 2 * 2;
-    int64_t waves = (device_lds_bytes() - fixed) / ((int64_t)nb * (int64_t)sizeof(int));
+    const int64_t row = (int64_t)mol::align_small_stride(nb) * (int64_t)sizeof(int);
+    int64_t waves = (device_lds_bytes() - fixed) / row;
     // walkers: one chunk of 64 pairs each for the smallest batches, two chunks each above
     // (more walkers shorten the walk but add counter rows to every bucket's sums)
     const int64_t useful = numel <= 256 ? cdiv64(numel, 64) : cdiv64(numel, 128);
     if (waves > useful) waves = useful;
     if (waves > 16) waves = 16;
     if (waves < 1) waves = 1;
-    const size_t lds = (size_t)waves * nb * sizeof(int) + (size_t)fixed;
+    const size_t lds = (size_t)(waves * row + fixed);
     if ((int64_t)lds > device_lds_bytes()) return MOL_E_LIMIT;
     // workgroups that split the output writes (each one rebuilds the routing in LDS)
     const int groups = (int)std::max<int64_t>(1, std::min<int64_t>(16, cdiv64(numel, 16)));

@@ -130,21 +130,55 @@ __device__ __forceinline__ uint64_t match_key13(int key, bool valid) {
   return peers;
 }
 
+// N consecutive ints of LDS at an N-int-aligned address (N a power of two), moved as one
+// access of up to 16 bytes at a time.
+template <int N>
+struct LdsInts {
+  int v[N];
+  __device__ __forceinline__ void load(const int* p) {
+    if constexpr (N == 1) {
+      v[0] = p[0];
+    } else if constexpr (N == 2) {
+      const int2 t = *reinterpret_cast<const int2*>(p);
+      v[0] = t.x; v[1] = t.y;
+    } else {
+#pragma unroll
+      for (int j = 0; j < N; j += 4) {
+        const int4 t = *reinterpret_cast<const int4*>(p + j);
+        v[j] = t.x; v[j + 1] = t.y; v[j + 2] = t.z; v[j + 3] = t.w;
+      }
+    }
+  }
+  __device__ __forceinline__ void store(int* p) const {
+    if constexpr (N == 1) {
+      p[0] = v[0];
+    } else if constexpr (N == 2) {
+      *reinterpret_cast<int2*>(p) = make_int2(v[0], v[1]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < N; j += 4)
+        *reinterpret_cast<int4*>(p + j) = make_int4(v[j], v[j + 1], v[j + 2], v[j + 3]);
+    }
+  }
+};
+
 // numel <= 4096: G workgroups of 1024 threads. Every workgroup builds the whole routing in
 // its own LDS (the ids are a few KiB, so the repeated reads hit L2), then writes only
 // its share of the outputs: the pairs p with p % G == g, and the expert ids and padding
 // of the buckets b with b % G == g. No workgroup waits for another.
-// LDS: `waves` counter rows of V+1 ints, the V+1 bucket starts, 64 ints of scan scratch,
-// then per pair its bucket id and its rank among the earlier pairs of the same bucket in
-// its wave's range (uint16 each).
+// LDS: `waves` counter rows of V+1 ints (each padded to a multiple of BPT), the V+1 bucket
+// starts, 64 ints of scan scratch, then per pair its bucket id and its rank among the earlier
+// pairs of the same bucket in its wave's range (uint16 each).
 //   A  every thread: bucket ids of its pairs (ids and slots loaded together) -> LDS;
 //      counter rows zeroed.
 //   B  wave w walks its contiguous range in chunks of 64, in order: ballot-matched peers
 //      give each pair's rank in the chunk, the group leader adds the group to row w and
 //      hands the row's previous value to its peers, so rank_in_range = old + rank.
-//   C  thread t owns BPT consecutive buckets. One pass over the rows, four at a time, with
-//      every owned bucket's reads of a round issued together: row w of bucket b becomes
-//      the pairs of b in ranges before w, and b's total stays in a register. After the
+//   C  thread t owns BPT consecutive buckets, one aligned BPT-int access per row (the
+//      threads of a wave read and write consecutive 4*BPT-byte pieces, so no LDS bank is
+//      hit twice). One pass over the rows, four at a time, every read of a round issued
+//      together: row w of bucket b becomes the pairs of b in ranges before w, and b's total
+//      stays in a register. After the
 //      padded exclusive scan, start[b] = off_b and the expert ids are written; nothing
 //      is read back from LDS.
 //   D  sorted[start[b(p)] + row[w(p)][b(p)] + rank_in_range(p)] = p for this workgroup's
@@ -159,10 +193,11 @@ __global__ void __launch_bounds__(1024)
     align_small_kernel(const int32_t* ids, const int32_t* lora, int32_t numel_, uint32_t tk_m,
                        uint32_t tk_l, int32_t keys_off, int32_t E, int32_t S, AlignArgs a,
                        int waves) {
-  extern __shared__ int lds[];
+  extern __shared__ __attribute__((aligned(16))) int lds[];
   const int NB = a.V + 1;
-  int* table = lds;                                   // [waves][NB]
-  int* start = lds + waves * NB;                      // [NB] padded bucket starts
+  const int NBP = align_small_stride(NB);             // = NB rounded up to a multiple of BPT
+  int* table = lds;                                   // [waves][NBP]
+  int* start = lds + waves * NBP;                     // [NB] padded bucket starts
   int* sh = start + NB;                               // scan scratch (64 ints)
   uint16_t* keys = reinterpret_cast<uint16_t*>(lds + keys_off);  // = sh + 64
   uint16_t* rel = keys + ((numel_ + 1) & ~1);
@@ -194,13 +229,15 @@ __global__ void __launch_bounds__(1024)
       }
     }
   }
-  for (int i = tid; i < waves * NB; i += blockDim.x) table[i] = 0;
+  // the rows as 16-byte stores (the last one may run up to 3 ints into start, set later)
+  for (int i = tid; i < (waves * NBP + 3) / 4; i += blockDim.x)
+    reinterpret_cast<int4*>(table)[i] = make_int4(0, 0, 0, 0);
   __syncthreads();
 
   // B
   const int per = a.per;  // a multiple of 64, per * waves >= numel
   if (wid < waves) {
-    int* row = table + wid * NB;
+    int* row = table + wid * NBP;
     const int begin = min(numel, wid * per);
     const int end = min(numel, begin + per);
     for (int c = begin; c < end; c += 64) {
@@ -227,21 +264,23 @@ __global__ void __launch_bounds__(1024)
   int run[BPT];
 #pragma unroll
   for (int k = 0; k < BPT; ++k) run[k] = 0;
-  for (int w0 = 0; w0 < waves; w0 += 4) {
-    int x[BPT][4];
+  if (nown > 0) {
+    // b0 is a multiple of BPT below NB, so b0 + BPT <= NBP: the access stays in the row; the
+    // row's padding entries are never incremented, so they read 0 and add nothing
+    for (int w0 = 0; w0 < waves; w0 += 4) {
+      LdsInts<BPT> x[4];
 #pragma unroll
-    for (int k = 0; k < BPT; ++k) {
-      const int b = min(b0 + k, NB - 1);  // a valid address for buckets not owned
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[k][i] = table[min(w0 + i, waves - 1) * NB + b];
-    }
-#pragma unroll
-    for (int k = 0; k < BPT; ++k) {
+      for (int i = 0; i < 4; ++i) x[i].load(table + min(w0 + i, waves - 1) * NBP + b0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (k < nown && w0 + i < waves) {
-          table[(w0 + i) * NB + b0 + k] = run[k];
-          run[k] += x[k][i];
+        if (w0 + i < waves) {
+          LdsInts<BPT> y;
+#pragma unroll
+          for (int k = 0; k < BPT; ++k) {
+            y.v[k] = run[k];
+            run[k] += x[i].v[k];
+          }
+          y.store(table + (w0 + i) * NBP + b0);
         }
       }
     }
@@ -306,7 +345,7 @@ __global__ void __launch_bounds__(1024)
   for (int p = g + tid * G; p < numel; p += (int)blockDim.x * G) {
     const int w = fdiv(p, a.f_per);
     const int key = keys[p];
-    const int r = table[w * NB + key] + rel[p];  // the pair's rank within its bucket
+    const int r = table[w * NBP + key] + rel[p];  // the pair's rank within its bucket
     a.sorted[start[key] + r] = p;
   }
   // padding: the wave's lanes fill one padded bucket after another
@@ -523,11 +562,11 @@ hipError_t launch_virtual_topk(const int32_t* topk_ids, const int32_t* lora_ids,
 
 hipError_t launch_align_small(const AlignArgs& a, int waves, int groups, size_t lds_bytes,
                               hipStream_t stream) {
-  // buckets per thread, rounded up to a power of two (V + 1 <= 8192 = 8 x 1024)
-  const int bpt = (a.V + 1 + 1023) / 1024;
+  // buckets per thread, a power of two (V + 1 <= 8192 = 8 x 1024)
+  const int bpt = align_small_bpt(a.V + 1);
   const dim3 grid(groups), block(1024);
   // ints before the key array: counter rows, bucket starts, scan scratch
-  const int keys_off = (waves + 1) * (a.V + 1) + 64;
+  const int keys_off = waves * align_small_stride(a.V + 1) + (a.V + 1) + 64;
 #define MOL_ALIGN_SMALL(BPT)                                                                \
   hipLaunchKernelGGL(align_small_kernel<BPT>, grid, block, lds_bytes, stream, a.ids, a.lora, \
                      a.numel, a.f_topk.m, a.f_topk.l, keys_off, a.lora ? a.E : a.V,       \

@@ -10,6 +10,16 @@ namespace mol {
 
 constexpr int kMaxBuckets = 8192;     // V + 1 <= 8192
 constexpr int kAlignSmallMax = 4096;  // pairs the one-workgroup align handles
+
+// The small align's buckets per thread (V + 1 buckets over 1024 threads, rounded up to a power
+// of two) and the stride of its counter rows in ints: V + 1 rounded up to a multiple of that,
+// so that one thread's buckets of one row are a single aligned LDS access.
+__host__ __device__ constexpr int align_small_bpt(int nb) {
+  return nb <= 1024 ? 1 : nb <= 2048 ? 2 : nb <= 4096 ? 4 : 8;
+}
+__host__ __device__ constexpr int align_small_stride(int nb) {
+  return (nb + align_small_bpt(nb) - 1) / align_small_bpt(nb) * align_small_bpt(nb);
+}
 constexpr int kShrinkItemBytes = 32768;  // target weight bytes per shrink work item
 constexpr int kMfmaMinNumel = 4096;      // MFMA kernels are launched from this many pairs
 constexpr int kMaxRankVecs = 16;         // 16-byte vectors in one rank row slice (256 bytes)
