@@ -334,11 +334,15 @@ def test_edge_cases(cfg):
 
 # Batch sizes at the align kernels' selection bounds (one wave per workgroup up to 256
 # pairs; 16-wave workgroups up to 4096; three kernels above), each with small and large
-# virtual expert counts, out-of-range ids and no-adapter tokens.
+# virtual expert counts, out-of-range ids and no-adapter tokens. The bucket counts V + 1
+# (8, 1025, 3001, 4097, 8191) cover each number of buckets a thread owns in the small align
+# (1, 2, 4, 8, 8), whose counter rows are padded to a multiple of it (1025 -> 1026,
+# 3001 -> 3004, 4097 -> 4104, 8191 -> 8192; 8 needs none).
 ALIGN_BOUNDS = [(M, k, E, S, bm) for (M, k) in ((1, 1), (63, 1), (16, 4), (65, 1), (32, 4),
                                                 (255, 1), (32, 8), (257, 1), (1024, 4),
                                                 (4097, 1))
-                for (E, S, bm) in ((7, 1, 16), (128, 8, 64), (4095, 2, 48))]
+                for (E, S, bm) in ((7, 1, 16), (128, 8, 64), (1000, 3, 16), (1024, 4, 32),
+                                   (4095, 2, 48))]
 
 
 @pytest.mark.parametrize("M,k,E,S,bm", ALIGN_BOUNDS)
